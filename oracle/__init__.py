@@ -1,0 +1,8 @@
+"""Float64 CPU oracle for the Gated Delta Rule-2 token mixer.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the benchmark's
+CPU-baseline leg, never by the library. It shares no code with the HIP path.
+"""
+from .gdn2_oracle import gdn2_decode_steps, gdn2_forward, gdn2_step
+
+__all__ = ["gdn2_step", "gdn2_forward", "gdn2_decode_steps"]
