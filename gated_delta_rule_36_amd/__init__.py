@@ -1,0 +1,11 @@
+"""Gated Delta Rule-2 token mixer for MI355X (gfx950): HIP kernels behind a C ABI.
+
+    from gated_delta_rule_36_amd import chunk_fwd, decode_step
+
+`chunk_fwd` runs the chunkwise-parallel forward over whole (optionally packed)
+sequences; `decode_step` advances a pool of recurrent states by one token. Both call
+libgdn2.so, built in-tree by `python -m gated_delta_rule_36_amd.build`.
+"""
+from ._lib import Gdn2Error, chunk_fwd, decode_step, lib, lib_path
+
+__all__ = ["chunk_fwd", "decode_step", "lib", "lib_path", "Gdn2Error"]

@@ -1,0 +1,150 @@
+"""ctypes binding of libgdn2.so (the C ABI declared in include/gdn2.h).
+
+Argument marshalling only: shapes and dtypes are checked, outputs are allocated with
+torch on the inputs' device, and the call is issued on torch's current HIP stream.
+Every step of the computation runs in the library's HIP kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn2.so")
+_lib = None
+
+GDN2_BF16 = 0
+GDN2_F32 = 1
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 4: "launch failed"}
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+
+
+class Gdn2Error(RuntimeError):
+    """A nonzero status returned by the library."""
+
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed with status {status} ({lib().gdn2_status_string(status).decode()})")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libgdn2.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it first "
+                               "(python -m gated_delta_rule_36_amd.build)")
+        L = ctypes.CDLL(_LIB_PATH)
+        L.gdn2_chunk_fwd.argtypes = [_P] * 10 + [_I] * 7 + [_P]
+        L.gdn2_chunk_fwd.restype = _I
+        L.gdn2_chunk_fwd_sliced.argtypes = [_P] * 10 + [_I] * 8 + [_P]
+        L.gdn2_chunk_fwd_sliced.restype = _I
+        L.gdn2_decode_step.argtypes = [_P] * 8 + [_I] * 5 + [_P]
+        L.gdn2_decode_step.restype = _I
+        L.gdn2_status_string.argtypes = [_I]
+        L.gdn2_status_string.restype = ctypes.c_char_p
+        L.gdn2_version.argtypes = []
+        L.gdn2_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(dt):
+    if dt == torch.bfloat16:
+        return GDN2_BF16
+    if dt == torch.float32:
+        return GDN2_F32
+    raise TypeError(f"unsupported dtype {dt}; use bfloat16 or float32")
+
+
+def _check(name, t, shape, dtype, device):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def chunk_fwd(q, k, v, g, b, w, initial_state=None, cu_seqlens=None,
+              output_final_state=True, value_slice=0):
+    """Gated Delta Rule-2 chunkwise forward.
+
+    q, k, g, b: [B, T, H, d_k]; v, w: [B, T, H, d_v] (bf16 or fp32, same dtype, on a HIP
+    device); g = log(alpha) <= 0. initial_state: [N, H, d_k, d_v] fp32 or None.
+    cu_seqlens: int32 [N+1] on the device (packed batch, B == 1) or None (N = B).
+    Returns (o [B, T, H, d_v] in the input dtype, final_state [N, H, d_k, d_v] fp32 or None).
+    """
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, d_k]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(dt)
+    for name, t, d in (("q", q, dk), ("k", k, dk), ("g", g, dk), ("b", b, dk),
+                       ("v", v, dv), ("w", w, dv)):
+        _check(name, t, (B, T, H, d), dt, dev)
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != dev or cu_seqlens.dim() != 1:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor on the inputs' device")
+        if B != 1:
+            raise ValueError("packed (cu_seqlens) inputs must have B == 1")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if initial_state is not None:
+        _check("initial_state", initial_state, (N, H, dk, dv), torch.float32, dev)
+    o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    sN = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if output_final_state else None
+    L = lib()
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), _ptr(initial_state), _ptr(o),
+            _ptr(sN), _ptr(cu_seqlens), B, T, H, dk, dv, N, code]
+    if value_slice:
+        st = L.gdn2_chunk_fwd_sliced(*args, int(value_slice), _stream(dev))
+        fn = "gdn2_chunk_fwd_sliced"
+    else:
+        st = L.gdn2_chunk_fwd(*args, _stream(dev))
+        fn = "gdn2_chunk_fwd"
+    if st != 0:
+        raise Gdn2Error(fn, st)
+    return o, sN
+
+
+def decode_step(q, k, v, g, b, w, state):
+    """One recurrent decode step; `state` [N, H, d_k, d_v] fp32 is updated in place.
+
+    q, k, g, b: [N, H, d_k]; v, w: [N, H, d_v]. Returns o [N, H, d_v] (input dtype).
+    """
+    if q.dim() != 3:
+        raise ValueError("q must be [N, H, d_k]")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(dt)
+    for name, t, d in (("q", q, dk), ("k", k, dk), ("g", g, dk), ("b", b, dk),
+                       ("v", v, dv), ("w", w, dv)):
+        _check(name, t, (N, H, d), dt, dev)
+    _check("state", state, (N, H, dk, dv), torch.float32, dev)
+    o = torch.empty((N, H, dv), dtype=dt, device=dev)
+    st = lib().gdn2_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w),
+                                _ptr(state), _ptr(o), N, H, dk, dv, code, _stream(dev))
+    if st != 0:
+        raise Gdn2Error("gdn2_decode_step", st)
+    return o

@@ -1,0 +1,125 @@
+// C ABI of the GDN-2 library: argument validation, tile selection, launch.
+// Declarations and the contract of every entry point are in include/gdn2.h.
+#include "../../include/gdn2.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+
+#include "gdn2_launch.h"
+
+namespace {
+
+constexpr int kChunk = 64;
+constexpr int kTargetWorkgroups = 256;  // one per compute unit of an MI355X
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool width_ok(int d) { return d == 64 || d == 128; }
+
+// Widest value slice that still yields about one workgroup per compute unit; wider
+// slices recompute less key-side work per token, narrower ones expose more chains.
+int pick_nv(int dtype, int d_k, int d_v, long chains) {
+  const int cands[4] = {128, 64, 32, 16};
+  int best = 0;
+  for (int nv : cands) {
+    if (!gdn2::chunk_nv_supported(dtype, d_k, d_v, nv)) continue;
+    best = nv;  // narrowest supported so far
+    if (chains * (d_v / nv) >= kTargetWorkgroups) return nv;
+  }
+  return best;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? GDN2_OK : GDN2_LAUNCH_FAILED; }
+
+int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* log_alpha,
+                   const void* b, const void* w, const float* initial_state, void* o,
+                   float* final_state, const int32_t* cu_seqlens, int B, int T, int H, int d_k,
+                   int d_v, int N, int dtype, void* hip_stream, int nv) {
+  if (dtype != GDN2_BF16 && dtype != GDN2_F32) return GDN2_INVALID_ARGUMENT;
+  if (B < 0 || T < 0 || H <= 0 || N < 0 || d_k <= 0 || d_v <= 0) return GDN2_INVALID_ARGUMENT;
+  if (cu_seqlens == nullptr) {
+    if (N != B) return GDN2_INVALID_ARGUMENT;
+  } else {
+    if (B != 1) return GDN2_INVALID_ARGUMENT;
+  }
+  if (!width_ok(d_k) || !width_ok(d_v)) return GDN2_UNSUPPORTED;
+  if (dtype == GDN2_F32 && d_k != 64) return GDN2_UNSUPPORTED;
+  const long tokens = (long)B * T;
+  if (tokens > 0 && (!q || !k || !v || !log_alpha || !b || !w || !o))
+    return GDN2_INVALID_ARGUMENT;
+  const void* ptrs[9] = {q, k, v, log_alpha, b, w, o, initial_state, final_state};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return GDN2_INVALID_ARGUMENT;
+  if (cu_seqlens && ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0))
+    return GDN2_INVALID_ARGUMENT;
+  // 64-bit element offsets are used in the kernels; the grid must fit one dimension.
+  if (tokens > (long)INT_MAX) return GDN2_INVALID_ARGUMENT;
+  if (N == 0) return GDN2_OK;
+  if (nv == 0) nv = pick_nv(dtype, d_k, d_v, (long)N * H);
+  if (!gdn2::chunk_nv_supported(dtype, d_k, d_v, nv)) return GDN2_UNSUPPORTED;
+  const long grid = (long)N * H * (d_v / nv);
+  if (grid > (long)INT_MAX) return GDN2_INVALID_ARGUMENT;
+
+  gdn2::ChunkArgs a;
+  a.q = q; a.k = k; a.v = v; a.g = log_alpha; a.b = b; a.w = w;
+  a.s0 = initial_state; a.o = o; a.sN = final_state; a.cu_seqlens = cu_seqlens;
+  a.B = B; a.T = T; a.H = H; a.d_k = d_k; a.d_v = d_v; a.N = N;
+  a.dtype = dtype; a.nv = nv; a.stream = hip_stream;
+  return status_of(gdn2::launch_chunk_fwd(a));
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn2_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                   const void* b, const void* w, const float* initial_state, void* o,
+                   float* final_state, const int32_t* cu_seqlens, int B, int T, int H,
+                   int d_k, int d_v, int N, int dtype, void* hip_stream) {
+  return chunk_fwd_impl(q, k, v, log_alpha, b, w, initial_state, o, final_state, cu_seqlens,
+                        B, T, H, d_k, d_v, N, dtype, hip_stream, 0);
+}
+
+int gdn2_chunk_fwd_sliced(const void* q, const void* k, const void* v, const void* log_alpha,
+                          const void* b, const void* w, const float* initial_state, void* o,
+                          float* final_state, const int32_t* cu_seqlens, int B, int T, int H,
+                          int d_k, int d_v, int N, int dtype, int value_slice,
+                          void* hip_stream) {
+  if (value_slice < 0) return GDN2_INVALID_ARGUMENT;
+  return chunk_fwd_impl(q, k, v, log_alpha, b, w, initial_state, o, final_state, cu_seqlens,
+                        B, T, H, d_k, d_v, N, dtype, hip_stream, value_slice);
+}
+
+int gdn2_decode_step(const void* q, const void* k, const void* v, const void* log_alpha,
+                     const void* b, const void* w, float* state, void* o, int N, int H,
+                     int d_k, int d_v, int dtype, void* hip_stream) {
+  if (dtype != GDN2_BF16 && dtype != GDN2_F32) return GDN2_INVALID_ARGUMENT;
+  if (N < 0 || H <= 0 || d_k <= 0 || d_v <= 0) return GDN2_INVALID_ARGUMENT;
+  if (!width_ok(d_k) || !width_ok(d_v)) return GDN2_UNSUPPORTED;
+  if (N == 0) return GDN2_OK;
+  if (!q || !k || !v || !log_alpha || !b || !w || !state || !o) return GDN2_INVALID_ARGUMENT;
+  const void* ptrs[8] = {q, k, v, log_alpha, b, w, state, o};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return GDN2_INVALID_ARGUMENT;
+  if ((long)N * H > (long)INT_MAX) return GDN2_INVALID_ARGUMENT;
+  gdn2::DecodeArgs a;
+  a.q = q; a.k = k; a.v = v; a.g = log_alpha; a.b = b; a.w = w;
+  a.state = state; a.o = o; a.N = N; a.H = H; a.d_k = d_k; a.d_v = d_v;
+  a.dtype = dtype; a.stream = hip_stream;
+  return status_of(gdn2::launch_decode_step(a));
+}
+
+const char* gdn2_status_string(int status) {
+  switch (status) {
+    case GDN2_OK: return "ok";
+    case GDN2_INVALID_ARGUMENT: return "invalid argument";
+    case GDN2_UNSUPPORTED: return "unsupported head width, dtype or value slice";
+    case GDN2_LAUNCH_FAILED: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* gdn2_version(void) { return "gdn2-mi355x 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+// Single-token recurrent decode step of Gated Delta Rule-2 on gfx950.
+//
+// Per (sequence, head) the step is the token recurrence of the GDN-2 reading note's §3
+// forward-pass paragraph (erase along k, see the C header):
+//   S_bar = Diag(alpha) S,  r = S_bar^T e,  S' = S_bar + k (z - r)^T,  o = S'^T q.
+// The readout is formed from the old state in the same pass as r:
+//   o = S_bar^T q + (q . k)(z - r)
+// so the 64 KB fp32 state is streamed from HBM once and written back once; everything
+// else (six d-vectors of inputs, one d_v output) is negligible traffic. The kernel is
+// bandwidth-bound: one workgroup of 256 threads per (sequence, head), the state slice is
+// held in registers between the read and the write, float4 accesses make every wave
+// touch whole contiguous rows.
+
+#include "gdn2_device.h"
+#include "gdn2_launch.h"
+
+namespace gdn2 {
+
+template <typename T, int DK, int DV>
+__global__ void __launch_bounds__(256)
+gdn2_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                   const T* __restrict__ g, const T* __restrict__ bg, const T* __restrict__ wg,
+                   float* __restrict__ state, T* __restrict__ o) {
+  constexpr int NT = 256;
+  constexpr int CG = DV / 4;        // float4 column groups per row
+  constexpr int RG = NT / CG;       // row groups
+  constexpr int RPT = DK / RG;      // rows per thread
+  __shared__ float s_alpha[DK], s_e[DK], s_q[DK], s_k[DK], s_z[DV];
+  __shared__ __attribute__((aligned(16))) float s_red[2][RG][DV];
+  __shared__ float s_qk;
+
+  const int tid = threadIdx.x;
+  const long unit = blockIdx.x;  // sequence * H + head
+  const int cg = tid % CG, rg = tid / CG;
+  float* S = state + unit * DK * DV;
+
+  // issue the state loads first: they are the whole cost of the step
+  f4 s[RPT];
+#pragma unroll
+  for (int j = 0; j < RPT; ++j)
+    s[j] = *reinterpret_cast<const f4*>(S + (long)(rg + j * RG) * DV + 4 * cg);
+
+  for (int c = tid; c < DK; c += NT) {
+    const float kk = to_f(k[unit * DK + c]);
+    s_alpha[c] = __expf(to_f(g[unit * DK + c]));
+    s_e[c] = to_f(bg[unit * DK + c]) * kk;
+    s_q[c] = to_f(q[unit * DK + c]);
+    s_k[c] = kk;
+  }
+  for (int c = tid; c < DV; c += NT) s_z[c] = to_f(wg[unit * DV + c]) * to_f(v[unit * DV + c]);
+  __syncthreads();
+
+  if (tid < 64) {  // q . k by wave 0
+    float p = 0.f;
+    for (int c = tid; c < DK; c += 64) p += s_q[c] * s_k[c];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off, 64);
+    if (tid == 0) s_qk = p;
+  }
+
+  f4 r = {0.f, 0.f, 0.f, 0.f}, sq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int c = rg + j * RG;
+    s[j] = s[j] * s_alpha[c];  // S_bar
+    r += s_e[c] * s[j];
+    sq += s_q[c] * s[j];
+  }
+  *reinterpret_cast<f4*>(&s_red[0][rg][4 * cg]) = r;
+  *reinterpret_cast<f4*>(&s_red[1][rg][4 * cg]) = sq;
+  __syncthreads();
+
+  r = f4{0.f, 0.f, 0.f, 0.f};
+  sq = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int x = 0; x < RG; ++x) {
+    r += *reinterpret_cast<const f4*>(&s_red[0][x][4 * cg]);
+    sq += *reinterpret_cast<const f4*>(&s_red[1][x][4 * cg]);
+  }
+  const f4 z = *reinterpret_cast<const f4*>(&s_z[4 * cg]);
+  const f4 d = z - r;  // what k writes: z minus the erased read
+  if (rg == 0) {
+    const f4 out = sq + s_qk * d;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[unit * DV + 4 * cg + i] = from_f<T>(out[i]);
+  }
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int c = rg + j * RG;
+    *reinterpret_cast<f4*>(S + (long)c * DV + 4 * cg) = s[j] + s_k[c] * d;
+  }
+}
+
+template <typename T, int DK, int DV>
+static hipError_t launch_dec(const DecodeArgs& a) {
+  hipLaunchKernelGGL((gdn2_decode_kernel<T, DK, DV>), dim3((unsigned)((long)a.N * a.H)), dim3(256),
+                     0, (hipStream_t)a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
+                     (const T*)a.g, (const T*)a.b, (const T*)a.w, a.state, (T*)a.o);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t dispatch_dec(const DecodeArgs& a) {
+  if (a.d_k == 64 && a.d_v == 64) return launch_dec<T, 64, 64>(a);
+  if (a.d_k == 64 && a.d_v == 128) return launch_dec<T, 64, 128>(a);
+  if (a.d_k == 128 && a.d_v == 64) return launch_dec<T, 128, 64>(a);
+  if (a.d_k == 128 && a.d_v == 128) return launch_dec<T, 128, 128>(a);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_step(const DecodeArgs& a) {
+  return a.dtype == 0 ? dispatch_dec<bf16>(a) : dispatch_dec<float>(a);
+}
+
+}  // namespace gdn2

@@ -1,0 +1,121 @@
+/*
+ * gdn2.h -- C ABI of the MI355X (gfx950) Gated Delta Rule-2 token mixer.
+ *
+ * The operation. For every sequence n and head h, with state S (d_k x d_v, fp32) and for
+ * each token t in order:
+ *     alpha = exp(g_t)              per key channel, g_t = log(alpha_t) <= 0
+ *     S_bar = Diag(alpha) S         decay along the key axis
+ *     e = b_t * k_t,  z = w_t * v_t gated key (erase gate b, key side) and
+ *                                   gated value (write gate w, value side)
+ *     r = S_bar^T e                 old read with the gated key
+ *     S = S_bar + k_t (z - r)^T     erase that read along k_t, write z along k_t
+ *     o_t = S^T q_t                 readout from the updated state
+ * This is the Gated Delta Rule-2 of "Gated DeltaNet-2: Decoupling Erase and Write in
+ * Linear Attention" (reading note, §2 fast-weight objective and §3 forward pass; the
+ * erase runs along k_t, as the objective's minimiser and the (I - k_t e_t^T) factor of
+ * §3's backward paragraph fix). No query scale is applied: scale q beforehand if wanted.
+ *
+ * Conventions common to every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library never
+ *     allocates, frees, synchronises, or keeps state between calls. Calls are
+ *     asynchronous on `hip_stream` (a hipStream_t; NULL = the null stream).
+ *   - Tensors are dense, row-major, contiguous, and 16-byte aligned.
+ *   - `dtype` selects the element type of q, k, v, log_alpha, b, w and o:
+ *     GDN2_BF16 (bfloat16) or GDN2_F32 (float). States are always fp32.
+ *   - Arguments are validated on the host before any launch; on error nothing is
+ *     launched and an error status is returned. Gate VALUES are not checked: b and w
+ *     outside [0, 1] are computed as given.
+ *   - Device faults surface at the caller's next synchronisation.
+ *   - Numeric range of the chunked forward: the per-channel decay accumulated over any
+ *     aligned 16-token block of a chunk must stay above -80 (log space), i.e. alpha
+ *     averaged over 16 tokens >= exp(-5). The decode step has no such limit.
+ */
+#ifndef GDN2_H_
+#define GDN2_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GDN2_BF16 = 0, GDN2_F32 = 1 } gdn2_dtype;
+
+enum {
+  GDN2_OK = 0,
+  GDN2_INVALID_ARGUMENT = 1, /* null required pointer, bad sizes, misaligned pointer */
+  GDN2_UNSUPPORTED = 2,      /* head widths / dtype combination not built */
+  GDN2_LAUNCH_FAILED = 4     /* the HIP runtime rejected a launch */
+};
+
+/*
+ * Chunkwise-parallel forward over whole sequences (the chunk form of the reading note's
+ * §3 chunkwise-training paragraph: a per-channel cumulative decay normalises the state
+ * inside a 64-token chunk, the chunk becomes an asymmetric delta recurrence, and the UT
+ * transform of the Gated DeltaNet visual reading turns it into triangular-inverse and
+ * matrix products). Result equals the token recurrence above up to rounding.
+ *
+ *   q, k, log_alpha, b : [B, T, H, d_k]   (dtype)
+ *   v, w               : [B, T, H, d_v]   (dtype)
+ *   initial_state      : [N, H, d_k, d_v] fp32, or NULL for a zero state
+ *   o                  : [B, T, H, d_v]   (dtype), written
+ *   final_state        : [N, H, d_k, d_v] fp32, or NULL (not written); may alias
+ *                        initial_state (each state is read before it is overwritten)
+ *   cu_seqlens         : NULL, or device int32 [N+1] offsets into the token axis of a
+ *                        packed batch (then B must be 1 and T is the packed length).
+ *                        Offsets must be non-decreasing with cu_seqlens[0] = 0 and
+ *                        cu_seqlens[N] = T; the kernel clamps them into [0, T] so a bad
+ *                        table cannot make it access memory out of bounds.
+ *   Without cu_seqlens, N must equal B and every sequence has length T.
+ *   Supported: GDN2_BF16 with d_k, d_v in {64, 128}; GDN2_F32 with d_k = 64 and
+ *   d_v in {64, 128}. T = 0 or N = 0 is a no-op (apart from final_state = initial).
+ * Returns GDN2_OK or an error status.
+ */
+int gdn2_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                   const void* b, const void* w, const float* initial_state, void* o,
+                   float* final_state, const int32_t* cu_seqlens, int B, int T, int H,
+                   int d_k, int d_v, int N, int dtype, void* hip_stream);
+
+/*
+ * gdn2_chunk_fwd with an explicit value-slice width: each workgroup carries
+ * `value_slice` columns of the state (16, 32, 64 or 128; a divisor of d_v; 16 only with
+ * d_k = 64; at most 64 for GDN2_F32). 0 selects the width automatically, exactly as
+ * gdn2_chunk_fwd does. Results do not depend on the width beyond rounding. Returns
+ * GDN2_UNSUPPORTED for a width that is not built.
+ */
+int gdn2_chunk_fwd_sliced(const void* q, const void* k, const void* v, const void* log_alpha,
+                          const void* b, const void* w, const float* initial_state, void* o,
+                          float* final_state, const int32_t* cu_seqlens, int B, int T, int H,
+                          int d_k, int d_v, int N, int dtype, int value_slice,
+                          void* hip_stream);
+
+/*
+ * One recurrent decode step for N independent sequences (the per-token procedure of
+ * the reading note's §3 forward-pass paragraph; constant memory per token, the
+ * abstract's decode property). The state is read once and written once in place; the
+ * readout is formed from the old state as o = Diag(alpha)-decayed read of q plus
+ * (q . k)(z - r), which equals S_t^T q_t.
+ *
+ *   q, k, log_alpha, b : [N, H, d_k]       (dtype), one token per sequence
+ *   v, w               : [N, H, d_v]       (dtype)
+ *   state              : [N, H, d_k, d_v]  fp32, read-modify-written in place
+ *   o                  : [N, H, d_v]       (dtype), written
+ *   Supported: d_k, d_v in {64, 128}, both dtypes. N = 0 is a no-op.
+ * Returns GDN2_OK or an error status.
+ */
+int gdn2_decode_step(const void* q, const void* k, const void* v, const void* log_alpha,
+                     const void* b, const void* w, float* state, void* o, int N, int H,
+                     int d_k, int d_v, int dtype, void* hip_stream);
+
+/* Human-readable text for a status code (static storage; never NULL). */
+const char* gdn2_status_string(int status);
+
+/* Library version string (static storage). */
+const char* gdn2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN2_H_ */

@@ -1,0 +1,94 @@
+"""Host-only checks of the C ABI: the library loads, exports every declared entry point,
+and rejects bad arguments before touching the GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_36_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn2.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.lib_path()),
+                                reason="libgdn2.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn2_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = _lib.lib()
+    names = declared_functions()
+    assert "gdn2_chunk_fwd" in names and "gdn2_decode_step" in names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    L = _lib.lib()
+    assert b"gfx950" in L.gdn2_version()
+    for s in (0, 1, 2, 4, 99):
+        assert L.gdn2_status_string(s)
+
+
+FAKE = ctypes.c_void_p(0x100000)  # 16-byte aligned, never dereferenced on error paths
+MIS = ctypes.c_void_p(0x100004)
+
+
+def _chunk(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, w=FAKE, s0=None, o=FAKE, sN=None, cu=None,
+             B=2, T=64, H=4, dk=128, dv=128, N=2, dtype=0)
+    a.update(kw)
+    return _lib.lib().gdn2_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["b"], a["w"], a["s0"],
+                                     a["o"], a["sN"], a["cu"], a["B"], a["T"], a["H"],
+                                     a["dk"], a["dv"], a["N"], a["dtype"], None)
+
+
+def test_chunk_fwd_error_paths():
+    assert _chunk(dtype=7) == 1
+    assert _chunk(N=3) == 1                 # N must equal B without cu_seqlens
+    assert _chunk(H=0) == 1
+    assert _chunk(T=-1) == 1
+    assert _chunk(dk=96) == 2
+    assert _chunk(dv=256) == 2
+    assert _chunk(dtype=1, dk=128) == 2     # fp32 path is built for d_k = 64
+    assert _chunk(q=None) == 1
+    assert _chunk(o=None) == 1
+    assert _chunk(k=MIS) == 1               # misaligned
+    assert _chunk(cu=FAKE, B=2) == 1        # packed batches have B == 1
+    assert _chunk(B=0, N=0, q=None, k=None, v=None, g=None, b=None, w=None, o=None) == 0
+
+
+def test_chunk_fwd_sliced_error_paths():
+    L = _lib.lib()
+
+    def call(nv, dk=128, dv=128, dtype=0):
+        return L.gdn2_chunk_fwd_sliced(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None,
+                                       1, 64, 2, dk, dv, 1, dtype, nv, None)
+    assert call(-1) == 1
+    assert call(48) == 2
+    assert call(16) == 2                    # 16-wide slices need d_k = 64
+    assert call(256) == 2
+    assert call(128, dk=64, dv=64) == 2     # wider than d_v
+    assert call(128, dk=64, dv=128, dtype=1) == 2
+
+
+def test_decode_error_paths():
+    L = _lib.lib()
+
+    def call(**kw):
+        a = dict(q=FAKE, state=FAKE, N=4, H=2, dk=128, dv=128, dtype=0)
+        a.update(kw)
+        return L.gdn2_decode_step(a["q"], FAKE, FAKE, FAKE, FAKE, FAKE, a["state"], FAKE,
+                                  a["N"], a["H"], a["dk"], a["dv"], a["dtype"], None)
+    assert call(dtype=2) == 1
+    assert call(N=-1) == 1
+    assert call(dk=32) == 2
+    assert call(q=None) == 1
+    assert call(state=MIS) == 1
+    assert call(N=0, q=None, state=None) == 0
