@@ -1,0 +1,177 @@
+"""Benchmark: GDN-2 chunkwise forward tokens/s on one MI355X, with roofline fractions.
+
+A step is one gdn2_chunk_fwd call over the 1.3B-layer workload (B=8, H=16, T=2048,
+d_k = d_v = 128, bf16 inputs, fp32 state, zero initial state), inputs resident in HBM.
+Prints ONE JSON line. Also reports (as extra fields) the recurrent decode step on the
+decode workload (256 sequences x 16 heads, fp32 128x128 states) and a CPU baseline: the
+float64 oracle timed on a bounded sample of the forward workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GDN-2 chunk-fwd tokens/s (H=16,d=128,bf16) + % MFMA/HBM roofline, 1 GPU"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+NAMES = ("q", "k", "v", "g", "b", "w")
+
+
+def fwd_bytes(B, T, H, dk, dv, N, elt=2, read_s0=False):
+    """Algorithmic HBM bytes of one forward call: read q,k,g,b,v,w once, write o once,
+    write the fp32 final state (and read the initial one if given)."""
+    tok = B * T * H
+    b = tok * (4 * dk + 2 * dv) * elt + tok * dv * elt + N * H * dk * dv * 4
+    if read_s0:
+        b += N * H * dk * dv * 4
+    return b
+
+
+def fwd_flops(B, T, H, dk, dv, C=64):
+    """Useful dense flops of the chunk form per call (triangular halves counted once):
+    A, P, W (d_k wide) and U~, P U (d_v wide) over the causal C x C half; W S, Q S, K^T U
+    (d_k x d_v per token); the UT transform ~C^2/3 per token."""
+    tok = B * T * H
+    tri = (C + 1) / 2.0  # average causal row length
+    per_tok = 2 * tri * dk * 3 + 2 * tri * dv * 2 + 2 * dk * dv * 3 + C * C / 3.0
+    return tok * per_tok
+
+
+def decode_bytes(N, H, dk, dv, elt=2):
+    return N * H * (2 * dk * dv * 4 + (4 * dk + 2 * dv) * elt + dv * elt)
+
+
+def cpu_baseline(x, tokens=1024):
+    """The float64 oracle (gdn2_forward, one process) on a bounded sample of the forward
+    workload: the first `tokens` tokens of every sequence, all heads."""
+    from oracle import gdn2_forward
+    B, T, H, dk = x["q"].shape
+    Ts = min(tokens, T)
+    sample = [x[n][:, :Ts] for n in NAMES]
+    t0 = time.perf_counter()
+    gdn2_forward(*sample)
+    dt = time.perf_counter() - t0
+    return {"value": round(B * Ts / dt, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {Ts} of {T} tokens of all {B} sequences x {H} heads "
+                      f"(float64 token loop, {dt:.1f} s, one process)",
+            "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--value-slice", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU (got --gpus {args.gpus}); the "
+              "chunk forward shards by sequence/head/value-column with no exchange, but "
+              "multi-GPU runs are not part of it.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_36_amd as G
+    from gdn2_inputs import CONFIGS, make_config_inputs, make_decode_inputs
+
+    dev = torch.device("cuda:0")
+    c = CONFIGS["layer1p3b_bf16"]
+    B, T, H, dk, dv = c["B"], c["T"], c["H"], c["dk"], c["dv"]
+    x = make_config_inputs("layer1p3b_bf16")
+    t = {n: torch.from_numpy(x[n]).to(dev).to(torch.bfloat16) for n in NAMES}
+    torch.cuda.synchronize()
+
+    def step():
+        return G.chunk_fwd(*(t[n] for n in NAMES), value_slice=args.value_slice)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        step()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms_per_step = wall * 1e3 / K
+    tokens = B * T
+    value = tokens * K / wall
+    nbytes = fwd_bytes(B, T, H, dk, dv, B)
+    flops = fwd_flops(B, T, H, dk, dv)
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), "
+                "log-alpha=-0.1*softplus(N(0,1)), b,w=sigmoid(N(0,1)))",
+        "config": {"workload": "GDN-2 chunk forward, 1.3B-layer shape: B=8 H=16 T=2048 "
+                               "d_k=d_v=128 C=64, bf16 in/out, fp32 state, zero S0",
+                   "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "gdn2_chunk_kernel<bf16,128,NV>",
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "kernel_ms": round(kern_ms, 4)},
+        "mfma": {"useful_flops_per_launch": round(flops),
+                 "achieved_tflops": round(flops / (kern_ms * 1e-3) / 1e12, 2),
+                 "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                 "frac": round(flops / (kern_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+    }
+
+    if not args.no_decode:
+        cd = CONFIGS["decode_bf16"]
+        N, Hd, dkd, dvd = cd["N"], cd["H"], cd["dk"], cd["dv"]
+        pool = 8
+        d = make_decode_inputs(N, Hd, dkd, dvd, pool, "bf16", seed=cd["seed"], s0_std=0.02)
+        td = {n: torch.from_numpy(d[n]).to(dev).to(torch.bfloat16) for n in NAMES}
+        states = [torch.from_numpy(d["s0"]).to(dev), torch.from_numpy(d["s0"]).to(dev)]
+        res = {}
+        for mode in ("one_pool", "two_pools"):
+            st = states[0]
+            for s in range(5):
+                G.decode_step(*(td[n][s % pool] for n in NAMES), st)
+            torch.cuda.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(cd["steps"])]
+            for s in range(cd["steps"]):
+                st = states[s & 1] if mode == "two_pools" else states[0]
+                evs[s][0].record()
+                G.decode_step(*(td[n][s % pool] for n in NAMES), st)
+                evs[s][1].record()
+            torch.cuda.synchronize()
+            us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+            gbs = decode_bytes(N, Hd, dkd, dvd) / (us * 1e-6) / 1e9
+            res[mode] = {"us_per_step": round(us, 2), "achieved_GBs": round(gbs, 1),
+                         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        out["decode"] = {"workload": f"decode step: N={N} sequences x H={Hd}, d_k=d_v={dkd}, "
+                                     f"fp32 state in place, {cd['steps']} consecutive steps",
+                         "bytes_per_step": decode_bytes(N, Hd, dkd, dvd), **res}
+
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(x)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -2,10 +2,10 @@
 //
 // One workgroup owns one (sequence, head, value-slice of NV columns) and walks that
 // sequence's 64-token chunks in order, keeping its d_k x NV slice of the fp32 state in
-// MFMA accumulator registers. The value columns of the state evolve independently (the
-// decay, the read r = S_bar^T e and the erase all act along the key axis), so slicing
-// d_v multiplies the number of independent chains; the key-side work of a chunk is
-// recomputed per slice.
+// MFMA accumulator registers (wave w owns columns [16w, 16w+16)). The value columns of
+// the state evolve independently (decay, read r = S_bar^T e and erase all act along the
+// key axis), so slicing d_v multiplies the number of independent chains; the key-side
+// work of a chunk is recomputed per slice.
 //
 // Per chunk (local tokens r, i in [0, 64), G = cumsum of log-decay, E = b*K, Z = w*V),
 // the chunk form of the GDN-2 reading note (§3, chunkwise-training paragraph: the
@@ -14,21 +14,28 @@
 // section):
 //   A = strict_lower( sum_c E[r,c] K[i,c] exp(G[r,c]-G[i,c]) )     (b*k) Gamma k^T
 //   P = lower_incl ( sum_c Q[r,c] K[i,c] exp(G[r,c]-G[i,c]) )
-//   T = (I + A)^{-1}
-//   W = T (E * exp(G)),  U~ = T Z
+//   [W | U~] = (I + A)^{-1} [E exp(G) | Z]      (UT transform, block forward substitution)
 //   U = U~ - W S
-//   O = (Q * exp(G)) S + P U
-//   S = Diag(exp(G_last)) S + (K * exp(G_last - G))^T U
+//   O = (Q exp(G)) S + P U
+//   S = Diag(exp(G_last)) S + (K exp(G_last - G))^T U
 //
-// Range safety. exp(G[r]-G[i]) is never formed as exp(G[r]) * exp(-G[i]) over a whole
-// chunk (that overflows fp32 once the chunk decays by more than ~88 nats). The chunk is
-// split into four 16-token blocks; every factor is referenced to a block boundary:
-//   a_r = G_r - Gs(R)      (Gs(R): cumulative decay at the start of r's block R)
-//   Ea = E exp(a), Qa = Q exp(a)  (<= |E|, |Q|)     Kn = K exp(-a)  (grows within a block)
+// Stages per chunk (barriers order LDS only; the next chunk's inputs are prefetched into
+// registers and stay in flight across them):
+//   (a) per-thread cumsum of log2-decay, (b) per-channel scan and decay factors,
+//   (c) gated / decayed operands into LDS, (d) A and P on MFMA,
+//   (e) 16x16 diagonal blocks of (I + A)^{-1} by forward substitution,
+//   (f) block forward substitution of [E exp(G) | Z] on K=16 MFMA (no barrier inside),
+//   (g) state-dependent part: U, O, state update, on this wave's 16 state columns.
+//
+// Range safety. exp(G[r]-G[i]) is formed as exp(G[r]) * exp(-G[i]) with G relative to
+// the chunk start when the chunk's total decay is below ~83 nats in every channel (the
+// usual case; both factors then fit fp32 / bf16). Otherwise the chunk takes a slower path
+// that references every factor to a 16-token block boundary:
+//   a_r = G_r - Gs(R)   (Gs(R): cumulative decay at the start of r's block R)
+//   Ea = E exp(a), Qa = Q exp(a)  (<= |E|, |Q|)     Kn = K exp(-a)  (grows inside a block)
 //   diagonal blocks:      Ea_R . Kn_R
 //   off-diagonal (R > I): Ea_R * exp(Gs(R) - Ge(I)) . Kn_I * exp(Ge(I) - Gs(I))
-// so every factor is <= 1 except exp(-a) inside one block, which is bounded by that
-// block's own decay (the API requires > -80 nats per 16 tokens).
+// so no factor exceeds one block's own decay (the API requires > -80 nats per 16 tokens).
 // All logs are kept in base 2 (g is scaled by log2(e) on load) so exp is one v_exp_f32.
 
 #include "gdn2_device.h"
@@ -39,7 +46,13 @@ namespace gdn2 {
 template <typename T, int DK, int NV>
 struct ChunkShape {
   static constexpr int C = 64;            // chunk length
-  static constexpr int NW = NV / 16;      // waves; wave w owns state columns [16w, 16w+16)
+  static constexpr int NWC = NV / 16;     // 16-wide state column tiles
+  // Row split: with bf16 and d_k = 128, two waves share each column tile, one per half of
+  // the key rows (two waves per SIMD for latency hiding); partial sums over the key rows
+  // are exchanged through LDS.
+  static constexpr int RS = (sizeof(T) == 2 && DK == 128 && NV <= 64) ? 2 : 1;
+  static constexpr int NW = NWC * RS;     // waves: wave w owns column tile w % NWC and
+                                          // key rows [(w / NWC) * DK / RS, ... + DK / RS)
   static constexpr int NT = 64 * NW;      // threads
   static constexpr int CG = DK / 8;       // key-side prep: 8 channels per thread
   static constexpr int TG = NT / CG;      // token groups
@@ -51,43 +64,54 @@ struct ChunkShape {
   static constexpr int PAD = 16 / (int)sizeof(T);  // 16-byte row padding (LDS banks)
   static constexpr int LDK = DK + PAD;    // pitch of [64][DK] arrays
   static constexpr int LDT = C + PAD;     // pitch of [x][64] arrays
-  static constexpr int LDA = C + 4;       // pitch of the fp32 A matrix
   static constexpr int KS = Mma<T>::KS;
   static constexpr int KPL = Mma<T>::KPL;
+  static constexpr int NCT = DK / 16;     // 16-wide key-channel tiles
 
-  // factor rows (fp32, [NF][DK])
-  static constexpr int F_ES = 0;   // exp(Gs(R))            R = 0..3
-  static constexpr int F_KB = 4;   // exp(Ge(R) - Gs(R))    R = 0..3
-  static constexpr int F_KN = 8;   // exp(Glast - Ge(R))    R = 0..3
-  static constexpr int F_GAM = 12; // exp(Glast)
-  static constexpr int F_OFF = 13; // exp(Gs(R) - Ge(I)) for (2,0), (3,0), (3,1)
-  static constexpr int NF = 16;
+  // factor rows (fp32, [NF][DK]); log2 units for G
+  static constexpr int F_ES = 0;    // exp(Gs(R))            R = 0..3   (block path)
+  static constexpr int F_KB = 4;    // exp(Ge(R) - Gs(R))    R = 0..3   (block path)
+  static constexpr int F_KNB = 8;   // exp(Glast - Gs(R))    R = 0..3   (block path)
+  static constexpr int F_GAM = 12;  // exp(Glast)
+  static constexpr int F_OFF = 13;  // exp(Gs(R) - Ge(I)) for (2,0), (3,0), (3,1)
+  static constexpr int F_GS = 16;   // Gs(R) (log2)          R = 0..3
+  static constexpr int NF = 20;
 
   // LDS layout (bytes)
   static constexpr int SZ_K = C * LDK * (int)sizeof(T);
-  static constexpr int OFF_EA = 0;                 // Ea, later -W
-  static constexpr int OFF_QA = OFF_EA + SZ_K;     // Qa (live until the output product)
-  static constexpr int OFF_KN = OFF_QA + SZ_K;     // Kn
+  static constexpr int OFF_E = 0;                  // E exp(G) (or Ea); later -W
+  static constexpr int OFF_Q = OFF_E + SZ_K;       // Q exp(G) (or Qa, rescaled in (e))
+  static constexpr int OFF_K = OFF_Q + SZ_K;       // K exp(-G) (or Kn)
   static constexpr int SZ_T = DK * LDT * (int)sizeof(T);
-  static constexpr int OFF_ET = OFF_KN + SZ_K;     // (E exp(G))^T        [DK][64]
+  static constexpr int OFF_ET = OFF_K + SZ_K;      // (E exp(G))^T        [DK][64]
   static constexpr int OFF_KT = OFF_ET + SZ_T;     // (K exp(Gl - G))^T   [DK][64]
   static constexpr int SZ_Z = NV * LDT * (int)sizeof(T);
   static constexpr int OFF_ZT = OFF_KT + SZ_T;     // Z^T                 [NV][64]
   static constexpr int SZ_P = C * LDT * (int)sizeof(T);
   static constexpr int OFF_P = OFF_ZT + SZ_Z;      // P                   [64][64]
-  static constexpr int OFF_TB = OFF_P + SZ_P;      // T = (I+A)^-1        [64][64]
+  static constexpr int OFF_A = OFF_P + SZ_P;       // -A                  [64][64]
+  static constexpr int OFF_TB = OFF_A + SZ_P;      // diagonal blocks of (I+A)^-1
   static constexpr int OFF_FAC = OFF_TB + SZ_P;
   static constexpr int SZ_FAC = NF * DK * 4;
-  static constexpr int OFF_AF = OFF_FAC + SZ_FAC;  // A fp32 [64][LDA]; cumsum scratch first
-  static constexpr int SZ_AF = C * LDA * 4;
-  static constexpr int LDS_BYTES = OFF_AF + SZ_AF;
+  static constexpr int OFF_FLAG = OFF_FAC + SZ_FAC;
+  static constexpr int LDS_BYTES = OFF_FLAG + 16;
+  // cumsum scratch [TG][DK] fp32 lives in the P and -A buffers (dead until (d))
+  static constexpr int OFF_TOT = OFF_P;
 
   static_assert(NV % 16 == 0 && NV >= 16 && NV <= 128, "value slice");
   static_assert(TPT >= 1 && TPT <= 16 && 16 % TPT == 0, "token groups must tile 16-blocks");
   static_assert(VTPT >= 1 && C % VTG == 0, "value prep mapping");
-  static_assert(32 * NT <= SZ_AF, "cumsum scratch fits in the A buffer");
+  static_assert(32 * NT <= 2 * SZ_P, "cumsum scratch fits in P and -A");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  // row-split exchange of partial sums (f4 per lane): U partials (4 tiles) in the K and
+  // E^T buffers, O partials (2 tiles) in the -A and T buffers; all dead in (g)
+  static_assert(RS == 1 || (NW <= 8 && 4 * 4096 <= SZ_K && 4 * 4096 <= SZ_T &&
+                            NW * 2048 <= 2 * SZ_P), "row-split exchange space");
 };
+
+// Threshold on a chunk's total log2-decay above which the block-referenced path runs:
+// 120 log2 units = 83 nats, so exp(-G) <= 1.3e36 stays finite in fp32 and bf16.
+constexpr float kFastPathMaxDecay2 = 120.f;
 
 // Number of K steps of a product whose K range is the causal prefix [0, 16(R+1)).
 template <int KS>
@@ -95,8 +119,94 @@ __device__ __forceinline__ constexpr int causal_steps(int R) {
   return (16 * (R + 1) + KS - 1) / KS;
 }
 
+// Causal 16x16 tile pairs (R, I), I <= R, in the order of the bits of a pair mask.
+__device__ __forceinline__ constexpr int pair_R(int p) { return p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3; }
+__device__ __forceinline__ constexpr int pair_I(int p) { return p - (pair_R(p) * (pair_R(p) + 1)) / 2; }
+
+// A (stored negated; strictly lower) and P (lower incl. diagonal) tiles for the pairs in
+// MASK_A / MASK_P, with the chunk-referenced operands: every tile is a plain product of
+// (E exp(G) | Q exp(G)) rows and K exp(-G) rows, K = d_k.
+template <typename T, int DK, int LDK, int LDT, int MASK_A, int MASK_P>
+__device__ __forceinline__ void ap_tiles(const T* sE, const T* sQ, const T* sK, T* sAm, T* sP,
+                                         int m16, int g4) {
+  using M = Mma<T>;
+  constexpr int MASK = MASK_A | MASK_P;
+  f4 accA[10], accP[10];
+#pragma unroll
+  for (int p = 0; p < 10; ++p) accA[p] = accP[p] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < DK / M::KS; ++s) {
+    const int kk = s * M::KS + M::KPL * g4;
+    typename M::frag kf[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      bool need = false;
+#pragma unroll
+      for (int p = 0; p < 10; ++p) need |= ((MASK >> p) & 1) && pair_I(p) == I;
+      if (need) kf[I] = M::load(sK, LDK, 16 * I + m16, kk);
+    }
+#pragma unroll
+    for (int p = 0; p < 10; ++p) {
+      const int R = pair_R(p), I = pair_I(p);
+      if ((MASK_A >> p) & 1) accA[p] = M::mma(M::load(sE, LDK, 16 * R + m16, kk), kf[I], accA[p]);
+      if ((MASK_P >> p) & 1) accP[p] = M::mma(M::load(sQ, LDK, 16 * R + m16, kk), kf[I], accP[p]);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < 10; ++p) {
+    const int R = pair_R(p), I = pair_I(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g4 + i, c = m16;
+      if ((MASK_A >> p) & 1) {
+        const float val = (I < R || c < r) ? -accA[p][i] : 0.f;
+        sAm[(16 * R + r) * LDT + 16 * I + c] = from_f<T>(val);
+      }
+      if ((MASK_P >> p) & 1) {
+        const float val = (I < R || c <= r) ? accP[p][i] : 0.f;
+        sP[(16 * R + r) * LDT + 16 * I + c] = from_f<T>(val);
+      }
+    }
+  }
+}
+
+// A run of N consecutive tokens of one channel row of a token-transposed array, built one
+// token at a time (j is a compile-time index after unrolling). bf16 runs are kept packed
+// two per register.
+template <typename T, int N> struct RunBuf {
+  float v[N];
+  __device__ __forceinline__ void put(int j, float x) { v[j] = x; }
+  __device__ __forceinline__ void store(T* row, int c, int r0) const { store_run_t<N>(row, c, r0, v); }
+};
+template <int N> struct RunBuf<bf16, N> {
+  static_assert(N == 1 || N % 2 == 0, "run length");
+  uint32_t w[N / 2 > 0 ? N / 2 : 1];
+  float pend;
+  __device__ __forceinline__ void put(int j, float x) {
+    if (N == 1) {
+      pend = x;
+    } else if (j & 1) {
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      w[j >> 1] = __builtin_bit_cast(uint32_t, bf16x2{static_cast<bf16>(pend), static_cast<bf16>(x)});
+    } else {
+      pend = x;
+    }
+  }
+  __device__ __forceinline__ void store(bf16* row, int c, int r0) const {
+    if constexpr (N == 1) {
+      row[tcol(c, r0)] = static_cast<bf16>(pend);
+    } else if constexpr (N == 2) {
+      *reinterpret_cast<uint32_t*>(row + tcol(c, r0)) = w[0];
+    } else {
+#pragma unroll
+      for (int q = 0; q < N / 4; ++q)
+        *reinterpret_cast<uint2*>(row + tcol(c, r0 + 4 * q)) = make_uint2(w[2 * q], w[2 * q + 1]);
+    }
+  }
+};
+
 template <typename T, int DK, int NV>
-__global__ void __launch_bounds__(4 * NV)
+__global__ void __launch_bounds__((ChunkShape<T, DK, NV>::NT))
 gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                   const T* __restrict__ g, const T* __restrict__ bg, const T* __restrict__ wg,
                   const float* s0, T* __restrict__ o, float* sN,
@@ -104,26 +214,39 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
   using Sh = ChunkShape<T, DK, NV>;
   using M = Mma<T>;
   constexpr int C = Sh::C, NW = Sh::NW, NT = Sh::NT, KS = Sh::KS, KPL = Sh::KPL;
-  constexpr int LDK = Sh::LDK, LDT = Sh::LDT, LDA = Sh::LDA;
+  constexpr int LDK = Sh::LDK, LDT = Sh::LDT, NCT = Sh::NCT;
   __shared__ __attribute__((aligned(16))) char smem[Sh::LDS_BYTES];
-  T* sEa = reinterpret_cast<T*>(smem + Sh::OFF_EA);
-  T* sWm = sEa;  // -W reuses the Ea buffer once A and P are formed
-  T* sQa = reinterpret_cast<T*>(smem + Sh::OFF_QA);
-  T* sKn = reinterpret_cast<T*>(smem + Sh::OFF_KN);
+  T* sE = reinterpret_cast<T*>(smem + Sh::OFF_E);
+  T* sWm = sE;  // -W reuses the E buffer once A and P are formed
+  T* sQ = reinterpret_cast<T*>(smem + Sh::OFF_Q);
+  T* sK = reinterpret_cast<T*>(smem + Sh::OFF_K);
   T* sEt = reinterpret_cast<T*>(smem + Sh::OFF_ET);
   T* sKt = reinterpret_cast<T*>(smem + Sh::OFF_KT);
   T* sZt = reinterpret_cast<T*>(smem + Sh::OFF_ZT);
   T* sP = reinterpret_cast<T*>(smem + Sh::OFF_P);
+  T* sAm = reinterpret_cast<T*>(smem + Sh::OFF_A);
   T* sT = reinterpret_cast<T*>(smem + Sh::OFF_TB);
   float* sFac = reinterpret_cast<float*>(smem + Sh::OFF_FAC);
-  float* sAf = reinterpret_cast<float*>(smem + Sh::OFF_AF);
-  float* sTot = sAf;  // cumsum scratch, dead before A is written
+  float* sTot = reinterpret_cast<float*>(smem + Sh::OFF_TOT);
+  int* sFlag = reinterpret_cast<int*>(smem + Sh::OFF_FLAG);
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int m16 = lane & 15;  // row (A operand) / column (B, D) inside a 16x16 tile
-  const int g4 = lane >> 4;   // lane group
+  constexpr int RS = Sh::RS, NWC = Sh::NWC;
+  constexpr int NMS = NCT / RS;       // state row tiles per wave
+  constexpr int KSH = DK / KS / RS;   // K steps per wave over its key rows
+  int tid = threadIdx.x;
+  int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wct = wave % NWC;         // this wave's state column tile
+  const int whw = wave / NWC;         // this wave's half of the key rows (row split)
+  int m16 = lane & 15;  // row (A operand) / column (B, D) inside a 16x16 tile
+  int g4 = lane >> 4;   // lane group
+  // re-derive the lane indices opaquely at each stage (see opaque())
+  auto fresh_lane = [&]() {
+    tid = opaque(tid);
+    lane = tid & 63;
+    m16 = lane & 15;
+    g4 = lane >> 4;
+  };
 
   const int slice = blockIdx.x % nslices;
   const int nh = blockIdx.x / nslices;
@@ -155,11 +278,19 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
   T* ob = o + row0 * vstride + (long)h * DV + col0;
 
   // ---- prep thread mapping
-  const int cg = tid % Sh::CG;        // channel group: channels [8cg, 8cg+8)
-  const int tg = tid / Sh::CG;        // token group: tokens [tg*TPT, tg*TPT+TPT)
-  const int blk = tg / Sh::GPB;       // 16-token block of those tokens
-  const int vcg = tid % Sh::VCG;      // value columns [8vcg, 8vcg+8)
-  const int vtg = tid / Sh::VCG;      // tokens [vtg*VTPT, ...)
+  int cg = tid % Sh::CG;        // channel group: channels [8cg, 8cg+8)
+  int tg = tid / Sh::CG;        // token group: tokens [tg*TPT, tg*TPT+TPT)
+  int blk = tg / Sh::GPB;       // 16-token block of those tokens
+  int vcg = tid % Sh::VCG;      // value columns [8vcg, 8vcg+8)
+  int vtg = tid / Sh::VCG;      // tokens [vtg*VTPT, ...)
+  auto fresh_prep = [&]() {
+    fresh_lane();
+    cg = tid % Sh::CG;
+    tg = tid / Sh::CG;
+    blk = tg / Sh::GPB;
+    vcg = tid % Sh::VCG;
+    vtg = tid / Sh::VCG;
+  };
 
   Vec8<T> rq[Sh::TPT], rk[Sh::TPT], rg[Sh::TPT], rb[Sh::TPT];
   Vec8<T> rv[Sh::VTPT], rw[Sh::VTPT];
@@ -191,28 +322,35 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
     }
   };
 
-  // ---- one-time LDS init: the upper 16x16 tiles (0,1) and (2,3) of P and T are read
-  // (as zeros) by the 32-wide K steps of the causal products and never written.
-  for (int idx = tid; idx < 2 * 256; idx += NT) {
-    const int t = idx >> 8, e = idx & 255;
-    const int r = (t == 0 ? 0 : 32) + (e >> 4), c = (t == 0 ? 16 : 48) + (e & 15);
-    sP[r * LDT + c] = from_f<T>(0.f);
-    sT[r * LDT + c] = from_f<T>(0.f);
-  }
-
-  // ---- state slice in accumulator registers: tile m holds rows [16m, 16m+16),
-  // columns col0 + 16*wave + m16; lane holds rows 16m + 4*g4 + i.
-  constexpr int NMT = DK / 16;
-  f4 S[NMT];
-  const long sbase = ((long)n * H + h) * DK * DV + col0 + 16 * wave + m16;
+  // ---- state slice in accumulator registers: local tile m holds key rows
+  // [16(whw*NMS + m), +16), columns col0 + 16*wct + m16; lane holds rows ... + 4*g4 + i.
+  f4 S[NMS];
+  const long sbase = ((long)n * H + h) * DK * DV + col0 + 16 * wct + m16;
 #pragma unroll
-  for (int mt = 0; mt < NMT; ++mt) {
+  for (int mt = 0; mt < NMS; ++mt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int ch = 16 * mt + 4 * g4 + i;
+      const int ch = 16 * (whw * NMS + mt) + 4 * g4 + i;
       S[mt][i] = (s0 != nullptr) ? s0[sbase + (long)ch * DV] : 0.f;
     }
   }
+
+  // Output tiles are staged in LDS (in the Z^T buffer, dead after (f)) and copied to HBM
+  // with 16-byte stores at the start of the next chunk, so the wait for the next prefetch
+  // (vmcnt counts stores too) never waits for freshly issued stores.
+  constexpr int OP = (64 * (NV + Sh::PAD) <= NV * LDT) ? NV + Sh::PAD : NV;  // staging pitch
+  constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  T* const sO = sZt;
+  int prev_c0 = 0, prev_n = 0;
+  auto copy_out = [&](int oc0, int on) {
+#pragma unroll
+    for (int idx = tid; idx < C * NV / EPC; idx += NT) {
+      const int r = idx / (NV / EPC), cc = idx % (NV / EPC);
+      if (r < on)
+        *reinterpret_cast<uint4*>(ob + (long)(oc0 + r) * vstride + cc * EPC) =
+            *reinterpret_cast<const uint4*>(sO + r * OP + cc * EPC);
+    }
+  };
 
   const int nchunks = (len + C - 1) / C;
   if (nchunks > 0) load_raw(0, len < C ? len : C);
@@ -220,289 +358,369 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
   for (int ci = 0; ci < nchunks; ++ci) {
     const int c0 = ci * C;
     const int nvalid = (len - c0) < C ? (len - c0) : C;
-    __syncthreads();  // previous chunk's readers of Qa, -W, P are done
+    lds_barrier();  // the previous chunk's readers of every buffer are done
+    fresh_prep();
 
-    // ---- (a) local cumsum of log2-decay over this thread's tokens
-    float gl[Sh::TPT][8];
-#pragma unroll
-    for (int j = 0; j < Sh::TPT; ++j) {
-      float f[8];
-      rg[j].to_float(f);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) gl[j][i] = (j ? gl[j - 1][i] : 0.f) + f[i] * kLog2e;
-    }
+    // ---- (a) previous chunk's output to HBM; per-thread totals of log2-decay
+    if (ci > 0) copy_out(prev_c0, prev_n);
     {
-      float* p = sTot + tg * DK + cg * 8;
-      reinterpret_cast<f4*>(p)[0] = f4{gl[Sh::TPT - 1][0], gl[Sh::TPT - 1][1], gl[Sh::TPT - 1][2], gl[Sh::TPT - 1][3]};
-      reinterpret_cast<f4*>(p)[1] = f4{gl[Sh::TPT - 1][4], gl[Sh::TPT - 1][5], gl[Sh::TPT - 1][6], gl[Sh::TPT - 1][7]};
+      float tot8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < Sh::TPT; ++j) {
+        float f[8];
+        rg[j].to_float(f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) tot8[i] += f[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) tot8[i] *= kLog2e;
+      store8(sTot + tg * DK + cg * 8, tot8);
     }
-    __syncthreads();
+    if (tid == 0) *sFlag = 0;
+    lds_barrier();
+    fresh_prep();
 
-    // ---- (b) per-channel scan over token groups; block-relative prefixes and factors
+    // ---- (b) per-channel scan over token groups: chunk-relative exclusive prefixes
+    // and the per-channel decay factors
     for (int ch = tid; ch < DK; ch += NT) {
+      float tot[Sh::TG];
+#pragma unroll
+      for (int x = 0; x < Sh::TG; ++x) tot[x] = sTot[x * DK + ch];
       float run = 0.f, gs[4];
 #pragma unroll
-      for (int R = 0; R < 4; ++R) {
-        gs[R] = run;
-        for (int qg = 0; qg < Sh::GPB; ++qg) {
-          float* p = sTot + (R * Sh::GPB + qg) * DK + ch;
-          const float t = *p;
-          *p = run - gs[R];
-          run += t;
-        }
+      for (int x = 0; x < Sh::TG; ++x) {
+        if (x % Sh::GPB == 0) gs[x / Sh::GPB] = run;
+        sTot[x * DK + ch] = run;
+        run += tot[x];
       }
       const float gn = run;
-      float ge[4] = {gs[1], gs[2], gs[3], gn};
+      const float ge[4] = {gs[1], gs[2], gs[3], gn};
 #pragma unroll
       for (int R = 0; R < 4; ++R) {
         sFac[(Sh::F_ES + R) * DK + ch] = fast_exp2(gs[R]);
         sFac[(Sh::F_KB + R) * DK + ch] = fast_exp2(ge[R] - gs[R]);
-        sFac[(Sh::F_KN + R) * DK + ch] = fast_exp2(gn - ge[R]);
+        sFac[(Sh::F_KNB + R) * DK + ch] = fast_exp2(gn - gs[R]);
+        sFac[(Sh::F_GS + R) * DK + ch] = gs[R];
       }
       sFac[Sh::F_GAM * DK + ch] = fast_exp2(gn);
       sFac[(Sh::F_OFF + 0) * DK + ch] = fast_exp2(gs[2] - ge[0]);
       sFac[(Sh::F_OFF + 1) * DK + ch] = fast_exp2(gs[3] - ge[0]);
       sFac[(Sh::F_OFF + 2) * DK + ch] = fast_exp2(gs[3] - ge[1]);
+      if (-gn > kFastPathMaxDecay2) *sFlag = 1;
     }
-    __syncthreads();
+    lds_barrier();
+    fresh_prep();
+    const bool block_path = __builtin_amdgcn_readfirstlane(*sFlag) != 0;
 
-    // ---- (c) gated, decay-referenced operands
+    // ---- (c) gated, decayed operands (token by token, running cumsum of log2-decay)
     {
-      float pre[8], fES[8], fKB[8], fKN[8];
+      float run[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pre[i] = sTot[tg * DK + cg * 8 + i];
-        fES[i] = sFac[(Sh::F_ES + blk) * DK + cg * 8 + i];
-        fKB[i] = sFac[(Sh::F_KB + blk) * DK + cg * 8 + i];
-        fKN[i] = sFac[(Sh::F_KN + blk) * DK + cg * 8 + i];
+      for (int i = 0; i < 8; ++i) run[i] = sTot[tg * DK + cg * 8 + i];
+      RunBuf<T, Sh::TPT> ev[8], kv[8];  // E exp(G) and K exp(Glast - G), per channel
+      float fA[8], fB[8], sub[8];
+      if (!block_path) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          fA[i] = 1.f;
+          fB[i] = sFac[Sh::F_GAM * DK + cg * 8 + i];
+          sub[i] = 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          fA[i] = sFac[(Sh::F_ES + blk) * DK + cg * 8 + i];
+          fB[i] = sFac[(Sh::F_KNB + blk) * DK + cg * 8 + i];
+          sub[i] = sFac[(Sh::F_GS + blk) * DK + cg * 8 + i];
+        }
       }
+      // chunk path: x = G (chunk-relative); block path: x = G - Gs(block)
 #pragma unroll
       for (int j = 0; j < Sh::TPT; ++j) {
         const int r = tg * Sh::TPT + j;
-        float fq[8], fk[8], fb[8], ea[8], qa[8], kn[8];
+        float fg[8], fq[8], fk[8], fb[8], e1[8], q1[8], k1[8];
+        rg[j].to_float(fg);
         rq[j].to_float(fq);
         rk[j].to_float(fk);
         rb[j].to_float(fb);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float a = pre[i] + gl[j][i];
-          const float xa = fast_exp2(a), xn = fast_exp2(-a);
-          ea[i] = fb[i] * fk[i] * xa;
-          qa[i] = fq[i] * xa;
-          kn[i] = fk[i] * xn;
-          sEt[(cg * 8 + i) * LDT + r] = from_f<T>(ea[i] * fES[i]);
-          sKt[(cg * 8 + i) * LDT + r] = from_f<T>(kn[i] * fKB[i] * fKN[i]);
+          run[i] += fg[i] * kLog2e;
+          const float x = run[i] - sub[i];
+          const float xe = fast_exp2(x), xk = fast_exp2(-x);
+          e1[i] = fb[i] * fk[i] * xe;
+          q1[i] = fq[i] * xe;
+          k1[i] = fk[i] * xk;
+          ev[i].put(j, e1[i] * fA[i]);
+          kv[i].put(j, k1[i] * fB[i]);
         }
-        store8(sEa + r * LDK + cg * 8, ea);
-        store8(sQa + r * LDK + cg * 8, qa);
-        store8(sKn + r * LDK + cg * 8, kn);
+        store8(sE + r * LDK + cg * 8, e1);
+        store8(sQ + r * LDK + cg * 8, q1);
+        store8(sK + r * LDK + cg * 8, k1);
       }
 #pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int c = cg * 8 + i;
+        ev[i].store(sEt + c * LDT, c, tg * Sh::TPT);
+        kv[i].store(sKt + c * LDT, c, tg * Sh::TPT);
+      }
+      RunBuf<T, Sh::VTPT> zv[8];
+#pragma unroll
       for (int j = 0; j < Sh::VTPT; ++j) {
-        const int r = vtg * Sh::VTPT + j;
         float fv[8], fw[8];
         rv[j].to_float(fv);
         rw[j].to_float(fw);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) sZt[(vcg * 8 + i) * LDT + r] = from_f<T>(fv[i] * fw[i]);
+        for (int i = 0; i < 8; ++i) zv[i].put(j, fv[i] * fw[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int c = vcg * 8 + i;
+        zv[i].store(sZt + c * LDT, c, vtg * Sh::VTPT);
       }
     }
-    // prefetch the next chunk while this one computes
+    // prefetch the next chunk; the loads stay in flight until (a) of the next chunk
     if (ci + 1 < nchunks) {
       const int nn = len - c0 - C;
       load_raw(c0 + C, nn < C ? nn : C);
     }
-    __syncthreads();
+    lds_barrier();
+    fresh_prep();
 
-    // ---- A and P: 10 lower 16x16 tiles each, K = DK
-    for (int job = wave; job < 20; job += NW) {
-      const int pair = job >> 1;
-      const bool isP = job & 1;
-      // pair -> (R, I) with I <= R: (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
-      const int R = pair < 1 ? 0 : pair < 3 ? 1 : pair < 6 ? 2 : 3;
-      const int I = pair - (R * (R + 1)) / 2;
-      const T* lhs = isP ? sQa : sEa;
-      const int off = (R - I >= 2) ? (R == 2 ? 0 : (I == 0 ? 1 : 2)) : -1;
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < DK / KS; ++s) {
-        const int kk = s * KS + KPL * g4;
-        typename M::frag a, b;
-        if (off >= 0)
-          a = M::load_scaled(lhs, LDK, 16 * R + m16, kk, sFac + (Sh::F_OFF + off) * DK + kk);
-        else
-          a = M::load(lhs, LDK, 16 * R + m16, kk);
-        if (I == R)
-          b = M::load(sKn, LDK, 16 * I + m16, kk);
-        else
-          b = M::load_scaled(sKn, LDK, 16 * I + m16, kk, sFac + (Sh::F_KB + I) * DK + kk);
-        acc = M::mma(a, b, acc);
+    // ---- (d) A (stored negated) and P
+    if (!block_path) {
+      // pair masks: rows {0,3} = 0x3C1, rows {1,2} = 0x3E
+      if constexpr (NW >= 8) {
+        switch (wave) {
+          case 0: ap_tiles<T, DK, LDK, LDT, 0x0C0, 0>(sE, sQ, sK, sAm, sP, m16, g4); break;
+          case 1: ap_tiles<T, DK, LDK, LDT, 0, 0x0C0>(sE, sQ, sK, sAm, sP, m16, g4); break;
+          case 2: ap_tiles<T, DK, LDK, LDT, 0x301, 0>(sE, sQ, sK, sAm, sP, m16, g4); break;
+          case 3: ap_tiles<T, DK, LDK, LDT, 0, 0x301>(sE, sQ, sK, sAm, sP, m16, g4); break;
+          case 4: ap_tiles<T, DK, LDK, LDT, 0x038, 0>(sE, sQ, sK, sAm, sP, m16, g4); break;
+          case 5: ap_tiles<T, DK, LDK, LDT, 0, 0x038>(sE, sQ, sK, sAm, sP, m16, g4); break;
+          case 6: ap_tiles<T, DK, LDK, LDT, 0x006, 0>(sE, sQ, sK, sAm, sP, m16, g4); break;
+          case 7: ap_tiles<T, DK, LDK, LDT, 0, 0x006>(sE, sQ, sK, sAm, sP, m16, g4); break;
+          default: break;
+        }
+      } else if constexpr (NW >= 4) {
+        switch (wave) {
+          case 0: ap_tiles<T, DK, LDK, LDT, 0x3C1, 0>(sE, sQ, sK, sAm, sP, m16, g4); break;
+          case 1: ap_tiles<T, DK, LDK, LDT, 0, 0x3C1>(sE, sQ, sK, sAm, sP, m16, g4); break;
+          case 2: ap_tiles<T, DK, LDK, LDT, 0x03E, 0>(sE, sQ, sK, sAm, sP, m16, g4); break;
+          case 3: ap_tiles<T, DK, LDK, LDT, 0, 0x03E>(sE, sQ, sK, sAm, sP, m16, g4); break;
+          default: break;
+        }
+      } else if constexpr (NW == 2) {
+        if (wave == 0) ap_tiles<T, DK, LDK, LDT, 0x3C1, 0x3C1>(sE, sQ, sK, sAm, sP, m16, g4);
+        else ap_tiles<T, DK, LDK, LDT, 0x03E, 0x03E>(sE, sQ, sK, sAm, sP, m16, g4);
+      } else {
+        ap_tiles<T, DK, LDK, LDT, 0x3FF, 0x3FF>(sE, sQ, sK, sAm, sP, m16, g4);
       }
+    } else {
+      // block-referenced tiles: rows of block R against Kn of block I; off-diagonal
+      // tiles scale Kn by exp(Ge(I)-Gs(I)) and, two or more blocks apart, the left
+      // operand by exp(Gs(R)-Ge(I)).
+      for (int job = wave; job < 20; job += NW) {
+        const int pair = job >> 1;
+        const bool isP = job & 1;
+        const int R = pair < 1 ? 0 : pair < 3 ? 1 : pair < 6 ? 2 : 3;
+        const int I = pair - (R * (R + 1)) / 2;
+        const T* lhs = isP ? sQ : sE;
+        const int off = (R - I >= 2) ? (R == 2 ? 0 : (I == 0 ? 1 : 2)) : -1;
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < DK / KS; ++s) {
+          const int kk = s * KS + KPL * g4;
+          typename M::frag a, b;
+          if (off >= 0)
+            a = M::load_scaled(lhs, LDK, 16 * R + m16, kk, sFac + (Sh::F_OFF + off) * DK + kk);
+          else
+            a = M::load(lhs, LDK, 16 * R + m16, kk);
+          if (I == R)
+            b = M::load(sK, LDK, 16 * I + m16, kk);
+          else
+            b = M::load_scaled(sK, LDK, 16 * I + m16, kk, sFac + (Sh::F_KB + I) * DK + kk);
+          acc = M::mma(a, b, acc);
+        }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * g4 + i, c = m16;  // inside the tile
-        const bool keep = (I < R) || (isP ? (c <= r) : (c < r));
-        const float val = keep ? acc[i] : 0.f;
-        if (isP)
-          sP[(16 * R + r) * LDT + 16 * I + c] = from_f<T>(val);
-        else
-          sAf[(16 * R + r) * LDA + 16 * I + c] = val;
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * g4 + i, c = m16;
+          const bool keep = (I < R) || (isP ? (c <= r) : (c < r));
+          const float val = keep ? (isP ? acc[i] : -acc[i]) : 0.f;
+          if (isP) sP[(16 * R + r) * LDT + 16 * I + c] = from_f<T>(val);
+          else sAm[(16 * R + r) * LDT + 16 * I + c] = from_f<T>(val);
+        }
       }
     }
-    __syncthreads();
+    // upper tiles (0,1) and (2,3) of P are read (as zeros) by the 32-wide K steps of P U
+    for (int idx = tid; idx < 2 * 256; idx += NT) {
+      const int t = idx >> 8, e = idx & 255;
+      sP[((t ? 32 : 0) + (e >> 4)) * LDT + (t ? 48 : 16) + (e & 15)] = from_f<T>(0.f);
+    }
+    lds_barrier();
+    fresh_prep();
 
-    // ---- T = (I + A)^{-1}: diagonal 16x16 blocks by forward substitution (fp32),
-    // one block per 16-lane group of wave 0, one column per lane.
+    // ---- (e) diagonal 16x16 blocks of (I + A)^{-1} by forward substitution (fp32),
+    // one block per 16-lane group of wave 0, one column per lane; the other waves
+    // rescale Qa to Q exp(G) on the block path.
     if (wave == 0) {
       const int jb = g4, c = m16;
-      const float* Ab = sAf + (16 * jb) * LDA + 16 * jb;
+      const T* Ab = sAm + (16 * jb) * LDT + 16 * jb;
+      float am[16][16];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) {
+#pragma unroll
+        for (int i = 0; i < r; ++i) am[r][i] = to_f(Ab[r * LDT + i]);
+      }
       float x[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float acc = (r == c) ? 1.f : 0.f;
+      for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
 #pragma unroll
-        for (int i = 0; i < r; ++i) acc -= Ab[r * LDA + i] * x[i];
-        x[r] = acc;
+      for (int i = 0; i < 16; ++i) {
+#pragma unroll
+        for (int r = i + 1; r < 16; ++r) x[r] += am[r][i] * x[i];  // am holds -A
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) sT[(16 * jb + r) * LDT + 16 * jb + c] = from_f<T>(x[r]);
     }
-    __syncthreads();
+    if (block_path) {
+      const int first = NW > 1 ? 64 : 0;
+      for (int idx = tid - first; idx >= 0 && idx < C * DK; idx += NT - first) {
+        const int r = idx / DK, ch = idx % DK;
+        sQ[r * LDK + ch] = from_f<T>(to_f(sQ[r * LDK + ch]) * sFac[(Sh::F_ES + r / 16) * DK + ch]);
+      }
+    }
+    lds_barrier();
+    fresh_prep();
 
-    // off-diagonal blocks, row block by row block:
-    //   T_RI = -T_RR * sum_{J=I}^{R-1} A_RJ T_JI
+    // ---- (f) [W | U~] = (I + A)^{-1} [E exp(G) | Z] by block forward substitution:
+    //   X_R = T_RR (RHS_R - sum_{J<R} A_RJ X_J)
+    // Each wave owns whole column tiles, so the rounds need no barrier. Key-channel tiles
+    // are dealt round-robin; the wave's own value tile gives U~ in registers.
+    f4 U[4];
+    {
+      constexpr int NE = (NCT + NW - 1) / NW;  // key-channel tiles per wave (max)
+      f4 X[NE + 1][4];
 #pragma unroll
-    for (int R = 1; R < 4; ++R) {
-      for (int I = wave; I < R; I += NW) {
-        f4 X = {0.f, 0.f, 0.f, 0.f};
-        f4 Y = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (KPL == 8) {  // bf16: K = 16 MFMA, 4 K-values per lane
-          for (int J = I; J < R; ++J) {
-            const float* ap = sAf + (16 * R + m16) * LDA + 16 * J + 4 * g4;
-            const f4 av = *reinterpret_cast<const f4*>(ap);
-            bf16x4 a = {static_cast<bf16>(av[0]), static_cast<bf16>(av[1]),
-                        static_cast<bf16>(av[2]), static_cast<bf16>(av[3])};
-            bf16x4 b;
+      for (int R = 0; R < 4; ++R) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) b[i] = sT[(16 * J + 4 * g4 + i) * LDT + 16 * I + m16];
-            X = M::mma16(a, b, X);
+        for (int t = 0; t <= NE; ++t) {
+          const int ct = wave + t * NW;
+          const bool isZ = (t == NE);
+          if constexpr (NCT % NW != 0) {
+            if (!isZ && ct >= NCT) continue;
           }
-          const bf16x4 a = *reinterpret_cast<const bf16x4*>(sT + (16 * R + m16) * LDT + 16 * R + 4 * g4);
-          const bf16x4 b = {static_cast<bf16>(X[0]), static_cast<bf16>(X[1]),
-                            static_cast<bf16>(X[2]), static_cast<bf16>(X[3])};
-          Y = M::mma16(a, b, Y);
-        } else {  // fp32: four 16x16x4 steps per 16-wide K block
-          for (int J = I; J < R; ++J) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              const float a = sAf[(16 * R + m16) * LDA + 16 * J + 4 * s + g4];
-              const float b = to_f(sT[(16 * J + 4 * s + g4) * LDT + 16 * I + m16]);
-              X = M::mma(from_f<T>(a), from_f<T>(b), X);
-            }
+          if constexpr (RS > 1) {
+            if (isZ && whw != 0) continue;
           }
+          const int crow = isZ ? 16 * wct + m16 : 16 * ct + m16;
+          const T* src = (isZ ? sZt : sEt) + crow * LDT;
+          f4 acc = load4f(src + tcol(crow, 16 * R + 4 * g4));  // RHS rows 16R+4g4+i, col m16
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const float a = to_f(sT[(16 * R + m16) * LDT + 16 * R + 4 * g4 + s]);
-            Y = M::mma(from_f<T>(a), from_f<T>(X[s]), Y);
-          }
+          for (int J = 0; J < R; ++J)
+            acc = mma16_acc(sAm + (16 * R + m16) * LDT + 16 * J, g4, X[t][J], acc);
+          X[t][R] = mma16_acc(sT + (16 * R + m16) * LDT + 16 * R, g4, acc, f4{0.f, 0.f, 0.f, 0.f});
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NE; ++t) {
+        const int ct = wave + t * NW;
+        if constexpr (NCT % NW != 0) {
+          if (ct >= NCT) continue;
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sT[(16 * R + 4 * g4 + i) * LDT + 16 * I + m16] = from_f<T>(-Y[i]);
-      }
-      __syncthreads();
-    }
-
-    // ---- W = T (E exp(G)) -> stored negated; U~ = T Z for this wave's columns
-    for (int job = wave; job < 4 * (DK / 16); job += NW) {
-      const int R = job / (DK / 16), ct = job % (DK / 16);
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int s = 0; s < causal_steps<KS>(R); ++s) {
-        const int kk = s * KS + KPL * g4;
-        acc = M::mma(M::load(sT, LDT, 16 * R + m16, kk), M::load(sEt, LDT, 16 * ct + m16, kk), acc);
+        for (int R = 0; R < 4; ++R) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sWm[(16 * R + 4 * g4 + i) * LDK + 16 * ct + m16] = from_f<T>(-X[t][R][i]);
+        }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sWm[(16 * R + 4 * g4 + i) * LDK + 16 * ct + m16] = from_f<T>(-acc[i]);
+      for (int R = 0; R < 4; ++R) U[R] = (RS == 1 || whw == 0) ? X[NE][R] : f4{0.f, 0.f, 0.f, 0.f};
     }
-    f4 U[4];
-#pragma unroll
-    for (int R = 0; R < 4; ++R) {
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < causal_steps<KS>(R); ++s) {
-        const int kk = s * KS + KPL * g4;
-        acc = M::mma(M::load(sT, LDT, 16 * R + m16, kk), M::load(sZt, LDT, 16 * wave + m16, kk), acc);
-      }
-      U[R] = acc;
-    }
-    __syncthreads();
+    lds_barrier();
+    fresh_prep();
 
-    // ---- state-dependent part (this wave's 16 columns)
-    typename M::frag sb[DK / KS];
+    // ---- (g) state-dependent part (this wave's 16 columns and key rows)
+    typename M::frag sb[KSH];
 #pragma unroll
-    for (int s = 0; s < DK / KS; ++s) sb[s] = M::from_acc(S, s);
+    for (int s = 0; s < KSH; ++s) sb[s] = M::from_acc(S, s);
 
+    // partial sums over this wave's key rows: U += -W S, Q exp(G) S
     f4 O[4];
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
       f4 acc = U[R];
       f4 oacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < DK / KS; ++s) {
-        acc = M::mma(M::load_perm(sWm, LDK, 16 * R + m16, s, g4), sb[s], acc);
-        // (Q exp(G)) = Qa * exp(Gs(R)), scaled per channel while loading
-        typename M::frag qa = M::load_perm(sQa, LDK, 16 * R + m16, s, g4);
-        if constexpr (KPL == 8) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            qa[i] = static_cast<bf16>(static_cast<float>(qa[i]) *
-                                      sFac[(Sh::F_ES + R) * DK + M::perm_k(s, g4, i)]);
-        } else {
-          qa = qa * sFac[(Sh::F_ES + R) * DK + M::perm_k(s, g4, 0)];
-        }
-        oacc = M::mma(qa, sb[s], oacc);
+      for (int s = 0; s < KSH; ++s) {
+        const int sg = whw * KSH + s;  // K step over all key rows
+        acc = M::mma(M::load_perm(sWm, LDK, 16 * R + m16, sg, g4), sb[s], acc);
+        oacc = M::mma(M::load_perm(sQ, LDK, 16 * R + m16, sg, g4), sb[s], oacc);
       }
       U[R] = acc;
       O[R] = oacc;
+    }
+    // output row tiles finished by this wave: all (no split) or {0,3} / {1,2}
+    const int oR0 = RS == 1 ? 0 : (whw == 0 ? 0 : 1);
+    const int oR1 = RS == 1 ? 3 : (whw == 0 ? 3 : 2);
+    if constexpr (RS > 1) {
+      // exchange partial sums with the partner wave (same columns, other key rows)
+      f4* xu_mine = reinterpret_cast<f4*>((wave < 4 ? smem + Sh::OFF_K : smem + Sh::OFF_ET)) +
+                    (wave & 3) * 256;
+      f4* xo_mine = reinterpret_cast<f4*>(smem + Sh::OFF_A) + wave * 128;
+      const int pw = wave ^ NWC;  // partner wave (NWC = 4 or 2 divides the wave index)
+      const f4* xu_part = reinterpret_cast<const f4*>((pw < 4 ? smem + Sh::OFF_K : smem + Sh::OFF_ET)) +
+                          (pw & 3) * 256;
+      const f4* xo_part = reinterpret_cast<const f4*>(smem + Sh::OFF_A) + pw * 128;
+#pragma unroll
+      for (int R = 0; R < 4; ++R) xu_mine[R * 64 + lane] = U[R];
+      // the partner finishes the other two output row tiles
+      xo_mine[lane] = whw == 0 ? O[1] : O[0];
+      xo_mine[64 + lane] = whw == 0 ? O[2] : O[3];
+      lds_barrier();
+#pragma unroll
+      for (int R = 0; R < 4; ++R) U[R] += xu_part[R * 64 + lane];
+      O[oR0] += xo_part[lane];
+      O[oR1] += xo_part[64 + lane];
     }
     typename M::frag ub[C / KS];
 #pragma unroll
     for (int s = 0; s < C / KS; ++s) ub[s] = M::from_acc(U, s);
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
+      if (RS > 1 && R != oR0 && R != oR1) continue;
 #pragma unroll
       for (int s = 0; s < causal_steps<KS>(R); ++s)
         O[R] = M::mma(M::load_perm(sP, LDT, 16 * R + m16, s, g4), ub[s], O[R]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sO[(16 * R + 4 * g4 + i) * OP + 16 * wct + m16] = from_f<T>(O[R][i]);
     }
-    // output rows r < nvalid
+    prev_c0 = c0;
+    prev_n = nvalid;
+    // S <- Diag(exp(Glast)) S + (K exp(Glast - G))^T U   (this wave's key rows)
 #pragma unroll
-    for (int R = 0; R < 4; ++R) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * R + 4 * g4 + i;
-        if (r < nvalid) ob[(long)(c0 + r) * vstride + 16 * wave + m16] = from_f<T>(O[R][i]);
-      }
-    }
-    // S <- Diag(exp(Glast)) S + (K exp(Glast - G))^T U
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) {
-      f4 acc;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = S[mt][i] * sFac[Sh::F_GAM * DK + 16 * mt + 4 * g4 + i];
+    for (int mt = 0; mt < NMS; ++mt) {
+      const int mg = whw * NMS + mt;
+      const f4 gam = *reinterpret_cast<const f4*>(sFac + Sh::F_GAM * DK + 16 * mg + 4 * g4);
+      f4 acc = S[mt] * gam;
 #pragma unroll
       for (int s = 0; s < C / KS; ++s)
-        acc = M::mma(M::load_perm(sKt, LDT, 16 * mt + m16, s, g4), ub[s], acc);
+        acc = M::mma(M::load_perm_t(sKt, LDT, 16 * mg + m16, s, g4), ub[s], acc);
       S[mt] = acc;
     }
   }
 
+  if (nchunks > 0) {
+    lds_barrier();
+    copy_out(prev_c0, prev_n);
+  }
   if (sN != nullptr) {
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) {
+    for (int mt = 0; mt < NMS; ++mt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int ch = 16 * mt + 4 * g4 + i;
+        const int ch = 16 * (whw * NMS + mt) + 4 * g4 + i;
         sN[sbase + (long)ch * DV] = S[mt][i];
       }
     }
@@ -513,7 +731,8 @@ template <typename T, int DK, int NV>
 static hipError_t launch_chunk(const ChunkArgs& a) {
   const int nslices = a.d_v / NV;
   const long grid = (long)a.N * a.H * nslices;
-  hipLaunchKernelGGL((gdn2_chunk_kernel<T, DK, NV>), dim3((unsigned)grid), dim3(4 * NV), 0,
+  hipLaunchKernelGGL((gdn2_chunk_kernel<T, DK, NV>), dim3((unsigned)grid),
+                     dim3(ChunkShape<T, DK, NV>::NT), 0,
                      (hipStream_t)a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
                      (const T*)a.g, (const T*)a.b, (const T*)a.w, a.s0, (T*)a.o, a.sN,
                      a.cu_seqlens, a.T, a.H, a.d_v, nslices);

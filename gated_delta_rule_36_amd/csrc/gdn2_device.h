@@ -27,6 +27,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2v __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(bf16 x) { return static_cast<float>(x); }
@@ -101,6 +102,9 @@ template <> struct Mma<bf16> {
     bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
+  // load_perm from a token-transposed (swizzled) array; `c` is the logical row.
+  static __device__ __forceinline__ frag load_perm_t(const bf16* base, int ld, int c, int s,
+                                                      int g);
   // Channel index of permuted slot i (for per-k scaling of a permuted fragment).
   static __device__ __forceinline__ int perm_k(int s, int g, int i) {
     return 32 * s + 4 * g + (i & 3) + ((i >> 2) << 4);
@@ -139,6 +143,8 @@ template <> struct Mma<float> {
                                                     int g) {
     return base[row * ld + 16 * (s >> 2) + 4 * g + (s & 3)];
   }
+  static __device__ __forceinline__ frag load_perm_t(const float* base, int ld, int c, int s,
+                                                      int g);
   static __device__ __forceinline__ int perm_k(int s, int g, int) {
     return 16 * (s >> 2) + 4 * g + (s & 3);
   }
@@ -150,7 +156,108 @@ template <> struct Mma<float> {
   }
 };
 
+// K = 16 product with B taken from a D tile (4 consecutive rows per lane = the B
+// fragment of a 16-deep product) and A row `arow` (16 values of row l%16 of A, in LDS).
+__device__ __forceinline__ f4 mma16_acc(const bf16* arow, int g, f4 bacc, f4 c) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x4 a = *reinterpret_cast<const bf16x4*>(arow + 4 * g);
+  const bf16x2 b01 = __builtin_convertvector((f2v{bacc[0], bacc[1]}), bf16x2);
+  const bf16x2 b23 = __builtin_convertvector((f2v{bacc[2], bacc[3]}), bf16x2);
+  const bf16x4 b = __builtin_shufflevector(b01, b23, 0, 1, 2, 3);
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, a),
+                                                   __builtin_bit_cast(short4v, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f4 mma16_acc(const float* arow, int g, f4 bacc, f4 c) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(arow[4 * g + s], bacc[s], c, 0, 0, 0);
+  return c;
+}
+
+// Four consecutive elements (a D-tile row group) from LDS, as floats.
+__device__ __forceinline__ f4 load4f(const bf16* p) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  return f4{static_cast<float>(v[0]), static_cast<float>(v[1]), static_cast<float>(v[2]),
+            static_cast<float>(v[3])};
+}
+__device__ __forceinline__ f4 load4f(const float* p) { return *reinterpret_cast<const f4*>(p); }
+
+// Store N consecutive values (N in {1, 2, 4, 8, 16}) from floats.
+template <int N>
+__device__ __forceinline__ void store_run(bf16* p, const float* v) {
+  if constexpr (N == 1) {
+    *p = static_cast<bf16>(v[0]);
+  } else if constexpr (N == 2) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    *reinterpret_cast<bf16x2*>(p) = bf16x2{static_cast<bf16>(v[0]), static_cast<bf16>(v[1])};
+  } else if constexpr (N == 4) {
+    *reinterpret_cast<bf16x4*>(p) = bf16x4{static_cast<bf16>(v[0]), static_cast<bf16>(v[1]),
+                                           static_cast<bf16>(v[2]), static_cast<bf16>(v[3])};
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; i += 8) store8(p + i, v + i);
+  }
+}
+template <int N>
+__device__ __forceinline__ void store_run(float* p, const float* v) {
+  if constexpr (N == 1) {
+    *p = v[0];
+  } else if constexpr (N == 2) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    *reinterpret_cast<f2*>(p) = f2{v[0], v[1]};
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; i += 4) *reinterpret_cast<f4*>(p + i) = f4{v[i], v[i + 1], v[i + 2], v[i + 3]};
+  }
+}
+
+// Token-transposed LDS arrays ([channel][64 tokens]) store 4-token groups XOR-swizzled by
+// the channel: group' = group ^ ((c >> 3) & 14). Writers (8 consecutive channels per lane,
+// lanes 8 channels apart) and MFMA readers (16 consecutive channels, one group) are then
+// both free of LDS bank conflicts.
+__device__ __forceinline__ int tswz(int c) { return (c >> 3) & 14; }
+__device__ __forceinline__ int tcol(int c, int r) { return ((((r >> 2) ^ tswz(c))) << 2) | (r & 3); }
+
+// Store a run of N tokens (N in {1, 2, 4, 8, 16}, aligned to N) of channel row `c`.
+template <int N, typename T>
+__device__ __forceinline__ void store_run_t(T* row, int c, int r0, const float* v) {
+  if constexpr (N <= 4) {
+    store_run<N>(row + tcol(c, r0), v);
+  } else {
+#pragma unroll
+    for (int j = 0; j < N; j += 4) store_run<4>(row + tcol(c, r0 + j), v + j);
+  }
+}
+
+// Workgroup barrier that orders LDS only: outstanding global loads (prefetches into
+// registers) stay in flight across it, unlike __syncthreads().
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Returns x unchanged but opaque to the optimiser, so values derived from it (per-lane LDS
+// addresses) are recomputed where used instead of being hoisted out of the chunk loop and
+// kept live (or spilled) across it. An empty asm statement: no instruction is emitted.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+__device__ __forceinline__ Mma<bf16>::frag Mma<bf16>::load_perm_t(const bf16* base, int ld, int c,
+                                                                  int s, int g) {
+  const bf16* row = base + c * ld;
+  const int sw = tswz(c);
+  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + (((8 * s + g) ^ sw) << 2));
+  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + (((8 * s + 4 + g) ^ sw) << 2));
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+__device__ __forceinline__ float Mma<float>::load_perm_t(const float* base, int ld, int c, int s,
+                                                         int g) {
+  return base[c * ld + ((((4 * (s >> 2) + g) ^ tswz(c))) << 2) + (s & 3)];
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 
