@@ -29,6 +29,22 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 NAMES = ("q", "k", "v", "g", "b", "w")
 
 
+def measured_traffic(key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when the
+    kernel's sources changed since the counters were taken (digest mismatch)."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "profiles", "counters.json")) as f:
+            rec = json.load(f)[key]
+    except (OSError, KeyError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for name in rec["sources"]:
+        with open(os.path.join(ROOT, "gated_delta_rule_36_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return rec["traffic_bytes"] if h.hexdigest() == rec["source_sha256"] else None
+
+
 def fwd_bytes(B, T, H, dk, dv, N, elt=2, read_s0=False):
     """Algorithmic HBM bytes of one forward call: read q,k,g,b,v,w once, write o once,
     write the fp32 final state (and read the initial one if given)."""
@@ -77,6 +93,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--value-slice", type=int, default=0)
+    ap.add_argument("--copy-calib-mb", type=int, default=0,
+                    help="before the timed region, run a plain device copy of this many MiB "
+                         "(3 times) so hardware byte counters can be calibrated against it")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU (got --gpus {args.gpus}); the "
@@ -94,6 +113,15 @@ def main():
     x = make_config_inputs("layer1p3b_bf16")
     t = {n: torch.from_numpy(x[n]).to(dev).to(torch.bfloat16) for n in NAMES}
     torch.cuda.synchronize()
+
+    if args.copy_calib_mb > 0:
+        src = torch.empty(args.copy_calib_mb << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step():
         return G.chunk_fwd(*(t[n] for n in NAMES), value_slice=args.value_slice)
@@ -130,7 +158,8 @@ def main():
                    "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "gdn2_chunk_kernel<bf16,128,NV>",
+                     "traffic": measured_traffic("chunk_fwd_layer1p3b_bf16"),
+                     "kernel": "gdn2_chunk_kernel<bf16,128,NV>",
                      "algorithmic_bytes_per_launch": nbytes,
                      "kernel_ms": round(kern_ms, 4)},
         "mfma": {"useful_flops_per_launch": round(flops),
@@ -166,7 +195,8 @@ def main():
                          "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
         out["decode"] = {"workload": f"decode step: N={N} sequences x H={Hd}, d_k=d_v={dkd}, "
                                      f"fp32 state in place, {cd['steps']} consecutive steps",
-                         "bytes_per_step": decode_bytes(N, Hd, dkd, dvd), **res}
+                         "bytes_per_step": decode_bytes(N, Hd, dkd, dvd),
+                         "traffic": measured_traffic("decode_step_n256_h16_bf16"), **res}
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(x)

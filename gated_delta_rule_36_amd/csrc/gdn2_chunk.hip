@@ -164,7 +164,7 @@ __device__ __forceinline__ void ap_tiles(const T* sE, const T* sQ, const T* sK, 
       }
       if ((MASK_P >> p) & 1) {
         const float val = (I < R || c <= r) ? accP[p][i] : 0.f;
-        sP[(16 * R + r) * LDT + 16 * I + c] = from_f<T>(val);
+        sP[(16 * R + r) * LDT + Mma<T>::phi(16 * I + c)] = from_f<T>(val);
       }
     }
   }
@@ -176,6 +176,7 @@ __device__ __forceinline__ void ap_tiles(const T* sE, const T* sQ, const T* sK, 
 template <typename T, int N> struct RunBuf {
   float v[N];
   __device__ __forceinline__ void put(int j, float x) { v[j] = x; }
+  template <bool PHI = false>
   __device__ __forceinline__ void store(T* row, int c, int r0) const { store_run_t<N>(row, c, r0, v); }
 };
 template <int N> struct RunBuf<bf16, N> {
@@ -192,15 +193,19 @@ template <int N> struct RunBuf<bf16, N> {
       pend = x;
     }
   }
+  // PHI: tokens stored in the phi order of Mma<bf16> (runs of 2 and aligned runs of 4 stay
+  // contiguous under it).
+  template <bool PHI = false>
   __device__ __forceinline__ void store(bf16* row, int c, int r0) const {
+    auto pos = [&](int r) { return tcol(c, PHI ? Mma<bf16>::phi(r) : r); };
     if constexpr (N == 1) {
-      row[tcol(c, r0)] = static_cast<bf16>(pend);
+      row[pos(r0)] = static_cast<bf16>(pend);
     } else if constexpr (N == 2) {
-      *reinterpret_cast<uint32_t*>(row + tcol(c, r0)) = w[0];
+      *reinterpret_cast<uint32_t*>(row + pos(r0)) = w[0];
     } else {
 #pragma unroll
       for (int q = 0; q < N / 4; ++q)
-        *reinterpret_cast<uint2*>(row + tcol(c, r0 + 4 * q)) = make_uint2(w[2 * q], w[2 * q + 1]);
+        *reinterpret_cast<uint2*>(row + pos(r0 + 4 * q)) = make_uint2(w[2 * q], w[2 * q + 1]);
     }
   }
 };
@@ -210,7 +215,8 @@ __global__ void __launch_bounds__((ChunkShape<T, DK, NV>::NT))
 gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                   const T* __restrict__ g, const T* __restrict__ bg, const T* __restrict__ wg,
                   const float* s0, T* __restrict__ o, float* sN,
-                  const int* __restrict__ cu_seqlens, int T_len, int H, int DV, int nslices) {
+                  const int* __restrict__ cu_seqlens, int T_len, int H, int DV, int nslices,
+                  int nunits) {
   using Sh = ChunkShape<T, DK, NV>;
   using M = Mma<T>;
   constexpr int C = Sh::C, NW = Sh::NW, NT = Sh::NT, KS = Sh::KS, KPL = Sh::KPL;
@@ -248,8 +254,16 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
     g4 = lane >> 4;
   };
 
-  const int slice = blockIdx.x % nslices;
-  const int nh = blockIdx.x / nslices;
+  // Workgroup -> (sequence, head, slice). Workgroups are dealt round-robin to the 8 XCDs
+  // (each with its own L2), so the slices of one (sequence, head) are given workgroup ids
+  // that are congruent mod 8: they run on the same XCD at the same time and the second
+  // read of the shared key-side inputs is served by that XCD's L2.
+  const int units = nunits;                       // sequences * heads
+  const int grp = blockIdx.x / (8 * nslices);     // group of 8 (sequence, head) units
+  const int gsz = min(8, units - grp * 8);        // units in this group
+  const int gi = blockIdx.x - grp * 8 * nslices;  // index inside the group
+  const int slice = gi / gsz;
+  const int nh = grp * 8 + gi % gsz;
   const int h = nh % H;
   const int n = nh / H;
   const int col0 = slice * NV;  // first state / value column of this workgroup
@@ -454,15 +468,15 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
           ev[i].put(j, e1[i] * fA[i]);
           kv[i].put(j, k1[i] * fB[i]);
         }
-        store8(sE + r * LDK + cg * 8, e1);
-        store8(sQ + r * LDK + cg * 8, q1);
-        store8(sK + r * LDK + cg * 8, k1);
+        store8_phi(sE + r * LDK, cg * 8, e1);
+        store8_phi(sQ + r * LDK, cg * 8, q1);
+        store8_phi(sK + r * LDK, cg * 8, k1);
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int c = cg * 8 + i;
         ev[i].store(sEt + c * LDT, c, tg * Sh::TPT);
-        kv[i].store(sKt + c * LDT, c, tg * Sh::TPT);
+        kv[i].template store<true>(sKt + c * LDT, c, tg * Sh::TPT);
       }
       RunBuf<T, Sh::VTPT> zv[8];
 #pragma unroll
@@ -529,16 +543,16 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
         const int off = (R - I >= 2) ? (R == 2 ? 0 : (I == 0 ? 1 : 2)) : -1;
         f4 acc = {0.f, 0.f, 0.f, 0.f};
         for (int s = 0; s < DK / KS; ++s) {
-          const int kk = s * KS + KPL * g4;
-          typename M::frag a, b;
-          if (off >= 0)
-            a = M::load_scaled(lhs, LDK, 16 * R + m16, kk, sFac + (Sh::F_OFF + off) * DK + kk);
-          else
-            a = M::load(lhs, LDK, 16 * R + m16, kk);
-          if (I == R)
-            b = M::load(sK, LDK, 16 * I + m16, kk);
-          else
-            b = M::load_scaled(sK, LDK, 16 * I + m16, kk, sFac + (Sh::F_KB + I) * DK + kk);
+          const int kk = s * KS + KPL * g4;  // physical (phi-ordered) K position
+          float fa[KPL], fb[KPL];
+#pragma unroll
+          for (int i = 0; i < KPL; ++i) {
+            const int ch = M::phi_inv(kk + i);  // logical key channel of that position
+            fa[i] = off >= 0 ? sFac[(Sh::F_OFF + off) * DK + ch] : 1.f;
+            fb[i] = I != R ? sFac[(Sh::F_KB + I) * DK + ch] : 1.f;
+          }
+          const typename M::frag a = M::load_scaled(lhs, LDK, 16 * R + m16, kk, fa);
+          const typename M::frag b = M::load_scaled(sK, LDK, 16 * I + m16, kk, fb);
           acc = M::mma(a, b, acc);
         }
 #pragma unroll
@@ -546,7 +560,7 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
           const int r = 4 * g4 + i, c = m16;
           const bool keep = (I < R) || (isP ? (c <= r) : (c < r));
           const float val = keep ? (isP ? acc[i] : -acc[i]) : 0.f;
-          if (isP) sP[(16 * R + r) * LDT + 16 * I + c] = from_f<T>(val);
+          if (isP) sP[(16 * R + r) * LDT + M::phi(16 * I + c)] = from_f<T>(val);
           else sAm[(16 * R + r) * LDT + 16 * I + c] = from_f<T>(val);
         }
       }
@@ -554,15 +568,34 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
     // upper tiles (0,1) and (2,3) of P are read (as zeros) by the 32-wide K steps of P U
     for (int idx = tid; idx < 2 * 256; idx += NT) {
       const int t = idx >> 8, e = idx & 255;
-      sP[((t ? 32 : 0) + (e >> 4)) * LDT + (t ? 48 : 16) + (e & 15)] = from_f<T>(0.f);
+      sP[((t ? 32 : 0) + (e >> 4)) * LDT + M::phi((t ? 48 : 16) + (e & 15))] = from_f<T>(0.f);
     }
     lds_barrier();
     fresh_prep();
 
     // ---- (e) diagonal 16x16 blocks of (I + A)^{-1} by forward substitution (fp32),
-    // one block per 16-lane group of wave 0, one column per lane; the other waves
-    // rescale Qa to Q exp(G) on the block path.
-    if (wave == 0) {
+    // one block per 16-lane group of the last wave, one column per lane. Meanwhile the
+    // other waves form their partial Q exp(G) S products (chunk path) or rescale Qa to
+    // Q exp(G) (block path).
+    constexpr int TDW = NW - 1;  // wave that forms the diagonal inverse blocks
+    typename M::frag sb[KSH];    // this wave's state rows as B operands
+#pragma unroll
+    for (int s = 0; s < KSH; ++s) sb[s] = M::from_acc(S, s);
+    f4 O[4];
+    auto o_partial = [&]() {  // O = Q exp(G) S over this wave's key rows
+      typename M::frag qf[4][KSH];
+#pragma unroll
+      for (int R = 0; R < 4; ++R)
+#pragma unroll
+        for (int s = 0; s < KSH; ++s) qf[R][s] = M::load_phi(sQ, LDK, 16 * R + m16, whw * KSH + s, g4);
+#pragma unroll
+      for (int R = 0; R < 4; ++R) {
+        O[R] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KSH; ++s) O[R] = M::mma(qf[R][s], sb[s], O[R]);
+      }
+    };
+    if (wave == TDW) {
       const int jb = g4, c = m16;
       const T* Ab = sAm + (16 * jb) * LDT + 16 * jb;
       float am[16][16];
@@ -581,12 +614,17 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) sT[(16 * jb + r) * LDT + 16 * jb + c] = from_f<T>(x[r]);
+    } else if (!block_path) {
+      o_partial();
     }
     if (block_path) {
-      const int first = NW > 1 ? 64 : 0;
-      for (int idx = tid - first; idx >= 0 && idx < C * DK; idx += NT - first) {
-        const int r = idx / DK, ch = idx % DK;
-        sQ[r * LDK + ch] = from_f<T>(to_f(sQ[r * LDK + ch]) * sFac[(Sh::F_ES + r / 16) * DK + ch]);
+      // threads outside the last wave (all threads when there is a single wave)
+      const int nthr = NW > 1 ? NT - 64 : NT;
+      const int t0 = (NW == 1 || tid < TDW * 64) ? tid : -1;
+      for (int idx = t0; idx >= 0 && idx < C * DK; idx += nthr) {
+        const int r = idx / DK, pc = idx % DK;
+        sQ[r * LDK + pc] = from_f<T>(to_f(sQ[r * LDK + pc]) *
+                                     sFac[(Sh::F_ES + r / 16) * DK + M::phi_inv(pc)]);
       }
     }
     lds_barrier();
@@ -631,34 +669,30 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
         for (int R = 0; R < 4; ++R) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            sWm[(16 * R + 4 * g4 + i) * LDK + 16 * ct + m16] = from_f<T>(-X[t][R][i]);
+            sWm[(16 * R + 4 * g4 + i) * LDK + M::phi(16 * ct + m16)] = from_f<T>(-X[t][R][i]);
         }
       }
 #pragma unroll
       for (int R = 0; R < 4; ++R) U[R] = (RS == 1 || whw == 0) ? X[NE][R] : f4{0.f, 0.f, 0.f, 0.f};
     }
+    if (wave == TDW && !block_path) o_partial();
     lds_barrier();
     fresh_prep();
 
     // ---- (g) state-dependent part (this wave's 16 columns and key rows)
-    typename M::frag sb[KSH];
+    if (block_path) o_partial();
+    // partial sums over this wave's key rows: U = U~ - W S
+    {
+      typename M::frag wf[4][KSH];
 #pragma unroll
-    for (int s = 0; s < KSH; ++s) sb[s] = M::from_acc(S, s);
-
-    // partial sums over this wave's key rows: U += -W S, Q exp(G) S
-    f4 O[4];
+      for (int R = 0; R < 4; ++R)
 #pragma unroll
-    for (int R = 0; R < 4; ++R) {
-      f4 acc = U[R];
-      f4 oacc = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < KSH; ++s) wf[R][s] = M::load_phi(sWm, LDK, 16 * R + m16, whw * KSH + s, g4);
 #pragma unroll
-      for (int s = 0; s < KSH; ++s) {
-        const int sg = whw * KSH + s;  // K step over all key rows
-        acc = M::mma(M::load_perm(sWm, LDK, 16 * R + m16, sg, g4), sb[s], acc);
-        oacc = M::mma(M::load_perm(sQ, LDK, 16 * R + m16, sg, g4), sb[s], oacc);
+      for (int R = 0; R < 4; ++R) {
+#pragma unroll
+        for (int s = 0; s < KSH; ++s) U[R] = M::mma(wf[R][s], sb[s], U[R]);
       }
-      U[R] = acc;
-      O[R] = oacc;
     }
     // output row tiles finished by this wave: all (no split) or {0,3} / {1,2}
     const int oR0 = RS == 1 ? 0 : (whw == 0 ? 0 : 1);
@@ -691,7 +725,7 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
       if (RS > 1 && R != oR0 && R != oR1) continue;
 #pragma unroll
       for (int s = 0; s < causal_steps<KS>(R); ++s)
-        O[R] = M::mma(M::load_perm(sP, LDT, 16 * R + m16, s, g4), ub[s], O[R]);
+        O[R] = M::mma(M::load_phi(sP, LDT, 16 * R + m16, s, g4), ub[s], O[R]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         sO[(16 * R + 4 * g4 + i) * OP + 16 * wct + m16] = from_f<T>(O[R][i]);
@@ -706,7 +740,7 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
       f4 acc = S[mt] * gam;
 #pragma unroll
       for (int s = 0; s < C / KS; ++s)
-        acc = M::mma(M::load_perm_t(sKt, LDT, 16 * mg + m16, s, g4), ub[s], acc);
+        acc = M::mma(M::load_phi_t(sKt, LDT, 16 * mg + m16, s, g4), ub[s], acc);
       S[mt] = acc;
     }
   }
@@ -735,7 +769,7 @@ static hipError_t launch_chunk(const ChunkArgs& a) {
                      dim3(ChunkShape<T, DK, NV>::NT), 0,
                      (hipStream_t)a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
                      (const T*)a.g, (const T*)a.b, (const T*)a.w, a.s0, (T*)a.o, a.sN,
-                     a.cu_seqlens, a.T, a.H, a.d_v, nslices);
+                     a.cu_seqlens, a.T, a.H, a.d_v, nslices, a.N * a.H);
   return hipGetLastError();
 }
 

@@ -73,6 +73,17 @@ __device__ __forceinline__ void store8(float* p, const float* f) {
   reinterpret_cast<f4*>(p)[1] = f4{f[4], f[5], f[6], f[7]};
 }
 
+// Store 8 consecutive logical K-values k0..k0+7 (k0 % 8 == 0) into a phi-ordered row:
+// bf16 rows are phi-permuted (two 8-byte pieces), fp32 rows are in logical order.
+__device__ __forceinline__ void store8_phi(bf16* row, int k0, const float* f) {
+  const int p0 = (k0 & ~31) | (((k0 >> 2) & 3) << 3) | (((k0 >> 4) & 1) << 2);
+  *reinterpret_cast<bf16x4*>(row + p0) = bf16x4{static_cast<bf16>(f[0]), static_cast<bf16>(f[1]),
+                                                static_cast<bf16>(f[2]), static_cast<bf16>(f[3])};
+  *reinterpret_cast<bf16x4*>(row + p0 + 8) = bf16x4{static_cast<bf16>(f[4]), static_cast<bf16>(f[5]),
+                                                    static_cast<bf16>(f[6]), static_cast<bf16>(f[7])};
+}
+__device__ __forceinline__ void store8_phi(float* row, int k0, const float* f) { store8(row + k0, f); }
+
 // ---------------------------------------------------------------- MFMA traits
 template <typename T> struct Mma;
 
@@ -102,6 +113,21 @@ template <> struct Mma<bf16> {
     bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
+  // Storage permutation of a K axis inside each 32-wide block: logical
+  // k = 32s + 16h + 4g + i is stored at 32s + 8g + 4h + i, so the 8 K-values of a permuted
+  // fragment (K step s, lane group g) are 8 contiguous elements: one 16-byte LDS read.
+  static __device__ __forceinline__ int phi(int k) {
+    return (k & ~31) | (((k >> 2) & 3) << 3) | (((k >> 4) & 1) << 2) | (k & 3);
+  }
+  static __device__ __forceinline__ int phi_inv(int p) {
+    return (p & ~31) | (((p >> 2) & 1) << 4) | (((p >> 3) & 3) << 2) | (p & 3);
+  }
+  // Permuted fragment from a phi-stored [row][k] array.
+  static __device__ __forceinline__ frag load_phi(const bf16* base, int ld, int row, int s, int g) {
+    return *reinterpret_cast<const bf16x8*>(base + row * ld + 32 * s + 8 * g);
+  }
+  // Same from a token-transposed (swizzled) array stored in phi order along the tokens.
+  static __device__ __forceinline__ frag load_phi_t(const bf16* base, int ld, int c, int s, int g);
   // load_perm from a token-transposed (swizzled) array; `c` is the logical row.
   static __device__ __forceinline__ frag load_perm_t(const bf16* base, int ld, int c, int s,
                                                       int g);
@@ -145,6 +171,14 @@ template <> struct Mma<float> {
   }
   static __device__ __forceinline__ frag load_perm_t(const float* base, int ld, int c, int s,
                                                       int g);
+  static __device__ __forceinline__ int phi(int k) { return k; }
+  static __device__ __forceinline__ int phi_inv(int p) { return p; }
+  static __device__ __forceinline__ frag load_phi(const float* base, int ld, int row, int s, int g) {
+    return load_perm(base, ld, row, s, g);
+  }
+  static __device__ __forceinline__ frag load_phi_t(const float* base, int ld, int c, int s, int g) {
+    return load_perm_t(base, ld, c, s, g);
+  }
   static __device__ __forceinline__ int perm_k(int s, int g, int) {
     return 16 * (s >> 2) + 4 * g + (s & 3);
   }
@@ -253,6 +287,11 @@ __device__ __forceinline__ Mma<bf16>::frag Mma<bf16>::load_perm_t(const bf16* ba
   const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + (((8 * s + g) ^ sw) << 2));
   const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + (((8 * s + 4 + g) ^ sw) << 2));
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+__device__ __forceinline__ Mma<bf16>::frag Mma<bf16>::load_phi_t(const bf16* base, int ld, int c,
+                                                                 int s, int g) {
+  // groups (8s + 2g, 8s + 2g + 1) stay adjacent under the even XOR swizzle
+  return *reinterpret_cast<const bf16x8*>(base + c * ld + (((8 * s + 2 * g) ^ tswz(c)) << 2));
 }
 __device__ __forceinline__ float Mma<float>::load_perm_t(const float* base, int ld, int c, int s,
                                                          int g) {
