@@ -93,7 +93,12 @@ struct ChunkShape {
   static constexpr int OFF_TB = OFF_A + SZ_P;      // diagonal blocks of (I+A)^-1
   static constexpr int OFF_FAC = OFF_TB + SZ_P;
   static constexpr int SZ_FAC = NF * DK * 4;
-  static constexpr int OFF_FLAG = OFF_FAC + SZ_FAC;
+  // fp32 copy of the four diagonal 16x16 blocks of -A for the triangular inverse (the
+  // fp32 path reads them from the -A buffer itself)
+  static constexpr int LDD = 20;  // pitch (floats)
+  static constexpr int SZ_AD = sizeof(T) == 4 ? 0 : 4 * 16 * LDD * 4;
+  static constexpr int OFF_AD = OFF_FAC + SZ_FAC;
+  static constexpr int OFF_FLAG = OFF_AD + SZ_AD;
   static constexpr int LDS_BYTES = OFF_FLAG + 16;
   // cumsum scratch [TG][DK] fp32 lives in the P and -A buffers (dead until (d))
   static constexpr int OFF_TOT = OFF_P;
@@ -128,7 +133,8 @@ __device__ __forceinline__ constexpr int pair_I(int p) { return p - (pair_R(p) *
 // (E exp(G) | Q exp(G)) rows and K exp(-G) rows, K = d_k.
 template <typename T, int DK, int LDK, int LDT, int MASK_A, int MASK_P>
 __device__ __forceinline__ void ap_tiles(const T* sE, const T* sQ, const T* sK, T* sAm, T* sP,
-                                         int m16, int g4) {
+                                         float* sAd, int m16, int g4) {
+  const int lane = 16 * g4 + m16;
   using M = Mma<T>;
   constexpr int MASK = MASK_A | MASK_P;
   f4 accA[10], accP[10];
@@ -155,17 +161,25 @@ __device__ __forceinline__ void ap_tiles(const T* sE, const T* sQ, const T* sK, 
 #pragma unroll
   for (int p = 0; p < 10; ++p) {
     const int R = pair_R(p), I = pair_I(p);
+    if ((MASK_A >> p) & 1) {
+      f4 val;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * g4 + i, c = m16;
-      if ((MASK_A >> p) & 1) {
-        const float val = (I < R || c < r) ? -accA[p][i] : 0.f;
-        sAm[(16 * R + r) * LDT + 16 * I + c] = from_f<T>(val);
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g4 + i, c = m16;
+        val[i] = (I < R || c < r) ? -accA[p][i] : 0.f;
+        if (sizeof(T) == 2 && I == R) sAd[R * 16 * 20 + r * 20 + c] = val[i];
       }
-      if ((MASK_P >> p) & 1) {
-        const float val = (I < R || c <= r) ? accP[p][i] : 0.f;
-        sP[(16 * R + r) * LDT + Mma<T>::phi(16 * I + c)] = from_f<T>(val);
+      store_tile_pairs(sAm + (16 * R) * LDT + 16 * I, LDT, lane, val, [](int c) { return c; });
+    }
+    if ((MASK_P >> p) & 1) {
+      f4 val;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g4 + i, c = m16;
+        val[i] = (I < R || c <= r) ? accP[p][i] : 0.f;
       }
+      store_tile_pairs(sP + (16 * R) * LDT, LDT, lane, val,
+                       [&](int c) { return Mma<T>::phi(16 * I + c); });
     }
   }
 }
@@ -178,6 +192,14 @@ template <typename T, int N> struct RunBuf {
   __device__ __forceinline__ void put(int j, float x) { v[j] = x; }
   template <bool PHI = false>
   __device__ __forceinline__ void store(T* row, int c, int r0) const { store_run_t<N>(row, c, r0, v); }
+  template <bool PHI = false>
+  __device__ __forceinline__ void store_sw(T* row, int sw, int r0) const {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int r = PHI ? Mma<T>::phi(r0 + j) : r0 + j;
+      row[((((r >> 2) ^ sw)) << 2) | (r & 3)] = v[j];
+    }
+  }
 };
 template <int N> struct RunBuf<bf16, N> {
   static_assert(N == 1 || N % 2 == 0, "run length");
@@ -196,8 +218,14 @@ template <int N> struct RunBuf<bf16, N> {
   // PHI: tokens stored in the phi order of Mma<bf16> (runs of 2 and aligned runs of 4 stay
   // contiguous under it).
   template <bool PHI = false>
-  __device__ __forceinline__ void store(bf16* row, int c, int r0) const {
-    auto pos = [&](int r) { return tcol(c, PHI ? Mma<bf16>::phi(r) : r); };
+  __device__ __forceinline__ void store(bf16* row, int c, int r0) const { store_sw<PHI>(row, tswz(c), r0); }
+  // sw: the token-group swizzle of the row (shared by the 8 channels of a thread)
+  template <bool PHI = false>
+  __device__ __forceinline__ void store_sw(bf16* row, int sw, int r0) const {
+    auto pos = [&](int r) {
+      const int rr = PHI ? Mma<bf16>::phi(r) : r;
+      return ((((rr >> 2) ^ sw)) << 2) | (rr & 3);
+    };
     if constexpr (N == 1) {
       row[pos(r0)] = static_cast<bf16>(pend);
     } else if constexpr (N == 2) {
@@ -235,6 +263,11 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
   float* sFac = reinterpret_cast<float*>(smem + Sh::OFF_FAC);
   float* sTot = reinterpret_cast<float*>(smem + Sh::OFF_TOT);
   int* sFlag = reinterpret_cast<int*>(smem + Sh::OFF_FLAG);
+  // diagonal blocks of -A in fp32: block jb, row r, column i at sAd[jb*ADB + r*ADP + i]
+  constexpr int ADB = sizeof(T) == 4 ? 16 * LDT + 16 : 16 * Sh::LDD;
+  constexpr int ADP = sizeof(T) == 4 ? LDT : Sh::LDD;
+  float* sAd = sizeof(T) == 4 ? reinterpret_cast<float*>(smem + Sh::OFF_A)
+                              : reinterpret_cast<float*>(smem + Sh::OFF_AD);
 
   constexpr int RS = Sh::RS, NWC = Sh::NWC;
   constexpr int NMS = NCT / RS;       // state row tiles per wave
@@ -349,20 +382,31 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
     }
   }
 
-  // Output tiles are staged in LDS (in the Z^T buffer, dead after (f)) and copied to HBM
-  // with 16-byte stores at the start of the next chunk, so the wait for the next prefetch
-  // (vmcnt counts stores too) never waits for freshly issued stores.
+  // Output tiles are staged in LDS (in the Z^T buffer, dead after (f)). The next chunk
+  // reads the staging into registers in (a) and issues the 16-byte global stores at the end
+  // of (c), just before its prefetch loads: the wait for those loads (vmcnt counts stores
+  // too) then comes one full chunk after the stores.
   constexpr int OP = (64 * (NV + Sh::PAD) <= NV * LDT) ? NV + Sh::PAD : NV;  // staging pitch
-  constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  constexpr int EPC = 16 / (int)sizeof(T);        // elements per 16-byte chunk
+  constexpr int CPT = C * NV / EPC / NT;          // chunks per thread
+  static_assert(CPT * NT * EPC == C * NV, "output staging mapping");
   T* const sO = sZt;
   int prev_c0 = 0, prev_n = 0;
-  auto copy_out = [&](int oc0, int on) {
+  uint4 ostage[CPT];
+  auto stage_load = [&]() {
 #pragma unroll
-    for (int idx = tid; idx < C * NV / EPC; idx += NT) {
+    for (int j = 0; j < CPT; ++j) {
+      const int idx = tid + j * NT;
       const int r = idx / (NV / EPC), cc = idx % (NV / EPC);
-      if (r < on)
-        *reinterpret_cast<uint4*>(ob + (long)(oc0 + r) * vstride + cc * EPC) =
-            *reinterpret_cast<const uint4*>(sO + r * OP + cc * EPC);
+      ostage[j] = *reinterpret_cast<const uint4*>(sO + r * OP + cc * EPC);
+    }
+  };
+  auto stage_store = [&](int oc0, int on) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int idx = tid + j * NT;
+      const int r = idx / (NV / EPC), cc = idx % (NV / EPC);
+      if (r < on) *reinterpret_cast<uint4*>(ob + (long)(oc0 + r) * vstride + cc * EPC) = ostage[j];
     }
   };
 
@@ -376,7 +420,7 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
     fresh_prep();
 
     // ---- (a) previous chunk's output to HBM; per-thread totals of log2-decay
-    if (ci > 0) copy_out(prev_c0, prev_n);
+    if (ci > 0) stage_load();
     {
       float tot8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -432,25 +476,8 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
 #pragma unroll
       for (int i = 0; i < 8; ++i) run[i] = sTot[tg * DK + cg * 8 + i];
       RunBuf<T, Sh::TPT> ev[8], kv[8];  // E exp(G) and K exp(Glast - G), per channel
-      float fA[8], fB[8], sub[8];
-      if (!block_path) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          fA[i] = 1.f;
-          fB[i] = sFac[Sh::F_GAM * DK + cg * 8 + i];
-          sub[i] = 0.f;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          fA[i] = sFac[(Sh::F_ES + blk) * DK + cg * 8 + i];
-          fB[i] = sFac[(Sh::F_KNB + blk) * DK + cg * 8 + i];
-          sub[i] = sFac[(Sh::F_GS + blk) * DK + cg * 8 + i];
-        }
-      }
-      // chunk path: x = G (chunk-relative); block path: x = G - Gs(block)
-#pragma unroll
-      for (int j = 0; j < Sh::TPT; ++j) {
+      // one token of this thread: x = G (chunk path) or G - Gs(block) (block path)
+      auto token = [&](int j, const float* sub, const float* fA, const float* fB, bool scaled) {
         const int r = tg * Sh::TPT + j;
         float fg[8], fq[8], fk[8], fb[8], e1[8], q1[8], k1[8];
         rg[j].to_float(fg);
@@ -460,23 +487,40 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           run[i] += fg[i] * kLog2e;
-          const float x = run[i] - sub[i];
+          const float x = scaled ? run[i] - sub[i] : run[i];
           const float xe = fast_exp2(x), xk = fast_exp2(-x);
           e1[i] = fb[i] * fk[i] * xe;
           q1[i] = fq[i] * xe;
           k1[i] = fk[i] * xk;
-          ev[i].put(j, e1[i] * fA[i]);
+          ev[i].put(j, scaled ? e1[i] * fA[i] : e1[i]);
           kv[i].put(j, k1[i] * fB[i]);
         }
         store8_phi(sE + r * LDK, cg * 8, e1);
         store8_phi(sQ + r * LDK, cg * 8, q1);
         store8_phi(sK + r * LDK, cg * 8, k1);
+      };
+      if (!block_path) {
+        float gam[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) gam[i] = sFac[Sh::F_GAM * DK + cg * 8 + i];
+#pragma unroll
+        for (int j = 0; j < Sh::TPT; ++j) token(j, nullptr, nullptr, gam, false);
+      } else {
+        float fA[8], fB[8], sub[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          fA[i] = sFac[(Sh::F_ES + blk) * DK + cg * 8 + i];
+          fB[i] = sFac[(Sh::F_KNB + blk) * DK + cg * 8 + i];
+          sub[i] = sFac[(Sh::F_GS + blk) * DK + cg * 8 + i];
+        }
+#pragma unroll
+        for (int j = 0; j < Sh::TPT; ++j) token(j, sub, fA, fB, true);
       }
+      const int sw = tswz(cg * 8);  // same for the thread's 8 channels
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int c = cg * 8 + i;
-        ev[i].store(sEt + c * LDT, c, tg * Sh::TPT);
-        kv[i].template store<true>(sKt + c * LDT, c, tg * Sh::TPT);
+        ev[i].store_sw(sEt + (cg * 8 + i) * LDT, sw, tg * Sh::TPT);
+        kv[i].template store_sw<true>(sKt + (cg * 8 + i) * LDT, sw, tg * Sh::TPT);
       }
       RunBuf<T, Sh::VTPT> zv[8];
 #pragma unroll
@@ -487,12 +531,11 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
 #pragma unroll
         for (int i = 0; i < 8; ++i) zv[i].put(j, fv[i] * fw[i]);
       }
+      const int zsw = tswz(vcg * 8);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int c = vcg * 8 + i;
-        zv[i].store(sZt + c * LDT, c, vtg * Sh::VTPT);
-      }
+      for (int i = 0; i < 8; ++i) zv[i].store_sw(sZt + (vcg * 8 + i) * LDT, zsw, vtg * Sh::VTPT);
     }
+    if (ci > 0) stage_store(prev_c0, prev_n);
     // prefetch the next chunk; the loads stay in flight until (a) of the next chunk
     if (ci + 1 < nchunks) {
       const int nn = len - c0 - C;
@@ -501,34 +544,89 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
     lds_barrier();
     fresh_prep();
 
-    // ---- (d) A (stored negated) and P
+    // ---- (d) A (stored negated) and P, and the diagonal blocks of (I + A)^{-1}.
+    // Chunk path: the last wave (TDW) forms the four diagonal A tiles itself and goes
+    // straight on to their inverses (fp32 forward substitution, one block per 16-lane group,
+    // one column per lane), with no barrier in between; the other waves form the other 16
+    // tiles and then their partial Q exp(G) S products.
+    constexpr int TDW = NW - 1;  // wave that forms the diagonal inverse blocks
+    typename M::frag sb[KSH];    // this wave's state rows as B operands
+#pragma unroll
+    for (int s = 0; s < KSH; ++s) sb[s] = M::from_acc(S, s);
+    f4 O[4];
+    auto o_partial = [&]() {  // O = Q exp(G) S over this wave's key rows
+      typename M::frag qf[4][KSH];
+#pragma unroll
+      for (int R = 0; R < 4; ++R)
+#pragma unroll
+        for (int s = 0; s < KSH; ++s) qf[R][s] = M::load_phi(sQ, LDK, 16 * R + m16, whw * KSH + s, g4);
+#pragma unroll
+      for (int R = 0; R < 4; ++R) {
+        O[R] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KSH; ++s) O[R] = M::mma(qf[R][s], sb[s], O[R]);
+      }
+    };
+    auto tdiag = [&]() {
+      const int jb = g4, c = m16;
+      const float* Ab = sAd + jb * ADB;
+      float am[16][16];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) {
+#pragma unroll
+        for (int i4 = 0; i4 < r; i4 += 4) {
+          const f4 v = *reinterpret_cast<const f4*>(Ab + r * ADP + i4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) am[r][i4 + j] = v[j];
+        }
+      }
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+#pragma unroll
+        for (int r = i + 1; r < 16; ++r) x[r] += am[r][i] * x[i];  // am holds -A
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sT[(16 * jb + r) * LDT + 16 * jb + c] = from_f<T>(x[r]);
+    };
+    // pair bits: (0,0)=0 (1,0)=1 (1,1)=2 (2,0)=3 (2,1)=4 (2,2)=5 (3,0)=6 (3,1)=7 (3,2)=8 (3,3)=9
+    constexpr int DIAG = 0x225;     // (0,0) (1,1) (2,2) (3,3)
+    constexpr int OFFD = 0x1DA;     // off-diagonal pairs
     if (!block_path) {
-      // pair masks: rows {0,3} = 0x3C1, rows {1,2} = 0x3E
-      if constexpr (NW >= 8) {
-        switch (wave) {
-          case 0: ap_tiles<T, DK, LDK, LDT, 0x0C0, 0>(sE, sQ, sK, sAm, sP, m16, g4); break;
-          case 1: ap_tiles<T, DK, LDK, LDT, 0, 0x0C0>(sE, sQ, sK, sAm, sP, m16, g4); break;
-          case 2: ap_tiles<T, DK, LDK, LDT, 0x301, 0>(sE, sQ, sK, sAm, sP, m16, g4); break;
-          case 3: ap_tiles<T, DK, LDK, LDT, 0, 0x301>(sE, sQ, sK, sAm, sP, m16, g4); break;
-          case 4: ap_tiles<T, DK, LDK, LDT, 0x038, 0>(sE, sQ, sK, sAm, sP, m16, g4); break;
-          case 5: ap_tiles<T, DK, LDK, LDT, 0, 0x038>(sE, sQ, sK, sAm, sP, m16, g4); break;
-          case 6: ap_tiles<T, DK, LDK, LDT, 0x006, 0>(sE, sQ, sK, sAm, sP, m16, g4); break;
-          case 7: ap_tiles<T, DK, LDK, LDT, 0, 0x006>(sE, sQ, sK, sAm, sP, m16, g4); break;
-          default: break;
+      if (wave == TDW) {
+        if constexpr (NW == 1) {
+          ap_tiles<T, DK, LDK, LDT, 0x3FF, 0x3FF>(sE, sQ, sK, sAm, sP, sAd, m16, g4);
+        } else if constexpr (NW == 2) {
+          ap_tiles<T, DK, LDK, LDT, DIAG, 0x3C1>(sE, sQ, sK, sAm, sP, sAd, m16, g4);
+        } else {
+          ap_tiles<T, DK, LDK, LDT, DIAG, 0>(sE, sQ, sK, sAm, sP, sAd, m16, g4);
         }
-      } else if constexpr (NW >= 4) {
-        switch (wave) {
-          case 0: ap_tiles<T, DK, LDK, LDT, 0x3C1, 0>(sE, sQ, sK, sAm, sP, m16, g4); break;
-          case 1: ap_tiles<T, DK, LDK, LDT, 0, 0x3C1>(sE, sQ, sK, sAm, sP, m16, g4); break;
-          case 2: ap_tiles<T, DK, LDK, LDT, 0x03E, 0>(sE, sQ, sK, sAm, sP, m16, g4); break;
-          case 3: ap_tiles<T, DK, LDK, LDT, 0, 0x03E>(sE, sQ, sK, sAm, sP, m16, g4); break;
-          default: break;
-        }
-      } else if constexpr (NW == 2) {
-        if (wave == 0) ap_tiles<T, DK, LDK, LDT, 0x3C1, 0x3C1>(sE, sQ, sK, sAm, sP, m16, g4);
-        else ap_tiles<T, DK, LDK, LDT, 0x03E, 0x03E>(sE, sQ, sK, sAm, sP, m16, g4);
+        tdiag();  // reads only what this wave just wrote: no barrier needed
       } else {
-        ap_tiles<T, DK, LDK, LDT, 0x3FF, 0x3FF>(sE, sQ, sK, sAm, sP, m16, g4);
+        if constexpr (NW >= 8) {
+          switch (wave) {
+            case 0: ap_tiles<T, DK, LDK, LDT, 0x0C0, 0>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
+            case 1: ap_tiles<T, DK, LDK, LDT, 0x118, 0>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
+            case 2: ap_tiles<T, DK, LDK, LDT, 0x002, 0x001>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
+            case 3: ap_tiles<T, DK, LDK, LDT, 0, 0x0C0>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
+            case 4: ap_tiles<T, DK, LDK, LDT, 0, 0x300>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
+            case 5: ap_tiles<T, DK, LDK, LDT, 0, 0x038>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
+            case 6: ap_tiles<T, DK, LDK, LDT, 0, 0x006>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
+            default: break;
+          }
+        } else if constexpr (NW >= 4) {
+          switch (wave) {
+            case 0: ap_tiles<T, DK, LDK, LDT, OFFD, 0>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
+            case 1: ap_tiles<T, DK, LDK, LDT, 0, 0x3C1>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
+            case 2: ap_tiles<T, DK, LDK, LDT, 0, 0x03E>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
+            default: break;
+          }
+        } else if constexpr (NW == 2) {
+          ap_tiles<T, DK, LDK, LDT, OFFD, 0x03E>(sE, sQ, sK, sAm, sP, sAd, m16, g4);
+        }
+        o_partial();
       }
     } else {
       // block-referenced tiles: rows of block R against Kn of block I; off-diagonal
@@ -555,14 +653,19 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
           const typename M::frag b = M::load_scaled(sK, LDK, 16 * I + m16, kk, fb);
           acc = M::mma(a, b, acc);
         }
+        f4 val;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * g4 + i, c = m16;
           const bool keep = (I < R) || (isP ? (c <= r) : (c < r));
-          const float val = keep ? (isP ? acc[i] : -acc[i]) : 0.f;
-          if (isP) sP[(16 * R + r) * LDT + M::phi(16 * I + c)] = from_f<T>(val);
-          else sAm[(16 * R + r) * LDT + 16 * I + c] = from_f<T>(val);
+          val[i] = keep ? (isP ? acc[i] : -acc[i]) : 0.f;
+          if (!isP && sizeof(T) == 2 && I == R) sAd[R * ADB + r * ADP + c] = val[i];
         }
+        if (isP)
+          store_tile_pairs(sP + (16 * R) * LDT, LDT, lane, val,
+                           [&](int c) { return M::phi(16 * I + c); });
+        else
+          store_tile_pairs(sAm + (16 * R) * LDT + 16 * I, LDT, lane, val, [](int c) { return c; });
       }
     }
     // upper tiles (0,1) and (2,3) of P are read (as zeros) by the 32-wide K steps of P U
@@ -572,53 +675,9 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
     }
     lds_barrier();
     fresh_prep();
-
-    // ---- (e) diagonal 16x16 blocks of (I + A)^{-1} by forward substitution (fp32),
-    // one block per 16-lane group of the last wave, one column per lane. Meanwhile the
-    // other waves form their partial Q exp(G) S products (chunk path) or rescale Qa to
-    // Q exp(G) (block path).
-    constexpr int TDW = NW - 1;  // wave that forms the diagonal inverse blocks
-    typename M::frag sb[KSH];    // this wave's state rows as B operands
-#pragma unroll
-    for (int s = 0; s < KSH; ++s) sb[s] = M::from_acc(S, s);
-    f4 O[4];
-    auto o_partial = [&]() {  // O = Q exp(G) S over this wave's key rows
-      typename M::frag qf[4][KSH];
-#pragma unroll
-      for (int R = 0; R < 4; ++R)
-#pragma unroll
-        for (int s = 0; s < KSH; ++s) qf[R][s] = M::load_phi(sQ, LDK, 16 * R + m16, whw * KSH + s, g4);
-#pragma unroll
-      for (int R = 0; R < 4; ++R) {
-        O[R] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KSH; ++s) O[R] = M::mma(qf[R][s], sb[s], O[R]);
-      }
-    };
-    if (wave == TDW) {
-      const int jb = g4, c = m16;
-      const T* Ab = sAm + (16 * jb) * LDT + 16 * jb;
-      float am[16][16];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) {
-#pragma unroll
-        for (int i = 0; i < r; ++i) am[r][i] = to_f(Ab[r * LDT + i]);
-      }
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-#pragma unroll
-        for (int r = i + 1; r < 16; ++r) x[r] += am[r][i] * x[i];  // am holds -A
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sT[(16 * jb + r) * LDT + 16 * jb + c] = from_f<T>(x[r]);
-    } else if (!block_path) {
-      o_partial();
-    }
     if (block_path) {
-      // threads outside the last wave (all threads when there is a single wave)
+      // block path: inverse blocks by the last wave; the others rescale Qa to Q exp(G)
+      if (wave == TDW) tdiag();
       const int nthr = NW > 1 ? NT - 64 : NT;
       const int t0 = (NW == 1 || tid < TDW * 64) ? tid : -1;
       for (int idx = t0; idx >= 0 && idx < C * DK; idx += nthr) {
@@ -626,9 +685,9 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
         sQ[r * LDK + pc] = from_f<T>(to_f(sQ[r * LDK + pc]) *
                                      sFac[(Sh::F_ES + r / 16) * DK + M::phi_inv(pc)]);
       }
+      lds_barrier();
+      fresh_prep();
     }
-    lds_barrier();
-    fresh_prep();
 
     // ---- (f) [W | U~] = (I + A)^{-1} [E exp(G) | Z] by block forward substitution:
     //   X_R = T_RR (RHS_R - sum_{J<R} A_RJ X_J)
@@ -637,7 +696,17 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
     f4 U[4];
     {
       constexpr int NE = (NCT + NW - 1) / NW;  // key-channel tiles per wave (max)
+      using F16 = Frag16<T>;
+      // the A_RJ (J < R) and T_RR fragments are the same for every tile of this wave
+      typename F16::type fa[4][4];
+#pragma unroll
+      for (int R = 0; R < 4; ++R) {
+#pragma unroll
+        for (int J = 0; J < R; ++J) fa[R][J] = F16::load(sAm + (16 * R + m16) * LDT + 16 * J + 4 * g4);
+        fa[R][R] = F16::load(sT + (16 * R + m16) * LDT + 16 * R + 4 * g4);
+      }
       f4 X[NE + 1][4];
+      typename F16::type Xb[NE + 1][4];  // X as B fragments, converted once
 #pragma unroll
       for (int R = 0; R < 4; ++R) {
 #pragma unroll
@@ -654,9 +723,9 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
           const T* src = (isZ ? sZt : sEt) + crow * LDT;
           f4 acc = load4f(src + tcol(crow, 16 * R + 4 * g4));  // RHS rows 16R+4g4+i, col m16
 #pragma unroll
-          for (int J = 0; J < R; ++J)
-            acc = mma16_acc(sAm + (16 * R + m16) * LDT + 16 * J, g4, X[t][J], acc);
-          X[t][R] = mma16_acc(sT + (16 * R + m16) * LDT + 16 * R, g4, acc, f4{0.f, 0.f, 0.f, 0.f});
+          for (int J = 0; J < R; ++J) acc = mma16_frag(fa[R][J], Xb[t][J], acc);
+          X[t][R] = mma16_frag(fa[R][R], F16::from_acc(acc), f4{0.f, 0.f, 0.f, 0.f});
+          Xb[t][R] = F16::from_acc(X[t][R]);
         }
       }
 #pragma unroll
@@ -666,11 +735,9 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
           if (ct >= NCT) continue;
         }
 #pragma unroll
-        for (int R = 0; R < 4; ++R) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            sWm[(16 * R + 4 * g4 + i) * LDK + M::phi(16 * ct + m16)] = from_f<T>(-X[t][R][i]);
-        }
+        for (int R = 0; R < 4; ++R)
+          store_tile_pairs(sWm + (16 * R) * LDK, LDK, lane, -X[t][R],
+                           [&](int c) { return M::phi(16 * ct + c); });
       }
 #pragma unroll
       for (int R = 0; R < 4; ++R) U[R] = (RS == 1 || whw == 0) ? X[NE][R] : f4{0.f, 0.f, 0.f, 0.f};
@@ -695,8 +762,6 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
       }
     }
     // output row tiles finished by this wave: all (no split) or {0,3} / {1,2}
-    const int oR0 = RS == 1 ? 0 : (whw == 0 ? 0 : 1);
-    const int oR1 = RS == 1 ? 3 : (whw == 0 ? 3 : 2);
     if constexpr (RS > 1) {
       // exchange partial sums with the partner wave (same columns, other key rows)
       f4* xu_mine = reinterpret_cast<f4*>((wave < 4 ? smem + Sh::OFF_K : smem + Sh::OFF_ET)) +
@@ -709,26 +774,34 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
 #pragma unroll
       for (int R = 0; R < 4; ++R) xu_mine[R * 64 + lane] = U[R];
       // the partner finishes the other two output row tiles
-      xo_mine[lane] = whw == 0 ? O[1] : O[0];
-      xo_mine[64 + lane] = whw == 0 ? O[2] : O[3];
+      if (whw == 0) {
+        xo_mine[lane] = O[1];
+        xo_mine[64 + lane] = O[2];
+      } else {
+        xo_mine[lane] = O[0];
+        xo_mine[64 + lane] = O[3];
+      }
       lds_barrier();
 #pragma unroll
       for (int R = 0; R < 4; ++R) U[R] += xu_part[R * 64 + lane];
-      O[oR0] += xo_part[lane];
-      O[oR1] += xo_part[64 + lane];
+      if (whw == 0) {
+        O[0] += xo_part[lane];
+        O[3] += xo_part[64 + lane];
+      } else {
+        O[1] += xo_part[lane];
+        O[2] += xo_part[64 + lane];
+      }
     }
     typename M::frag ub[C / KS];
 #pragma unroll
     for (int s = 0; s < C / KS; ++s) ub[s] = M::from_acc(U, s);
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
-      if (RS > 1 && R != oR0 && R != oR1) continue;
+      if (RS > 1 && (whw == 0 ? (R == 1 || R == 2) : (R == 0 || R == 3))) continue;
 #pragma unroll
       for (int s = 0; s < causal_steps<KS>(R); ++s)
         O[R] = M::mma(M::load_phi(sP, LDT, 16 * R + m16, s, g4), ub[s], O[R]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sO[(16 * R + 4 * g4 + i) * OP + 16 * wct + m16] = from_f<T>(O[R][i]);
+      store_tile_pairs(sO + (16 * R) * OP + 16 * wct, OP, lane, O[R], [](int c) { return c; });
     }
     prev_c0 = c0;
     prev_n = nvalid;
@@ -747,7 +820,9 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
 
   if (nchunks > 0) {
     lds_barrier();
-    copy_out(prev_c0, prev_n);
+    fresh_lane();
+    stage_load();
+    stage_store(prev_c0, prev_n);
   }
   if (sN != nullptr) {
 #pragma unroll

@@ -207,6 +207,65 @@ __device__ __forceinline__ f4 mma16_acc(const float* arow, int g, f4 bacc, f4 c)
   return c;
 }
 
+// Two floats -> packed bf16 pair (RNE), one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v{a, b}), bf16x2));
+}
+
+// Store a 16x16 D tile (lane: column l%16, rows 4g..4g+3) into a row-major [row][col]
+// array with 2-element stores: neighbouring lanes swap two rows so that each lane writes
+// (row, cols 2j..2j+1) pairs; no two lanes share an LDS dword. `colmap` maps the tile's
+// pair-aligned logical column to its stored column (identity or a permutation that keeps
+// pairs (2j, 2j+1) adjacent and in order).
+template <typename T, typename F>
+__device__ __forceinline__ void store_tile_pairs(T* base, int ld, int lane, f4 v, F colmap) {
+  const int n = lane & 15, g = lane >> 4;
+  const bool odd = n & 1;
+  // even lane keeps rows 4g, 4g+1 and receives them from the odd neighbour;
+  // odd lane keeps rows 4g+2, 4g+3 and receives them from the even neighbour
+  const float s0 = odd ? v[0] : v[2], s1 = odd ? v[1] : v[3];
+  const float r0 = __shfl_xor(s0, 1, 64), r1 = __shfl_xor(s1, 1, 64);
+  const int c0 = colmap(n & ~1);
+  const int ra = 4 * g + (odd ? 2 : 0);
+  float a0, a1, b0, b1;  // (row ra: col c0, c0+1), (row ra+1: col c0, c0+1)
+  if (!odd) { a0 = v[0]; a1 = r0; b0 = v[1]; b1 = r1; }
+  else      { a0 = r0; a1 = v[2]; b0 = r1; b1 = v[3]; }
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<uint32_t*>(base + ra * ld + c0) = pack_bf16(a0, a1);
+    *reinterpret_cast<uint32_t*>(base + (ra + 1) * ld + c0) = pack_bf16(b0, b1);
+  } else {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    *reinterpret_cast<f2*>(base + ra * ld + c0) = f2{a0, a1};
+    *reinterpret_cast<f2*>(base + (ra + 1) * ld + c0) = f2{b0, b1};
+  }
+}
+
+// K = 16 product with a preloaded A fragment (row l%16 of A, K-values 4g..4g+3) and B from
+// a D tile, converted here (fp32 path: the 4 K-values as 4 fp32 16x16x4 steps).
+__device__ __forceinline__ f4 mma16_frag(bf16x4 a, bf16x4 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, a),
+                                                   __builtin_bit_cast(short4v, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f4 mma16_frag(f4 a, f4 b, f4 c) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], c, 0, 0, 0);
+  return c;
+}
+template <typename T> struct Frag16;
+template <> struct Frag16<bf16> {
+  typedef bf16x4 type;
+  static __device__ __forceinline__ type load(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
+  static __device__ __forceinline__ type from_acc(f4 v) {
+    return __builtin_bit_cast(bf16x4, make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])));
+  }
+};
+template <> struct Frag16<float> {
+  typedef f4 type;
+  static __device__ __forceinline__ type load(const float* p) { return *reinterpret_cast<const f4*>(p); }
+  static __device__ __forceinline__ type from_acc(f4 v) { return v; }
+};
+
 // Four consecutive elements (a D-tile row group) from LDS, as floats.
 __device__ __forceinline__ f4 load4f(const bf16* p) {
   const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
