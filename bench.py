@@ -92,6 +92,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--path", choices=("auto", "split", "fused"), default="auto",
+                    help="chunk-forward path: two-phase (split), single fused kernel, or auto")
     ap.add_argument("--value-slice", type=int, default=0)
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="before the timed region, run a plain device copy of this many MiB "
@@ -123,8 +125,13 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    ws_bytes = G.workspace_bytes(B, T, H, dk, dv, B)
+    use_split = args.path != "fused" and not args.value_slice and ws_bytes > 0
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if use_split else None
+
     def step():
-        return G.chunk_fwd(*(t[n] for n in NAMES), value_slice=args.value_slice)
+        return G.chunk_fwd(*(t[n] for n in NAMES), value_slice=args.value_slice,
+                           path="split" if use_split else "fused", workspace=ws)
 
     for _ in range(args.warmup):
         step()

@@ -3,9 +3,10 @@
     from gated_delta_rule_36_amd import chunk_fwd, decode_step
 
 `chunk_fwd` runs the chunkwise-parallel forward over whole (optionally packed)
-sequences; `decode_step` advances a pool of recurrent states by one token. Both call
-libgdn2.so, built in-tree by `python -m gated_delta_rule_36_amd.build`.
+sequences, two-phase (with a workspace) or fused; `decode_step` advances a pool of
+recurrent states by one token. Both call libgdn2.so, built in-tree by
+`python -m gated_delta_rule_36_amd.build`.
 """
-from ._lib import Gdn2Error, chunk_fwd, decode_step, lib, lib_path
+from ._lib import Gdn2Error, chunk_fwd, decode_step, lib, lib_path, workspace_bytes
 
-__all__ = ["chunk_fwd", "decode_step", "lib", "lib_path", "Gdn2Error"]
+__all__ = ["chunk_fwd", "decode_step", "workspace_bytes", "lib", "lib_path", "Gdn2Error"]

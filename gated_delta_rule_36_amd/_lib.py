@@ -16,10 +16,12 @@ _lib = None
 
 GDN2_BF16 = 0
 GDN2_F32 = 1
-STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 4: "launch failed"}
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small",
+          4: "launch failed"}
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
+_Z = ctypes.c_size_t
 
 
 class Gdn2Error(RuntimeError):
@@ -42,8 +44,10 @@ def lib():
             raise RuntimeError(f"{_LIB_PATH} is missing: build it first "
                                "(python -m gated_delta_rule_36_amd.build)")
         L = ctypes.CDLL(_LIB_PATH)
-        L.gdn2_chunk_fwd.argtypes = [_P] * 10 + [_I] * 7 + [_P]
+        L.gdn2_chunk_fwd.argtypes = [_P] * 10 + [_I] * 7 + [_P, _Z, _P]
         L.gdn2_chunk_fwd.restype = _I
+        L.gdn2_chunk_fwd_workspace_bytes.argtypes = [_I] * 7
+        L.gdn2_chunk_fwd_workspace_bytes.restype = _Z
         L.gdn2_chunk_fwd_sliced.argtypes = [_P] * 10 + [_I] * 8 + [_P]
         L.gdn2_chunk_fwd_sliced.restype = _I
         L.gdn2_decode_step.argtypes = [_P] * 8 + [_I] * 5 + [_P]
@@ -83,17 +87,28 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def workspace_bytes(B, T, H, dk, dv, N, dtype=torch.bfloat16):
+    """Device workspace the two-phase chunk forward needs (0: that path is not built)."""
+    return int(lib().gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, _dtype_code(dtype)))
+
+
 def chunk_fwd(q, k, v, g, b, w, initial_state=None, cu_seqlens=None,
-              output_final_state=True, value_slice=0):
+              output_final_state=True, path="auto", value_slice=0, workspace=None):
     """Gated Delta Rule-2 chunkwise forward.
 
     q, k, g, b: [B, T, H, d_k]; v, w: [B, T, H, d_v] (bf16 or fp32, same dtype, on a HIP
     device); g = log(alpha) <= 0. initial_state: [N, H, d_k, d_v] fp32 or None.
     cu_seqlens: int32 [N+1] on the device (packed batch, B == 1) or None (N = B).
+    path: "split" (two-phase: parallel chunk factors into a workspace, then the per-sequence
+    recurrence), "fused" (one kernel per sequence, no workspace) or "auto" (split where it
+    is built, i.e. bf16). value_slice selects the fused kernel's value-slice width.
+    workspace: optional uint8 device tensor reused across calls (allocated when None).
     Returns (o [B, T, H, d_v] in the input dtype, final_state [N, H, d_k, d_v] fp32 or None).
     """
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, d_k]")
+    if path not in ("auto", "split", "fused"):
+        raise ValueError(f"unknown path {path!r}")
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
@@ -111,16 +126,30 @@ def chunk_fwd(q, k, v, g, b, w, initial_state=None, cu_seqlens=None,
         N = B
     if initial_state is not None:
         _check("initial_state", initial_state, (N, H, dk, dv), torch.float32, dev)
+    L = lib()
+    need = int(L.gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, code))
+    if path == "split" and need == 0:
+        raise ValueError("the two-phase path is built for bf16 with d_k, d_v in {64, 128}")
+    if value_slice and path == "split":
+        raise ValueError("value_slice applies to the fused path")
+    use_split = need > 0 and path != "fused" and not value_slice
+    if use_split:
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        elif workspace.device != dev:
+            raise ValueError("workspace must be on the inputs' device")
+    else:
+        workspace = None
     o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
     sN = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if output_final_state else None
-    L = lib()
     args = [_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w), _ptr(initial_state), _ptr(o),
             _ptr(sN), _ptr(cu_seqlens), B, T, H, dk, dv, N, code]
     if value_slice:
         st = L.gdn2_chunk_fwd_sliced(*args, int(value_slice), _stream(dev))
         fn = "gdn2_chunk_fwd_sliced"
     else:
-        st = L.gdn2_chunk_fwd(*args, _stream(dev))
+        wsz = workspace.numel() if workspace is not None else 0
+        st = L.gdn2_chunk_fwd(*args, _ptr(workspace), wsz, _stream(dev))
         fn = "gdn2_chunk_fwd"
     if st != 0:
         raise Gdn2Error(fn, st)

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cstdint>
 
@@ -32,10 +33,25 @@ int pick_nv(int dtype, int d_k, int d_v, long chains) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? GDN2_OK : GDN2_LAUNCH_FAILED; }
 
+bool split_built(int dtype, int d_k, int d_v) {
+  return dtype == GDN2_BF16 && width_ok(d_k) && width_ok(d_v);
+}
+
+// Value-slice width of the two-phase path's recurrence kernel: 64 columns per workgroup
+// unless that leaves fewer workgroups than compute units.
+int pick_split_nv(int d_v, long chains) {
+  return chains * (d_v / 64) >= kTargetWorkgroups ? 64 : 32;
+}
+
+size_t workspace_need(bool varlen, int B, int T, int H, int d_k, int d_v, int N) {
+  return gdn2::split_workspace_bytes(varlen, B, T, H, d_k, d_v, N);
+}
+
 int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* log_alpha,
                    const void* b, const void* w, const float* initial_state, void* o,
                    float* final_state, const int32_t* cu_seqlens, int B, int T, int H, int d_k,
-                   int d_v, int N, int dtype, void* hip_stream, int nv) {
+                   int d_v, int N, int dtype, void* workspace, size_t workspace_bytes,
+                   void* hip_stream, int nv) {
   if (dtype != GDN2_BF16 && dtype != GDN2_F32) return GDN2_INVALID_ARGUMENT;
   if (B < 0 || T < 0 || H <= 0 || N < 0 || d_k <= 0 || d_v <= 0) return GDN2_INVALID_ARGUMENT;
   if (cu_seqlens == nullptr) {
@@ -48,24 +64,35 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* log_
   const long tokens = (long)B * T;
   if (tokens > 0 && (!q || !k || !v || !log_alpha || !b || !w || !o))
     return GDN2_INVALID_ARGUMENT;
-  const void* ptrs[9] = {q, k, v, log_alpha, b, w, o, initial_state, final_state};
+  const void* ptrs[10] = {q, k, v, log_alpha, b, w, o, initial_state, final_state, workspace};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return GDN2_INVALID_ARGUMENT;
   if (cu_seqlens && ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0))
     return GDN2_INVALID_ARGUMENT;
   // 64-bit element offsets are used in the kernels; the grid must fit one dimension.
   if (tokens > (long)INT_MAX) return GDN2_INVALID_ARGUMENT;
+  const bool split = workspace != nullptr && split_built(dtype, d_k, d_v);
+  if (split && workspace_bytes < workspace_need(cu_seqlens != nullptr, B, T, H, d_k, d_v, N))
+    return GDN2_WORKSPACE_TOO_SMALL;
   if (N == 0) return GDN2_OK;
-  if (nv == 0) nv = pick_nv(dtype, d_k, d_v, (long)N * H);
-  if (!gdn2::chunk_nv_supported(dtype, d_k, d_v, nv)) return GDN2_UNSUPPORTED;
-  const long grid = (long)N * H * (d_v / nv);
-  if (grid > (long)INT_MAX) return GDN2_INVALID_ARGUMENT;
 
   gdn2::ChunkArgs a;
   a.q = q; a.k = k; a.v = v; a.g = log_alpha; a.b = b; a.w = w;
   a.s0 = initial_state; a.o = o; a.sN = final_state; a.cu_seqlens = cu_seqlens;
   a.B = B; a.T = T; a.H = H; a.d_k = d_k; a.d_v = d_v; a.N = N;
-  a.dtype = dtype; a.nv = nv; a.stream = hip_stream;
+  a.dtype = dtype; a.stream = hip_stream;
+  a.workspace = split ? workspace : nullptr;
+  a.workspace_bytes = split ? workspace_bytes : 0;
+  if (split) {
+    a.nv = pick_split_nv(d_v, (long)N * H);
+    if ((long)N * H * (d_v / a.nv) > (long)INT_MAX) return GDN2_INVALID_ARGUMENT;
+    return status_of(gdn2::launch_chunk_fwd_split(a));
+  }
+  if (nv == 0) nv = pick_nv(dtype, d_k, d_v, (long)N * H);
+  if (!gdn2::chunk_nv_supported(dtype, d_k, d_v, nv)) return GDN2_UNSUPPORTED;
+  const long grid = (long)N * H * (d_v / nv);
+  if (grid > (long)INT_MAX) return GDN2_INVALID_ARGUMENT;
+  a.nv = nv;
   return status_of(gdn2::launch_chunk_fwd(a));
 }
 
@@ -73,12 +100,21 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* log_
 
 extern "C" {
 
+size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int N,
+                                      int dtype) {
+  if (B < 0 || T < 0 || H <= 0 || N < 0 || !split_built(dtype, d_k, d_v)) return 0;
+  const size_t a = workspace_need(false, B, T, H, d_k, d_v, N);
+  const size_t c = workspace_need(true, B, (int)std::min<long>((long)B * T, INT_MAX), H, d_k, d_v, N);
+  return a > c ? a : c;
+}
+
 int gdn2_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
                    const void* b, const void* w, const float* initial_state, void* o,
                    float* final_state, const int32_t* cu_seqlens, int B, int T, int H,
-                   int d_k, int d_v, int N, int dtype, void* hip_stream) {
+                   int d_k, int d_v, int N, int dtype, void* workspace,
+                   size_t workspace_bytes, void* hip_stream) {
   return chunk_fwd_impl(q, k, v, log_alpha, b, w, initial_state, o, final_state, cu_seqlens,
-                        B, T, H, d_k, d_v, N, dtype, hip_stream, 0);
+                        B, T, H, d_k, d_v, N, dtype, workspace, workspace_bytes, hip_stream, 0);
 }
 
 int gdn2_chunk_fwd_sliced(const void* q, const void* k, const void* v, const void* log_alpha,
@@ -88,7 +124,7 @@ int gdn2_chunk_fwd_sliced(const void* q, const void* k, const void* v, const voi
                           void* hip_stream) {
   if (value_slice < 0) return GDN2_INVALID_ARGUMENT;
   return chunk_fwd_impl(q, k, v, log_alpha, b, w, initial_state, o, final_state, cu_seqlens,
-                        B, T, H, d_k, d_v, N, dtype, hip_stream, value_slice);
+                        B, T, H, d_k, d_v, N, dtype, nullptr, 0, hip_stream, value_slice);
 }
 
 int gdn2_decode_step(const void* q, const void* k, const void* v, const void* log_alpha,
@@ -115,11 +151,12 @@ const char* gdn2_status_string(int status) {
     case GDN2_OK: return "ok";
     case GDN2_INVALID_ARGUMENT: return "invalid argument";
     case GDN2_UNSUPPORTED: return "unsupported head width, dtype or value slice";
+    case GDN2_WORKSPACE_TOO_SMALL: return "workspace too small";
     case GDN2_LAUNCH_FAILED: return "kernel launch failed";
     default: return "unknown status";
   }
 }
 
-const char* gdn2_version(void) { return "gdn2-mi355x 0.1.0 (gfx950)"; }
+const char* gdn2_version(void) { return "gdn2-mi355x 0.2.0 (gfx950)"; }
 
 }  // extern "C"

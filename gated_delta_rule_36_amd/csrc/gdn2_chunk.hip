@@ -38,7 +38,7 @@
 // so no factor exceeds one block's own decay (the API requires > -80 nats per 16 tokens).
 // All logs are kept in base 2 (g is scaled by log2(e) on load) so exp is one v_exp_f32.
 
-#include "gdn2_device.h"
+#include "gdn2_chunk_common.h"
 #include "gdn2_launch.h"
 
 namespace gdn2 {
@@ -68,14 +68,7 @@ struct ChunkShape {
   static constexpr int KPL = Mma<T>::KPL;
   static constexpr int NCT = DK / 16;     // 16-wide key-channel tiles
 
-  // factor rows (fp32, [NF][DK]); log2 units for G
-  static constexpr int F_ES = 0;    // exp(Gs(R))            R = 0..3   (block path)
-  static constexpr int F_KB = 4;    // exp(Ge(R) - Gs(R))    R = 0..3   (block path)
-  static constexpr int F_KNB = 8;   // exp(Glast - Gs(R))    R = 0..3   (block path)
-  static constexpr int F_GAM = 12;  // exp(Glast)
-  static constexpr int F_OFF = 13;  // exp(Gs(R) - Ge(I)) for (2,0), (3,0), (3,1)
-  static constexpr int F_GS = 16;   // Gs(R) (log2)          R = 0..3
-  static constexpr int NF = 20;
+  static constexpr int NF = Fac::N;  // factor rows (fp32, [NF][DK])
 
   // LDS layout (bytes)
   static constexpr int SZ_K = C * LDK * (int)sizeof(T);
@@ -114,129 +107,6 @@ struct ChunkShape {
                             NW * 2048 <= 2 * SZ_P), "row-split exchange space");
 };
 
-// Threshold on a chunk's total log2-decay above which the block-referenced path runs:
-// 120 log2 units = 83 nats, so exp(-G) <= 1.3e36 stays finite in fp32 and bf16.
-constexpr float kFastPathMaxDecay2 = 120.f;
-
-// Number of K steps of a product whose K range is the causal prefix [0, 16(R+1)).
-template <int KS>
-__device__ __forceinline__ constexpr int causal_steps(int R) {
-  return (16 * (R + 1) + KS - 1) / KS;
-}
-
-// Causal 16x16 tile pairs (R, I), I <= R, in the order of the bits of a pair mask.
-__device__ __forceinline__ constexpr int pair_R(int p) { return p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3; }
-__device__ __forceinline__ constexpr int pair_I(int p) { return p - (pair_R(p) * (pair_R(p) + 1)) / 2; }
-
-// A (stored negated; strictly lower) and P (lower incl. diagonal) tiles for the pairs in
-// MASK_A / MASK_P, with the chunk-referenced operands: every tile is a plain product of
-// (E exp(G) | Q exp(G)) rows and K exp(-G) rows, K = d_k.
-template <typename T, int DK, int LDK, int LDT, int MASK_A, int MASK_P>
-__device__ __forceinline__ void ap_tiles(const T* sE, const T* sQ, const T* sK, T* sAm, T* sP,
-                                         float* sAd, int m16, int g4) {
-  const int lane = 16 * g4 + m16;
-  using M = Mma<T>;
-  constexpr int MASK = MASK_A | MASK_P;
-  f4 accA[10], accP[10];
-#pragma unroll
-  for (int p = 0; p < 10; ++p) accA[p] = accP[p] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < DK / M::KS; ++s) {
-    const int kk = s * M::KS + M::KPL * g4;
-    typename M::frag kf[4];
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      bool need = false;
-#pragma unroll
-      for (int p = 0; p < 10; ++p) need |= ((MASK >> p) & 1) && pair_I(p) == I;
-      if (need) kf[I] = M::load(sK, LDK, 16 * I + m16, kk);
-    }
-#pragma unroll
-    for (int p = 0; p < 10; ++p) {
-      const int R = pair_R(p), I = pair_I(p);
-      if ((MASK_A >> p) & 1) accA[p] = M::mma(M::load(sE, LDK, 16 * R + m16, kk), kf[I], accA[p]);
-      if ((MASK_P >> p) & 1) accP[p] = M::mma(M::load(sQ, LDK, 16 * R + m16, kk), kf[I], accP[p]);
-    }
-  }
-#pragma unroll
-  for (int p = 0; p < 10; ++p) {
-    const int R = pair_R(p), I = pair_I(p);
-    if ((MASK_A >> p) & 1) {
-      f4 val;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * g4 + i, c = m16;
-        val[i] = (I < R || c < r) ? -accA[p][i] : 0.f;
-        if (sizeof(T) == 2 && I == R) sAd[R * 16 * 20 + r * 20 + c] = val[i];
-      }
-      store_tile_pairs(sAm + (16 * R) * LDT + 16 * I, LDT, lane, val, [](int c) { return c; });
-    }
-    if ((MASK_P >> p) & 1) {
-      f4 val;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * g4 + i, c = m16;
-        val[i] = (I < R || c <= r) ? accP[p][i] : 0.f;
-      }
-      store_tile_pairs(sP + (16 * R) * LDT, LDT, lane, val,
-                       [&](int c) { return Mma<T>::phi(16 * I + c); });
-    }
-  }
-}
-
-// A run of N consecutive tokens of one channel row of a token-transposed array, built one
-// token at a time (j is a compile-time index after unrolling). bf16 runs are kept packed
-// two per register.
-template <typename T, int N> struct RunBuf {
-  float v[N];
-  __device__ __forceinline__ void put(int j, float x) { v[j] = x; }
-  template <bool PHI = false>
-  __device__ __forceinline__ void store(T* row, int c, int r0) const { store_run_t<N>(row, c, r0, v); }
-  template <bool PHI = false>
-  __device__ __forceinline__ void store_sw(T* row, int sw, int r0) const {
-#pragma unroll
-    for (int j = 0; j < N; ++j) {
-      const int r = PHI ? Mma<T>::phi(r0 + j) : r0 + j;
-      row[((((r >> 2) ^ sw)) << 2) | (r & 3)] = v[j];
-    }
-  }
-};
-template <int N> struct RunBuf<bf16, N> {
-  static_assert(N == 1 || N % 2 == 0, "run length");
-  uint32_t w[N / 2 > 0 ? N / 2 : 1];
-  float pend;
-  __device__ __forceinline__ void put(int j, float x) {
-    if (N == 1) {
-      pend = x;
-    } else if (j & 1) {
-      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-      w[j >> 1] = __builtin_bit_cast(uint32_t, bf16x2{static_cast<bf16>(pend), static_cast<bf16>(x)});
-    } else {
-      pend = x;
-    }
-  }
-  // PHI: tokens stored in the phi order of Mma<bf16> (runs of 2 and aligned runs of 4 stay
-  // contiguous under it).
-  template <bool PHI = false>
-  __device__ __forceinline__ void store(bf16* row, int c, int r0) const { store_sw<PHI>(row, tswz(c), r0); }
-  // sw: the token-group swizzle of the row (shared by the 8 channels of a thread)
-  template <bool PHI = false>
-  __device__ __forceinline__ void store_sw(bf16* row, int sw, int r0) const {
-    auto pos = [&](int r) {
-      const int rr = PHI ? Mma<bf16>::phi(r) : r;
-      return ((((rr >> 2) ^ sw)) << 2) | (rr & 3);
-    };
-    if constexpr (N == 1) {
-      row[pos(r0)] = static_cast<bf16>(pend);
-    } else if constexpr (N == 2) {
-      *reinterpret_cast<uint32_t*>(row + pos(r0)) = w[0];
-    } else {
-#pragma unroll
-      for (int q = 0; q < N / 4; ++q)
-        *reinterpret_cast<uint2*>(row + pos(r0 + 4 * q)) = make_uint2(w[2 * q], w[2 * q + 1]);
-    }
-  }
-};
 
 template <typename T, int DK, int NV>
 __global__ void __launch_bounds__((ChunkShape<T, DK, NV>::NT))
@@ -440,32 +310,7 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
 
     // ---- (b) per-channel scan over token groups: chunk-relative exclusive prefixes
     // and the per-channel decay factors
-    for (int ch = tid; ch < DK; ch += NT) {
-      float tot[Sh::TG];
-#pragma unroll
-      for (int x = 0; x < Sh::TG; ++x) tot[x] = sTot[x * DK + ch];
-      float run = 0.f, gs[4];
-#pragma unroll
-      for (int x = 0; x < Sh::TG; ++x) {
-        if (x % Sh::GPB == 0) gs[x / Sh::GPB] = run;
-        sTot[x * DK + ch] = run;
-        run += tot[x];
-      }
-      const float gn = run;
-      const float ge[4] = {gs[1], gs[2], gs[3], gn};
-#pragma unroll
-      for (int R = 0; R < 4; ++R) {
-        sFac[(Sh::F_ES + R) * DK + ch] = fast_exp2(gs[R]);
-        sFac[(Sh::F_KB + R) * DK + ch] = fast_exp2(ge[R] - gs[R]);
-        sFac[(Sh::F_KNB + R) * DK + ch] = fast_exp2(gn - gs[R]);
-        sFac[(Sh::F_GS + R) * DK + ch] = gs[R];
-      }
-      sFac[Sh::F_GAM * DK + ch] = fast_exp2(gn);
-      sFac[(Sh::F_OFF + 0) * DK + ch] = fast_exp2(gs[2] - ge[0]);
-      sFac[(Sh::F_OFF + 1) * DK + ch] = fast_exp2(gs[3] - ge[0]);
-      sFac[(Sh::F_OFF + 2) * DK + ch] = fast_exp2(gs[3] - ge[1]);
-      if (-gn > kFastPathMaxDecay2) *sFlag = 1;
-    }
+    channel_scan<DK, Sh::TG, Sh::GPB, NT>(sTot, sFac, sFlag, tid);
     lds_barrier();
     fresh_prep();
     const bool block_path = __builtin_amdgcn_readfirstlane(*sFlag) != 0;
@@ -502,16 +347,16 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
       if (!block_path) {
         float gam[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) gam[i] = sFac[Sh::F_GAM * DK + cg * 8 + i];
+        for (int i = 0; i < 8; ++i) gam[i] = sFac[Fac::GAM * DK + cg * 8 + i];
 #pragma unroll
         for (int j = 0; j < Sh::TPT; ++j) token(j, nullptr, nullptr, gam, false);
       } else {
         float fA[8], fB[8], sub[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          fA[i] = sFac[(Sh::F_ES + blk) * DK + cg * 8 + i];
-          fB[i] = sFac[(Sh::F_KNB + blk) * DK + cg * 8 + i];
-          sub[i] = sFac[(Sh::F_GS + blk) * DK + cg * 8 + i];
+          fA[i] = sFac[(Fac::ES + blk) * DK + cg * 8 + i];
+          fB[i] = sFac[(Fac::KNB + blk) * DK + cg * 8 + i];
+          sub[i] = sFac[(Fac::GS + blk) * DK + cg * 8 + i];
         }
 #pragma unroll
         for (int j = 0; j < Sh::TPT; ++j) token(j, sub, fA, fB, true);
@@ -567,30 +412,7 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
         for (int s = 0; s < KSH; ++s) O[R] = M::mma(qf[R][s], sb[s], O[R]);
       }
     };
-    auto tdiag = [&]() {
-      const int jb = g4, c = m16;
-      const float* Ab = sAd + jb * ADB;
-      float am[16][16];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) {
-#pragma unroll
-        for (int i4 = 0; i4 < r; i4 += 4) {
-          const f4 v = *reinterpret_cast<const f4*>(Ab + r * ADP + i4);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) am[r][i4 + j] = v[j];
-        }
-      }
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-#pragma unroll
-        for (int r = i + 1; r < 16; ++r) x[r] += am[r][i] * x[i];  // am holds -A
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sT[(16 * jb + r) * LDT + 16 * jb + c] = from_f<T>(x[r]);
-    };
+    auto tdiag = [&]() { diag_inverse<T, LDT, ADB, ADP>(sAd, sT, m16, g4); };
     // pair bits: (0,0)=0 (1,0)=1 (1,1)=2 (2,0)=3 (2,1)=4 (2,2)=5 (3,0)=6 (3,1)=7 (3,2)=8 (3,3)=9
     constexpr int DIAG = 0x225;     // (0,0) (1,1) (2,2) (3,3)
     constexpr int OFFD = 0x1DA;     // off-diagonal pairs
@@ -629,50 +451,9 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
         o_partial();
       }
     } else {
-      // block-referenced tiles: rows of block R against Kn of block I; off-diagonal
-      // tiles scale Kn by exp(Ge(I)-Gs(I)) and, two or more blocks apart, the left
-      // operand by exp(Gs(R)-Ge(I)).
-      for (int job = wave; job < 20; job += NW) {
-        const int pair = job >> 1;
-        const bool isP = job & 1;
-        const int R = pair < 1 ? 0 : pair < 3 ? 1 : pair < 6 ? 2 : 3;
-        const int I = pair - (R * (R + 1)) / 2;
-        const T* lhs = isP ? sQ : sE;
-        const int off = (R - I >= 2) ? (R == 2 ? 0 : (I == 0 ? 1 : 2)) : -1;
-        f4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < DK / KS; ++s) {
-          const int kk = s * KS + KPL * g4;  // physical (phi-ordered) K position
-          float fa[KPL], fb[KPL];
-#pragma unroll
-          for (int i = 0; i < KPL; ++i) {
-            const int ch = M::phi_inv(kk + i);  // logical key channel of that position
-            fa[i] = off >= 0 ? sFac[(Sh::F_OFF + off) * DK + ch] : 1.f;
-            fb[i] = I != R ? sFac[(Sh::F_KB + I) * DK + ch] : 1.f;
-          }
-          const typename M::frag a = M::load_scaled(lhs, LDK, 16 * R + m16, kk, fa);
-          const typename M::frag b = M::load_scaled(sK, LDK, 16 * I + m16, kk, fb);
-          acc = M::mma(a, b, acc);
-        }
-        f4 val;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * g4 + i, c = m16;
-          const bool keep = (I < R) || (isP ? (c <= r) : (c < r));
-          val[i] = keep ? (isP ? acc[i] : -acc[i]) : 0.f;
-          if (!isP && sizeof(T) == 2 && I == R) sAd[R * ADB + r * ADP + c] = val[i];
-        }
-        if (isP)
-          store_tile_pairs(sP + (16 * R) * LDT, LDT, lane, val,
-                           [&](int c) { return M::phi(16 * I + c); });
-        else
-          store_tile_pairs(sAm + (16 * R) * LDT + 16 * I, LDT, lane, val, [](int c) { return c; });
-      }
+      ap_tiles_block<T, DK, LDK, LDT, ADB, ADP, NW>(sE, sQ, sK, sAm, sP, sAd, sFac, wave, lane);
     }
-    // upper tiles (0,1) and (2,3) of P are read (as zeros) by the 32-wide K steps of P U
-    for (int idx = tid; idx < 2 * 256; idx += NT) {
-      const int t = idx >> 8, e = idx & 255;
-      sP[((t ? 32 : 0) + (e >> 4)) * LDT + M::phi((t ? 48 : 16) + (e & 15))] = from_f<T>(0.f);
-    }
+    zero_p_upper<T, LDT, NT>(sP, tid);
     lds_barrier();
     fresh_prep();
     if (block_path) {
@@ -683,7 +464,7 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
       for (int idx = t0; idx >= 0 && idx < C * DK; idx += nthr) {
         const int r = idx / DK, pc = idx % DK;
         sQ[r * LDK + pc] = from_f<T>(to_f(sQ[r * LDK + pc]) *
-                                     sFac[(Sh::F_ES + r / 16) * DK + M::phi_inv(pc)]);
+                                     sFac[(Fac::ES + r / 16) * DK + M::phi_inv(pc)]);
       }
       lds_barrier();
       fresh_prep();
@@ -809,7 +590,7 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
 #pragma unroll
     for (int mt = 0; mt < NMS; ++mt) {
       const int mg = whw * NMS + mt;
-      const f4 gam = *reinterpret_cast<const f4*>(sFac + Sh::F_GAM * DK + 16 * mg + 4 * g4);
+      const f4 gam = *reinterpret_cast<const f4*>(sFac + Fac::GAM * DK + 16 * mg + 4 * g4);
       f4 acc = S[mt] * gam;
 #pragma unroll
       for (int s = 0; s < C / KS; ++s)

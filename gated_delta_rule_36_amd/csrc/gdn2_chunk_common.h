@@ -1,0 +1,272 @@
+// Chunk-stage building blocks shared by the fused chunk kernel (gdn2_chunk.hip) and the
+// two-phase path (gdn2_split.hip): causal tile pairs, the A / P tile products, the per-
+// channel decay scan and factors, the 16x16 diagonal inverses, and packed LDS runs.
+//
+// Notation (one 64-token chunk, local tokens r, i; 16-token blocks R, I; log2 units):
+//   G[r]   cumulative log2-decay of the chunk up to and including token r (per channel)
+//   Gs(R)  G just before block R starts, Ge(R) = Gs(R + 1), Glast = G[63]
+//   A      strictly lower, sum_c E[r,c] K[i,c] 2^(G[r,c]-G[i,c])  (stored negated)
+//   P      lower incl. diagonal, the same with Q in place of E
+#pragma once
+
+#include "gdn2_device.h"
+
+namespace gdn2 {
+
+// Rows of the per-channel factor table (fp32 [Fac::N][d_k]); the block rows are used only
+// by the block-referenced path.
+struct Fac {
+  static constexpr int ES = 0;    // 2^Gs(R)                R = 0..3
+  static constexpr int KB = 4;    // 2^(Ge(R) - Gs(R))      R = 0..3
+  static constexpr int KNB = 8;   // 2^(Glast - Gs(R))      R = 0..3
+  static constexpr int GAM = 12;  // 2^Glast: the chunk's decay of the state
+  static constexpr int OFF = 13;  // 2^(Gs(R) - Ge(I)) for (R, I) = (2,0), (3,0), (3,1)
+  static constexpr int GS = 16;   // Gs(R)                  R = 0..3
+  static constexpr int N = 20;
+};
+
+// Threshold on a chunk's total log2-decay above which the block-referenced path runs:
+// 120 log2 units = 83 nats, so exp(-G) <= 1.3e36 stays finite in fp32 and bf16.
+constexpr float kFastPathMaxDecay2 = 120.f;
+
+// Number of K steps of a product whose K range is the causal prefix [0, 16(R+1)).
+template <int KS>
+__device__ __forceinline__ constexpr int causal_steps(int R) {
+  return (16 * (R + 1) + KS - 1) / KS;
+}
+
+// Causal 16x16 tile pairs (R, I), I <= R, in the order of the bits of a pair mask.
+__device__ __forceinline__ constexpr int pair_R(int p) { return p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3; }
+__device__ __forceinline__ constexpr int pair_I(int p) { return p - (pair_R(p) * (pair_R(p) + 1)) / 2; }
+
+// A (stored negated; strictly lower) and P (lower incl. diagonal) tiles for the pairs in
+// MASK_A / MASK_P, with the chunk-referenced operands: every tile is a plain product of
+// (E exp(G) | Q exp(G)) rows and K exp(-G) rows, K = d_k.
+template <typename T, int DK, int LDK, int LDT, int MASK_A, int MASK_P>
+__device__ __forceinline__ void ap_tiles(const T* sE, const T* sQ, const T* sK, T* sAm, T* sP,
+                                         float* sAd, int m16, int g4) {
+  const int lane = 16 * g4 + m16;
+  using M = Mma<T>;
+  constexpr int MASK = MASK_A | MASK_P;
+  f4 accA[10], accP[10];
+#pragma unroll
+  for (int p = 0; p < 10; ++p) accA[p] = accP[p] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < DK / M::KS; ++s) {
+    const int kk = s * M::KS + M::KPL * g4;
+    typename M::frag kf[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      bool need = false;
+#pragma unroll
+      for (int p = 0; p < 10; ++p) need |= ((MASK >> p) & 1) && pair_I(p) == I;
+      if (need) kf[I] = M::load(sK, LDK, 16 * I + m16, kk);
+    }
+#pragma unroll
+    for (int p = 0; p < 10; ++p) {
+      const int R = pair_R(p), I = pair_I(p);
+      if ((MASK_A >> p) & 1) accA[p] = M::mma(M::load(sE, LDK, 16 * R + m16, kk), kf[I], accA[p]);
+      if ((MASK_P >> p) & 1) accP[p] = M::mma(M::load(sQ, LDK, 16 * R + m16, kk), kf[I], accP[p]);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < 10; ++p) {
+    const int R = pair_R(p), I = pair_I(p);
+    if ((MASK_A >> p) & 1) {
+      f4 val;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g4 + i, c = m16;
+        val[i] = (I < R || c < r) ? -accA[p][i] : 0.f;
+        if (sizeof(T) == 2 && I == R) sAd[R * 16 * 20 + r * 20 + c] = val[i];
+      }
+      store_tile_pairs(sAm + (16 * R) * LDT + 16 * I, LDT, lane, val, [](int c) { return c; });
+    }
+    if ((MASK_P >> p) & 1) {
+      f4 val;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g4 + i, c = m16;
+        val[i] = (I < R || c <= r) ? accP[p][i] : 0.f;
+      }
+      store_tile_pairs(sP + (16 * R) * LDT, LDT, lane, val,
+                       [&](int c) { return Mma<T>::phi(16 * I + c); });
+    }
+  }
+}
+
+// A run of N consecutive tokens of one channel row of a token-transposed array, built one
+// token at a time (j is a compile-time index after unrolling). bf16 runs are kept packed
+// two per register.
+template <typename T, int N> struct RunBuf {
+  float v[N];
+  __device__ __forceinline__ void put(int j, float x) { v[j] = x; }
+  template <bool PHI = false>
+  __device__ __forceinline__ void store(T* row, int c, int r0) const { store_run_t<N>(row, c, r0, v); }
+  template <bool PHI = false>
+  __device__ __forceinline__ void store_sw(T* row, int sw, int r0) const {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int r = PHI ? Mma<T>::phi(r0 + j) : r0 + j;
+      row[((((r >> 2) ^ sw)) << 2) | (r & 3)] = v[j];
+    }
+  }
+};
+template <int N> struct RunBuf<bf16, N> {
+  static_assert(N == 1 || N % 2 == 0, "run length");
+  uint32_t w[N / 2 > 0 ? N / 2 : 1];
+  float pend;
+  __device__ __forceinline__ void put(int j, float x) {
+    if (N == 1) {
+      pend = x;
+    } else if (j & 1) {
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      w[j >> 1] = __builtin_bit_cast(uint32_t, bf16x2{static_cast<bf16>(pend), static_cast<bf16>(x)});
+    } else {
+      pend = x;
+    }
+  }
+  // PHI: tokens stored in the phi order of Mma<bf16> (runs of 2 and aligned runs of 4 stay
+  // contiguous under it).
+  template <bool PHI = false>
+  __device__ __forceinline__ void store(bf16* row, int c, int r0) const { store_sw<PHI>(row, tswz(c), r0); }
+  // sw: the token-group swizzle of the row (shared by the 8 channels of a thread)
+  template <bool PHI = false>
+  __device__ __forceinline__ void store_sw(bf16* row, int sw, int r0) const {
+    auto pos = [&](int r) {
+      const int rr = PHI ? Mma<bf16>::phi(r) : r;
+      return ((((rr >> 2) ^ sw)) << 2) | (rr & 3);
+    };
+    if constexpr (N == 1) {
+      row[pos(r0)] = static_cast<bf16>(pend);
+    } else if constexpr (N == 2) {
+      *reinterpret_cast<uint32_t*>(row + pos(r0)) = w[0];
+    } else {
+#pragma unroll
+      for (int q = 0; q < N / 4; ++q)
+        *reinterpret_cast<uint2*>(row + pos(r0 + 4 * q)) = make_uint2(w[2 * q], w[2 * q + 1]);
+    }
+  }
+};
+
+// Per-channel scan of a chunk's log2-decay. On entry sTot ([TG][DK], fp32) holds each
+// token group's total; on exit it holds the chunk-relative exclusive prefix of each group,
+// sFac the factor rows (Fac), and *sFlag is set when some channel's total decay exceeds
+// kFastPathMaxDecay2 (the caller clears it beforehand).
+template <int DK, int TG, int GPB, int NT>
+__device__ __forceinline__ void channel_scan(float* sTot, float* sFac, int* sFlag, int tid) {
+  for (int ch = tid; ch < DK; ch += NT) {
+    float tot[TG];
+#pragma unroll
+    for (int x = 0; x < TG; ++x) tot[x] = sTot[x * DK + ch];
+    float run = 0.f, gs[4];
+#pragma unroll
+    for (int x = 0; x < TG; ++x) {
+      if (x % GPB == 0) gs[x / GPB] = run;
+      sTot[x * DK + ch] = run;
+      run += tot[x];
+    }
+    const float gn = run;
+    const float ge[4] = {gs[1], gs[2], gs[3], gn};
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+      sFac[(Fac::ES + R) * DK + ch] = fast_exp2(gs[R]);
+      sFac[(Fac::KB + R) * DK + ch] = fast_exp2(ge[R] - gs[R]);
+      sFac[(Fac::KNB + R) * DK + ch] = fast_exp2(gn - gs[R]);
+      sFac[(Fac::GS + R) * DK + ch] = gs[R];
+    }
+    sFac[Fac::GAM * DK + ch] = fast_exp2(gn);
+    sFac[(Fac::OFF + 0) * DK + ch] = fast_exp2(gs[2] - ge[0]);
+    sFac[(Fac::OFF + 1) * DK + ch] = fast_exp2(gs[3] - ge[0]);
+    sFac[(Fac::OFF + 2) * DK + ch] = fast_exp2(gs[3] - ge[1]);
+    if (-gn > kFastPathMaxDecay2) *sFlag = 1;
+  }
+}
+
+// The four 16x16 diagonal blocks of (I + A)^{-1} by fp32 forward substitution, one block
+// per 16-lane group and one column per lane, from the fp32 copy of the diagonal blocks of
+// -A (block jb, row r, column i at sAd[jb * ADB + r * ADP + i]); written to the diagonal
+// blocks of sT ([64][LDT]).
+template <typename T, int LDT, int ADB, int ADP>
+__device__ __forceinline__ void diag_inverse(const float* sAd, T* sT, int m16, int g4) {
+  const int jb = g4, c = m16;
+  const float* Ab = sAd + jb * ADB;
+  float am[16][16];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) {
+#pragma unroll
+    for (int i4 = 0; i4 < r; i4 += 4) {
+      const f4 v = *reinterpret_cast<const f4*>(Ab + r * ADP + i4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) am[r][i4 + j] = v[j];
+    }
+  }
+  float x[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+#pragma unroll
+    for (int r = i + 1; r < 16; ++r) x[r] += am[r][i] * x[i];  // am holds -A
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sT[(16 * jb + r) * LDT + 16 * jb + c] = from_f<T>(x[r]);
+}
+
+// Block-referenced A and P tiles (chunks whose total decay is too large for the chunk-
+// referenced factors): rows of block R against Kn of block I; off-diagonal tiles scale Kn
+// by 2^(Ge(I)-Gs(I)) and, two or more blocks apart, the left operand by 2^(Gs(R)-Ge(I)).
+// The 20 tiles are dealt round-robin to the NW waves.
+template <typename T, int DK, int LDK, int LDT, int ADB, int ADP, int NW>
+__device__ __forceinline__ void ap_tiles_block(const T* sE, const T* sQ, const T* sK, T* sAm,
+                                               T* sP, float* sAd, const float* sFac, int wave,
+                                               int lane) {
+  using M = Mma<T>;
+  constexpr int KS = M::KS, KPL = M::KPL;
+  const int m16 = lane & 15, g4 = lane >> 4;
+  for (int job = wave; job < 20; job += NW) {
+    const int pair = job >> 1;
+    const bool isP = job & 1;
+    const int R = pair_R(pair), I = pair_I(pair);
+    const T* lhs = isP ? sQ : sE;
+    const int off = (R - I >= 2) ? (R == 2 ? 0 : (I == 0 ? 1 : 2)) : -1;
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < DK / KS; ++s) {
+      const int kk = s * KS + KPL * g4;  // physical (phi-ordered) K position
+      float fa[KPL], fb[KPL];
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) {
+        const int ch = M::phi_inv(kk + i);  // logical key channel of that position
+        fa[i] = off >= 0 ? sFac[(Fac::OFF + off) * DK + ch] : 1.f;
+        fb[i] = I != R ? sFac[(Fac::KB + I) * DK + ch] : 1.f;
+      }
+      const typename M::frag a = M::load_scaled(lhs, LDK, 16 * R + m16, kk, fa);
+      const typename M::frag b = M::load_scaled(sK, LDK, 16 * I + m16, kk, fb);
+      acc = M::mma(a, b, acc);
+    }
+    f4 val;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g4 + i, c = m16;
+      const bool keep = (I < R) || (isP ? (c <= r) : (c < r));
+      val[i] = keep ? (isP ? acc[i] : -acc[i]) : 0.f;
+      if (!isP && sizeof(T) == 2 && I == R) sAd[R * ADB + r * ADP + c] = val[i];
+    }
+    if (isP)
+      store_tile_pairs(sP + (16 * R) * LDT, LDT, lane, val, [&](int c) { return M::phi(16 * I + c); });
+    else
+      store_tile_pairs(sAm + (16 * R) * LDT + 16 * I, LDT, lane, val, [](int c) { return c; });
+  }
+}
+
+// The upper tiles (0,1) and (2,3) of P (phi-ordered columns) are read as zeros by the
+// 32-wide K steps of products with P.
+template <typename T, int LDT, int NT>
+__device__ __forceinline__ void zero_p_upper(T* sP, int tid) {
+  for (int idx = tid; idx < 2 * 256; idx += NT) {
+    const int t = idx >> 8, e = idx & 255;
+    sP[((t ? 32 : 0) + (e >> 4)) * LDT + Mma<T>::phi((t ? 48 : 16) + (e & 15))] = from_f<T>(0.f);
+  }
+}
+
+}  // namespace gdn2

@@ -16,6 +16,8 @@ struct ChunkArgs {
   int dtype;  // 0 = bf16, 1 = fp32
   int nv;     // value-slice width per workgroup
   void* stream;
+  void* workspace;        // two-phase path only: per-chunk factors (see SplitLayout)
+  size_t workspace_bytes;
 };
 
 struct DecodeArgs {
@@ -34,7 +36,42 @@ inline bool chunk_nv_supported(int dtype, int d_k, int d_v, int nv) {
   return d_k == 64 && (nv == 16 || nv == 32 || nv == 64);
 }
 
+// Two-phase chunk forward (bf16). Phase 1 turns every (64-token chunk, head) into the
+// factors the state recurrence needs; phase 2 walks each sequence's chunks in order.
+// Per (chunk slot, head) unit the workspace holds, in MFMA fragment order (1 KiB blocks of
+// 64 lanes x 8 bf16; key channels / tokens phi-ordered inside each 32-wide K step):
+//   -W    [64 tokens][d_k]     blocks (R, s)   R = token tile, s = 32-channel step
+//   Qbar  [64 tokens][d_k]     blocks (R, s)   Q 2^G
+//   Kt    [d_k][64 tokens]     blocks (m, s)   (K 2^(Glast - G))^T, m = channel tile
+//   P     [64][64]             blocks (R, s)
+//   U~    D tiles (ct, R) of 16x16, lane-major, 4 bf16 per lane (512 B)
+//   gamma [d_k] fp32           2^Glast
+struct SplitLayout {
+  long w, q, kt, p, u, g, bytes;
+  static constexpr int kChunk = 64;
+  constexpr SplitLayout(int d_k, int d_v)
+      : w(0),
+        q(w + 4L * (d_k / 32) * 1024),
+        kt(q + 4L * (d_k / 32) * 1024),
+        p(kt + (d_k / 16) * 2L * 1024),
+        u(p + 8L * 1024),
+        g(u + (d_v / 16) * 4L * 512),
+        bytes(((g + 4L * d_k) + 255) / 256 * 256) {}
+};
+
+// Chunk slots of a call: without cu_seqlens, sequence n owns slots [n*ceil(T/64), ...);
+// with cu_seqlens, sequence n owns the slots from floor(cu[n]/64) + n on (disjoint for
+// any non-decreasing table, all below floor(T/64) + N).
+inline long split_slots(bool varlen, int B, int T, int N) {
+  const int C = SplitLayout::kChunk;
+  return varlen ? (long)T / C + N : (long)B * ((T + C - 1) / C);
+}
+inline size_t split_workspace_bytes(bool varlen, int B, int T, int H, int d_k, int d_v, int N) {
+  return (size_t)split_slots(varlen, B, T, N) * H * SplitLayout(d_k, d_v).bytes;
+}
+
 hipError_t launch_chunk_fwd(const ChunkArgs& a);
+hipError_t launch_chunk_fwd_split(const ChunkArgs& a);
 hipError_t launch_decode_step(const DecodeArgs& a);
 
 }  // namespace gdn2

@@ -1,0 +1,758 @@
+// Two-phase chunkwise forward of Gated Delta Rule-2 on gfx950 (bf16 inputs).
+//
+// The chunk form (GDN-2 reading note, §3 chunkwise-training paragraph; UT transform of the
+// Gated DeltaNet visual reading, chunkwise section) splits into work that depends only on
+// the chunk's own tokens and a short recurrence over the state:
+//   chunk-local:  A, P, T = (I + A)^{-1}, W = T (E 2^G), U~ = T Z, Qbar = Q 2^G,
+//                 Kt = (K 2^(Glast - G))^T, gamma = 2^Glast
+//   recurrence:   U = U~ - W S,  O = Qbar S + P U,  S <- Diag(gamma) S + Kt U
+// Phase 1 (gdn2_prep_kernel) computes the chunk-local factors of every (chunk, head) in
+// parallel and stores them in MFMA fragment order (SplitLayout). Phase 2
+// (gdn2_state_kernel) walks each (sequence, head, value slice)'s chunks in order with the
+// state in accumulator registers; its per-chunk operands do not depend on the state, so
+// they are staged into LDS one chunk ahead and its critical path is three MFMA products.
+//
+// Compared with the fused kernel (gdn2_chunk.hip) this moves the triangular inverse and
+// the A / P products off the sequential path and computes them once per head instead of
+// once per value slice, at the cost of writing and reading back the factors.
+
+#include "gdn2_chunk_common.h"
+#include "gdn2_launch.h"
+
+namespace gdn2 {
+
+// ------------------------------------------------------------------ phase 1: factors
+template <int DK, int DV>
+struct PrepShape {
+  typedef bf16 T;
+  static constexpr int C = 64;
+  static constexpr int NW = 8;            // waves
+  static constexpr int NT = 64 * NW;
+  static constexpr int CG = DK / 8;       // key-side prep: 8 channels per thread
+  static constexpr int TG = NT / CG;      // token groups
+  static constexpr int TPT = C / TG;      // tokens per thread (inside one 16-token block)
+  static constexpr int GPB = 16 / TPT;    // token groups per 16-token block
+  static constexpr int VCG = DV / 8;      // value-side prep: 8 columns per thread
+  static constexpr int VTG = NT / VCG;
+  static constexpr int VTPT = C / VTG;
+  static constexpr int PAD = 8;           // 16-byte row padding
+  static constexpr int LDK = DK + PAD;
+  static constexpr int LDT = C + PAD;
+  static constexpr int NCT = DK / 16;     // key-channel tiles
+  static constexpr int NVT = DV / 16;     // value-column tiles
+  static constexpr int NTT = NCT + NVT;   // forward-substitution column tiles
+  static constexpr int NTW = (NTT + NW - 1) / NW;  // ... per wave (max)
+
+  static constexpr int SZ_K = C * LDK * 2;
+  static constexpr int OFF_E = 0;                  // E 2^G (or Ea); later -W
+  static constexpr int OFF_Q = OFF_E + SZ_K;       // Q 2^G (or Qa, rescaled)
+  static constexpr int OFF_K = OFF_Q + SZ_K;       // K 2^-G (or Kn)
+  static constexpr int SZ_T = DK * LDT * 2;
+  static constexpr int OFF_ET = OFF_K + SZ_K;      // (E 2^G)^T          [DK][64]
+  static constexpr int OFF_KT = OFF_ET + SZ_T;     // (K 2^(Gl - G))^T   [DK][64]
+  static constexpr int SZ_Z = DV * LDT * 2;
+  static constexpr int OFF_ZT = OFF_KT + SZ_T;     // Z^T                [DV][64]
+  static constexpr int SZ_P = C * LDT * 2;
+  static constexpr int OFF_P = OFF_ZT + SZ_Z;      // P
+  static constexpr int OFF_A = OFF_P + SZ_P;       // -A
+  static constexpr int OFF_TB = OFF_A + SZ_P;      // diagonal blocks of (I + A)^{-1}
+  static constexpr int OFF_FAC = OFF_TB + SZ_P;
+  static constexpr int SZ_FAC = Fac::N * DK * 4;
+  static constexpr int LDD = 20;                   // fp32 diagonal blocks of -A
+  static constexpr int OFF_AD = OFF_FAC + SZ_FAC;
+  static constexpr int OFF_FLAG = OFF_AD + 4 * 16 * LDD * 4;
+  // U~ tiles in workspace order, written in (f): into the K buffer (dead since (d)) when it
+  // is large enough, else into a buffer of their own
+  static constexpr int SZ_U = NVT * 4 * 512;
+  static constexpr int OFF_U = SZ_U <= SZ_K ? OFF_K : OFF_FLAG + 16;
+  static constexpr int LDS_BYTES = (SZ_U <= SZ_K ? OFF_FLAG + 16 : OFF_U + SZ_U);
+  static constexpr int OFF_TOT = OFF_P;            // cumsum scratch [TG][DK] in P and -A
+
+  static_assert(TPT >= 1 && TPT <= 16 && 16 % TPT == 0, "token groups must tile 16-blocks");
+  static_assert(VTPT >= 1 && C % VTG == 0, "value prep mapping");
+  static_assert(TG * DK * 4 <= 2 * SZ_P, "cumsum scratch fits in P and -A");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+// 16-byte pieces of one unit's factors held per thread between (g) and the stores: counts
+// per workspace region (-W, Qbar, Kt, U~ each a whole number of pieces per thread; P one;
+// gamma one on the first d_k / 4 threads) and their index in the thread's register array.
+template <int DK, int DV>
+struct PrepPieces {
+  static constexpr int NT = PrepShape<DK, DV>::NT;
+  static constexpr int NW_ = 4 * (DK / 32) * 64 / NT;
+  static constexpr int NK_ = (DK / 16) * 2 * 64 / NT;
+  static constexpr int NU_ = (DV / 16) * 4 * 32 / NT;
+  static constexpr int J_W = 0, J_Q = NW_, J_K = 2 * NW_, J_P = J_K + NK_, J_U = J_P + 1,
+                       J_G = J_U + NU_, N = J_G + 1;
+  static_assert(4 * (DK / 32) * 64 % NT == 0 && (DK / 16) * 2 * 64 % NT == 0 &&
+                (DV / 16) * 4 * 32 % NT == 0 && 8 * 64 == NT && DK / 4 <= NT,
+                "factor pieces tile the workgroup");
+};
+
+// Where a (chunk slot, head) unit's tokens are: first row of the packed token axis and
+// the number of valid tokens (0: an unused slot).
+struct ChunkUnit {
+  long row;
+  int nvalid;
+  int h;
+};
+
+// Maps unit u = slot * H + h to its tokens. Without cu_seqlens the slots of sequence n are
+// n * nch + c. With cu_seqlens, sequence n's slots start at floor(a_n / 64) + n (a_n its
+// clamped first token); the owner of a slot is found by a 64-way ballot search over the
+// table (wave-uniform result).
+__device__ __forceinline__ ChunkUnit map_unit(long u, int H, const int* cu_seqlens, int N,
+                                              int T_len, int lane) {
+  constexpr int C = 64;
+  ChunkUnit r;
+  const long slot = u / H;
+  r.h = (int)(u - slot * H);
+  if (cu_seqlens == nullptr) {
+    const int nch = (T_len + C - 1) / C;
+    const long n = slot / nch;
+    const int c = (int)(slot - n * nch);
+    r.row = n * T_len + (long)c * C;
+    r.nvalid = min(C, T_len - c * C);
+    return r;
+  }
+  auto clamp_cu = [&](int i) { const int x = cu_seqlens[i]; return x < 0 ? 0 : (x > T_len ? T_len : x); };
+  // largest n in [0, N) with start slot s_n = floor(a_n / 64) + n <= slot
+  int lo = 0, hi = N;
+  if ((long)(clamp_cu(0) / C) > slot) {
+    r.row = 0; r.nvalid = 0;
+    return r;
+  }
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 63) / 64;
+    const int cand = lo + lane * step;
+    const bool ok = cand < hi && (long)(clamp_cu(cand) / C + cand) <= slot;
+    const unsigned long long m = __ballot(ok);
+    const int kk = __popcll(m) - 1;  // lane 0 (cand = lo) always passes
+    lo = lo + kk * step;
+    hi = min(lo + step, hi);
+  }
+  const int n = __builtin_amdgcn_readfirstlane(lo);
+  const int a = clamp_cu(n);
+  int b = clamp_cu(n + 1);
+  b = b < a ? a : b;
+  const long c = slot - (long)(a / C + n);
+  const int len = b - a;
+  if (c < 0 || c * C >= len) {
+    r.row = 0; r.nvalid = 0;
+    return r;
+  }
+  r.row = a + c * C;
+  r.nvalid = len - c * C < C ? (int)(len - c * C) : C;
+  return r;
+}
+
+template <int DK, int DV>
+__global__ void __launch_bounds__(512)
+gdn2_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                 const bf16* __restrict__ v, const bf16* __restrict__ g,
+                 const bf16* __restrict__ bg, const bf16* __restrict__ wg,
+                 char* __restrict__ ws, const int* __restrict__ cu_seqlens, int N, int T_len,
+                 int H, long nunits) {
+  typedef bf16 T;
+  using Sh = PrepShape<DK, DV>;
+  using M = Mma<T>;
+  constexpr SplitLayout L(DK, DV);
+  constexpr int C = Sh::C, NW = Sh::NW, NT = Sh::NT;
+  constexpr int LDK = Sh::LDK, LDT = Sh::LDT, NCT = Sh::NCT;
+  constexpr int ADB = 16 * Sh::LDD, ADP = Sh::LDD;
+  __shared__ __attribute__((aligned(16))) char smem[Sh::LDS_BYTES];
+  T* sE = reinterpret_cast<T*>(smem + Sh::OFF_E);
+  T* sWm = sE;  // -W reuses the E buffer once A and P are formed
+  T* sQ = reinterpret_cast<T*>(smem + Sh::OFF_Q);
+  T* sK = reinterpret_cast<T*>(smem + Sh::OFF_K);
+  T* sEt = reinterpret_cast<T*>(smem + Sh::OFF_ET);
+  T* sKt = reinterpret_cast<T*>(smem + Sh::OFF_KT);
+  T* sZt = reinterpret_cast<T*>(smem + Sh::OFF_ZT);
+  T* sP = reinterpret_cast<T*>(smem + Sh::OFF_P);
+  T* sAm = reinterpret_cast<T*>(smem + Sh::OFF_A);
+  T* sT = reinterpret_cast<T*>(smem + Sh::OFF_TB);
+  float* sFac = reinterpret_cast<float*>(smem + Sh::OFF_FAC);
+  float* sTot = reinterpret_cast<float*>(smem + Sh::OFF_TOT);
+  float* sAd = reinterpret_cast<float*>(smem + Sh::OFF_AD);
+  int* sFlag = reinterpret_cast<int*>(smem + Sh::OFF_FLAG);
+
+  int tid = threadIdx.x;
+  int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int m16 = lane & 15, g4 = lane >> 4;
+  int cg = tid % Sh::CG, tg = tid / Sh::CG, blk = tg / Sh::GPB;
+  int vcg = tid % Sh::VCG, vtg = tid / Sh::VCG;
+  auto fresh = [&]() {  // re-derive lane indices at each stage (see opaque())
+    tid = opaque(tid);
+    lane = tid & 63;
+    m16 = lane & 15;
+    g4 = lane >> 4;
+    cg = tid % Sh::CG;
+    tg = tid / Sh::CG;
+    blk = tg / Sh::GPB;
+    vcg = tid % Sh::VCG;
+    vtg = tid / Sh::VCG;
+  };
+  const long kstride = (long)H * DK, vstride = (long)H * DV;
+
+  Vec8<T> rq[Sh::TPT], rk[Sh::TPT], rg[Sh::TPT], rb[Sh::TPT];
+  Vec8<T> rv[Sh::VTPT], rw[Sh::VTPT];
+  auto load_raw = [&](const ChunkUnit& cu) {
+    const long kb = cu.row * kstride + (long)cu.h * DK + cg * 8;
+#pragma unroll
+    for (int j = 0; j < Sh::TPT; ++j) {
+      const int r = tg * Sh::TPT + j;
+      if (r < cu.nvalid) {
+        const long off = kb + (long)r * kstride;
+        rq[j].load(q + off);
+        rk[j].load(k + off);
+        rg[j].load(g + off);
+        rb[j].load(bg + off);
+      } else {
+        rq[j].zero(); rk[j].zero(); rg[j].zero(); rb[j].zero();
+      }
+    }
+    const long vb = cu.row * vstride + (long)cu.h * DV + vcg * 8;
+#pragma unroll
+    for (int j = 0; j < Sh::VTPT; ++j) {
+      const int r = vtg * Sh::VTPT + j;
+      if (r < cu.nvalid) {
+        const long off = vb + (long)r * vstride;
+        rv[j].load(v + off);
+        rw[j].load(wg + off);
+      } else {
+        rv[j].zero(); rw[j].zero();
+      }
+    }
+  };
+
+  // this thread's pieces of the previous unit's factors (see (g)) and their destination
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int KSK = DK / 32;
+  using Op = PrepPieces<DK, DV>;
+  u32x4 ost[Op::N];
+  char* prev_out = nullptr;
+  auto flush = [&]() {
+    if (prev_out == nullptr) return;
+#pragma unroll
+    for (int q = 0; q < Op::NW_; ++q) {
+      *reinterpret_cast<u32x4*>(prev_out + L.w + (tid + q * NT) * 16) = ost[Op::J_W + q];
+      *reinterpret_cast<u32x4*>(prev_out + L.q + (tid + q * NT) * 16) = ost[Op::J_Q + q];
+    }
+#pragma unroll
+    for (int q = 0; q < Op::NK_; ++q)
+      *reinterpret_cast<u32x4*>(prev_out + L.kt + (tid + q * NT) * 16) = ost[Op::J_K + q];
+    const int pb = tid >> 6;  // P blocks (0,1) and (1,1) are never read
+    if (pb != 1 && pb != 3) *reinterpret_cast<u32x4*>(prev_out + L.p + tid * 16) = ost[Op::J_P];
+#pragma unroll
+    for (int q = 0; q < Op::NU_; ++q)
+      *reinterpret_cast<u32x4*>(prev_out + L.u + (tid + q * NT) * 16) = ost[Op::J_U + q];
+    if (tid < DK / 4) *reinterpret_cast<u32x4*>(prev_out + L.g + tid * 16) = ost[Op::J_G];
+  };
+
+  // An unused slot (nvalid = 0) goes through the same steps on zero inputs and fills its
+  // own workspace unit, which nothing reads; the loads are unconditional (the prefetch
+  // after the last unit re-reads it) so the compiler's waits stay precise.
+  long u = blockIdx.x;
+  ChunkUnit cur = map_unit(u, H, cu_seqlens, N, T_len, lane);
+  load_raw(cur);
+
+  for (; u < nunits; u += gridDim.x) {
+    const long un = u + gridDim.x;
+    const ChunkUnit nxt = map_unit(un < nunits ? un : u, H, cu_seqlens, N, T_len, lane);
+    char* out = ws + u * L.bytes;
+
+    lds_barrier();  // the previous unit's readers of every buffer are done
+    fresh();
+    // ---- (a) per-thread totals of log2-decay
+    {
+      float tot8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < Sh::TPT; ++j) {
+        float f[8];
+        rg[j].to_float(f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) tot8[i] += f[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) tot8[i] *= kLog2e;
+      store8(sTot + tg * DK + cg * 8, tot8);
+    }
+    if (tid == 0) *sFlag = 0;
+    lds_barrier();
+    fresh();
+
+    // ---- (b) per-channel scan and decay factors
+    channel_scan<DK, Sh::TG, Sh::GPB, NT>(sTot, sFac, sFlag, tid);
+    lds_barrier();
+    fresh();
+    const bool block_path = __builtin_amdgcn_readfirstlane(*sFlag) != 0;
+
+    // ---- (c) gated, decayed operands
+    {
+      float run[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) run[i] = sTot[tg * DK + cg * 8 + i];
+      RunBuf<T, Sh::TPT> ev[8], kv[8];  // E 2^G and K 2^(Glast - G), per channel
+      auto token = [&](int j, const float* sub, const float* fA, const float* fB, bool scaled) {
+        const int r = tg * Sh::TPT + j;
+        float fg[8], fq[8], fk[8], fb[8], e1[8], q1[8], k1[8];
+        rg[j].to_float(fg);
+        rq[j].to_float(fq);
+        rk[j].to_float(fk);
+        rb[j].to_float(fb);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          run[i] += fg[i] * kLog2e;
+          const float x = scaled ? run[i] - sub[i] : run[i];
+          const float xe = fast_exp2(x), xk = fast_exp2(-x);
+          e1[i] = fb[i] * fk[i] * xe;
+          q1[i] = fq[i] * xe;
+          k1[i] = fk[i] * xk;
+          ev[i].put(j, scaled ? e1[i] * fA[i] : e1[i]);
+          kv[i].put(j, k1[i] * fB[i]);
+        }
+        store8_phi(sE + r * LDK, cg * 8, e1);
+        store8_phi(sQ + r * LDK, cg * 8, q1);
+        store8_phi(sK + r * LDK, cg * 8, k1);
+      };
+      if (!block_path) {
+        float gam[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) gam[i] = sFac[Fac::GAM * DK + cg * 8 + i];
+#pragma unroll
+        for (int j = 0; j < Sh::TPT; ++j) token(j, nullptr, nullptr, gam, false);
+      } else {
+        float fA[8], fB[8], sub[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          fA[i] = sFac[(Fac::ES + blk) * DK + cg * 8 + i];
+          fB[i] = sFac[(Fac::KNB + blk) * DK + cg * 8 + i];
+          sub[i] = sFac[(Fac::GS + blk) * DK + cg * 8 + i];
+        }
+#pragma unroll
+        for (int j = 0; j < Sh::TPT; ++j) token(j, sub, fA, fB, true);
+      }
+      const int sw = tswz(cg * 8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ev[i].store_sw(sEt + (cg * 8 + i) * LDT, sw, tg * Sh::TPT);
+        kv[i].template store_sw<true>(sKt + (cg * 8 + i) * LDT, sw, tg * Sh::TPT);
+      }
+      RunBuf<T, Sh::VTPT> zv[8];
+#pragma unroll
+      for (int j = 0; j < Sh::VTPT; ++j) {
+        float fv[8], fw[8];
+        rv[j].to_float(fv);
+        rw[j].to_float(fw);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) zv[i].put(j, fv[i] * fw[i]);
+      }
+      const int zsw = tswz(vcg * 8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) zv[i].store_sw(sZt + (vcg * 8 + i) * LDT, zsw, vtg * Sh::VTPT);
+    }
+    // the previous unit's factors to the workspace, then the next unit's prefetch: the
+    // wait for these loads (next unit's (a)) then covers stores issued before them rather
+    // than after (the waits cannot tell late stores from the loads)
+    flush();
+    load_raw(nxt);
+    lds_barrier();
+    fresh();
+
+    // ---- (d) A (negated) and P; the last wave forms the diagonal A tiles and inverts
+    // them in the same stage
+    constexpr int TDW = NW - 1;
+    if (!block_path) {
+      switch (wave) {
+        case 0: ap_tiles<T, DK, LDK, LDT, 0x0C0, 0>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
+        case 1: ap_tiles<T, DK, LDK, LDT, 0x118, 0>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
+        case 2: ap_tiles<T, DK, LDK, LDT, 0x002, 0x001>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
+        case 3: ap_tiles<T, DK, LDK, LDT, 0, 0x0C0>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
+        case 4: ap_tiles<T, DK, LDK, LDT, 0, 0x300>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
+        case 5: ap_tiles<T, DK, LDK, LDT, 0, 0x038>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
+        case 6: ap_tiles<T, DK, LDK, LDT, 0, 0x006>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
+        default:
+          ap_tiles<T, DK, LDK, LDT, 0x225, 0>(sE, sQ, sK, sAm, sP, sAd, m16, g4);
+          diag_inverse<T, LDT, ADB, ADP>(sAd, sT, m16, g4);
+          break;
+      }
+    } else {
+      ap_tiles_block<T, DK, LDK, LDT, ADB, ADP, NW>(sE, sQ, sK, sAm, sP, sAd, sFac, wave, lane);
+    }
+    zero_p_upper<T, LDT, NT>(sP, tid);
+    lds_barrier();
+    fresh();
+    if (block_path) {
+      // inverse blocks by the last wave; the others rescale Qa to Q 2^G
+      if (wave == TDW) diag_inverse<T, LDT, ADB, ADP>(sAd, sT, m16, g4);
+      for (int idx = tid; wave != TDW && idx < C * DK; idx += NT - 64) {
+        const int r = idx / DK, pc = idx % DK;
+        sQ[r * LDK + pc] = from_f<T>(to_f(sQ[r * LDK + pc]) *
+                                     sFac[(Fac::ES + r / 16) * DK + M::phi_inv(pc)]);
+      }
+      lds_barrier();
+      fresh();
+    }
+
+    // ---- (f) [W | U~] = (I + A)^{-1} [E 2^G | Z] by block forward substitution:
+    //   X_R = T_RR (RHS_R - sum_{J<R} A_RJ X_J)
+    // Column tiles (key tiles, then value tiles) are dealt round-robin to the waves.
+    {
+      using F16 = Frag16<T>;
+      typename F16::type fa[4][4];
+#pragma unroll
+      for (int R = 0; R < 4; ++R) {
+#pragma unroll
+        for (int J = 0; J < R; ++J) fa[R][J] = F16::load(sAm + (16 * R + m16) * LDT + 16 * J + 4 * g4);
+        fa[R][R] = F16::load(sT + (16 * R + m16) * LDT + 16 * R + 4 * g4);
+      }
+#pragma unroll
+      for (int t = 0; t < Sh::NTW; ++t) {
+        const int idx = wave + t * NW;
+        if (idx >= Sh::NTT) continue;
+        const bool isZ = idx >= NCT;
+        const int ct = isZ ? idx - NCT : idx;
+        const int crow = 16 * ct + m16;
+        const T* src = (isZ ? sZt : sEt) + crow * LDT;
+        f4 X[4];
+        typename F16::type Xb[4];
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+          f4 acc = load4f(src + tcol(crow, 16 * R + 4 * g4));
+#pragma unroll
+          for (int J = 0; J < R; ++J) acc = mma16_frag(fa[R][J], Xb[J], acc);
+          X[R] = mma16_frag(fa[R][R], F16::from_acc(acc), f4{0.f, 0.f, 0.f, 0.f});
+          Xb[R] = F16::from_acc(X[R]);
+        }
+        if (!isZ) {
+#pragma unroll
+          for (int R = 0; R < 4; ++R)
+            store_tile_pairs(sWm + (16 * R) * LDK, LDK, lane, -X[R],
+                             [&](int c) { return M::phi(16 * ct + c); });
+        } else {
+          // U~ D tile (ct, R), lane-major with 4 bf16 per lane (its workspace order)
+#pragma unroll
+          for (int R = 0; R < 4; ++R)
+            *reinterpret_cast<uint2*>(smem + Sh::OFF_U + ((ct * 4 + R) * 64 + lane) * 8) =
+                make_uint2(pack_bf16(X[R][0], X[R][1]), pack_bf16(X[R][2], X[R][3]));
+        }
+      }
+    }
+    lds_barrier();
+    fresh();
+
+    // ---- (g) this unit's factors, in workspace order, from LDS into registers; they are
+    // stored during the next unit (or after the loop), just before its prefetch loads
+    {
+#pragma unroll
+      for (int q = 0; q < Op::NW_; ++q) {  // -W and Qbar
+        const int p = tid + q * NT, bi = p >> 6, l = p & 63;
+        const int row = 16 * (bi / KSK) + (l & 15), col = 32 * (bi % KSK) + 8 * (l >> 4);
+        ost[Op::J_W + q] = *reinterpret_cast<const u32x4*>(sWm + row * LDK + col);
+        ost[Op::J_Q + q] = *reinterpret_cast<const u32x4*>(sQ + row * LDK + col);
+      }
+#pragma unroll
+      for (int q = 0; q < Op::NK_; ++q) {  // Kt: [channel][phi-ordered tokens], swizzled
+        const int p = tid + q * NT, bi = p >> 6, l = p & 63;
+        const int row = 16 * (bi >> 1) + (l & 15), grp = 8 * (bi & 1) + 2 * (l >> 4);
+        ost[Op::J_K + q] = *reinterpret_cast<const u32x4*>(sKt + row * LDT + ((grp ^ tswz(row)) << 2));
+      }
+      {  // P
+        const int p = tid, bi = p >> 6, l = p & 63;
+        const int row = 16 * (bi >> 1) + (l & 15), col = 32 * (bi & 1) + 8 * (l >> 4);
+        ost[Op::J_P] = *reinterpret_cast<const u32x4*>(sP + row * LDT + col);
+      }
+#pragma unroll
+      for (int q = 0; q < Op::NU_; ++q)  // U~ tiles
+        ost[Op::J_U + q] = *reinterpret_cast<const u32x4*>(smem + Sh::OFF_U + (tid + q * NT) * 16);
+      if (tid < DK / 4)  // gamma
+        ost[Op::J_G] = *reinterpret_cast<const u32x4*>(sFac + Fac::GAM * DK + 4 * tid);
+    }
+    prev_out = out;
+    cur = nxt;
+  }
+  lds_barrier();
+  flush();
+}
+
+// ------------------------------------------------------------------ phase 2: recurrence
+template <int DK, int DV, int NV>
+struct StateShape {
+  static constexpr int C = 64;
+  static constexpr int NWV = NV / 16;     // waves: wave w owns state columns [16w, 16w+16)
+  static constexpr int NT = 64 * NWV;
+  static constexpr int KSK = DK / 32;     // 32-channel K steps
+  static constexpr int NMT = DK / 16;     // 16-row state tiles per wave
+  static constexpr SplitLayout L = SplitLayout(DK, DV);
+  // one staged chunk: [-W | Qbar | Kt | P] (contiguous in the workspace), this slice's U~
+  // tiles, gamma
+  static constexpr int SZ_A = (int)L.u;
+  static constexpr int SZ_U = NWV * 4 * 512;
+  static constexpr int OFF_U = SZ_A;
+  static constexpr int OFF_G = OFF_U + SZ_U;
+  static constexpr int NPIECE = (OFF_G + DK * 4) / 16;  // 16-byte pieces per chunk
+  static constexpr int PPT = (NPIECE + NT - 1) / NT;    // pieces per thread
+  // every thread moves PPT pieces (the tail ones re-read the last piece into padding),
+  // so the staging code has no branches and its registers stay registers
+  static constexpr int STAGE = PPT * NT * 16;
+  static constexpr int OP = NV + 8;                   // output staging pitch
+  static constexpr int SZ_O = C * OP * 2;
+  static constexpr int OFF_O = 2 * STAGE;             // two output staging buffers
+  static constexpr int LDS_BYTES = OFF_O + 2 * SZ_O;
+  static_assert(STAGE % 16 == 0, "stage");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+template <int DK, int DV, int NV>
+__global__ void __launch_bounds__((StateShape<DK, DV, NV>::NT)) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict__ o,
+                  float* sN, const int* __restrict__ cu_seqlens, int T_len, int H,
+                  int nslices, int nunits) {
+  typedef bf16 T;
+  using Sh = StateShape<DK, DV, NV>;
+  using M = Mma<T>;
+  constexpr SplitLayout L(DK, DV);
+  constexpr int C = Sh::C, NT = Sh::NT, KSK = Sh::KSK, NMT = Sh::NMT, OP = Sh::OP;
+  __shared__ __attribute__((aligned(16))) char smem[Sh::LDS_BYTES];
+
+  int tid = threadIdx.x;
+  int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int m16 = lane & 15, g4 = lane >> 4;
+
+  // workgroup -> (sequence, head, slice); slices of one head on one XCD (ids congruent
+  // mod 8) so the shared factor reads of the second slice hit that XCD's L2
+  const int grp = blockIdx.x / (8 * nslices);
+  const int gsz = min(8, nunits - grp * 8);
+  const int gi = blockIdx.x - grp * 8 * nslices;
+  const int slice = gi / gsz;
+  const int nh = grp * 8 + gi % gsz;
+  const int h = nh % H;
+  const int n = nh / H;
+  const int col0 = slice * NV;
+
+  long row0, slot0;
+  int len;
+  if (cu_seqlens != nullptr) {
+    int a = cu_seqlens[n], b = cu_seqlens[n + 1];
+    a = a < 0 ? 0 : (a > T_len ? T_len : a);
+    b = b < a ? a : (b > T_len ? T_len : b);
+    row0 = a;
+    len = b - a;
+    slot0 = a / C + n;
+  } else {
+    row0 = (long)n * T_len;
+    len = T_len;
+    slot0 = (long)n * ((T_len + C - 1) / C);
+  }
+  const int nch = (len + C - 1) / C;
+  const long vstride = (long)H * DV;
+  T* ob = o + row0 * vstride + (long)h * DV + col0;
+
+  // state: tile mt holds key rows [16mt, 16mt+16), column col0 + 16*wave + m16; lane holds
+  // rows 16mt + 4*g4 + i
+  f4 S[NMT];
+  const long sbase = ((long)n * H + h) * DK * DV + col0 + 16 * wave + m16;
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      S[mt][i] = (s0 != nullptr) ? s0[sbase + (long)(16 * mt + 4 * g4 + i) * DV] : 0.f;
+
+  // Staging of the chunk operands: global -> registers -> LDS, one chunk ahead: at the end
+  // of chunk c the registers (chunk c+1) go to the LDS buffer that chunk c-1 used and are
+  // refilled with chunk c+2. (A plain vector type: an array of HIP's uint4 struct of this
+  // length is kept in scratch memory.)
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 stg[Sh::PPT];
+  // workspace offset of staged piece p: [-W | Qbar | Kt | P] as is, then this slice's U~
+  // tiles, then gamma (selects, no branches)
+  static_assert(Sh::OFF_U == (int)L.u, "staged prefix matches the workspace prefix");
+  const int u_shift = slice * Sh::SZ_U;
+  auto piece_src = [&](int p, long chunk) -> const u32x4* {
+    const char* unit = ws + ((slot0 + chunk) * H + h) * L.bytes;
+    const int off = p * 16 + (p >= Sh::OFF_U / 16 && p < Sh::OFF_G / 16 ? u_shift : 0) +
+                    (p >= Sh::OFF_G / 16 ? (int)L.g - Sh::OFF_G : 0);
+    return reinterpret_cast<const u32x4*>(unit + off);
+  };
+  auto stage_load = [&](long chunk) {
+#pragma unroll
+    for (int j = 0; j < Sh::PPT; ++j) {
+      const int p = tid + j * NT;
+      stg[j] = *piece_src(p < Sh::NPIECE ? p : Sh::NPIECE - 1, chunk);
+    }
+  };
+  auto stage_store = [&](char* buf) {
+#pragma unroll
+    for (int j = 0; j < Sh::PPT; ++j) *reinterpret_cast<u32x4*>(buf + (tid + j * NT) * 16) = stg[j];
+  };
+  // output rows of the previous chunk: staging buffer -> HBM (16-byte pieces)
+  constexpr int OPR = NV / 8;  // pieces per row
+  static_assert((C * OPR) % NT == 0, "output pieces per thread");
+  auto out_store = [&](const T* so, long c0, int nrows) {
+#pragma unroll
+    for (int j = 0; j < C * OPR / NT; ++j) {
+      const int p = tid + j * NT;
+      const int r = p / OPR, cc = p % OPR;
+      if (r < nrows)
+        *reinterpret_cast<uint4*>(ob + (c0 + r) * vstride + cc * 8) =
+            *reinterpret_cast<const uint4*>(so + r * OP + cc * 8);
+    }
+  };
+
+  if (nch > 0) {
+    stage_load(0);
+    stage_store(smem);
+    stage_load(nch > 1 ? 1 : 0);
+  }
+  lds_barrier();
+
+  for (int ci = 0; ci < nch; ++ci) {
+    tid = opaque(tid);
+    lane = tid & 63;
+    m16 = lane & 15;
+    g4 = lane >> 4;
+    const char* B = smem + (ci & 1) * Sh::STAGE;
+    T* so = reinterpret_cast<T*>(smem + Sh::OFF_O + (ci & 1) * Sh::SZ_O);
+    auto frag = [&](int off, int blk) {
+      return *reinterpret_cast<const typename M::frag*>(B + off + blk * 1024 + lane * 16);
+    };
+    typename M::frag sb[KSK];
+#pragma unroll
+    for (int s = 0; s < KSK; ++s) sb[s] = M::from_acc(S, s);
+    // U = U~ - W S
+    f4 U[4];
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+      const bf16x4 ut = *reinterpret_cast<const bf16x4*>(B + Sh::OFF_U + ((wave * 4 + R) * 64 + lane) * 8);
+      U[R] = f4{to_f(ut[0]), to_f(ut[1]), to_f(ut[2]), to_f(ut[3])};
+    }
+    // Fragments are read from LDS in batches ahead of their products, so that many reads
+    // are in flight at once (one wave per SIMD: nothing else hides LDS latency).
+    typename M::frag fw[4 * KSK];
+#pragma unroll
+    for (int i = 0; i < 4 * KSK; ++i) fw[i] = frag((int)L.w, i);
+    typename M::frag fq[4 * KSK];
+#pragma unroll
+    for (int i = 0; i < 4 * KSK; ++i) fq[i] = frag((int)L.q, i);
+    __builtin_amdgcn_sched_barrier(0);  // all of the above is issued before any product
+    typename M::frag fk[2 * NMT], fp[6];
+#pragma unroll
+    for (int i = 0; i < 2 * NMT; ++i) fk[i] = frag((int)L.kt, i);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) fp[i] = frag((int)L.p, i < 2 ? 2 * i : i + 2);  // blocks 0,2,4,5,6,7
+    f4 gam[NMT];
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) gam[mt] = *reinterpret_cast<const f4*>(B + Sh::OFF_G + (16 * mt + 4 * g4) * 4);
+#pragma unroll
+    for (int R = 0; R < 4; ++R)
+#pragma unroll
+      for (int s = 0; s < KSK; ++s) U[R] = M::mma(fw[R * KSK + s], sb[s], U[R]);
+    // O = Qbar S + P U
+    f4 O[4];
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+      O[R] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KSK; ++s) O[R] = M::mma(fq[R * KSK + s], sb[s], O[R]);
+    }
+    typename M::frag ub[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) ub[s] = M::from_acc(U, s);
+    // S <- Diag(gamma) S + Kt U
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      f4 acc = S[mt] * gam[mt];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) acc = M::mma(fk[mt * 2 + s], ub[s], acc);
+      S[mt] = acc;
+    }
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+#pragma unroll
+      for (int s = 0; s < causal_steps<32>(R); ++s) O[R] = M::mma(fp[R < 2 ? R : 2 * R - 2 + s], ub[s], O[R]);
+      store_tile_pairs(so + (16 * R) * OP + 16 * wave, OP, lane, O[R], [](int c) { return c; });
+    }
+    // next chunk's operands into the other buffer (its last readers finished before the
+    // previous barrier); the previous chunk's output (staged before the last barrier) to
+    // HBM; then the loads for the chunk after (unconditional: past the end they re-read the
+    // last chunk). Issuing the stores before the loads matters: the wait for these loads
+    // at the end of the next chunk then also covers stores a whole chunk old, instead of
+    // stores issued after the loads (which the waits cannot tell apart from them).
+    if (ci + 1 < nch) stage_store(smem + ((ci + 1) & 1) * Sh::STAGE);
+    if (ci > 0) {
+      const int pv = len - (ci - 1) * C;
+      out_store(reinterpret_cast<const T*>(smem + Sh::OFF_O + ((ci - 1) & 1) * Sh::SZ_O),
+                (long)(ci - 1) * C, pv < C ? pv : C);
+    }
+    stage_load(ci + 2 < nch ? ci + 2 : nch - 1);
+    lds_barrier();
+  }
+  if (nch > 0) {
+    const int pv = len - (nch - 1) * C;
+    out_store(reinterpret_cast<const T*>(smem + Sh::OFF_O + ((nch - 1) & 1) * Sh::SZ_O),
+              (long)(nch - 1) * C, pv < C ? pv : C);
+  }
+  if (sN != nullptr) {
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sN[sbase + (long)(16 * mt + 4 * g4 + i) * DV] = S[mt][i];
+  }
+}
+
+// ------------------------------------------------------------------ launch
+static int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <int DK, int DV, int NV>
+static hipError_t launch_split(const ChunkArgs& a) {
+  const bool varlen = a.cu_seqlens != nullptr;
+  const long nunits = split_slots(varlen, a.B, a.T, a.N) * a.H;
+  hipStream_t st = (hipStream_t)a.stream;
+  if (nunits > 0) {
+    const long grid1 = nunits < cu_count() ? nunits : cu_count();
+    hipLaunchKernelGGL((gdn2_prep_kernel<DK, DV>), dim3((unsigned)grid1), dim3(512), 0, st,
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.g,
+                       (const bf16*)a.b, (const bf16*)a.w, (char*)a.workspace, a.cu_seqlens,
+                       a.N, a.T, a.H, nunits);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int nslices = DV / NV;
+  const long grid2 = (long)a.N * a.H * nslices;
+  hipLaunchKernelGGL((gdn2_state_kernel<DK, DV, NV>), dim3((unsigned)grid2),
+                     dim3(StateShape<DK, DV, NV>::NT), 0, st, (const char*)a.workspace, a.s0,
+                     (bf16*)a.o, a.sN, a.cu_seqlens, a.T, a.H, nslices, a.N * a.H);
+  return hipGetLastError();
+}
+
+template <int DK, int DV>
+static hipError_t dispatch_split_nv(const ChunkArgs& a) {
+  if (a.nv == 32) return launch_split<DK, DV, 32>(a);
+  if (a.nv == 64) return launch_split<DK, DV, 64>(a);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_fwd_split(const ChunkArgs& a) {
+  if (a.dtype != 0) return hipErrorInvalidValue;
+  if (a.d_k == 64 && a.d_v == 64) return dispatch_split_nv<64, 64>(a);
+  if (a.d_k == 64 && a.d_v == 128) return dispatch_split_nv<64, 128>(a);
+  if (a.d_k == 128 && a.d_v == 64) return dispatch_split_nv<128, 64>(a);
+  if (a.d_k == 128 && a.d_v == 128) return dispatch_split_nv<128, 128>(a);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdn2

@@ -46,6 +46,7 @@ enum {
   GDN2_OK = 0,
   GDN2_INVALID_ARGUMENT = 1, /* null required pointer, bad sizes, misaligned pointer */
   GDN2_UNSUPPORTED = 2,      /* head widths / dtype combination not built */
+  GDN2_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below gdn2_chunk_fwd_workspace_bytes */
   GDN2_LAUNCH_FAILED = 4     /* the HIP runtime rejected a launch */
 };
 
@@ -65,20 +66,43 @@ enum {
  *   cu_seqlens         : NULL, or device int32 [N+1] offsets into the token axis of a
  *                        packed batch (then B must be 1 and T is the packed length).
  *                        Offsets must be non-decreasing with cu_seqlens[0] = 0 and
- *                        cu_seqlens[N] = T; the kernel clamps them into [0, T] so a bad
- *                        table cannot make it access memory out of bounds.
+ *                        cu_seqlens[N] = T; the kernels clamp them into [0, T] so a bad
+ *                        table cannot make them access memory out of bounds (its
+ *                        results are then undefined).
+ *   workspace          : NULL, or device scratch of at least
+ *                        gdn2_chunk_fwd_workspace_bytes(...) bytes (16-byte aligned),
+ *                        owned by the caller and free for the call's duration on
+ *                        `hip_stream`. With a workspace the call runs the two-phase path:
+ *                        one kernel computes every chunk's factors in parallel into the
+ *                        workspace, a second walks the chunks of each sequence in order.
+ *                        Without one, a single fused kernel does both per sequence.
+ *                        Results agree to rounding. Ignored when
+ *                        gdn2_chunk_fwd_workspace_bytes returns 0 for the dtype/widths.
  *   Without cu_seqlens, N must equal B and every sequence has length T.
  *   Supported: GDN2_BF16 with d_k, d_v in {64, 128}; GDN2_F32 with d_k = 64 and
- *   d_v in {64, 128}. T = 0 or N = 0 is a no-op (apart from final_state = initial).
- * Returns GDN2_OK or an error status.
+ *   d_v in {64, 128} (fused path only). T = 0 or N = 0 is a no-op (apart from
+ *   final_state = initial).
+ * Returns GDN2_OK or an error status (GDN2_WORKSPACE_TOO_SMALL when workspace_bytes is
+ * below the requirement).
  */
 int gdn2_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
                    const void* b, const void* w, const float* initial_state, void* o,
                    float* final_state, const int32_t* cu_seqlens, int B, int T, int H,
-                   int d_k, int d_v, int N, int dtype, void* hip_stream);
+                   int d_k, int d_v, int N, int dtype, void* workspace,
+                   size_t workspace_bytes, void* hip_stream);
 
 /*
- * gdn2_chunk_fwd with an explicit value-slice width: each workgroup carries
+ * Device workspace, in bytes, that the two-phase path of gdn2_chunk_fwd needs for a call
+ * with these sizes, with or without cu_seqlens (about 1.13 KiB per token and head at
+ * d_k = d_v = 128, plus one chunk per sequence). 0 when the two-phase path is not built
+ * for dtype / d_k / d_v (GDN2_BF16 with d_k, d_v in {64, 128} is) or a size is negative.
+ */
+size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int N,
+                                      int dtype);
+
+/*
+ * The fused single-kernel path of gdn2_chunk_fwd (no workspace) with an explicit
+ * value-slice width: each workgroup carries
  * `value_slice` columns of the state (16, 32, 64 or 128; a divisor of d_v; 16 only with
  * d_k = 64; at most 64 for GDN2_F32). 0 selects the width automatically, exactly as
  * gdn2_chunk_fwd does. Results do not depend on the width beyond rounding. Returns

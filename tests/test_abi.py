@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
 def test_version_and_status_strings():
     L = _lib.lib()
     assert b"gfx950" in L.gdn2_version()
-    for s in (0, 1, 2, 4, 99):
+    for s in (0, 1, 2, 3, 4, 99):
         assert L.gdn2_status_string(s)
 
 
@@ -42,11 +42,12 @@ MIS = ctypes.c_void_p(0x100004)
 
 def _chunk(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, w=FAKE, s0=None, o=FAKE, sN=None, cu=None,
-             B=2, T=64, H=4, dk=128, dv=128, N=2, dtype=0)
+             B=2, T=64, H=4, dk=128, dv=128, N=2, dtype=0, ws=None, wsz=0)
     a.update(kw)
     return _lib.lib().gdn2_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["b"], a["w"], a["s0"],
                                      a["o"], a["sN"], a["cu"], a["B"], a["T"], a["H"],
-                                     a["dk"], a["dv"], a["N"], a["dtype"], None)
+                                     a["dk"], a["dv"], a["N"], a["dtype"], a["ws"], a["wsz"],
+                                     None)
 
 
 def test_chunk_fwd_error_paths():
@@ -62,6 +63,32 @@ def test_chunk_fwd_error_paths():
     assert _chunk(k=MIS) == 1               # misaligned
     assert _chunk(cu=FAKE, B=2) == 1        # packed batches have B == 1
     assert _chunk(B=0, N=0, q=None, k=None, v=None, g=None, b=None, w=None, o=None) == 0
+    # two-phase path: the workspace must be aligned and large enough
+    # (sizes just below what this call needs: 2 sequences x 1 chunk x 4 heads x 74240 B, so
+    # nothing is launched)
+    need = 2 * 1 * 4 * 74240
+    assert _chunk(ws=MIS, wsz=need) == 1
+    assert _chunk(ws=FAKE, wsz=need - 1) == 3
+    assert _chunk(ws=FAKE, wsz=0) == 3
+    assert _chunk(ws=FAKE, wsz=need - 1, cu=FAKE, B=1, T=128, N=2) == 3  # packed: 4 slots
+    # fp32 has no two-phase path: the workspace is ignored (then the N check still applies)
+    assert _chunk(ws=FAKE, wsz=0, dtype=1, dk=64, N=3) == 1
+
+
+def test_workspace_bytes():
+    L = _lib.lib()
+    unit128 = 4 * 4 * 1024 * 3 + 8 * 1024 + 8 * 4 * 512 + 512  # -W, Qbar, Kt, P, U~, gamma
+    assert unit128 == 74240
+    # fixed length: B * ceil(T / 64) slots; packed: floor(T / 64) + N; the larger of the two
+    assert L.gdn2_chunk_fwd_workspace_bytes(2, 64, 4, 128, 128, 2, 0) == (2 + 2) * 4 * unit128
+    assert L.gdn2_chunk_fwd_workspace_bytes(1, 2048, 16, 128, 128, 1, 0) == 33 * 16 * unit128
+    assert L.gdn2_chunk_fwd_workspace_bytes(8, 2048, 16, 128, 128, 8, 0) == (256 + 8) * 16 * unit128
+    assert L.gdn2_chunk_fwd_workspace_bytes(64, 100, 1, 128, 128, 64, 0) == (100 + 64) * unit128
+    unit64 = 4 * 2 * 1024 * 3 + 8 * 1024 + 4 * 4 * 512 + 256
+    assert L.gdn2_chunk_fwd_workspace_bytes(1, 64, 1, 64, 64, 1, 0) == 2 * ((unit64 + 255) // 256 * 256)
+    assert L.gdn2_chunk_fwd_workspace_bytes(1, 64, 1, 64, 64, 1, 1) == 0    # fp32: fused only
+    assert L.gdn2_chunk_fwd_workspace_bytes(1, 64, 1, 96, 64, 1, 0) == 0
+    assert L.gdn2_chunk_fwd_workspace_bytes(1, -1, 1, 64, 64, 1, 0) == 0
 
 
 def test_chunk_fwd_sliced_error_paths():

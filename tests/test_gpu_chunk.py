@@ -1,5 +1,7 @@
 """GPU parity of the chunkwise forward (through the C ABI) against the float64 oracle.
 
+Both paths are covered: "fused" (one kernel per sequence, value-slice widths) and "split"
+(two-phase: parallel chunk factors into a workspace, then the per-sequence recurrence).
 Tolerances (normwise max relative error per tensor, on o and on the final state):
 1e-4 for fp32 runs, 2e-2 for bf16 runs.
 """
@@ -27,7 +29,7 @@ def _lib():
     return G
 
 
-def run_gpu(x, value_slice=0, s0=None, use_s0=True):
+def run_gpu(x, value_slice=0, s0=None, use_s0=True, path="auto"):
     G = _lib()
     dt = x["dtype"]
     t = {n: dev_tensor(x[n], dt) for n in NAMES}
@@ -35,7 +37,7 @@ def run_gpu(x, value_slice=0, s0=None, use_s0=True):
     s0_t = None if s0 is None else torch.from_numpy(np.ascontiguousarray(s0, np.float32)).cuda()
     cu = None if x["cu_seqlens"] is None else torch.from_numpy(x["cu_seqlens"]).cuda()
     o, sN = G.chunk_fwd(*(t[n] for n in NAMES), initial_state=s0_t, cu_seqlens=cu,
-                        value_slice=value_slice)
+                        value_slice=value_slice, path=path)
     torch.cuda.synchronize()
     return o, sN
 
@@ -81,6 +83,27 @@ def test_bf16_ragged_with_state(dk, dv, nv):
     assert_close("S", host64(sN), s_ref, TOL["bf16"])
 
 
+@pytest.mark.parametrize("dk,dv", [(dk, dv) for dk in (64, 128) for dv in (64, 128)])
+def test_bf16_ragged_split(dk, dv):
+    x = make_inputs(2, 200, 2, dk, dv, "bf16", seed=3 + dk + dv, s0_std=0.02)
+    say("bf16 ragged B2 T200 H2 split", dk, dv)
+    o, sN = run_gpu(x, path="split")
+    o_ref, s_ref = run_oracle(x)
+    assert_close("o", host64(o), o_ref, TOL["bf16"])
+    assert_close("S", host64(sN), s_ref, TOL["bf16"])
+
+
+def test_split_many_heads_value_slices():
+    # 2 x 70 chains: the recurrence kernel takes 64-wide slices (>= 256 workgroups) and
+    # the factor kernel loops over many (chunk, head) units per workgroup
+    x = make_inputs(2, 130, 70, 128, 128, "bf16", seed=17, s0_std=0.02)
+    say("split B2 T130 H70")
+    o, sN = run_gpu(x, path="split")
+    o_ref, s_ref = run_oracle(x)
+    assert_close("o", host64(o), o_ref, TOL["bf16"])
+    assert_close("S", host64(sN), s_ref, TOL["bf16"])
+
+
 @pytest.mark.parametrize("dv,nv", [(128, 16), (128, 32), (128, 64), (64, 32)])
 def test_fp32_ragged_with_state(dv, nv):
     x = make_inputs(1, 150, 3, 64, dv, "fp32", seed=31 + nv, s0_std=0.02)
@@ -91,69 +114,90 @@ def test_fp32_ragged_with_state(dv, nv):
     assert_close("S", host64(sN), s_ref, TOL["fp32"])
 
 
-@pytest.mark.parametrize("dt", ["bf16", "fp32"])
-def test_varlen_small_edges(dt):
+@pytest.mark.parametrize("dt,path", [("bf16", "fused"), ("bf16", "split"), ("fp32", "fused")])
+def test_varlen_small_edges(dt, path):
     lens = [1, 63, 64, 0, 65, 130, 7]
     dk = 128 if dt == "bf16" else 64
     x = make_inputs(1, sum(lens), 2, dk, 64, dt, seed=77, lengths=lens, s0_std=0.02)
-    say("varlen small", dt, lens)
-    o, sN = run_gpu(x)
+    say("varlen small", dt, path, lens)
+    o, sN = run_gpu(x, path=path)
     o_ref, s_ref = run_oracle(x)
     assert_close("o", host64(o), o_ref, TOL[dt])
     assert_close("S", host64(sN), s_ref, TOL[dt])
 
 
-def test_varlen_equals_separate_runs():
+def test_varlen_many_sequences_split():
+    # 150 sequences (lengths 0..200, several empty): the factor kernel finds each chunk's
+    # sequence with a 64-way search that needs more than one round here
+    rng = np.random.default_rng(123)
+    lens = [int(v) for v in rng.integers(0, 200, size=150)]
+    lens[3] = lens[77] = 0
+    x = make_inputs(1, sum(lens), 1, 64, 64, "bf16", seed=55, lengths=lens, s0_std=0.02)
+    say("varlen 150 sequences split", sum(lens), "tokens")
+    o, sN = run_gpu(x, path="split")
+    o_ref, s_ref = run_oracle(x)
+    assert_close("o", host64(o), o_ref, TOL["bf16"])
+    assert_close("S", host64(sN), s_ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("path", ["fused", "split"])
+def test_varlen_equals_separate_runs(path):
     lens = [70, 5, 128, 33]
     x = make_inputs(1, sum(lens), 2, 128, 128, "bf16", seed=91, lengths=lens, s0_std=0.02)
-    say("varlen vs separate", lens)
-    o, sN = run_gpu(x, 64)
+    say("varlen vs separate", path, lens)
+    vs = 64 if path == "fused" else 0
+    o, sN = run_gpu(x, vs, path=path)
     cu = x["cu_seqlens"]
     for n in range(len(lens)):
         sl = slice(cu[n], cu[n + 1])
         xn = {m: x[m][:, sl] for m in NAMES}
         xn.update(dtype="bf16", cu_seqlens=None, s0=x["s0"][n:n + 1])
-        on, sn = run_gpu(xn, 64)
+        on, sn = run_gpu(xn, vs, path=path)
         assert torch.equal(o[:, sl], on)
         assert torch.equal(sN[n:n + 1], sn)
 
 
-def test_deterministic():
+@pytest.mark.parametrize("path", ["fused", "split"])
+def test_deterministic(path):
     x = make_inputs(2, 300, 4, 128, 128, "bf16", seed=5)
-    say("determinism")
-    o1, s1 = run_gpu(x)
-    o2, s2 = run_gpu(x)
+    say("determinism", path)
+    o1, s1 = run_gpu(x, path=path)
+    o2, s2 = run_gpu(x, path=path)
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
 
 
-def test_zero_length_and_alias():
+@pytest.mark.parametrize("path", ["fused", "split"])
+def test_zero_length_and_alias(path):
     G = _lib()
     x = make_inputs(2, 96, 2, 128, 128, "bf16", seed=3, s0_std=0.02)
-    say("T=0 and aliasing")
+    say("T=0 and aliasing", path)
     t = {n: dev_tensor(x[n], "bf16") for n in NAMES}
     s0 = torch.from_numpy(x["s0"]).cuda()
     # T = 0: final state is the initial state
     empty = {n: t[n][:, :0].contiguous() for n in NAMES}
-    _, sN = G.chunk_fwd(*(empty[n] for n in NAMES), initial_state=s0)
+    _, sN = G.chunk_fwd(*(empty[n] for n in NAMES), initial_state=s0, path=path)
     torch.cuda.synchronize()
     assert torch.equal(sN, s0)
     # final_state aliasing initial_state through the C ABI
     import ctypes
     from gated_delta_rule_36_amd import _lib as L
-    o_ref, s_ref = run_gpu(x)
+    o_ref, s_ref = run_gpu(x, path=path)
     st = s0.clone()
     o = torch.empty_like(t["v"])
     p = lambda a: ctypes.c_void_p(a.data_ptr())
+    nws = L.lib().gdn2_chunk_fwd_workspace_bytes(2, 96, 2, 128, 128, 2, 0) if path == "split" else 0
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
     rc = L.lib().gdn2_chunk_fwd(*(p(t[n]) for n in NAMES), p(st), p(o), p(st), None,
-                                2, 96, 2, 128, 128, 2, 0,
+                                2, 96, 2, 128, 128, 2, 0, p(ws) if nws else None, nws,
                                 ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     torch.cuda.synchronize()
     assert rc == 0
     assert torch.equal(o, o_ref) and torch.equal(st, s_ref)
 
 
+@pytest.mark.parametrize("path", ["fused", "split"])
 @pytest.mark.parametrize("case", ["all_g_-5", "b0", "b1_w1", "w0", "b2"])
-def test_extreme_gates(case):
+def test_extreme_gates(case, path):
     x = make_inputs(1, 160, 2, 128, 128, "bf16", seed=13, s0_std=0.02)
     if case == "all_g_-5":
         x["g"][:] = -5.0
@@ -166,8 +210,8 @@ def test_extreme_gates(case):
         x["w"][:] = 0.0
     elif case == "b2":  # erase gate widened to [0, 2]
         x["b"] = (2.0 * x["b"]).astype(np.float32)
-    say("extreme gates", case)
-    o, sN = run_gpu(x)
+    say("extreme gates", case, path)
+    o, sN = run_gpu(x, path=path)
     o_ref, s_ref = run_oracle(x)
     assert_close("o", host64(o), o_ref, TOL["bf16"])
     assert_close("S", host64(sN), s_ref, TOL["bf16"])
@@ -226,25 +270,28 @@ def _check_chains(x, o, sN, chains):
         assert_close("S", host64(sN[n:n + 1, h:h + 1]), s_ref, TOL["bf16"])
 
 
-def test_layer1p3b_full_size_sampled():
+@pytest.mark.parametrize("path", ["fused", "split"])
+def test_layer1p3b_full_size_sampled(path):
     x = _full("layer1p3b_bf16")
-    say("layer1p3b B8 H16 T2048 d128 bf16 (auto slice)")
-    o, sN = run_gpu(x)
+    say("layer1p3b B8 H16 T2048 d128 bf16 (auto slice)", path)
+    o, sN = run_gpu(x, path=path)
     _check_chains(x, o, sN, [(0, 0), (3, 7), (7, 15)])
 
 
-def test_longctx_full_size_sampled():
+@pytest.mark.parametrize("path", ["fused", "split"])
+def test_longctx_full_size_sampled(path):
     x = _full("longctx_bf16")
-    say("longctx B1 H16 T32768 d128 bf16, 10% near-resets")
-    o, sN = run_gpu(x)
+    say("longctx B1 H16 T32768 d128 bf16, 10% near-resets", path)
+    o, sN = run_gpu(x, path=path)
     _check_chains(x, o, sN, [(0, 0), (0, 11)])
 
 
-def test_varlen_full_size_sampled():
+@pytest.mark.parametrize("path", ["fused", "split"])
+def test_varlen_full_size_sampled(path):
     x = _full("varlen_bf16")
     lens = np.diff(x["cu_seqlens"])
-    say("varlen 16 seqs", int(lens.sum()), "tokens")
-    o, sN = run_gpu(x)
+    say("varlen 16 seqs", int(lens.sum()), "tokens", path)
+    o, sN = run_gpu(x, path=path)
     longest = int(np.argmax(lens))
     shortest = int(np.argmin(lens))
     _check_chains(x, o, sN, [(longest, 3), (shortest, 9), (5, 15)])
