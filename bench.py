@@ -1,12 +1,15 @@
 """Benchmark: GDN-2 chunkwise forward tokens/s on one MI355X, with roofline fractions.
 
 A step is one gdn2_chunk_fwd call over the 1.3B-layer workload (B=8, H=16, T=2048,
-d_k = d_v = 128, bf16 inputs, fp32 state, zero initial state), inputs resident in HBM.
+d_k = d_v = 128, bf16 inputs, fp32 state, zero initial state), inputs resident in HBM;
+with the path chunk_fwd's "auto" picks (two-phase: its two launches are timed together as
+one call).
 Prints ONE JSON line. Also reports (as extra fields) the recurrent decode step on the
 decode workload (256 sequences x 16 heads, fp32 128x128 states) and a CPU baseline: the
 float64 oracle timed on a bounded sample of the forward workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+                    [--path auto|split|fused] [--workload layer1p3b|longctx|varlen]
 """
 from __future__ import annotations
 
@@ -30,8 +33,9 @@ NAMES = ("q", "k", "v", "g", "b", "w")
 
 
 def measured_traffic(key):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when the
-    kernel's sources changed since the counters were taken (digest mismatch)."""
+    """HBM bytes per call from the committed rocprofv3 counter summary (summed over the
+    call's kernels), or None when a kernel's sources changed since the counters were taken
+    (digest mismatch) or no record exists."""
     import hashlib
     try:
         with open(os.path.join(ROOT, "profiles", "counters.json")) as f:
@@ -93,7 +97,13 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--path", choices=("auto", "split", "fused"), default="auto",
-                    help="chunk-forward path: two-phase (split), single fused kernel, or auto")
+                    help="chunk-forward path: two-phase (split), single fused kernel, or auto "
+                         "(as chunk_fwd chooses)")
+    ap.add_argument("--workload", choices=("layer1p3b", "longctx", "varlen"),
+                    default="layer1p3b",
+                    help="layer1p3b (the reported metric), or one of the other synthetic "
+                         "workloads for information: B1 H16 T32768 with 10%% near-resets, or "
+                         "16 packed sequences of 512..8192 tokens")
     ap.add_argument("--value-slice", type=int, default=0)
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="before the timed region, run a plain device copy of this many MiB "
@@ -110,10 +120,14 @@ def main():
     from gdn2_inputs import CONFIGS, make_config_inputs, make_decode_inputs
 
     dev = torch.device("cuda:0")
-    c = CONFIGS["layer1p3b_bf16"]
-    B, T, H, dk, dv = c["B"], c["T"], c["H"], c["dk"], c["dv"]
-    x = make_config_inputs("layer1p3b_bf16")
+    cfg = args.workload + "_bf16"
+    x = make_config_inputs(cfg)
+    B, T, H, dk = x["q"].shape
+    dv = x["v"].shape[-1]
     t = {n: torch.from_numpy(x[n]).to(dev).to(torch.bfloat16) for n in NAMES}
+    cu = None if x["cu_seqlens"] is None else torch.from_numpy(x["cu_seqlens"]).to(dev)
+    s0 = None if x["s0"] is None else torch.from_numpy(x["s0"]).to(dev)
+    N = B if cu is None else cu.numel() - 1
     torch.cuda.synchronize()
 
     if args.copy_calib_mb > 0:
@@ -125,12 +139,13 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    ws_bytes = G.workspace_bytes(B, T, H, dk, dv, B)
-    use_split = args.path != "fused" and not args.value_slice and ws_bytes > 0
+    ws_bytes = G.workspace_bytes(B, T, H, dk, dv, N)
+    use_split = G.uses_split(B, T, N, ws_bytes, args.path, args.value_slice)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if use_split else None
 
     def step():
-        return G.chunk_fwd(*(t[n] for n in NAMES), value_slice=args.value_slice,
+        return G.chunk_fwd(*(t[n] for n in NAMES), initial_state=s0, cu_seqlens=cu,
+                           value_slice=args.value_slice,
                            path="split" if use_split else "fused", workspace=ws)
 
     for _ in range(args.warmup):
@@ -151,22 +166,37 @@ def main():
     ms_per_step = wall * 1e3 / K
     tokens = B * T
     value = tokens * K / wall
-    nbytes = fwd_bytes(B, T, H, dk, dv, B)
+    nbytes = fwd_bytes(B, T, H, dk, dv, N, read_s0=s0 is not None)
     flops = fwd_flops(B, T, H, dk, dv)
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    if use_split:
+        kernel = (f"gdn2_prep_kernel<{dk},{dv}> + gdn2_state_kernel<{dk},{dv},NV> "
+                  "(the two launches of one call)")
+        tkey = f"chunk_fwd_split_{cfg}"
+    else:
+        kernel = f"gdn2_chunk_kernel<bf16,{dk},NV>"
+        tkey = f"chunk_fwd_{cfg}"
+    workloads = {
+        "layer1p3b": "GDN-2 chunk forward, 1.3B-layer shape: B=8 H=16 T=2048 d_k=d_v=128 "
+                     "C=64, bf16 in/out, fp32 state, zero S0",
+        "longctx": "GDN-2 chunk forward, long context: B=1 H=16 T=32768 d_k=d_v=128 C=64, "
+                   "10% of (token, head) decays at g=-5, bf16, zero S0",
+        "varlen": "GDN-2 chunk forward, packed: 16 sequences of 512..8192 tokens, H=16 "
+                  "d_k=d_v=128 C=64, bf16, S0 ~ N(0, 0.02^2)",
+    }
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), "
                 "log-alpha=-0.1*softplus(N(0,1)), b,w=sigmoid(N(0,1)))",
-        "config": {"workload": "GDN-2 chunk forward, 1.3B-layer shape: B=8 H=16 T=2048 "
-                               "d_k=d_v=128 C=64, bf16 in/out, fp32 state, zero S0",
-                   "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
+        "config": {"workload": workloads[args.workload], "global_batch": B, "seq_len": T,
+                   "sequences": N, "path": "split" if use_split else "fused",
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("chunk_fwd_layer1p3b_bf16"),
-                     "kernel": "gdn2_chunk_kernel<bf16,128,NV>",
+                     "traffic": measured_traffic(tkey),
+                     "kernel": kernel,
                      "algorithmic_bytes_per_launch": nbytes,
                      "kernel_ms": round(kern_ms, 4)},
         "mfma": {"useful_flops_per_launch": round(flops),
@@ -175,7 +205,7 @@ def main():
                  "frac": round(flops / (kern_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
     }
 
-    if not args.no_decode:
+    if not args.no_decode and args.workload == "layer1p3b":
         cd = CONFIGS["decode_bf16"]
         N, Hd, dkd, dvd = cd["N"], cd["H"], cd["dk"], cd["dv"]
         pool = 8
@@ -205,7 +235,7 @@ def main():
                          "bytes_per_step": decode_bytes(N, Hd, dkd, dvd),
                          "traffic": measured_traffic("decode_step_n256_h16_bf16"), **res}
 
-    if not args.no_cpu:
+    if not args.no_cpu and args.workload == "layer1p3b":
         out["cpu_baseline"] = cpu_baseline(x)
     print(json.dumps(out), flush=True)
 

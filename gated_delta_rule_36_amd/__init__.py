@@ -7,6 +7,8 @@ sequences, two-phase (with a workspace) or fused; `decode_step` advances a pool 
 recurrent states by one token. Both call libgdn2.so, built in-tree by
 `python -m gated_delta_rule_36_amd.build`.
 """
-from ._lib import Gdn2Error, chunk_fwd, decode_step, lib, lib_path, workspace_bytes
+from ._lib import (Gdn2Error, chunk_fwd, decode_step, lib, lib_path, uses_split,
+                   workspace_bytes)
 
-__all__ = ["chunk_fwd", "decode_step", "workspace_bytes", "lib", "lib_path", "Gdn2Error"]
+__all__ = ["chunk_fwd", "decode_step", "workspace_bytes", "uses_split", "lib", "lib_path",
+           "Gdn2Error"]
