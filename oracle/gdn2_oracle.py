@@ -28,12 +28,18 @@ Readings taken where the pages are garbled or silent (each is pinned by a test):
   * No query scale; alpha is passed as g = log(alpha) <= 0.
   * Decay is applied before the read (the forward-pass paragraph's order).
   * Varlen: each cu_seqlens segment is an independent sequence with its own state.
+
+Backward ([note §3], gate-aware backward paragraph: the gradient of the state flows through
+the asymmetric factor, dS_{t-1} = Diag(alpha_t) (I - e_t k_t^T) dS_t, plus the readout's
+q_t do_t^T). gdn2_backward is the reverse token loop: the chain rule applied to the step
+above in float64, one token at a time, with the forward states recomputed and kept.
 """
 from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["gdn2_step", "gdn2_forward", "gdn2_decode_steps"]
+__all__ = ["gdn2_step", "gdn2_forward", "gdn2_decode_steps", "gdn2_step_backward",
+           "gdn2_backward"]
 
 
 def gdn2_step(S, q, k, v, g, b, w):
@@ -112,3 +118,80 @@ def gdn2_decode_steps(S, q, k, v, g, b, w):
     for s in range(steps):
         o[s], S = gdn2_step(S, q[s], k[s], v[s], g[s], b[s], w[s])
     return o, S
+
+
+def gdn2_step_backward(S_prev, q, k, v, g, b, w, do, dS):
+    """Reverse of gdn2_step for one token (one state; no batch axes).
+
+    S_prev: [d_k, d_v] state before the token; q, k, g, b: [d_k]; v, w: [d_v];
+    do: [d_v] gradient of o_t; dS: [d_k, d_v] gradient of S_t from later tokens.
+    Returns (dq, dk, dv, dg, db, dw, dS_prev).
+
+    With S_bar = Diag(alpha) S_prev, e = b*k, z = w*v, r = S_bar^T e,
+    S_t = S_bar + k (z - r)^T and o_t = S_t^T q:
+      dS_t   = dS + q do^T            dq = S_t do
+      dz     = dS_t^T k               dr = -dz
+      dk     = dS_t (z - r) + b * de  de = S_bar dr   (r = S_bar^T e)
+      dS_bar = dS_t + e dr^T  = (I - e k^T) dS_t
+      dalpha = rowsum(dS_bar * S_prev), dg = alpha * dalpha
+      dS_prev = Diag(alpha) dS_bar
+      db = de * k,  dw = dz * v,  dv = dz * w
+    """
+    alpha = np.exp(g)
+    e = b * k
+    z = w * v
+    S_bar = alpha[:, None] * S_prev
+    r = S_bar.T @ e
+    S_t = S_bar + np.outer(k, z - r)
+    dS_t = dS + np.outer(q, do)
+    dq = S_t @ do
+    dz = dS_t.T @ k
+    dr = -dz
+    de = S_bar @ dr
+    dk = dS_t @ (z - r) + b * de
+    dS_bar = dS_t + np.outer(e, dr)
+    dg = alpha * np.sum(dS_bar * S_prev, axis=1)
+    dS_prev = alpha[:, None] * dS_bar
+    return dq, dk, dz * w, dg, de * k, dz * v, dS_prev
+
+
+def gdn2_backward(q, k, v, g, b, w, do, dS_final=None, s0=None, cu_seqlens=None):
+    """Gradients of gdn2_forward for upstream gradients `do` (of o, [B, T, H, d_v]) and
+    `dS_final` (of the final states, [N, H, d_k, d_v], or None for zero).
+
+    Same shapes and conventions as gdn2_forward. Returns
+    (dq, dk, dv, dg, db, dw, ds0): gradients of q, k, v, g (= log alpha), b, w with the
+    inputs' shapes, and of the initial states [N, H, d_k, d_v]; all float64.
+    """
+    q, k, v, g, b, w, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, g, b, w, do))
+    B, T, H, dk_ = q.shape
+    dv_ = v.shape[-1]
+    if cu_seqlens is None:
+        bounds = [(n, 0, T) for n in range(B)]
+    else:
+        cu = [int(x) for x in np.asarray(cu_seqlens)]
+        if B != 1:
+            raise ValueError("varlen inputs are packed with B == 1")
+        bounds = [(0, cu[n], cu[n + 1]) for n in range(len(cu) - 1)]
+    N = len(bounds)
+    s0 = np.zeros((N, H, dk_, dv_)) if s0 is None else np.asarray(s0, np.float64)
+    dS_final = np.zeros((N, H, dk_, dv_)) if dS_final is None else np.asarray(dS_final, np.float64)
+    grads = [np.zeros_like(x) for x in (q, k, v, g, b, w)]
+    ds0 = np.zeros((N, H, dk_, dv_))
+    for n, (bi, t0, t1) in enumerate(bounds):
+        for h in range(H):
+            # forward states before every token of this sequence
+            states = [s0[n, h].copy()]
+            for t in range(t0, t1):
+                _, S = gdn2_step(states[-1], q[bi, t, h], k[bi, t, h], v[bi, t, h],
+                                 g[bi, t, h], b[bi, t, h], w[bi, t, h])
+                states.append(S)
+            dS = dS_final[n, h].copy()
+            for t in range(t1 - 1, t0 - 1, -1):
+                out = gdn2_step_backward(states[t - t0], q[bi, t, h], k[bi, t, h], v[bi, t, h],
+                                         g[bi, t, h], b[bi, t, h], w[bi, t, h], do[bi, t, h], dS)
+                for gr, d in zip(grads, out[:6]):
+                    gr[bi, t, h] = d
+                dS = out[6]
+            ds0[n, h] = dS
+    return (*grads, ds0)

@@ -53,3 +53,77 @@ def chunked_forward(q, k, v, g, b, w, s0, C):
         sl = slice(c0, min(c0 + C, L))
         o[sl], S = chunk_step(S, q[sl], k[sl], v[sl], g[sl], b[sl], w[sl])
     return o, S
+
+
+def chunk_step_backward(S0, q, k, v, g, b, w, dO, dSn):
+    """Reverse of chunk_step for one chunk of one head.
+
+    S0: [d_k, d_v] state entering the chunk; dO: [n, d_v] gradient of the chunk's output;
+    dSn: [d_k, d_v] gradient of the state leaving it. Returns
+    (dq, dk, dv, dg, db, dw, dS0). With the chunk quantities of chunk_step and
+    Ebar = E exp(G), Qbar = q exp(G), Khat = k exp(-G), Ktil = k exp(G_last - G):
+      dU    = P^T dO + Ktil dSn                dQbar = dO S0^T + dP Khat
+      dP    = lower_incl(dO U^T)               dKtil = U dSn^T
+      dW    = -dU S0^T                         dZ    = T^T dU
+      dA    = -strict(dZ U~^T + (T^T dW) W^T)  (T = (I + A)^{-1})
+      dEbar = T^T dW + dA Khat                 dKhat = dA^T Ebar + dP^T Qbar
+      dS0   = Qbar^T dO + Diag(exp(G_last)) dSn - W^T dU
+    and the elementwise chain through exp(+-G), e = b*k, z = w*v and G = cumsum(g).
+    """
+    n = q.shape[0]
+    G = np.cumsum(g, axis=0)
+    Gam = np.exp(G)
+    Gn = G[-1]
+    E = b * k
+    Z = w * v
+    incl = np.tril(np.ones((n, n)))
+    strict = np.tril(np.ones((n, n)), -1)
+    Ebar, Qbar, Khat = E * Gam, q * Gam, k / Gam
+    Ktil = k * np.exp(Gn[None, :] - G)
+    A = (Ebar @ Khat.T) * strict
+    P = (Qbar @ Khat.T) * incl
+    T = np.linalg.inv(np.eye(n) + A)
+    W = T @ Ebar
+    Ut = T @ Z
+    U = Ut - W @ S0
+    dU = P.T @ dO + Ktil @ dSn
+    dP = (dO @ U.T) * incl
+    dQbar = dO @ S0.T + dP @ Khat
+    dKtil = U @ dSn.T
+    dW = -dU @ S0.T
+    dZ = T.T @ dU
+    dEbarT = T.T @ dW
+    dA = -(dZ @ Ut.T + dEbarT @ W.T) * strict
+    dEbar = dEbarT + dA @ Khat
+    dKhat = dA.T @ Ebar + dP.T @ Qbar
+    dS0 = Qbar.T @ dO + np.exp(Gn)[:, None] * dSn - W.T @ dU
+    dE = dEbar * Gam
+    dq = dQbar * Gam
+    dk = dKhat / Gam + dKtil * np.exp(Gn[None, :] - G) + dE * b
+    dG = dEbar * Ebar + dQbar * Qbar - dKhat * Khat - dKtil * Ktil
+    dG[-1] += np.sum(dKtil * Ktil, axis=0) + np.sum(dSn * np.exp(Gn)[:, None] * S0, axis=1)
+    dg = np.cumsum(dG[::-1], axis=0)[::-1]
+    return dq, dk, dZ * w, dg, dE * k, dZ * v, dS0
+
+
+def chunked_backward(q, k, v, g, b, w, s0, dO, dSn, C):
+    """Whole-sequence backward for one head with chunk size C: a forward pass keeps the
+    state entering every chunk, then the chunks run in reverse carrying dS."""
+    L = q.shape[0]
+    starts = list(range(0, L, C))
+    S = np.array(s0, dtype=np.float64)
+    states = []
+    for c0 in starts:
+        states.append(S)
+        sl = slice(c0, min(c0 + C, L))
+        _, S = chunk_step(S, q[sl], k[sl], v[sl], g[sl], b[sl], w[sl])
+    grads = [np.zeros_like(x) for x in (q, k, v, g, b, w)]
+    dS = np.array(dSn, dtype=np.float64)
+    for ci in range(len(starts) - 1, -1, -1):
+        sl = slice(starts[ci], min(starts[ci] + C, L))
+        out = chunk_step_backward(states[ci], q[sl], k[sl], v[sl], g[sl], b[sl], w[sl],
+                                  dO[sl], dS)
+        for gr, d in zip(grads, out[:6]):
+            gr[sl] = d
+        dS = out[6]
+    return (*grads, dS)
