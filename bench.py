@@ -69,6 +69,13 @@ def fwd_flops(B, T, H, dk, dv, C=64):
     return tok * per_tok
 
 
+def bwd_bytes(B, T, H, dk, dv, N, elt=2):
+    """Algorithmic HBM bytes of one backward call: read q, k, g, b, v, w and do once, write
+    the six input gradients once, and the fp32 initial-state gradient."""
+    tok = B * T * H
+    return tok * (4 * dk + 3 * dv) * elt + tok * (4 * dk + 2 * dv) * elt + N * H * dk * dv * 4
+
+
 def decode_bytes(N, H, dk, dv, elt=2):
     return N * H * (2 * dk * dv * 4 + (4 * dk + 2 * dv) * elt + dv * elt)
 
@@ -96,6 +103,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--path", choices=("auto", "split", "fused"), default="auto",
                     help="chunk-forward path: two-phase (split), single fused kernel, or auto "
                          "(as chunk_fwd chooses)")
@@ -204,6 +212,40 @@ def main():
                  "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
                  "frac": round(flops / (kern_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
     }
+
+    if not args.no_backward and args.workload == "layer1p3b":
+        rng = np.random.default_rng(7)
+        do = torch.from_numpy(rng.normal(size=(B, T, H, dv)).astype(np.float32)).to(dev)
+        do = do.to(torch.bfloat16)
+        bws = torch.empty(int(G.lib().gdn2_chunk_bwd_workspace_bytes(B, T, H, dk, dv, N, 0)),
+                          dtype=torch.uint8, device=dev)
+
+        def bstep(check=False):
+            return G.chunk_bwd(*(t[n] for n in NAMES), do, initial_state=s0, cu_seqlens=cu,
+                               workspace=bws, check_range=check)
+        bstep(check=True)
+        for _ in range(3):
+            bstep()
+        torch.cuda.synchronize()
+        KB = max(5, K // 5)
+        evb = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(KB)]
+        for a, b2 in evb:
+            a.record()
+            bstep()
+            b2.record()
+        torch.cuda.synchronize()
+        bms = float(np.mean([a.elapsed_time(b2) for a, b2 in evb]))
+        bb = bwd_bytes(B, T, H, dk, dv, N)
+        out["backward"] = {
+            "workload": "chunk backward on the same workload (gradients of q, k, v, g, b, w "
+                        "and the initial state for a random bf16 gradient of o)",
+            "ms_per_call": round(bms, 4), "tokens_per_s": round(B * T / (bms * 1e-3), 1),
+            "kernels": "factor kernel (backward layout) + forward chain + reverse chain + "
+                       "local gradients", "calls_timed": KB,
+            "algorithmic_bytes": bb, "achieved_GBs": round(bb / (bms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(bb / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del bws
 
     if not args.no_decode and args.workload == "layer1p3b":
         cd = CONFIGS["decode_bf16"]

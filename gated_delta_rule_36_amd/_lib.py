@@ -49,6 +49,10 @@ def lib():
         L.gdn2_chunk_fwd.restype = _I
         L.gdn2_chunk_fwd_workspace_bytes.argtypes = [_I] * 7
         L.gdn2_chunk_fwd_workspace_bytes.restype = _Z
+        L.gdn2_chunk_bwd.argtypes = [_P] * 18 + [_I] * 7 + [_P, _Z, _P]
+        L.gdn2_chunk_bwd.restype = _I
+        L.gdn2_chunk_bwd_workspace_bytes.argtypes = [_I] * 7
+        L.gdn2_chunk_bwd_workspace_bytes.restype = _Z
         L.gdn2_chunk_fwd_sliced.argtypes = [_P] * 10 + [_I] * 8 + [_P]
         L.gdn2_chunk_fwd_sliced.restype = _I
         L.gdn2_decode_step.argtypes = [_P] * 8 + [_I] * 5 + [_P]
@@ -165,6 +169,61 @@ def chunk_fwd(q, k, v, g, b, w, initial_state=None, cu_seqlens=None,
     if st != 0:
         raise Gdn2Error(fn, st)
     return o, sN
+
+
+class Gdn2RangeError(RuntimeError):
+    """A chunk's total decay exceeded the range of the backward's factors."""
+
+
+def chunk_bwd(q, k, v, g, b, w, do, initial_state=None, d_final_state=None, cu_seqlens=None,
+              workspace=None, check_range=True):
+    """Gradients of chunk_fwd (bf16).
+
+    do: [B, T, H, d_v] gradient of o (input dtype); d_final_state: [N, H, d_k, d_v] fp32 or
+    None. Returns (dq, dk, dv, dg, db, dw, d_initial_state): the first six in the input dtype
+    and shapes, the last fp32 [N, H, d_k, d_v]. With check_range, synchronises once and
+    raises Gdn2RangeError when some chunk's total decay is outside the backward's range.
+    """
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, d_k]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(dt)
+    for name, t, d in (("q", q, dk), ("k", k, dk), ("g", g, dk), ("b", b, dk),
+                       ("v", v, dv), ("w", w, dv), ("do", do, dv)):
+        _check(name, t, (B, T, H, d), dt, dev)
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != dev or cu_seqlens.dim() != 1:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor on the inputs' device")
+        if B != 1:
+            raise ValueError("packed (cu_seqlens) inputs must have B == 1")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    for name, t in (("initial_state", initial_state), ("d_final_state", d_final_state)):
+        if t is not None:
+            _check(name, t, (N, H, dk, dv), torch.float32, dev)
+    L = lib()
+    need = int(L.gdn2_chunk_bwd_workspace_bytes(B, T, H, dk, dv, N, code))
+    if need == 0:
+        raise ValueError("the backward is built for bf16 with d_k, d_v in {64, 128}")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    grads = [torch.empty_like(x) for x in (q, k, v, g, b, w)]
+    ds0 = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    st = L.gdn2_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w),
+                          _ptr(initial_state), _ptr(do), _ptr(d_final_state),
+                          *(_ptr(x) for x in grads), _ptr(ds0), _ptr(flag), _ptr(cu_seqlens),
+                          B, T, H, dk, dv, N, code, _ptr(workspace), workspace.numel(),
+                          _stream(dev))
+    if st != 0:
+        raise Gdn2Error("gdn2_chunk_bwd", st)
+    if check_range and int(flag.item()) != 0:
+        raise Gdn2RangeError("a chunk's total decay exceeds the backward's range "
+                             "(about 83 nats over 64 tokens in some key channel)")
+    return (*grads, ds0)
 
 
 def decode_step(q, k, v, g, b, w, state):

@@ -96,6 +96,10 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* log_
   return status_of(gdn2::launch_chunk_fwd(a));
 }
 
+size_t bwd_workspace_need(bool varlen, int B, int T, int H, int d_k, int d_v, int N) {
+  return gdn2::bwd_workspace_bytes(varlen, B, T, H, d_k, d_v, N);
+}
+
 }  // namespace
 
 extern "C" {
@@ -125,6 +129,59 @@ int gdn2_chunk_fwd_sliced(const void* q, const void* k, const void* v, const voi
   if (value_slice < 0) return GDN2_INVALID_ARGUMENT;
   return chunk_fwd_impl(q, k, v, log_alpha, b, w, initial_state, o, final_state, cu_seqlens,
                         B, T, H, d_k, d_v, N, dtype, nullptr, 0, hip_stream, value_slice);
+}
+
+size_t gdn2_chunk_bwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int N,
+                                      int dtype) {
+  if (B < 0 || T < 0 || H <= 0 || N < 0 || !split_built(dtype, d_k, d_v)) return 0;
+  const size_t a = bwd_workspace_need(false, B, T, H, d_k, d_v, N);
+  const size_t c = bwd_workspace_need(true, B, (int)std::min<long>((long)B * T, INT_MAX), H, d_k, d_v, N);
+  return a > c ? a : c;
+}
+
+int gdn2_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                   const void* b, const void* w, const float* initial_state, const void* d_o,
+                   const float* d_final_state, void* dq, void* dk, void* dv, void* dlog_alpha,
+                   void* db, void* dw, float* d_initial_state, int32_t* range_flag,
+                   const int32_t* cu_seqlens, int B, int T, int H, int d_k, int d_v, int N,
+                   int dtype, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (dtype != GDN2_BF16 && dtype != GDN2_F32) return GDN2_INVALID_ARGUMENT;
+  if (B < 0 || T < 0 || H <= 0 || N < 0 || d_k <= 0 || d_v <= 0) return GDN2_INVALID_ARGUMENT;
+  if (cu_seqlens == nullptr) {
+    if (N != B) return GDN2_INVALID_ARGUMENT;
+  } else {
+    if (B != 1) return GDN2_INVALID_ARGUMENT;
+  }
+  if (!split_built(dtype, d_k, d_v)) return GDN2_UNSUPPORTED;
+  const long tokens = (long)B * T;
+  if (tokens > 0 && (!q || !k || !v || !log_alpha || !b || !w || !d_o || !dq || !dk || !dv ||
+                     !dlog_alpha || !db || !dw))
+    return GDN2_INVALID_ARGUMENT;
+  const void* ptrs[17] = {q, k, v, log_alpha, b, w, initial_state, d_o, d_final_state, dq,
+                          dk, dv, dlog_alpha, db, dw, d_initial_state, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return GDN2_INVALID_ARGUMENT;
+  if ((cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) ||
+      (range_flag && (reinterpret_cast<uintptr_t>(range_flag) & 3u) != 0))
+    return GDN2_INVALID_ARGUMENT;
+  if (tokens > (long)INT_MAX) return GDN2_INVALID_ARGUMENT;
+  if (workspace == nullptr ||
+      workspace_bytes < bwd_workspace_need(cu_seqlens != nullptr, B, T, H, d_k, d_v, N))
+    return GDN2_WORKSPACE_TOO_SMALL;
+  if (N == 0) return GDN2_OK;
+  if ((long)N * H * (d_v / 64) > (long)INT_MAX) return GDN2_INVALID_ARGUMENT;
+
+  gdn2::BwdArgs a;
+  gdn2::ChunkArgs& f = a.fwd;
+  f.q = q; f.k = k; f.v = v; f.g = log_alpha; f.b = b; f.w = w;
+  f.s0 = initial_state; f.o = nullptr; f.sN = nullptr; f.cu_seqlens = cu_seqlens;
+  f.B = B; f.T = T; f.H = H; f.d_k = d_k; f.d_v = d_v; f.N = N;
+  f.dtype = dtype; f.nv = 64; f.stream = hip_stream;
+  f.workspace = workspace; f.workspace_bytes = workspace_bytes;
+  a.d_o = d_o; a.d_sN = d_final_state;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dlog_alpha; a.db = db; a.dw = dw;
+  a.d_s0 = d_initial_state; a.range_flag = range_flag;
+  return status_of(gdn2::launch_chunk_bwd(a));
 }
 
 int gdn2_decode_step(const void* q, const void* k, const void* v, const void* log_alpha,

@@ -1,0 +1,667 @@
+// Chunkwise backward of Gated Delta Rule-2 on gfx950 (bf16 inputs).
+//
+// The gradient of the state flows backwards through the asymmetric factor of every token
+// (GDN-2 reading note, §3 gate-aware backward paragraph); in chunk form, with the chunk
+// quantities of the forward (gdn2_split.hip) and dSn the gradient of the state leaving
+// the chunk:
+//   recurrence (sequential over chunks, per value column):
+//     dU  = P^T dO + Ktil dSn,   dZ = T^T dU   (T = (I + A)^{-1}, block back-substitution)
+//     dS0 = Qbar^T dO + Diag(gamma) dSn - W^T dU           (gradient of the entering state)
+//   local (parallel over chunks), with U = U~ - W S0 and S0 the entering state:
+//     M1 = lower_incl(dO U^T),   M2 = -strict(dZ U^T)      (M2 is dA)
+//     dQbar = dO S0^T + M1 Khat,   dEbar = -dZ S0^T + M2 Khat,
+//     dKhat = M2^T Ebar + M1^T Qbar,   dKtil = U dSn^T
+//   then the elementwise chain through 2^(+-G), e = b*k, z = w*v and G = cumsum(g).
+// The regrouping T^T dW = -dZ S0^T (dW = -dU S0^T) leaves one triangular solve per chunk and
+// makes dA = -strict(dZ U^T), so the local part needs neither T nor A.
+//
+// Pipeline (all per (chunk slot, head) unit of the backward workspace, BwdLayout):
+//   1. factor kernel (backward layout) and forward chain storing S0 and U per chunk
+//      (gdn2_split.hip);
+//   2. gdn2_bwd_chain_kernel: the recurrence, storing dSn and dZ per chunk, and dS0 of the
+//      sequence;
+//   3. gdn2_bwd_local_kernel: every chunk's gradients of q, k, g, b (and v, w = dZ*w, dZ*v).
+// The local kernel forms Khat = K 2^-G, so it needs chunks whose total decay is in the
+// chunk-referenced range (below 83 nats per channel); it flags any chunk outside it.
+
+#include "gdn2_chunk_common.h"
+#include "gdn2_launch.h"
+
+namespace gdn2 {
+
+// ------------------------------------------------------------------ the recurrence
+template <int DK, int DV, int NV>
+struct ChainShape {
+  static constexpr int C = 64;
+  static constexpr int NWV = NV / 16;  // waves: wave w owns gradient columns [16w, 16w+16)
+  static constexpr int NT = 64 * NWV;
+  static constexpr int KSK = DK / 32;
+  static constexpr int NMT = DK / 16;
+  static constexpr BwdLayout LB = BwdLayout(DK, DV);
+  // staged per chunk: [Kr | Pt | Qt | Wt | Bt] (contiguous in the unit), gamma, dO^T slice
+  static constexpr int OFF_KR = 0;
+  static constexpr int OFF_PT = (int)(LB.pt - LB.kr);
+  static constexpr int OFF_QT = (int)(LB.qt - LB.kr);
+  static constexpr int OFF_WT = (int)(LB.wt - LB.kr);
+  static constexpr int OFF_BT = (int)(LB.bt - LB.kr);
+  static constexpr int SZ_F = (int)(LB.factors - LB.kr);
+  static constexpr int OFF_G = SZ_F;
+  static constexpr int NPF = (SZ_F + DK * 4) / 16;      // 16-byte pieces of factors + gamma
+  static constexpr int PPF = (NPF + NT - 1) / NT;       // ... per thread (tail re-reads)
+  static constexpr int LDO = C + 8;                     // dO^T pitch: [column][token]
+  static constexpr int OFF_DO = PPF * NT * 16;
+  static constexpr int NPD = C * NV / 8;                // dO pieces: 8 columns of a token
+  static constexpr int PPD = NPD / NT;
+  static constexpr int STAGE = OFF_DO + NV * LDO * 2;
+  static constexpr int LDS_BYTES = 2 * STAGE;
+  static_assert(NPD % NT == 0, "dO pieces per thread");
+  static_assert(STAGE % 16 == 0 && LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+template <int DK, int DV, int NV>
+__global__ void __launch_bounds__((ChainShape<DK, DV, NV>::NT)) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gdn2_bwd_chain_kernel(char* __restrict__ ws, const bf16* __restrict__ d_o,
+                      const float* __restrict__ d_sN, float* __restrict__ d_s0,
+                      const int* __restrict__ cu_seqlens, int T_len, int H, int nslices,
+                      int nunits) {
+  typedef bf16 T;
+  using Sh = ChainShape<DK, DV, NV>;
+  using M = Mma<T>;
+  constexpr BwdLayout LB(DK, DV);
+  constexpr int C = Sh::C, NT = Sh::NT, KSK = Sh::KSK, NMT = Sh::NMT;
+  __shared__ __attribute__((aligned(16))) char smem[Sh::LDS_BYTES];
+
+  int tid = threadIdx.x;
+  int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int m16 = lane & 15, g4 = lane >> 4;
+
+  // workgroup -> (sequence, head, slice); slices of one head share an XCD (ids congruent
+  // mod 8), as in the forward recurrence
+  const int grp = blockIdx.x / (8 * nslices);
+  const int gsz = min(8, nunits - grp * 8);
+  const int gi = blockIdx.x - grp * 8 * nslices;
+  const int slice = gi / gsz;
+  const int nh = grp * 8 + gi % gsz;
+  const int h = nh % H;
+  const int n = nh / H;
+  const int col0 = slice * NV;
+  const int ctg = slice * Sh::NWV + wave;  // this wave's column tile within d_v
+
+  long row0, slot0;
+  int len;
+  if (cu_seqlens != nullptr) {
+    int a = cu_seqlens[n], b = cu_seqlens[n + 1];
+    a = a < 0 ? 0 : (a > T_len ? T_len : a);
+    b = b < a ? a : (b > T_len ? T_len : b);
+    row0 = a;
+    len = b - a;
+    slot0 = a / C + n;
+  } else {
+    row0 = (long)n * T_len;
+    len = T_len;
+    slot0 = (long)n * ((T_len + C - 1) / C);
+  }
+  const int nch = (len + C - 1) / C;
+  const long vstride = (long)H * DV;
+
+  // gradient of the state leaving the current chunk: tile mt holds rows [16mt, +16),
+  // column col0 + 16*wave + m16 (lane rows 4*g4 + i)
+  f4 D[NMT];
+  const long sbase = ((long)n * H + h) * DK * DV + col0 + 16 * wave + m16;
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      D[mt][i] = d_sN != nullptr ? d_sN[sbase + (long)(16 * mt + 4 * g4 + i) * DV] : 0.f;
+
+  // staging (one chunk ahead, reverse order): factor pieces and this slice of dO
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 stf[Sh::PPF], std_[Sh::PPD];
+  auto unit_of = [&](int ci) { return ws + ((slot0 + ci) * H + h) * LB.bytes; };
+  auto stage_load = [&](int ci) {
+    const char* unit = unit_of(ci);
+#pragma unroll
+    for (int j = 0; j < Sh::PPF; ++j) {
+      int p = tid + j * NT;
+      p = p < Sh::NPF ? p : Sh::NPF - 1;
+      const long off = p < Sh::SZ_F / 16 ? LB.kr + p * 16 : LB.f.g + (p * 16 - Sh::SZ_F);
+      stf[j] = *reinterpret_cast<const u32x4*>(unit + off);
+    }
+    const int nvalid = min(C, len - ci * C);
+#pragma unroll
+    for (int j = 0; j < Sh::PPD; ++j) {
+      const int p = tid + j * NT, r = p / (NV / 8), cc = p % (NV / 8);
+      const T* src = d_o + (row0 + (long)ci * C + (r < nvalid ? r : 0)) * vstride +
+                     (long)h * DV + col0 + cc * 8;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(src);
+      std_[j] = r < nvalid ? x : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto stage_store = [&](char* buf) {
+#pragma unroll
+    for (int j = 0; j < Sh::PPF; ++j) *reinterpret_cast<u32x4*>(buf + (tid + j * NT) * 16) = stf[j];
+    T* dot = reinterpret_cast<T*>(buf + Sh::OFF_DO);
+#pragma unroll
+    for (int j = 0; j < Sh::PPD; ++j) {  // transpose: [column][token]
+      const int p = tid + j * NT, r = p / (NV / 8), cc = p % (NV / 8);
+      const bf16x8 x = __builtin_bit_cast(bf16x8, std_[j]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot[(cc * 8 + e) * Sh::LDO + r] = x[e];
+    }
+  };
+
+  if (nch > 0) {
+    stage_load(nch - 1);
+    stage_store(smem);
+    stage_load(nch > 1 ? nch - 2 : 0);
+  }
+  lds_barrier();
+
+  for (int k = 0; k < nch; ++k) {
+    const int ci = nch - 1 - k;
+    tid = opaque(tid);
+    lane = tid & 63;
+    m16 = lane & 15;
+    g4 = lane >> 4;
+    const char* B = smem + (k & 1) * Sh::STAGE;
+    auto frag = [&](int off, int blk) {
+      return *reinterpret_cast<const typename M::frag*>(B + off + blk * 1024 + lane * 16);
+    };
+    char* unit = unit_of(ci);
+    // dSn of this chunk, for the local kernel
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+      *reinterpret_cast<uint2*>(unit + LB.db + ((ctg * NMT + mt) * 64 + lane) * 8) =
+          make_uint2(pack_bf16(D[mt][0], D[mt][1]), pack_bf16(D[mt][2], D[mt][3]));
+    typename M::frag db[KSK], dob[2];
+#pragma unroll
+    for (int s = 0; s < KSK; ++s) db[s] = M::from_acc(D, s);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)  // dO^T of this wave's columns, tokens 32s + 8g4 .. + 8
+      dob[s] = *reinterpret_cast<const bf16x8*>(B + Sh::OFF_DO +
+                                                ((16 * wave + m16) * Sh::LDO + 32 * s + 8 * g4) * 2);
+    // dU = P^T dO + Ktil dSn   (P^T is upper: token tiles 2, 3 only see the second K step)
+    f4 dU[4];
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KSK; ++s) acc = M::mma(frag(Sh::OFF_KR, R * KSK + s), db[s], acc);
+#pragma unroll
+      for (int s = R < 2 ? 0 : 1; s < 2; ++s) acc = M::mma(frag(Sh::OFF_PT, R * 2 + s), dob[s], acc);
+      dU[R] = acc;
+    }
+    // dZ = T^T dU:  dZ_R = (T_RR)^T (dU_R + sum_{J > R} (-A_JR)^T dZ_J),  R = 3 .. 0
+    f4 dZ[4];
+    bf16x4 zb[4];
+    auto btf = [&](int R, int J) {
+      return *reinterpret_cast<const bf16x4*>(B + Sh::OFF_BT + ((R * 4 + J) * 64 + lane) * 8);
+    };
+#pragma unroll
+    for (int R = 3; R >= 0; --R) {
+      f4 acc = dU[R];
+#pragma unroll
+      for (int J = R + 1; J < 4; ++J) acc = mma16_frag(btf(R, J), zb[J], acc);
+      dZ[R] = mma16_frag(btf(R, R), Frag16<T>::from_acc(acc), f4{0.f, 0.f, 0.f, 0.f});
+      zb[R] = Frag16<T>::from_acc(dZ[R]);
+    }
+#pragma unroll
+    for (int R = 0; R < 4; ++R)
+      *reinterpret_cast<uint2*>(unit + LB.zb + ((ctg * 4 + R) * 64 + lane) * 8) =
+          make_uint2(pack_bf16(dZ[R][0], dZ[R][1]), pack_bf16(dZ[R][2], dZ[R][3]));
+    // dS0 = Diag(gamma) dSn + Qbar^T dO + (-W^T) dU
+    typename M::frag ub[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) ub[s] = M::from_acc(dU, s);
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      const f4 gam = *reinterpret_cast<const f4*>(B + Sh::OFF_G + (16 * mt + 4 * g4) * 4);
+      f4 acc = D[mt] * gam;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) acc = M::mma(frag(Sh::OFF_QT, mt * 2 + s), dob[s], acc);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) acc = M::mma(frag(Sh::OFF_WT, mt * 2 + s), ub[s], acc);
+      D[mt] = acc;
+    }
+    // next chunk (ci - 1) into the other buffer; then the loads for ci - 2
+    if (ci > 0) stage_store(smem + ((k + 1) & 1) * Sh::STAGE);
+    stage_load(ci > 1 ? ci - 2 : 0);
+    lds_barrier();
+  }
+  if (d_s0 != nullptr) {
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d_s0[sbase + (long)(16 * mt + 4 * g4 + i) * DV] = D[mt][i];
+  }
+}
+
+// ------------------------------------------------------------------ the local gradients
+template <int DK, int DV>
+struct LocalShape {
+  static constexpr int C = 64;
+  static constexpr int NW = DK / 16;      // wave w owns key channels [16w, 16w+16)
+  static constexpr int NT = 64 * NW;
+  static constexpr int CG = DK / 8;
+  static constexpr int TG = NT / CG;      // 32
+  static constexpr int TPT = C / TG;      // 2
+  static constexpr int GPB = 16 / TPT;
+  static constexpr int VCG = DV / 8;
+  static constexpr int VTG = NT / VCG;
+  static constexpr int VTPT = C / VTG;
+  static constexpr int LDV = DV + 8, LDK = DK + 8, LDT = C + 8;
+  static constexpr int NVT = DV / 16, NCT = DK / 16;
+  // LDS regions (bytes)
+  static constexpr int SZ_A = DK * LDV * 2;     // dSn, later S0: [DK][DV]
+  static constexpr int SZ_R = C * LDV * 2;      // dO, dZ, U: [64][DV]
+  static constexpr int SZ_ET = 2 * DK * LDT * 2;  // Ebar^T, Qbar^T
+  static constexpr int SZ_EL = C * DK * 4 + 3 * C * LDK * 2;  // G (fp32), q, k, b
+  static constexpr int SZ_BIG0 = SZ_A + 3 * SZ_R;
+  static constexpr int SZ_BIG = SZ_BIG0 > SZ_EL ? (SZ_BIG0 > SZ_ET ? SZ_BIG0 : SZ_ET)
+                                                : (SZ_EL > SZ_ET ? SZ_EL : SZ_ET);
+  static constexpr int OFF_A = 0, OFF_O = SZ_A, OFF_Z = OFF_O + SZ_R, OFF_U = OFF_Z + SZ_R;
+  static constexpr int OFF_KH = (SZ_BIG + 15) / 16 * 16;  // Khat^T [DK][64], swizzled
+  static constexpr int SZ_M = C * LDT * 2;
+  static constexpr int OFF_M1 = OFF_KH + DK * LDT * 2;    // M1, M2 row-major; then transposed
+  static constexpr int OFF_M2 = OFF_M1 + SZ_M;
+  static constexpr int OFF_M1T = OFF_M2 + SZ_M;
+  static constexpr int OFF_M2T = OFF_M1T + SZ_M;
+  static constexpr int OFF_FAC = OFF_M2T + SZ_M;
+  static constexpr int OFF_X = OFF_FAC + Fac::N * DK * 4;  // per-channel constant of dg
+  static constexpr int OFF_FLAG = OFF_X + DK * 4;
+  static constexpr int LDS_BYTES = OFF_FLAG + 16;
+  static constexpr int OFF_TOT = OFF_M1;                   // cumsum scratch in the M buffers
+  static_assert(TG * DK * 4 <= 4 * SZ_M, "cumsum scratch");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(TPT * TG == C && VTPT * VTG == C, "token mapping");
+};
+
+template <int DK, int DV>
+__global__ void __launch_bounds__((LocalShape<DK, DV>::NT))
+gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                      const bf16* __restrict__ v, const bf16* __restrict__ g,
+                      const bf16* __restrict__ bg, const bf16* __restrict__ wg,
+                      const bf16* __restrict__ d_o, const char* __restrict__ ws,
+                      bf16* __restrict__ dq, bf16* __restrict__ dk, bf16* __restrict__ dv,
+                      bf16* __restrict__ dg, bf16* __restrict__ db, bf16* __restrict__ dw,
+                      int* range_flag, const int* __restrict__ cu_seqlens, int N, int T_len,
+                      int H) {
+  typedef bf16 T;
+  using Sh = LocalShape<DK, DV>;
+  using M = Mma<T>;
+  constexpr BwdLayout LB(DK, DV);
+  constexpr int C = Sh::C, NT = Sh::NT, LDV = Sh::LDV, LDK = Sh::LDK, LDT = Sh::LDT;
+  constexpr int NVT = Sh::NVT;
+  __shared__ __attribute__((aligned(16))) char smem[Sh::LDS_BYTES];
+  T* sA = reinterpret_cast<T*>(smem + Sh::OFF_A);
+  T* sO = reinterpret_cast<T*>(smem + Sh::OFF_O);
+  T* sZ = reinterpret_cast<T*>(smem + Sh::OFF_Z);
+  T* sU = reinterpret_cast<T*>(smem + Sh::OFF_U);
+  T* sKh = reinterpret_cast<T*>(smem + Sh::OFF_KH);
+  T* sM1 = reinterpret_cast<T*>(smem + Sh::OFF_M1);
+  T* sM2 = reinterpret_cast<T*>(smem + Sh::OFF_M2);
+  T* sM1t = reinterpret_cast<T*>(smem + Sh::OFF_M1T);
+  T* sM2t = reinterpret_cast<T*>(smem + Sh::OFF_M2T);
+  float* sFac = reinterpret_cast<float*>(smem + Sh::OFF_FAC);
+  float* sX = reinterpret_cast<float*>(smem + Sh::OFF_X);
+  float* sTot = reinterpret_cast<float*>(smem + Sh::OFF_TOT);
+  int* sFlag = reinterpret_cast<int*>(smem + Sh::OFF_FLAG);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m16 = lane & 15, g4 = lane >> 4;
+  const int cg = tid % Sh::CG, tg = tid / Sh::CG;
+  const int vcg = tid % Sh::VCG, vtg = tid / Sh::VCG;
+
+  const ChunkUnit cu = map_unit(blockIdx.x, H, cu_seqlens, N, T_len, lane);
+  if (cu.nvalid == 0) return;  // an unused slot (uniform)
+  const char* unit = ws + (long)blockIdx.x * LB.bytes;
+  const long kstride = (long)H * DK, vstride = (long)H * DV;
+  const long kb0 = cu.row * kstride + (long)cu.h * DK;
+  const long vb0 = cu.row * vstride + (long)cu.h * DV;
+
+  // ---- loads: key-side inputs (this thread's tokens x 8 channels), value side, dO
+  Vec8<T> rq[Sh::TPT], rk[Sh::TPT], rg[Sh::TPT], rb[Sh::TPT], rv[Sh::VTPT], rw[Sh::VTPT];
+#pragma unroll
+  for (int j = 0; j < Sh::TPT; ++j) {
+    const int r = tg * Sh::TPT + j;
+    if (r < cu.nvalid) {
+      const long off = kb0 + (long)r * kstride + cg * 8;
+      rq[j].load(q + off); rk[j].load(k + off); rg[j].load(g + off); rb[j].load(bg + off);
+    } else {
+      rq[j].zero(); rk[j].zero(); rg[j].zero(); rb[j].zero();
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < Sh::VTPT; ++j) {
+    const int r = vtg * Sh::VTPT + j;
+    if (r < cu.nvalid) {
+      const long off = vb0 + (long)r * vstride + vcg * 8;
+      rv[j].load(v + off); rw[j].load(wg + off);
+    } else {
+      rv[j].zero(); rw[j].zero();
+    }
+  }
+  for (int p = tid; p < C * DV / 8; p += NT) {  // dO rows -> LDS
+    const int r = p / (DV / 8), cc = p % (DV / 8);
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (r < cu.nvalid) x = *reinterpret_cast<const uint4*>(d_o + vb0 + (long)r * vstride + cc * 8);
+    *reinterpret_cast<uint4*>(sO + r * LDV + cc * 8) = x;
+  }
+  // accumulator tiles (bf16, lane-major) -> row-major LDS arrays
+  auto tile_in = [&](long off, int tile) {
+    const bf16x4 x = *reinterpret_cast<const bf16x4*>(unit + off + (tile * 64 + lane) * 8);
+    return f4{to_f(x[0]), to_f(x[1]), to_f(x[2]), to_f(x[3])};
+  };
+  auto ident = [](int c) { return c; };
+  for (int t = wave; t < NVT * 4; t += Sh::NW) {  // dZ, U: tiles (ct, R)
+    const int ct = t / 4, R = t % 4;
+    store_tile_pairs(sZ + (16 * R) * LDV + 16 * ct, LDV, lane, tile_in(LB.zb, t), ident);
+    store_tile_pairs(sU + (16 * R) * LDV + 16 * ct, LDV, lane, tile_in(LB.ub, t), ident);
+  }
+  // dSn -> LDS; S0 stays in registers until dSn is dead; the dg constant
+  // X_c = sum_v dSn[c,v] S0[c,v] (times gamma_c later) from the two tiles' products
+  f4 s0t[NVT];
+  {
+    f4 xs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ct = 0; ct < NVT; ++ct) {
+      const f4 ds = tile_in(LB.db, ct * Sh::NCT + wave);
+      s0t[ct] = tile_in(LB.h, ct * Sh::NCT + wave);
+      store_tile_pairs(sA + (16 * wave) * LDV + 16 * ct, LDV, lane, ds, ident);
+      xs += ds * s0t[ct];
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xs[i] += __shfl_xor(xs[i], m, 64);
+    if (m16 == 0) *reinterpret_cast<f4*>(sX + 16 * wave + 4 * g4) = xs;
+  }
+
+  // ---- (a), (b): cumulative log2-decay and the chunk factors
+  {
+    float tot8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < Sh::TPT; ++j) {
+      float f[8];
+      rg[j].to_float(f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) tot8[i] += f[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tot8[i] *= kLog2e;
+    store8(sTot + tg * DK + cg * 8, tot8);
+  }
+  if (tid == 0) *sFlag = 0;
+  lds_barrier();
+  channel_scan<DK, Sh::TG, Sh::GPB, NT>(sTot, sFac, sFlag, tid);
+  lds_barrier();
+  if (tid == 0 && *sFlag != 0 && range_flag != nullptr) *range_flag = 1;
+  // per thread: G (log2) of its tokens; Khat^T = (K 2^-G)^T into LDS (natural token order)
+  float G2[Sh::TPT][8];
+  {
+    float run[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) run[i] = sTot[tg * DK + cg * 8 + i];
+    RunBuf<T, Sh::TPT> kh[8];
+#pragma unroll
+    for (int j = 0; j < Sh::TPT; ++j) {
+      float fg[8], fk[8];
+      rg[j].to_float(fg);
+      rk[j].to_float(fk);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        run[i] += fg[i] * kLog2e;
+        G2[j][i] = run[i];
+        kh[i].put(j, fk[i] * fast_exp2(-run[i]));
+      }
+    }
+    const int sw = tswz(cg * 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kh[i].store_sw(sKh + (cg * 8 + i) * LDT, sw, tg * Sh::TPT);
+  }
+  // dv = dZ * w, dw = dZ * v
+#pragma unroll
+  for (int j = 0; j < Sh::VTPT; ++j) {
+    const int r = vtg * Sh::VTPT + j;
+    float fz[8], fv[8], fw[8], o1[8], o2[8];
+    Vec8<T> z;
+    z.load(sZ + r * LDV + vcg * 8);
+    z.to_float(fz);
+    rv[j].to_float(fv);
+    rw[j].to_float(fw);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { o1[i] = fz[i] * fw[i]; o2[i] = fz[i] * fv[i]; }
+    if (r < cu.nvalid) {
+      const long off = vb0 + (long)r * vstride + vcg * 8;
+      store8(dv + off, o1);
+      store8(dw + off, o2);
+    }
+  }
+  lds_barrier();  // sTot (in the M buffers) is consumed; Khat^T, dO, dZ, U, dSn are in LDS
+
+  // ---- P1: M1 = lower_incl(dO U^T), M2 = -strict(dZ U^T); stored row-major and transposed
+  for (int t = wave; t < 32; t += Sh::NW) {
+    const int which = t >> 4, R = (t >> 2) & 3, I = t & 3;
+    const T* lhs = which ? sZ : sO;
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (I <= R) {
+#pragma unroll
+      for (int s = 0; s < DV / 32; ++s)
+        acc = M::mma(M::load(lhs, LDV, 16 * R + m16, 32 * s + 8 * g4),
+                     M::load(sU, LDV, 16 * I + m16, 32 * s + 8 * g4), acc);
+    }
+    f4 val;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g4 + i, c = m16;  // row (token t) within R, column (token i) within I
+      const bool keep = I < R || (which ? c < r : c <= r);
+      val[i] = keep ? (which ? -acc[i] : acc[i]) : 0.f;
+    }
+    T* Mr = which ? sM2 : sM1;
+    T* Mt = which ? sM2t : sM1t;
+    store_tile_pairs(Mr + (16 * R) * LDT + 16 * I, LDT, lane, val, ident);
+    *reinterpret_cast<uint2*>(Mt + (16 * I + m16) * LDT + 16 * R + 4 * g4) =
+        make_uint2(pack_bf16(val[0], val[1]), pack_bf16(val[2], val[3]));
+  }
+  // ---- P2: dKtil^T = dSn U^T   (rows: this wave's channels; columns: tokens)
+  f4 dKt[4];
+#pragma unroll
+  for (int Tt = 0; Tt < 4; ++Tt) {
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < DV / 32; ++s)
+      acc = M::mma(M::load(sA, LDV, 16 * wave + m16, 32 * s + 8 * g4),
+                   M::load(sU, LDV, 16 * Tt + m16, 32 * s + 8 * g4), acc);
+    dKt[Tt] = acc;
+  }
+  lds_barrier();  // dSn and U are dead
+#pragma unroll
+  for (int ct = 0; ct < NVT; ++ct)
+    store_tile_pairs(sA + (16 * wave) * LDV + 16 * ct, LDV, lane, s0t[ct], ident);
+  lds_barrier();
+  // ---- P3: dQbar^T = S0 dO^T + Khat^T M1^T,  dEbar^T = -S0 dZ^T + Khat^T M2^T
+  f4 dQb[4], dEb[4];
+#pragma unroll
+  for (int Tt = 0; Tt < 4; ++Tt) {
+    f4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < DV / 32; ++s) {
+      const typename M::frag sf = M::load(sA, LDV, 16 * wave + m16, 32 * s + 8 * g4);
+      a1 = M::mma(sf, M::load(sO, LDV, 16 * Tt + m16, 32 * s + 8 * g4), a1);
+      a2 = M::mma(sf, M::load(sZ, LDV, 16 * Tt + m16, 32 * s + 8 * g4), a2);
+    }
+    a2 = -a2;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const typename M::frag kf = M::load_phi_t(sKh, LDT, 16 * wave + m16, s, g4);
+      a1 = M::mma(kf, M::load(sM1, LDT, 16 * Tt + m16, 32 * s + 8 * g4), a1);
+      a2 = M::mma(kf, M::load(sM2, LDT, 16 * Tt + m16, 32 * s + 8 * g4), a2);
+    }
+    dQb[Tt] = a1;
+    dEb[Tt] = a2;
+  }
+  lds_barrier();  // S0, dO, dZ are dead
+  // Ebar^T = (b k 2^G)^T and Qbar^T = (q 2^G)^T, natural token order, into the big region
+  T* sEt = reinterpret_cast<T*>(smem);
+  T* sQt = sEt + DK * LDT;
+  {
+    RunBuf<T, Sh::TPT> ev[8], qv[8];
+#pragma unroll
+    for (int j = 0; j < Sh::TPT; ++j) {
+      float fq[8], fk[8], fb[8];
+      rq[j].to_float(fq);
+      rk[j].to_float(fk);
+      rb[j].to_float(fb);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float gm = fast_exp2(G2[j][i]);
+        ev[i].put(j, fb[i] * fk[i] * gm);
+        qv[i].put(j, fq[i] * gm);
+      }
+    }
+    const int sw = tswz(cg * 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ev[i].store_sw(sEt + (cg * 8 + i) * LDT, sw, tg * Sh::TPT);
+      qv[i].store_sw(sQt + (cg * 8 + i) * LDT, sw, tg * Sh::TPT);
+    }
+  }
+  lds_barrier();
+  // ---- P4: dKhat^T = Ebar^T M2 + Qbar^T M1
+  f4 dKh[4];
+#pragma unroll
+  for (int Tt = 0; Tt < 4; ++Tt) {
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      acc = M::mma(M::load_phi_t(sEt, LDT, 16 * wave + m16, s, g4),
+                   M::load(sM2t, LDT, 16 * Tt + m16, 32 * s + 8 * g4), acc);
+      acc = M::mma(M::load_phi_t(sQt, LDT, 16 * wave + m16, s, g4),
+                   M::load(sM1t, LDT, 16 * Tt + m16, 32 * s + 8 * g4), acc);
+    }
+    dKh[Tt] = acc;
+  }
+  lds_barrier();  // everything but the factors is dead
+  // G (log2, fp32) and q, k, b row-major for the elementwise step
+  float* sG = reinterpret_cast<float*>(smem);
+  T* sq = reinterpret_cast<T*>(smem + C * DK * 4);
+  T* sk = sq + C * LDK;
+  T* sb = sk + C * LDK;
+#pragma unroll
+  for (int j = 0; j < Sh::TPT; ++j) {
+    const int r = tg * Sh::TPT + j;
+    store8(sG + r * DK + cg * 8, G2[j]);
+    *reinterpret_cast<uint4*>(sq + r * LDK + cg * 8) = rq[j].r;
+    *reinterpret_cast<uint4*>(sk + r * LDK + cg * 8) = rk[j].r;
+    *reinterpret_cast<uint4*>(sb + r * LDK + cg * 8) = rb[j].r;
+  }
+  lds_barrier();
+
+  // ---- elementwise: lane = token 16*Tt + m16, channels c0 .. c0 + 3 of this wave
+  const int c0 = 16 * wave + 4 * g4;
+  const f4 gam = *reinterpret_cast<const f4*>(sFac + Fac::GAM * DK + c0);
+  const f4 xc = *reinterpret_cast<const f4*>(sX + c0);
+  f4 dgv[4], outq[4], outk[4], outb[4];
+  f4 totB = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int Tt = 0; Tt < 4; ++Tt) {
+    const int t = 16 * Tt + m16;
+    const f4 G = *reinterpret_cast<const f4*>(sG + t * DK + c0);
+    const f4 fq = load4f(sq + t * LDK + c0), fk = load4f(sk + t * LDK + c0);
+    const f4 fb = load4f(sb + t * LDK + c0);
+    f4 A, Bv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float gm = fast_exp2(G[i]), ig = fast_exp2(-G[i]);
+      const float dE = dEb[Tt][i] * gm;
+      outq[Tt][i] = dQb[Tt][i] * gm;
+      outk[Tt][i] = (dKh[Tt][i] + dKt[Tt][i] * gam[i]) * ig + dE * fb[i];
+      outb[Tt][i] = dE * fk[i];
+      // dG = dEbar Ebar + dQbar Qbar - dKhat Khat - dKtil Ktil, split as A - B
+      A[i] = gm * (dEb[Tt][i] * fb[i] * fk[i] + dQb[Tt][i] * fq[i]) - dKh[Tt][i] * fk[i] * ig;
+      Bv[i] = dKt[Tt][i] * fk[i] * gam[i] * ig;
+    }
+    dgv[Tt] = A - Bv;
+    totB += Bv;
+  }
+  // dg_t = sum_{t' >= t} (A - B)_{t'} + sum_all B + gamma X   (suffix sums over 64 tokens)
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) totB[i] += __shfl_xor(totB[i], m, 64);
+  f4 carry = totB + gam * xc;
+#pragma unroll
+  for (int Tt = 3; Tt >= 0; --Tt) {
+    f4 x = dgv[Tt];
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float y = __shfl_down(x[i], d, 16);
+        x[i] += (m16 + d < 16) ? y : 0.f;
+      }
+    }
+    f4 tile_tot;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tile_tot[i] = __shfl(x[i], lane & ~15, 64);
+    dgv[Tt] = x + carry;
+    carry += tile_tot;
+  }
+#pragma unroll
+  for (int Tt = 0; Tt < 4; ++Tt) {
+    const int t = 16 * Tt + m16;
+    if (t < cu.nvalid) {
+      const long off = kb0 + (long)t * kstride + c0;
+      auto put4 = [&](bf16* p, f4 x) {
+        *reinterpret_cast<uint2*>(p + off) = make_uint2(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]));
+      };
+      put4(dq, outq[Tt]);
+      put4(dk, outk[Tt]);
+      put4(db, outb[Tt]);
+      put4(dg, dgv[Tt]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launch
+template <int DK, int DV>
+static hipError_t launch_bwd(const BwdArgs& a) {
+  const ChunkArgs& f = a.fwd;
+  hipStream_t st = (hipStream_t)f.stream;
+  hipError_t e = launch_bwd_forward_part(f);
+  if (e != hipSuccess) return e;
+  constexpr int NV = 64 <= DV ? 64 : DV;
+  const int nslices = DV / NV;
+  hipLaunchKernelGGL((gdn2_bwd_chain_kernel<DK, DV, NV>), dim3((unsigned)(f.N * f.H * nslices)),
+                     dim3(ChainShape<DK, DV, NV>::NT), 0, st, (char*)f.workspace,
+                     (const bf16*)a.d_o, a.d_sN, a.d_s0, f.cu_seqlens, f.T, f.H, nslices,
+                     f.N * f.H);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long nunits = split_slots(f.cu_seqlens != nullptr, f.B, f.T, f.N) * f.H;
+  if (nunits > 0) {
+    hipLaunchKernelGGL((gdn2_bwd_local_kernel<DK, DV>), dim3((unsigned)nunits),
+                       dim3(LocalShape<DK, DV>::NT), 0, st, (const bf16*)f.q, (const bf16*)f.k,
+                       (const bf16*)f.v, (const bf16*)f.g, (const bf16*)f.b, (const bf16*)f.w,
+                       (const bf16*)a.d_o, (const char*)f.workspace, (bf16*)a.dq, (bf16*)a.dk,
+                       (bf16*)a.dv, (bf16*)a.dg, (bf16*)a.db, (bf16*)a.dw, a.range_flag,
+                       f.cu_seqlens, f.N, f.T, f.H);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+hipError_t launch_chunk_bwd(const BwdArgs& a) {
+  const ChunkArgs& f = a.fwd;
+  if (f.dtype != 0) return hipErrorInvalidValue;
+  if (f.d_k == 64 && f.d_v == 64) return launch_bwd<64, 64>(a);
+  if (f.d_k == 64 && f.d_v == 128) return launch_bwd<64, 128>(a);
+  if (f.d_k == 128 && f.d_v == 64) return launch_bwd<128, 64>(a);
+  if (f.d_k == 128 && f.d_v == 128) return launch_bwd<128, 128>(a);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdn2

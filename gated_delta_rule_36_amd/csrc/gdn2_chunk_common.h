@@ -269,4 +269,61 @@ __device__ __forceinline__ void zero_p_upper(T* sP, int tid) {
   }
 }
 
+// Where a (chunk slot, head) unit's tokens are: first row of the packed token axis and
+// the number of valid tokens (0: an unused slot).
+struct ChunkUnit {
+  long row;
+  int nvalid;
+  int h;
+};
+
+// Maps unit u = slot * H + h to its tokens. Without cu_seqlens the slots of sequence n are
+// n * nch + c. With cu_seqlens, sequence n's slots start at floor(a_n / 64) + n (a_n its
+// clamped first token); the owner of a slot is found by a 64-way ballot search over the
+// table (wave-uniform result).
+__device__ __forceinline__ ChunkUnit map_unit(long u, int H, const int* cu_seqlens, int N,
+                                              int T_len, int lane) {
+  constexpr int C = 64;
+  ChunkUnit r;
+  const long slot = u / H;
+  r.h = (int)(u - slot * H);
+  if (cu_seqlens == nullptr) {
+    const int nch = (T_len + C - 1) / C;
+    const long n = slot / nch;
+    const int c = (int)(slot - n * nch);
+    r.row = n * T_len + (long)c * C;
+    r.nvalid = min(C, T_len - c * C);
+    return r;
+  }
+  auto clamp_cu = [&](int i) { const int x = cu_seqlens[i]; return x < 0 ? 0 : (x > T_len ? T_len : x); };
+  // largest n in [0, N) with start slot s_n = floor(a_n / 64) + n <= slot
+  int lo = 0, hi = N;
+  if ((long)(clamp_cu(0) / C) > slot) {
+    r.row = 0; r.nvalid = 0;
+    return r;
+  }
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 63) / 64;
+    const int cand = lo + lane * step;
+    const bool ok = cand < hi && (long)(clamp_cu(cand) / C + cand) <= slot;
+    const unsigned long long m = __ballot(ok);
+    const int kk = __popcll(m) - 1;  // lane 0 (cand = lo) always passes
+    lo = lo + kk * step;
+    hi = min(lo + step, hi);
+  }
+  const int n = __builtin_amdgcn_readfirstlane(lo);
+  const int a = clamp_cu(n);
+  int b = clamp_cu(n + 1);
+  b = b < a ? a : b;
+  const long c = slot - (long)(a / C + n);
+  const int len = b - a;
+  if (c < 0 || c * C >= len) {
+    r.row = 0; r.nvalid = 0;
+    return r;
+  }
+  r.row = a + c * C;
+  r.nvalid = len - c * C < C ? (int)(len - c * C) : C;
+  return r;
+}
+
 }  // namespace gdn2

@@ -70,8 +70,59 @@ inline size_t split_workspace_bytes(bool varlen, int B, int T, int H, int d_k, i
   return (size_t)split_slots(varlen, B, T, N) * H * SplitLayout(d_k, d_v).bytes;
 }
 
+// Backward workspace, per (chunk slot, head) unit: the forward factors (SplitLayout) followed
+// by the reverse chain's operands, then four per-chunk tensors passed between the kernels.
+// All bf16 and in MFMA fragment order unless noted:
+//   Kr   Ktil = K 2^(Glast - G)   [64 tokens][d_k]  blocks (R, s), K = channels (phi)
+//   Pt   P^T                      [64][64]          blocks (R, s), K = tokens (natural)
+//   Qt   Qbar^T                   [d_k][64]         blocks (m, s), K = tokens (natural)
+//   Wt   -W^T                     [d_k][64]         blocks (m, s), K = tokens (phi)
+//   Bt   back-substitution blocks (R, J), J >= R: (-A_JR)^T for J > R, (T_RR)^T for J = R,
+//        16x16 K=16 fragments (64 lanes x 4 bf16)
+//   H    state entering the chunk [d_k][d_v]       16x16 accumulator tiles (ct, mt)
+//   Ub   U = U~ - W S             [64][d_v]         tiles (ct, R)
+//   Db   gradient of the state leaving the chunk [d_k][d_v]  tiles (ct, mt)
+//   Zb   dZ = T^T dU              [64][d_v]         tiles (ct, R)
+// (accumulator tiles: 64 lanes x 4 bf16 = 512 B, lane l holds column l % 16, rows
+// 4 (l / 16) .. + 3, the order the chain kernels hold them in registers)
+struct BwdLayout {
+  SplitLayout f;
+  long kr, pt, qt, wt, bt, factors, h, ub, db, zb, bytes;
+  constexpr BwdLayout(int d_k, int d_v)
+      : f(d_k, d_v),
+        kr(f.bytes),
+        pt(kr + 4L * (d_k / 32) * 1024),
+        qt(pt + 8L * 1024),
+        wt(qt + (d_k / 16) * 2L * 1024),
+        bt(wt + (d_k / 16) * 2L * 1024),
+        factors(bt + 16L * 512),
+        h(factors),
+        ub(h + (long)(d_k / 16) * (d_v / 16) * 512),
+        db(ub + 4L * (d_v / 16) * 512),
+        zb(db + (long)(d_k / 16) * (d_v / 16) * 512),
+        bytes(zb + 4L * (d_v / 16) * 512) {}
+};
+
+inline size_t bwd_workspace_bytes(bool varlen, int B, int T, int H, int d_k, int d_v, int N) {
+  return (size_t)split_slots(varlen, B, T, N) * H * BwdLayout(d_k, d_v).bytes;
+}
+
+struct BwdArgs {
+  ChunkArgs fwd;            // q..w, s0 (initial state), cu_seqlens, sizes, dtype, stream,
+                            // workspace; fwd.o / fwd.sN unused
+  const void* d_o;          // [B, T, H, d_v]
+  const float* d_sN;        // [N, H, d_k, d_v] or null
+  void *dq, *dk, *dv, *dg, *db, *dw;
+  float* d_s0;              // [N, H, d_k, d_v] or null
+  int* range_flag;          // device int, set to 1 when a chunk is outside the fast range
+};
+
 hipError_t launch_chunk_fwd(const ChunkArgs& a);
 hipError_t launch_chunk_fwd_split(const ChunkArgs& a);
+hipError_t launch_chunk_bwd(const BwdArgs& a);
+// pieces of the backward shared with the two-phase forward (gdn2_split.hip)
+hipError_t launch_bwd_forward_part(const ChunkArgs& a);
+int cu_count();  // compute units of the current device
 hipError_t launch_decode_step(const DecodeArgs& a);
 
 }  // namespace gdn2

@@ -90,64 +90,9 @@ struct PrepPieces {
                 "factor pieces tile the workgroup");
 };
 
-// Where a (chunk slot, head) unit's tokens are: first row of the packed token axis and
-// the number of valid tokens (0: an unused slot).
-struct ChunkUnit {
-  long row;
-  int nvalid;
-  int h;
-};
-
-// Maps unit u = slot * H + h to its tokens. Without cu_seqlens the slots of sequence n are
-// n * nch + c. With cu_seqlens, sequence n's slots start at floor(a_n / 64) + n (a_n its
-// clamped first token); the owner of a slot is found by a 64-way ballot search over the
-// table (wave-uniform result).
-__device__ __forceinline__ ChunkUnit map_unit(long u, int H, const int* cu_seqlens, int N,
-                                              int T_len, int lane) {
-  constexpr int C = 64;
-  ChunkUnit r;
-  const long slot = u / H;
-  r.h = (int)(u - slot * H);
-  if (cu_seqlens == nullptr) {
-    const int nch = (T_len + C - 1) / C;
-    const long n = slot / nch;
-    const int c = (int)(slot - n * nch);
-    r.row = n * T_len + (long)c * C;
-    r.nvalid = min(C, T_len - c * C);
-    return r;
-  }
-  auto clamp_cu = [&](int i) { const int x = cu_seqlens[i]; return x < 0 ? 0 : (x > T_len ? T_len : x); };
-  // largest n in [0, N) with start slot s_n = floor(a_n / 64) + n <= slot
-  int lo = 0, hi = N;
-  if ((long)(clamp_cu(0) / C) > slot) {
-    r.row = 0; r.nvalid = 0;
-    return r;
-  }
-  while (hi - lo > 1) {
-    const int step = (hi - lo + 63) / 64;
-    const int cand = lo + lane * step;
-    const bool ok = cand < hi && (long)(clamp_cu(cand) / C + cand) <= slot;
-    const unsigned long long m = __ballot(ok);
-    const int kk = __popcll(m) - 1;  // lane 0 (cand = lo) always passes
-    lo = lo + kk * step;
-    hi = min(lo + step, hi);
-  }
-  const int n = __builtin_amdgcn_readfirstlane(lo);
-  const int a = clamp_cu(n);
-  int b = clamp_cu(n + 1);
-  b = b < a ? a : b;
-  const long c = slot - (long)(a / C + n);
-  const int len = b - a;
-  if (c < 0 || c * C >= len) {
-    r.row = 0; r.nvalid = 0;
-    return r;
-  }
-  r.row = a + c * C;
-  r.nvalid = len - c * C < C ? (int)(len - c * C) : C;
-  return r;
-}
-
-template <int DK, int DV>
+// BWD: also write the reverse chain's operands (BwdLayout) after the forward factors, and
+// use the backward unit stride.
+template <int DK, int DV, bool BWD>
 __global__ void __launch_bounds__(512)
 gdn2_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                  const bf16* __restrict__ v, const bf16* __restrict__ g,
@@ -158,6 +103,8 @@ gdn2_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   using Sh = PrepShape<DK, DV>;
   using M = Mma<T>;
   constexpr SplitLayout L(DK, DV);
+  constexpr BwdLayout LB(DK, DV);
+  constexpr long UNIT = BWD ? LB.bytes : L.bytes;
   constexpr int C = Sh::C, NW = Sh::NW, NT = Sh::NT;
   constexpr int LDK = Sh::LDK, LDT = Sh::LDT, NCT = Sh::NCT;
   constexpr int ADB = 16 * Sh::LDD, ADP = Sh::LDD;
@@ -261,7 +208,7 @@ gdn2_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   for (; u < nunits; u += gridDim.x) {
     const long un = u + gridDim.x;
     const ChunkUnit nxt = map_unit(un < nunits ? un : u, H, cu_seqlens, N, T_len, lane);
-    char* out = ws + u * L.bytes;
+    char* out = ws + u * UNIT;
 
     lds_barrier();  // the previous unit's readers of every buffer are done
     fresh();
@@ -470,6 +417,71 @@ gdn2_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       if (tid < DK / 4)  // gamma
         ost[Op::J_G] = *reinterpret_cast<const u32x4*>(sFac + Fac::GAM * DK + 4 * tid);
     }
+    if constexpr (BWD) {
+      // the reverse chain's operands, stored at once (16-byte pieces; transposed reads of
+      // the LDS arrays, two bf16 per 4-byte word)
+      auto put8 = [&](long off, const float* f) {
+        *reinterpret_cast<uint4*>(out + off) =
+            make_uint4(pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]),
+                       pack_bf16(f[6], f[7]));
+      };
+      constexpr int KSK = DK / 32;
+#pragma unroll
+      for (int qq = 0; qq < 4 * KSK * 64 / NT; ++qq) {  // Ktil, row-major: rows = tokens
+        // from the token-transposed copy (K 2^(Glast - G) on both paths; phi-ordered,
+        // swizzled tokens)
+        const int p = tid + qq * NT, bi = p >> 6, l = p & 63;
+        const int r = 16 * (bi / KSK) + (l & 15), p0 = 32 * (bi % KSK) + 8 * (l >> 4);
+        float f[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int c = M::phi_inv(p0 + j);
+          f[j] = to_f(sKt[c * LDT + tcol(c, M::phi(r))]);
+        }
+        put8(LB.kr + p * 16, f);
+      }
+      {  // P^T: rows r, K = tokens i (natural); blocks (2,0), (3,0) are zero
+        const int p = tid, bi = p >> 6, l = p & 63;
+        const int r = 16 * (bi >> 1) + (l & 15), i0 = 32 * (bi & 1) + 8 * (l >> 4);
+        if (!(bi == 4 || bi == 6)) {
+          float f[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) f[j] = to_f(sP[(i0 + j) * LDT + M::phi(r)]);
+          put8(LB.pt + p * 16, f);
+        }
+      }
+#pragma unroll
+      for (int qq = 0; qq < NCT * 2 * 64 / NT; ++qq) {  // Qbar^T and -W^T: rows = channels
+        const int p = tid + qq * NT, bi = p >> 6, l = p & 63;
+        const int c = 16 * (bi >> 1) + (l & 15), t0 = 32 * (bi & 1) + 8 * (l >> 4);
+        float fq[8], fw[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          fq[j] = to_f(sQ[(t0 + j) * LDK + M::phi(c)]);            // tokens natural
+          fw[j] = to_f(sWm[M::phi_inv(t0 + j) * LDK + M::phi(c)]);  // tokens phi-ordered
+        }
+        put8(LB.qt + p * 16, fq);
+        put8(LB.wt + p * 16, fw);
+      }
+      {  // back-substitution blocks (R, J), J >= R: 2 lanes x 4 bf16 per 16-byte piece
+        const int p = tid, bi = p >> 5, l0 = 2 * (p & 31);
+        const int R = bi >> 2, J = bi & 3;
+        if (J >= R) {
+          float f[8];
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int a = (l0 + h2) & 15, gq = (l0 + h2) >> 4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int c = 4 * gq + i;
+              f[4 * h2 + i] = J > R ? to_f(sAm[(16 * J + c) * LDT + 16 * R + a])
+                                    : to_f(sT[(16 * R + c) * LDT + 16 * R + a]);
+            }
+          }
+          put8(LB.bt + p * 16, f);
+        }
+      }
+    }
     prev_out = out;
     cur = nxt;
   }
@@ -505,7 +517,9 @@ struct StateShape {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int DK, int DV, int NV>
+// STORE (backward's forward pass): no output; instead the state entering every chunk and
+// that chunk's U are stored into the backward workspace (BwdLayout::h, ::ub).
+template <int DK, int DV, int NV, bool STORE>
 __global__ void __launch_bounds__((StateShape<DK, DV, NV>::NT)) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict__ o,
                   float* sN, const int* __restrict__ cu_seqlens, int T_len, int H,
@@ -514,6 +528,8 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
   using Sh = StateShape<DK, DV, NV>;
   using M = Mma<T>;
   constexpr SplitLayout L(DK, DV);
+  constexpr BwdLayout LB(DK, DV);
+  constexpr long UNIT = STORE ? LB.bytes : L.bytes;
   constexpr int C = Sh::C, NT = Sh::NT, KSK = Sh::KSK, NMT = Sh::NMT, OP = Sh::OP;
   __shared__ __attribute__((aligned(16))) char smem[Sh::LDS_BYTES];
 
@@ -572,7 +588,7 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
   static_assert(Sh::OFF_U == (int)L.u, "staged prefix matches the workspace prefix");
   const int u_shift = slice * Sh::SZ_U;
   auto piece_src = [&](int p, long chunk) -> const u32x4* {
-    const char* unit = ws + ((slot0 + chunk) * H + h) * L.bytes;
+    const char* unit = ws + ((slot0 + chunk) * H + h) * UNIT;
     const int off = p * 16 + (p >= Sh::OFF_U / 16 && p < Sh::OFF_G / 16 ? u_shift : 0) +
                     (p >= Sh::OFF_G / 16 ? (int)L.g - Sh::OFF_G : 0);
     return reinterpret_cast<const u32x4*>(unit + off);
@@ -622,6 +638,14 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
     typename M::frag sb[KSK];
 #pragma unroll
     for (int s = 0; s < KSK; ++s) sb[s] = M::from_acc(S, s);
+    char* const bunit = const_cast<char*>(ws) + ((slot0 + ci) * H + h) * UNIT;
+    const int ctg = slice * Sh::NWV + wave;  // this wave's column tile within d_v
+    if constexpr (STORE) {  // the state entering this chunk
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+        *reinterpret_cast<uint2*>(bunit + LB.h + ((ctg * NMT + mt) * 64 + lane) * 8) =
+            make_uint2(pack_bf16(S[mt][0], S[mt][1]), pack_bf16(S[mt][2], S[mt][3]));
+    }
     // U = U~ - W S
     f4 U[4];
 #pragma unroll
@@ -635,14 +659,18 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
 #pragma unroll
     for (int i = 0; i < 4 * KSK; ++i) fw[i] = frag((int)L.w, i);
     typename M::frag fq[4 * KSK];
+    if constexpr (!STORE) {
 #pragma unroll
-    for (int i = 0; i < 4 * KSK; ++i) fq[i] = frag((int)L.q, i);
+      for (int i = 0; i < 4 * KSK; ++i) fq[i] = frag((int)L.q, i);
+    }
     __builtin_amdgcn_sched_barrier(0);  // all of the above is issued before any product
     typename M::frag fk[2 * NMT], fp[6];
 #pragma unroll
     for (int i = 0; i < 2 * NMT; ++i) fk[i] = frag((int)L.kt, i);
+    if constexpr (!STORE) {
 #pragma unroll
-    for (int i = 0; i < 6; ++i) fp[i] = frag((int)L.p, i < 2 ? 2 * i : i + 2);  // blocks 0,2,4,5,6,7
+      for (int i = 0; i < 6; ++i) fp[i] = frag((int)L.p, i < 2 ? 2 * i : i + 2);  // blocks 0,2,4,5,6,7
+    }
     f4 gam[NMT];
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) gam[mt] = *reinterpret_cast<const f4*>(B + Sh::OFF_G + (16 * mt + 4 * g4) * 4);
@@ -652,11 +680,18 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
       for (int s = 0; s < KSK; ++s) U[R] = M::mma(fw[R * KSK + s], sb[s], U[R]);
     // O = Qbar S + P U
     f4 O[4];
+    if constexpr (!STORE) {
 #pragma unroll
-    for (int R = 0; R < 4; ++R) {
-      O[R] = f4{0.f, 0.f, 0.f, 0.f};
+      for (int R = 0; R < 4; ++R) {
+        O[R] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KSK; ++s) O[R] = M::mma(fq[R * KSK + s], sb[s], O[R]);
+        for (int s = 0; s < KSK; ++s) O[R] = M::mma(fq[R * KSK + s], sb[s], O[R]);
+      }
+    } else {
+#pragma unroll
+      for (int R = 0; R < 4; ++R)
+        *reinterpret_cast<uint2*>(bunit + LB.ub + ((ctg * 4 + R) * 64 + lane) * 8) =
+            make_uint2(pack_bf16(U[R][0], U[R][1]), pack_bf16(U[R][2], U[R][3]));
     }
     typename M::frag ub[2];
 #pragma unroll
@@ -669,11 +704,13 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
       for (int s = 0; s < 2; ++s) acc = M::mma(fk[mt * 2 + s], ub[s], acc);
       S[mt] = acc;
     }
+    if constexpr (!STORE) {
 #pragma unroll
-    for (int R = 0; R < 4; ++R) {
+      for (int R = 0; R < 4; ++R) {
 #pragma unroll
-      for (int s = 0; s < causal_steps<32>(R); ++s) O[R] = M::mma(fp[R < 2 ? R : 2 * R - 2 + s], ub[s], O[R]);
-      store_tile_pairs(so + (16 * R) * OP + 16 * wave, OP, lane, O[R], [](int c) { return c; });
+        for (int s = 0; s < causal_steps<32>(R); ++s) O[R] = M::mma(fp[R < 2 ? R : 2 * R - 2 + s], ub[s], O[R]);
+        store_tile_pairs(so + (16 * R) * OP + 16 * wave, OP, lane, O[R], [](int c) { return c; });
+      }
     }
     // next chunk's operands into the other buffer (its last readers finished before the
     // previous barrier); the previous chunk's output (staged before the last barrier) to
@@ -682,7 +719,7 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
     // at the end of the next chunk then also covers stores a whole chunk old, instead of
     // stores issued after the loads (which the waits cannot tell apart from them).
     if (ci + 1 < nch) stage_store(smem + ((ci + 1) & 1) * Sh::STAGE);
-    if (ci > 0) {
+    if (!STORE && ci > 0) {
       const int pv = len - (ci - 1) * C;
       out_store(reinterpret_cast<const T*>(smem + Sh::OFF_O + ((ci - 1) & 1) * Sh::SZ_O),
                 (long)(ci - 1) * C, pv < C ? pv : C);
@@ -690,7 +727,7 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
     stage_load(ci + 2 < nch ? ci + 2 : nch - 1);
     lds_barrier();
   }
-  if (nch > 0) {
+  if (!STORE && nch > 0) {
     const int pv = len - (nch - 1) * C;
     out_store(reinterpret_cast<const T*>(smem + Sh::OFF_O + ((nch - 1) & 1) * Sh::SZ_O),
               (long)(nch - 1) * C, pv < C ? pv : C);
@@ -704,7 +741,7 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
 }
 
 // ------------------------------------------------------------------ launch
-static int cu_count() {
+int cu_count() {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -724,7 +761,7 @@ static hipError_t launch_split(const ChunkArgs& a) {
   hipStream_t st = (hipStream_t)a.stream;
   if (nunits > 0) {
     const long grid1 = nunits < cu_count() ? nunits : cu_count();
-    hipLaunchKernelGGL((gdn2_prep_kernel<DK, DV>), dim3((unsigned)grid1), dim3(512), 0, st,
+    hipLaunchKernelGGL((gdn2_prep_kernel<DK, DV, false>), dim3((unsigned)grid1), dim3(512), 0, st,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.g,
                        (const bf16*)a.b, (const bf16*)a.w, (char*)a.workspace, a.cu_seqlens,
                        a.N, a.T, a.H, nunits);
@@ -733,10 +770,43 @@ static hipError_t launch_split(const ChunkArgs& a) {
   }
   const int nslices = DV / NV;
   const long grid2 = (long)a.N * a.H * nslices;
-  hipLaunchKernelGGL((gdn2_state_kernel<DK, DV, NV>), dim3((unsigned)grid2),
+  hipLaunchKernelGGL((gdn2_state_kernel<DK, DV, NV, false>), dim3((unsigned)grid2),
                      dim3(StateShape<DK, DV, NV>::NT), 0, st, (const char*)a.workspace, a.s0,
                      (bf16*)a.o, a.sN, a.cu_seqlens, a.T, a.H, nslices, a.N * a.H);
   return hipGetLastError();
+}
+
+// Backward's forward part: the factors in the backward layout, then the forward chain that
+// stores every chunk's entering state and U (no output).
+template <int DK, int DV>
+static hipError_t launch_bwd_forward(const ChunkArgs& a) {
+  const bool varlen = a.cu_seqlens != nullptr;
+  const long nunits = split_slots(varlen, a.B, a.T, a.N) * a.H;
+  hipStream_t st = (hipStream_t)a.stream;
+  if (nunits > 0) {
+    const long grid1 = nunits < cu_count() ? nunits : cu_count();
+    hipLaunchKernelGGL((gdn2_prep_kernel<DK, DV, true>), dim3((unsigned)grid1), dim3(512), 0, st,
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.g,
+                       (const bf16*)a.b, (const bf16*)a.w, (char*)a.workspace, a.cu_seqlens,
+                       a.N, a.T, a.H, nunits);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  constexpr int NV = 64 <= DV ? 64 : DV;
+  const int nslices = DV / NV;
+  hipLaunchKernelGGL((gdn2_state_kernel<DK, DV, NV, true>), dim3((unsigned)(a.N * a.H * nslices)),
+                     dim3(StateShape<DK, DV, NV>::NT), 0, st, (const char*)a.workspace, a.s0,
+                     nullptr, nullptr, a.cu_seqlens, a.T, a.H, nslices, a.N * a.H);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_forward_part(const ChunkArgs& a) {
+  if (a.dtype != 0) return hipErrorInvalidValue;
+  if (a.d_k == 64 && a.d_v == 64) return launch_bwd_forward<64, 64>(a);
+  if (a.d_k == 64 && a.d_v == 128) return launch_bwd_forward<64, 128>(a);
+  if (a.d_k == 128 && a.d_v == 64) return launch_bwd_forward<128, 64>(a);
+  if (a.d_k == 128 && a.d_v == 128) return launch_bwd_forward<128, 128>(a);
+  return hipErrorInvalidValue;
 }
 
 template <int DK, int DV>

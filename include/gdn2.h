@@ -101,6 +101,44 @@ size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int
                                       int dtype);
 
 /*
+ * Chunkwise backward: gradients of gdn2_chunk_fwd for upstream gradients of o and of the
+ * final states (the gate-aware backward of the reading note's §3: the state gradient flows
+ * through the asymmetric factor Diag(alpha_t)(I - e_t k_t^T) of every token; here in chunk
+ * form, with one triangular solve per chunk). Inputs and conventions as gdn2_chunk_fwd:
+ *
+ *   q, k, log_alpha, b, v, w, initial_state, cu_seqlens, B, T, H, d_k, d_v, N : as forward
+ *   d_o               : [B, T, H, d_v] (dtype), gradient of o
+ *   d_final_state     : [N, H, d_k, d_v] fp32, or NULL for zero
+ *   dq, dk, dlog_alpha, db : [B, T, H, d_k] (dtype), written
+ *   dv, dw            : [B, T, H, d_v] (dtype), written
+ *   d_initial_state   : [N, H, d_k, d_v] fp32, or NULL (not written)
+ *   range_flag        : NULL, or a device int32 that the call sets to 1 (and otherwise leaves
+ *                       alone) when some chunk's total decay, in some key channel, exceeds
+ *                       the range of the backward's chunk-referenced factors (about 83 nats
+ *                       over 64 tokens); the gradients of such chunks are not valid. The
+ *                       caller clears it beforehand and checks it afterwards.
+ *   workspace         : required, at least gdn2_chunk_bwd_workspace_bytes(...) bytes, 16-byte
+ *                       aligned, free for the call's duration on `hip_stream`.
+ *   Supported: GDN2_BF16 with d_k, d_v in {64, 128}.
+ * Returns GDN2_OK or an error status (GDN2_UNSUPPORTED for GDN2_F32,
+ * GDN2_WORKSPACE_TOO_SMALL for a missing or short workspace).
+ */
+int gdn2_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                   const void* b, const void* w, const float* initial_state, const void* d_o,
+                   const float* d_final_state, void* dq, void* dk, void* dv, void* dlog_alpha,
+                   void* db, void* dw, float* d_initial_state, int32_t* range_flag,
+                   const int32_t* cu_seqlens, int B, int T, int H, int d_k, int d_v, int N,
+                   int dtype, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Device workspace, in bytes, that gdn2_chunk_bwd needs for these sizes, with or without
+ * cu_seqlens (about 3.7 KiB per token and head at d_k = d_v = 128, plus one chunk per
+ * sequence); 0 where the backward is not built.
+ */
+size_t gdn2_chunk_bwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int N,
+                                      int dtype);
+
+/*
  * The fused single-kernel path of gdn2_chunk_fwd (no workspace) with an explicit
  * value-slice width: each workgroup carries
  * `value_slice` columns of the state (16, 32, 64 or 128; a divisor of d_v; 16 only with

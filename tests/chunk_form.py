@@ -127,3 +127,51 @@ def chunked_backward(q, k, v, g, b, w, s0, dO, dSn, C):
             gr[sl] = d
         dS = out[6]
     return (*grads, dS)
+
+
+def chunk_backward_parts(S0, q, k, v, g, b, w, dO, dSn):
+    """chunk_step_backward regrouped the way the GPU backward computes it:
+
+      recurrence part (sequential over chunks, per value column):
+        dU  = P^T dO + Ktil dSn,    dZ = T^T dU,    dv = dZ * w,   dw = dZ * v,
+        dS0 = Qbar^T dO + Diag(exp(G_last)) dSn - W^T dU
+      local part (per chunk, needs only U = U~ - W S0, S0, dSn, dO, dZ and exp(+-G)):
+        M1 = lower_incl(dO U^T),    M2 = -strict(dZ U^T)             (M2 = dA)
+        dQbar = dO S0^T + M1 Khat,  dEbar = -dZ S0^T + M2 Khat,   dKhat = M2^T Ebar + M1^T Qbar,
+        dKtil = U dSn^T
+    The regrouping uses T^T dW = -(T^T dU) S0^T = -dZ S0^T, so that
+    dA = -strict(dZ U~^T + (T^T dW) W^T) = -strict(dZ (U~ - W S0)^T) = -strict(dZ U^T):
+    one triangular solve per chunk instead of two, and no use of T or A in the local part.
+    Returns the same tuple as chunk_step_backward.
+    """
+    n = q.shape[0]
+    G = np.cumsum(g, axis=0)
+    Gam = np.exp(G)
+    Gn = G[-1]
+    E, Z = b * k, w * v
+    incl = np.tril(np.ones((n, n)))
+    strict = np.tril(np.ones((n, n)), -1)
+    Ebar, Qbar, Khat = E * Gam, q * Gam, k / Gam
+    Ktil = k * np.exp(Gn[None, :] - G)
+    A = (Ebar @ Khat.T) * strict
+    P = (Qbar @ Khat.T) * incl
+    T = np.linalg.inv(np.eye(n) + A)
+    W = T @ Ebar
+    U = T @ Z - W @ S0
+    # recurrence part
+    dU = P.T @ dO + Ktil @ dSn
+    dZ = T.T @ dU
+    dS0 = Qbar.T @ dO + np.exp(Gn)[:, None] * dSn - W.T @ dU
+    # local part
+    M1 = (dO @ U.T) * incl
+    M2 = -(dZ @ U.T) * strict
+    dQbar = dO @ S0.T + M1 @ Khat
+    dEbar = -dZ @ S0.T + M2 @ Khat
+    dKhat = M2.T @ Ebar + M1.T @ Qbar
+    dKtil = U @ dSn.T
+    dE = dEbar * Gam
+    dk = dKhat / Gam + dKtil * np.exp(Gn[None, :] - G) + dE * b
+    dG = dEbar * Ebar + dQbar * Qbar - dKhat * Khat - dKtil * Ktil
+    dG[-1] += np.sum(dKtil * Ktil, axis=0) + np.sum(dSn * np.exp(Gn)[:, None] * S0, axis=1)
+    dg = np.cumsum(dG[::-1], axis=0)[::-1]
+    return dQbar * Gam, dk, dZ * w, dg, dE * k, dZ * v, dS0

@@ -119,3 +119,31 @@ def test_decode_error_paths():
     assert call(q=None) == 1
     assert call(state=MIS) == 1
     assert call(N=0, q=None, state=None) == 0
+
+
+def _bwd(**kw):
+    a = dict(B=2, T=64, H=4, dk=128, dv=128, N=2, dtype=0, ws=None, wsz=0, q=FAKE, flag=None)
+    a.update(kw)
+    L = _lib.lib()
+    return L.gdn2_chunk_bwd(a["q"], FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
+                            FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, a["flag"], None,
+                            a["B"], a["T"], a["H"], a["dk"], a["dv"], a["N"], a["dtype"],
+                            a["ws"], a["wsz"], None)
+
+
+def test_chunk_bwd_error_paths():
+    L = _lib.lib()
+    need = 2 * 1 * 4 * 238080  # two sequences x one chunk x 4 heads x the d=128 unit
+    assert L.gdn2_chunk_bwd_workspace_bytes(2, 64, 4, 128, 128, 2, 0) == (2 + 2) * 4 * 238080
+    assert L.gdn2_chunk_bwd_workspace_bytes(2, 64, 4, 64, 64, 2, 1) == 0      # fp32: not built
+    assert _bwd(dtype=1, dk=64, dv=64) == 2
+    assert _bwd(dtype=7) == 1
+    assert _bwd(dk=96) == 2
+    assert _bwd(N=3) == 1
+    assert _bwd(q=None) == 1
+    assert _bwd(q=MIS, ws=FAKE, wsz=need) == 1
+    assert _bwd(ws=None, wsz=need) == 3                 # the workspace is required
+    assert _bwd(ws=FAKE, wsz=need - 1) == 3
+    assert _bwd(ws=MIS, wsz=need) == 1
+    assert _bwd(flag=ctypes.c_void_p(0x100002), ws=FAKE, wsz=need) == 1  # misaligned flag
+    assert _bwd(B=0, N=0, q=None, ws=FAKE, wsz=0) == 0

@@ -1,0 +1,116 @@
+"""GPU parity of the chunkwise backward (through the C ABI) against the oracle's reverse token
+loop (float64). Tolerance: normwise max relative error 2e-2 per gradient (bf16 runs)."""
+import numpy as np
+import pytest
+import torch
+
+from gdn2_inputs import make_inputs, round_to_bf16
+from oracle import gdn2_backward
+from tests.gpu_util import TOL, assert_close, dev_tensor, host64, say
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("q", "k", "v", "g", "b", "w")
+GRADS = ("dq", "dk", "dv", "dg", "db", "dw")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _upstream(x, seed, with_dsn=True):
+    rng = np.random.default_rng(seed)
+    B, T, H, _ = x["q"].shape
+    dv = x["v"].shape[-1]
+    dk = x["q"].shape[-1]
+    N = B if x["cu_seqlens"] is None else len(x["cu_seqlens"]) - 1
+    do = round_to_bf16(rng.normal(size=(B, T, H, dv)).astype(np.float32))
+    dsn = rng.normal(size=(N, H, dk, dv)).astype(np.float32) * 0.1 if with_dsn else None
+    return do, dsn
+
+
+def run_bwd(x, do, dsn):
+    import gated_delta_rule_36_amd as G
+    t = {n: dev_tensor(x[n], "bf16") for n in NAMES}
+    s0 = None if x["s0"] is None else torch.from_numpy(x["s0"]).cuda()
+    cu = None if x["cu_seqlens"] is None else torch.from_numpy(x["cu_seqlens"]).cuda()
+    dsn_t = None if dsn is None else torch.from_numpy(dsn).cuda()
+    out = G.chunk_bwd(*(t[n] for n in NAMES), dev_tensor(do, "bf16"), initial_state=s0,
+                      d_final_state=dsn_t, cu_seqlens=cu)
+    torch.cuda.synchronize()
+    return out
+
+
+def check(x, do, dsn, tol=TOL["bf16"]):
+    out = run_bwd(x, do, dsn)
+    ref = gdn2_backward(*(x[n] for n in NAMES), do, dS_final=dsn, s0=x["s0"],
+                        cu_seqlens=x["cu_seqlens"])
+    for name, a, r in zip(GRADS + ("ds0",), out, ref):
+        assert_close(name, host64(a), r, tol)
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_bwd_ragged_with_state(dk, dv):
+    x = make_inputs(2, 200, 2, dk, dv, "bf16", seed=300 + dk + dv, s0_std=0.02)
+    do, dsn = _upstream(x, 1 + dk + dv)
+    say("bwd ragged B2 T200 H2", dk, dv)
+    check(x, do, dsn)
+
+
+def test_bwd_no_state_grads_in():
+    x = make_inputs(1, 130, 3, 128, 128, "bf16", seed=311)
+    do, _ = _upstream(x, 7, with_dsn=False)
+    say("bwd zero S0, no final-state gradient")
+    check(x, do, None)
+
+
+def test_bwd_varlen():
+    lens = [1, 63, 64, 0, 65, 130, 7]
+    x = make_inputs(1, sum(lens), 2, 128, 64, "bf16", seed=312, lengths=lens, s0_std=0.02)
+    do, dsn = _upstream(x, 8)
+    say("bwd varlen", lens)
+    check(x, do, dsn)
+
+
+@pytest.mark.parametrize("case", ["b0", "b1_w1", "b2"])
+def test_bwd_gate_cases(case):
+    x = make_inputs(1, 160, 2, 128, 128, "bf16", seed=313, s0_std=0.02)
+    if case == "b0":
+        x["b"][:] = 0.0
+    elif case == "b1_w1":
+        x["b"][:] = 1.0
+        x["w"][:] = 1.0
+    elif case == "b2":
+        x["b"] = (2.0 * x["b"]).astype(np.float32)
+    do, dsn = _upstream(x, 9)
+    say("bwd gates", case)
+    check(x, do, dsn)
+
+
+def test_bwd_range_flag():
+    import gated_delta_rule_36_amd as G
+    x = make_inputs(1, 128, 1, 64, 64, "bf16", seed=314)
+    x["g"][:, 64:] = -5.0  # the second chunk decays by 320 nats
+    do, _ = _upstream(x, 10, with_dsn=False)
+    say("bwd range flag")
+    with pytest.raises(G.Gdn2RangeError):
+        run_bwd(x, do, None)
+
+
+def test_bwd_layer1p3b_full_size_sampled():
+    from gdn2_inputs import make_config_inputs
+    from oracle import gdn2_backward as ref_bwd
+    x = make_config_inputs("layer1p3b_bf16")
+    do, dsn = _upstream(x, 11)
+    say("bwd layer1p3b B8 H16 T2048 d128 (sampled chains)")
+    out = run_bwd(x, do, dsn)
+    for (n, h) in [(0, 0), (5, 9)]:
+        sel = {m: x[m][n:n + 1, :, h:h + 1] for m in NAMES}
+        ref = ref_bwd(*(sel[m] for m in NAMES), do[n:n + 1, :, h:h + 1],
+                      dS_final=dsn[n:n + 1, h:h + 1])
+        print(f" chain (n={n}, h={h})", flush=True)
+        for name, a, r in zip(GRADS, out[:6], ref[:6]):
+            assert_close(name, host64(a[n:n + 1, :, h:h + 1]), r, TOL["bf16"])
+        assert_close("ds0", host64(out[6][n:n + 1, h:h + 1]), ref[6], TOL["bf16"])

@@ -131,3 +131,19 @@ def test_chunked_backward_equals_sequential(C, L):
     for name, a, r in zip(NAMES, got[:6], ref[:6]):
         assert _max_rel(a, r[0, :, 0]) < 1e-9, name
     assert _max_rel(got[6], ref[6][0, 0]) < 1e-9
+
+
+@pytest.mark.parametrize("n", [1, 5, 64])
+def test_backward_regrouping_equals_chunk_backward(n):
+    from tests.chunk_form import chunk_backward_parts, chunk_step_backward
+    rng = np.random.default_rng(40 + n)
+    dk, dv = 8, 6
+    x = _problem(rng, 1, n, 1, dk, dv)
+    args = [x[m][0, :, 0] for m in NAMES]
+    S0 = rng.normal(size=(dk, dv))
+    dO = rng.normal(size=(n, dv))
+    dSn = rng.normal(size=(dk, dv))
+    ref = chunk_step_backward(S0, *args, dO, dSn)
+    got = chunk_backward_parts(S0, *args, dO, dSn)
+    for a, r in zip(got, ref):
+        assert _max_rel(a, r) < 1e-10
