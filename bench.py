@@ -276,6 +276,28 @@ def main():
                                      f"fp32 state in place, {cd['steps']} consecutive steps",
                          "bytes_per_step": decode_bytes(N, Hd, dkd, dvd),
                          "traffic": measured_traffic("decode_step_n256_h16_bf16"), **res}
+        # several tokens per call against the pool (draft verification / multi-token decode)
+        Lv = 4
+        vt = {n: torch.stack([td[n][s % pool] for s in range(Lv)], dim=1).contiguous()
+              for n in NAMES}
+        vstate = states[0]
+        for _ in range(5):
+            G.decode_tokens(*(vt[n] for n in NAMES), vstate)
+        torch.cuda.synchronize()
+        evv = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(50)]
+        for a, b2 in evv:
+            a.record()
+            G.decode_tokens(*(vt[n] for n in NAMES), vstate)
+            b2.record()
+        torch.cuda.synchronize()
+        vus = float(np.mean([a.elapsed_time(b2) for a, b2 in evv])) * 1e3
+        vbytes = N * Hd * (2 * dkd * dvd * 4 + Lv * ((4 * dkd + 2 * dvd) * 2 + dvd * 2))
+        out["decode"]["tokens_per_call_L4"] = {
+            "us_per_call": round(vus, 2), "tokens_per_s": round(N * Lv / (vus * 1e-6), 1),
+            "bytes_per_call": vbytes, "achieved_GBs": round(vbytes / (vus * 1e-6) / 1e9, 1),
+            "hbm_frac": round(vbytes / (vus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "vs_four_single_steps": round(4 * res["one_pool"]["us_per_step"] / vus, 3)}
 
     if not args.no_cpu and args.workload == "layer1p3b":
         out["cpu_baseline"] = cpu_baseline(x)

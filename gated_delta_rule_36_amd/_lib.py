@@ -57,6 +57,8 @@ def lib():
         L.gdn2_chunk_fwd_sliced.restype = _I
         L.gdn2_decode_step.argtypes = [_P] * 8 + [_I] * 5 + [_P]
         L.gdn2_decode_step.restype = _I
+        L.gdn2_decode_tokens.argtypes = [_P] * 11 + [_I] * 7 + [_P]
+        L.gdn2_decode_tokens.restype = _I
         L.gdn2_status_string.argtypes = [_I]
         L.gdn2_status_string.restype = ctypes.c_char_p
         L.gdn2_version.argtypes = []
@@ -247,3 +249,40 @@ def decode_step(q, k, v, g, b, w, state):
     if st != 0:
         raise Gdn2Error("gdn2_decode_step", st)
     return o
+
+
+def decode_tokens(q, k, v, g, b, w, state_pool, state_indices=None, commit_len=None,
+                  return_step_states=False):
+    """L consecutive tokens per sequence against a pool of fp32 states (decode of several
+    tokens, or verification of draft tokens).
+
+    q, k, g, b: [N, L, H, d_k]; v, w: [N, L, H, d_v]; state_pool: [P, H, d_k, d_v] fp32,
+    updated in place for the committed prefix; state_indices: int32 [N] (slot per sequence,
+    negative to skip) or None (slot n); commit_len: int32 [N] or None (all L tokens).
+    Returns (o [N, L, H, d_v], step_states [N, L, H, d_k, d_v] fp32 or None).
+    """
+    if q.dim() != 4:
+        raise ValueError("q must be [N, L, H, d_k]")
+    N, L, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(dt)
+    for name, t, d in (("q", q, dk), ("k", k, dk), ("g", g, dk), ("b", b, dk),
+                       ("v", v, dv), ("w", w, dv)):
+        _check(name, t, (N, L, H, d), dt, dev)
+    if state_pool.dim() != 4:
+        raise ValueError("state_pool must be [P, H, d_k, d_v]")
+    P = state_pool.shape[0]
+    _check("state_pool", state_pool, (P, H, dk, dv), torch.float32, dev)
+    for name, t in (("state_indices", state_indices), ("commit_len", commit_len)):
+        if t is not None and (t.dtype != torch.int32 or t.device != dev or tuple(t.shape) != (N,)):
+            raise ValueError(f"{name} must be an int32 [N] tensor on the inputs' device")
+    o = torch.empty((N, L, H, dv), dtype=dt, device=dev)
+    steps = (torch.empty((N, L, H, dk, dv), dtype=torch.float32, device=dev)
+             if return_step_states else None)
+    st = lib().gdn2_decode_tokens(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w),
+                                  _ptr(state_pool), _ptr(state_indices), _ptr(commit_len),
+                                  _ptr(o), _ptr(steps), N, L, H, dk, dv, P, code, _stream(dev))
+    if st != 0:
+        raise Gdn2Error("gdn2_decode_tokens", st)
+    return o, steps

@@ -203,6 +203,32 @@ int gdn2_decode_step(const void* q, const void* k, const void* v, const void* lo
   return status_of(gdn2::launch_decode_step(a));
 }
 
+int gdn2_decode_tokens(const void* q, const void* k, const void* v, const void* log_alpha,
+                       const void* b, const void* w, float* state_pool,
+                       const int32_t* state_indices, const int32_t* commit_len, void* o,
+                       float* step_states, int N, int L, int H, int d_k, int d_v, int P,
+                       int dtype, void* hip_stream) {
+  if (dtype != GDN2_BF16 && dtype != GDN2_F32) return GDN2_INVALID_ARGUMENT;
+  if (N < 0 || L < 0 || H <= 0 || P < 0 || d_k <= 0 || d_v <= 0) return GDN2_INVALID_ARGUMENT;
+  if (!width_ok(d_k) || !width_ok(d_v)) return GDN2_UNSUPPORTED;
+  if (N == 0 || L == 0) return GDN2_OK;
+  if (!q || !k || !v || !log_alpha || !b || !w || !state_pool || !o) return GDN2_INVALID_ARGUMENT;
+  if (state_indices == nullptr && P < N) return GDN2_INVALID_ARGUMENT;
+  const void* ptrs[9] = {q, k, v, log_alpha, b, w, state_pool, o, step_states};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return GDN2_INVALID_ARGUMENT;
+  if ((state_indices && (reinterpret_cast<uintptr_t>(state_indices) & 3u) != 0) ||
+      (commit_len && (reinterpret_cast<uintptr_t>(commit_len) & 3u) != 0))
+    return GDN2_INVALID_ARGUMENT;
+  if ((long)N * H > (long)INT_MAX || (long)N * L * H > (long)INT_MAX) return GDN2_INVALID_ARGUMENT;
+  gdn2::DecodeTokensArgs a;
+  a.q = q; a.k = k; a.v = v; a.g = log_alpha; a.b = b; a.w = w;
+  a.pool = state_pool; a.indices = state_indices; a.commit = commit_len; a.o = o;
+  a.step_states = step_states; a.N = N; a.L = L; a.H = H; a.d_k = d_k; a.d_v = d_v; a.P = P;
+  a.dtype = dtype; a.stream = hip_stream;
+  return status_of(gdn2::launch_decode_tokens(a));
+}
+
 const char* gdn2_status_string(int status) {
   switch (status) {
     case GDN2_OK: return "ok";

@@ -91,6 +91,100 @@ gdn2_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   }
 }
 
+// L consecutive tokens per (sequence, head) against a pool of states (serving: decode of a
+// few tokens at once, or verification of draft tokens). The state of pool slot
+// indices[n] is read once, advanced through the L tokens in registers, and, after token
+// commit[n] - 1, written back to its slot (commit 0: the pool is left alone); with
+// step_states every intermediate state is also written out. Same per-token arithmetic as
+// gdn2_decode_kernel; the token inputs are double-buffered in LDS by token parity, so a
+// token costs two barriers.
+template <typename T, int DK, int DV>
+__global__ void __launch_bounds__(256)
+gdn2_decode_tokens_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                          const T* __restrict__ v, const T* __restrict__ g,
+                          const T* __restrict__ bg, const T* __restrict__ wg,
+                          float* __restrict__ pool, const int* __restrict__ indices,
+                          const int* __restrict__ commit, T* __restrict__ o,
+                          float* __restrict__ step_states, int L, int H, int P) {
+  constexpr int NT = 256;
+  constexpr int CG = DV / 4;
+  constexpr int RG = NT / CG;
+  constexpr int RPT = DK / RG;
+  __shared__ float s_alpha[2][DK], s_e[2][DK], s_q[2][DK], s_k[2][DK], s_z[2][DV];
+  __shared__ __attribute__((aligned(16))) float s_red[2][2][RG][DV];
+  __shared__ float s_qk[2];
+
+  const int tid = threadIdx.x;
+  const int n = blockIdx.x / H, h = blockIdx.x % H;
+  const int slot = indices != nullptr ? indices[n] : n;
+  if (slot < 0 || slot >= P) return;  // no state for this sequence (uniform)
+  int ncommit = commit != nullptr ? commit[n] : L;
+  ncommit = ncommit < 0 ? 0 : (ncommit > L ? L : ncommit);
+  const int cg = tid % CG, rg = tid / CG;
+  float* S = pool + ((long)slot * H + h) * DK * DV;
+
+  f4 s[RPT];
+#pragma unroll
+  for (int j = 0; j < RPT; ++j)
+    s[j] = *reinterpret_cast<const f4*>(S + (long)(rg + j * RG) * DV + 4 * cg);
+
+  for (int t = 0; t < L; ++t) {
+    const int par = t & 1;
+    const long tk = (((long)n * L + t) * H + h);  // token row of [N, L, H, d]
+    for (int c = tid; c < DK; c += NT) {
+      const float kk = to_f(k[tk * DK + c]);
+      s_alpha[par][c] = __expf(to_f(g[tk * DK + c]));
+      s_e[par][c] = to_f(bg[tk * DK + c]) * kk;
+      s_q[par][c] = to_f(q[tk * DK + c]);
+      s_k[par][c] = kk;
+    }
+    for (int c = tid; c < DV; c += NT) s_z[par][c] = to_f(wg[tk * DV + c]) * to_f(v[tk * DV + c]);
+    __syncthreads();
+    if (tid < 64) {
+      float p = 0.f;
+      for (int c = tid; c < DK; c += 64) p += s_q[par][c] * s_k[par][c];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off, 64);
+      if (tid == 0) s_qk[par] = p;
+    }
+    f4 r = {0.f, 0.f, 0.f, 0.f}, sq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      const int c = rg + j * RG;
+      s[j] = s[j] * s_alpha[par][c];
+      r += s_e[par][c] * s[j];
+      sq += s_q[par][c] * s[j];
+    }
+    *reinterpret_cast<f4*>(&s_red[par][0][rg][4 * cg]) = r;
+    *reinterpret_cast<f4*>(&s_red[par][1][rg][4 * cg]) = sq;
+    __syncthreads();
+    r = f4{0.f, 0.f, 0.f, 0.f};
+    sq = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int x = 0; x < RG; ++x) {
+      r += *reinterpret_cast<const f4*>(&s_red[par][0][x][4 * cg]);
+      sq += *reinterpret_cast<const f4*>(&s_red[par][1][x][4 * cg]);
+    }
+    const f4 d = *reinterpret_cast<const f4*>(&s_z[par][4 * cg]) - r;
+    if (rg == 0) {
+      const f4 out = sq + s_qk[par] * d;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[tk * DV + 4 * cg + i] = from_f<T>(out[i]);
+    }
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) s[j] = s[j] + s_k[par][rg + j * RG] * d;
+    if (step_states != nullptr) {
+      float* St = step_states + tk * DK * DV;
+#pragma unroll
+      for (int j = 0; j < RPT; ++j) *reinterpret_cast<f4*>(St + (long)(rg + j * RG) * DV + 4 * cg) = s[j];
+    }
+    if (t + 1 == ncommit) {
+#pragma unroll
+      for (int j = 0; j < RPT; ++j) *reinterpret_cast<f4*>(S + (long)(rg + j * RG) * DV + 4 * cg) = s[j];
+    }
+  }
+}
+
 template <typename T, int DK, int DV>
 static hipError_t launch_dec(const DecodeArgs& a) {
   hipLaunchKernelGGL((gdn2_decode_kernel<T, DK, DV>), dim3((unsigned)((long)a.N * a.H)), dim3(256),
@@ -110,6 +204,28 @@ static hipError_t dispatch_dec(const DecodeArgs& a) {
 
 hipError_t launch_decode_step(const DecodeArgs& a) {
   return a.dtype == 0 ? dispatch_dec<bf16>(a) : dispatch_dec<float>(a);
+}
+
+template <typename T, int DK, int DV>
+static hipError_t launch_dec_tokens(const DecodeTokensArgs& a) {
+  hipLaunchKernelGGL((gdn2_decode_tokens_kernel<T, DK, DV>), dim3((unsigned)((long)a.N * a.H)),
+                     dim3(256), 0, (hipStream_t)a.stream, (const T*)a.q, (const T*)a.k,
+                     (const T*)a.v, (const T*)a.g, (const T*)a.b, (const T*)a.w, a.pool,
+                     a.indices, a.commit, (T*)a.o, a.step_states, a.L, a.H, a.P);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t dispatch_dec_tokens(const DecodeTokensArgs& a) {
+  if (a.d_k == 64 && a.d_v == 64) return launch_dec_tokens<T, 64, 64>(a);
+  if (a.d_k == 64 && a.d_v == 128) return launch_dec_tokens<T, 64, 128>(a);
+  if (a.d_k == 128 && a.d_v == 64) return launch_dec_tokens<T, 128, 64>(a);
+  if (a.d_k == 128 && a.d_v == 128) return launch_dec_tokens<T, 128, 128>(a);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_tokens(const DecodeTokensArgs& a) {
+  return a.dtype == 0 ? dispatch_dec_tokens<bf16>(a) : dispatch_dec_tokens<float>(a);
 }
 
 }  // namespace gdn2

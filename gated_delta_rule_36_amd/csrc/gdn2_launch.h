@@ -29,6 +29,18 @@ struct DecodeArgs {
   void* stream;
 };
 
+struct DecodeTokensArgs {
+  const void *q, *k, *v, *g, *b, *w;  // [N, L, H, d]
+  float* pool;                        // [P, H, d_k, d_v]
+  const int32_t* indices;             // [N] pool slot per sequence, or null (slot n)
+  const int32_t* commit;              // [N] tokens whose update is committed, or null (L)
+  void* o;                            // [N, L, H, d_v]
+  float* step_states;                 // [N, L, H, d_k, d_v] or null
+  int N, L, H, d_k, d_v, P;
+  int dtype;
+  void* stream;
+};
+
 // Value-slice widths the chunk kernel is built for, given dtype and d_k.
 inline bool chunk_nv_supported(int dtype, int d_k, int d_v, int nv) {
   if (nv > d_v || d_v % nv != 0) return false;
@@ -124,5 +136,6 @@ hipError_t launch_chunk_bwd(const BwdArgs& a);
 hipError_t launch_bwd_forward_part(const ChunkArgs& a);
 int cu_count();  // compute units of the current device
 hipError_t launch_decode_step(const DecodeArgs& a);
+hipError_t launch_decode_tokens(const DecodeTokensArgs& a);
 
 }  // namespace gdn2

@@ -170,6 +170,34 @@ int gdn2_decode_step(const void* q, const void* k, const void* v, const void* lo
                      const void* b, const void* w, float* state, void* o, int N, int H,
                      int d_k, int d_v, int dtype, void* hip_stream);
 
+/*
+ * L consecutive tokens for each of N sequences against a pool of recurrent states: decode
+ * of a few tokens at once, or verification of draft tokens in speculative decoding (the
+ * reading note's §7 names speculative decoding as the serving direction). Per (sequence,
+ * head) the state of slot state_indices[n] is read once, advanced through the L tokens with
+ * the decode step's arithmetic, and the state after token commit_len[n] - 1 is written back
+ * to that slot (commit_len[n] = 0 leaves the slot unchanged). Outputs of all L tokens are
+ * written either way.
+ *
+ *   q, k, log_alpha, b : [N, L, H, d_k]   (dtype)
+ *   v, w               : [N, L, H, d_v]   (dtype)
+ *   state_pool         : [P, H, d_k, d_v] fp32, read and (partly) written in place
+ *   state_indices      : device int32 [N], the slot of each sequence; a negative or >= P
+ *                        slot skips the sequence (its outputs are not written). NULL: slot n
+ *                        (then P >= N is required). Two sequences must not share a slot.
+ *   commit_len         : device int32 [N] in [0, L] (clamped), or NULL for L
+ *   o                  : [N, L, H, d_v]   (dtype), written
+ *   step_states        : NULL, or [N, L, H, d_k, d_v] fp32: the state after every token
+ *                        (so that an accepted prefix can be committed without recomputing)
+ *   Supported: d_k, d_v in {64, 128}, both dtypes. N = 0 or L = 0 is a no-op.
+ * Returns GDN2_OK or an error status.
+ */
+int gdn2_decode_tokens(const void* q, const void* k, const void* v, const void* log_alpha,
+                       const void* b, const void* w, float* state_pool,
+                       const int32_t* state_indices, const int32_t* commit_len, void* o,
+                       float* step_states, int N, int L, int H, int d_k, int d_v, int P,
+                       int dtype, void* hip_stream);
+
 /* Human-readable text for a status code (static storage; never NULL). */
 const char* gdn2_status_string(int status);
 

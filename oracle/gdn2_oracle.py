@@ -38,8 +38,8 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["gdn2_step", "gdn2_forward", "gdn2_decode_steps", "gdn2_step_backward",
-           "gdn2_backward"]
+__all__ = ["gdn2_step", "gdn2_forward", "gdn2_decode_steps", "gdn2_decode_tokens",
+           "gdn2_step_backward", "gdn2_backward"]
 
 
 def gdn2_step(S, q, k, v, g, b, w):
@@ -118,6 +118,38 @@ def gdn2_decode_steps(S, q, k, v, g, b, w):
     for s in range(steps):
         o[s], S = gdn2_step(S, q[s], k[s], v[s], g[s], b[s], w[s])
     return o, S
+
+
+def gdn2_decode_tokens(pool, q, k, v, g, b, w, indices=None, commit=None):
+    """L consecutive tokens per sequence against a pool of states (the per-token procedure of
+    [note §3], applied L times; serving use: decode or draft verification, [note §7]).
+
+    pool: [P, H, d_k, d_v]; q, k, g, b: [N, L, H, d_k]; v, w: [N, L, H, d_v].
+    indices: [N] pool slot per sequence (None: slot n); a slot outside [0, P) skips the
+    sequence (its outputs stay zero). commit: [N] number of leading tokens whose update is
+    written back to the slot (clamped to [0, L]; None: L).
+    Returns (o [N, L, H, d_v], step_states [N, L, H, d_k, d_v] (the state after every
+    token), new_pool); all float64.
+    """
+    pool = np.asarray(pool, dtype=np.float64)
+    q, k, v, g, b, w = (np.asarray(x, dtype=np.float64) for x in (q, k, v, g, b, w))
+    N, L = q.shape[:2]
+    P = pool.shape[0]
+    new_pool = pool.copy()
+    o = np.zeros(v.shape)
+    states = np.zeros((N, L) + pool.shape[1:])
+    for n in range(N):
+        slot = n if indices is None else int(indices[n])
+        if slot < 0 or slot >= P:
+            continue
+        c = L if commit is None else min(max(int(commit[n]), 0), L)
+        S = pool[slot].copy()
+        for t in range(L):
+            o[n, t], S = gdn2_step(S, q[n, t], k[n, t], v[n, t], g[n, t], b[n, t], w[n, t])
+            states[n, t] = S
+            if t + 1 == c:
+                new_pool[slot] = S
+    return o, states, new_pool
 
 
 def gdn2_step_backward(S_prev, q, k, v, g, b, w, do, dS):

@@ -147,3 +147,23 @@ def test_chunk_bwd_error_paths():
     assert _bwd(ws=MIS, wsz=need) == 1
     assert _bwd(flag=ctypes.c_void_p(0x100002), ws=FAKE, wsz=need) == 1  # misaligned flag
     assert _bwd(B=0, N=0, q=None, ws=FAKE, wsz=0) == 0
+
+
+def test_decode_tokens_error_paths():
+    L = _lib.lib()
+
+    def call(**kw):
+        a = dict(N=2, Lt=4, H=2, dk=128, dv=128, P=2, dtype=0, idx=None, pool=FAKE, steps=None)
+        a.update(kw)
+        return L.gdn2_decode_tokens(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["pool"], a["idx"], None,
+                                    FAKE, a["steps"], a["N"], a["Lt"], a["H"], a["dk"], a["dv"],
+                                    a["P"], a["dtype"], None)
+    assert call(dtype=5) == 1
+    assert call(dk=32) == 2
+    assert call(P=1) == 1                 # without indices the pool needs a slot per sequence
+    assert call(pool=None) == 1
+    assert call(pool=MIS) == 1
+    assert call(steps=MIS) == 1
+    assert call(idx=ctypes.c_void_p(0x100002)) == 1
+    assert call(N=0, pool=None) == 0
+    assert call(Lt=0, pool=None) == 0
