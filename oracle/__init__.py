@@ -6,5 +6,8 @@ CPU-baseline leg, never by the library. It shares no code with the HIP path.
 from .gdn2_oracle import (gdn2_backward, gdn2_decode_steps, gdn2_decode_tokens, gdn2_forward,
                           gdn2_step, gdn2_step_backward)
 
+from .gdn2_block import epilogue as block_epilogue
+from .gdn2_block import prologue as block_prologue
+
 __all__ = ["gdn2_step", "gdn2_forward", "gdn2_decode_steps", "gdn2_decode_tokens",
-           "gdn2_step_backward", "gdn2_backward"]
+           "gdn2_step_backward", "gdn2_backward", "block_prologue", "block_epilogue"]
