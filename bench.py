@@ -2,13 +2,13 @@
 
 A step is one gdn2_chunk_fwd call over the 1.3B-layer workload (B=8, H=16, T=2048,
 d_k = d_v = 128, bf16 inputs, fp32 state, zero initial state), inputs resident in HBM;
-with the path chunk_fwd's "auto" picks (two-phase: its two launches are timed together as
-one call).
+with the path chunk_fwd's "auto" picks (the fused kernel at this shape; where the two-phase
+path is picked, its two launches are timed together as one call).
 Prints ONE JSON line. Also reports (as extra fields) the recurrent decode step on the
 decode workload (256 sequences x 16 heads, fp32 128x128 states) and a CPU baseline: the
 float64 oracle timed on a bounded sample of the forward workload.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-block]
                     [--path auto|split|fused] [--workload layer1p3b|longctx|varlen]
 """
 from __future__ import annotations
@@ -103,6 +103,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-block", action="store_true",
+                    help="skip the block prologue / epilogue measurement")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--path", choices=("auto", "split", "fused"), default="auto",
                     help="chunk-forward path: two-phase (split), single fused kernel, or auto "
@@ -246,6 +248,46 @@ def main():
             "algorithmic_bytes": bb, "achieved_GBs": round(bb / (bms * 1e-3) / 1e9, 1),
             "hbm_frac": round(bb / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del bws
+
+    if not args.no_block and args.workload == "layer1p3b":
+        # prologue (projections -> q, k, v, g, b, w) and epilogue (gated RMSNorm) at this shape
+        gen = torch.Generator(device=dev).manual_seed(11)
+        shp = {"xq": dk, "xk": dk, "xv": dv, "xg": dk, "xb": dk, "xw": dv}
+        px = {n: torch.randn(B, T, H, d, generator=gen, device=dev).to(torch.bfloat16)
+              for n, d in shp.items()}
+        taps = [torch.randn(H * d, 4, generator=gen, device=dev) * 0.5 for d in (dk, dk, dv)]
+        dsc = torch.full((H * dk,), 0.1, device=dev)
+        og = [torch.randn(B, T, H, dv, generator=gen, device=dev).to(torch.bfloat16)
+              for _ in range(2)]
+        nw = torch.ones(dv, device=dev)
+
+        def timed(fn, reps=20):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(reps)]
+            for a, b2 in ev:
+                a.record()
+                fn()
+                b2.record()
+            torch.cuda.synchronize()
+            return float(np.mean([a.elapsed_time(b2) for a, b2 in ev])) * 1e3
+        pus = timed(lambda: G.block_prologue(*px.values(), *taps, dsc))
+        eus = timed(lambda: G.block_epilogue(og[0], og[1], nw))
+        rows = B * T * H
+        pbytes = rows * (4 * dk + 2 * dv) * 2 * 2  # each projection read once, each input written
+        ebytes = rows * dv * 2 * 3
+        out["block"] = {
+            "workload": "block prologue (conv/SiLU/L2 norm branches and gate activations) and "
+                        "epilogue (RMSNorm with SiLU gate) on the same tokens, bf16",
+            "prologue": {"us_per_call": round(pus, 2), "algorithmic_bytes": pbytes,
+                         "achieved_GBs": round(pbytes / (pus * 1e-6) / 1e9, 1),
+                         "hbm_frac": round(pbytes / (pus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+            "epilogue": {"us_per_call": round(eus, 2), "algorithmic_bytes": ebytes,
+                         "achieved_GBs": round(ebytes / (eus * 1e-6) / 1e9, 1),
+                         "hbm_frac": round(ebytes / (eus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}}
+        del px, og
 
     if not args.no_decode and args.workload == "layer1p3b":
         cd = CONFIGS["decode_bf16"]

@@ -5,11 +5,14 @@
 `chunk_fwd` runs the chunkwise-parallel forward over whole (optionally packed)
 sequences, two-phase (with a workspace) or fused; `chunk_bwd` its gradients;
 `decode_step` advances a pool of recurrent states by one token, `decode_tokens` by
-several (with slot indexing and committed prefixes, for serving). Both call libgdn2.so, built in-tree by
+several (with slot indexing and committed prefixes, for serving); `block_prologue` and
+`block_epilogue` are the block's branches around the mixer. Both call libgdn2.so, built in-tree by
 `python -m gated_delta_rule_36_amd.build`.
 """
-from ._lib import (Gdn2Error, Gdn2RangeError, chunk_bwd, chunk_fwd, decode_step,
-                   decode_tokens, lib, lib_path, uses_split, workspace_bytes)
+from ._lib import (Gdn2Error, Gdn2RangeError, block_epilogue, block_prologue, chunk_bwd,
+                   chunk_fwd, decode_step, decode_tokens, lib, lib_path, uses_split,
+                   workspace_bytes)
 
-__all__ = ["chunk_fwd", "chunk_bwd", "decode_step", "decode_tokens", "workspace_bytes",
-           "uses_split", "lib", "lib_path", "Gdn2Error", "Gdn2RangeError"]
+__all__ = ["chunk_fwd", "chunk_bwd", "decode_step", "decode_tokens", "block_prologue",
+           "block_epilogue", "workspace_bytes", "uses_split", "lib", "lib_path", "Gdn2Error",
+           "Gdn2RangeError"]

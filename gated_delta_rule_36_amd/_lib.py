@@ -59,6 +59,10 @@ def lib():
         L.gdn2_decode_step.restype = _I
         L.gdn2_decode_tokens.argtypes = [_P] * 11 + [_I] * 7 + [_P]
         L.gdn2_decode_tokens.restype = _I
+        L.gdn2_block_prologue.argtypes = [_P] * 10 + [ctypes.c_float] + [_P] * 7 + [_I] * 7 + [_P]
+        L.gdn2_block_prologue.restype = _I
+        L.gdn2_block_epilogue.argtypes = [_P] * 4 + [ctypes.c_long, _I, _I, _P]
+        L.gdn2_block_epilogue.restype = _I
         L.gdn2_status_string.argtypes = [_I]
         L.gdn2_status_string.restype = ctypes.c_char_p
         L.gdn2_version.argtypes = []
@@ -286,3 +290,44 @@ def decode_tokens(q, k, v, g, b, w, state_pool, state_indices=None, commit_len=N
     if st != 0:
         raise Gdn2Error("gdn2_decode_tokens", st)
     return o, steps
+
+
+def block_prologue(xq, xk, xv, xg, xb, xw, conv_q, conv_k, conv_v, decay_scale, b_max=1.0,
+                   cu_seqlens=None):
+    """Projections -> mixer inputs (q, k, v, g, b, w): conv/SiLU/L2-norm branches and gate
+    activations in one pass. xq, xk, xg, xb: [B, T, H, d_k]; xv, xw: [B, T, H, d_v];
+    conv_*: fp32 [H * d, 4]; decay_scale: fp32 [H * d_k]."""
+    B, T, H, dk = xq.shape
+    dv = xv.shape[-1]
+    dev, dt = xq.device, xq.dtype
+    code = _dtype_code(dt)
+    for name, t, d in (("xq", xq, dk), ("xk", xk, dk), ("xg", xg, dk), ("xb", xb, dk),
+                       ("xv", xv, dv), ("xw", xw, dv)):
+        _check(name, t, (B, T, H, d), dt, dev)
+    for name, t, shape in (("conv_q", conv_q, (H * dk, 4)), ("conv_k", conv_k, (H * dk, 4)),
+                           ("conv_v", conv_v, (H * dv, 4)), ("decay_scale", decay_scale, (H * dk,))):
+        _check(name, t, shape, torch.float32, dev)
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    outs = [torch.empty_like(x) for x in (xq, xk, xv, xg, xb, xw)]
+    st = lib().gdn2_block_prologue(*(_ptr(x) for x in (xq, xk, xv, xg, xb, xw)), _ptr(conv_q),
+                                   _ptr(conv_k), _ptr(conv_v), _ptr(decay_scale), float(b_max),
+                                   *(_ptr(x) for x in outs), _ptr(cu_seqlens), B, T, H, dk, dv,
+                                   N, code, _stream(dev))
+    if st != 0:
+        raise Gdn2Error("gdn2_block_prologue", st)
+    return tuple(outs)
+
+
+def block_epilogue(o, gate, weight):
+    """y = RMSNorm(o) * weight * SiLU(gate) over the last axis (d_v); weight fp32 [d_v]."""
+    dv = o.shape[-1]
+    _check("gate", gate, tuple(o.shape), o.dtype, o.device)
+    _check("weight", weight, (dv,), torch.float32, o.device)
+    if not o.is_contiguous():
+        raise ValueError("o must be contiguous")
+    y = torch.empty_like(o)
+    st = lib().gdn2_block_epilogue(_ptr(o), _ptr(gate), _ptr(weight), _ptr(y), o.numel() // dv,
+                                   dv, _dtype_code(o.dtype), _stream(o.device))
+    if st != 0:
+        raise Gdn2Error("gdn2_block_epilogue", st)
+    return y

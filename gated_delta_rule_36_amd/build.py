@@ -12,7 +12,8 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libgdn2.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["gdn2_api.cpp", "gdn2_chunk.hip", "gdn2_split.hip", "gdn2_bwd.hip", "gdn2_decode.hip"]
+SOURCES = ["gdn2_api.cpp", "gdn2_chunk.hip", "gdn2_split.hip", "gdn2_bwd.hip", "gdn2_decode.hip",
+           "gdn2_block.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU forms are kept out of generated code on purpose

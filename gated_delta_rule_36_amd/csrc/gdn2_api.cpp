@@ -8,6 +8,7 @@
 #include <climits>
 #include <cstdint>
 
+#include "gdn2_block_launch.h"
 #include "gdn2_launch.h"
 
 namespace {
@@ -227,6 +228,50 @@ int gdn2_decode_tokens(const void* q, const void* k, const void* v, const void* 
   a.step_states = step_states; a.N = N; a.L = L; a.H = H; a.d_k = d_k; a.d_v = d_v; a.P = P;
   a.dtype = dtype; a.stream = hip_stream;
   return status_of(gdn2::launch_decode_tokens(a));
+}
+
+int gdn2_block_prologue(const void* xq, const void* xk, const void* xv, const void* xg,
+                        const void* xb, const void* xw, const float* conv_q,
+                        const float* conv_k, const float* conv_v, const float* decay_scale,
+                        float b_max, void* q, void* k, void* v, void* log_alpha, void* b,
+                        void* w, const int32_t* cu_seqlens, int B, int T, int H, int d_k,
+                        int d_v, int N, int dtype, void* hip_stream) {
+  if (dtype != GDN2_BF16 && dtype != GDN2_F32) return GDN2_INVALID_ARGUMENT;
+  if (B < 0 || T < 0 || H <= 0 || N < 0 || d_k <= 0 || d_v <= 0) return GDN2_INVALID_ARGUMENT;
+  if (cu_seqlens == nullptr ? N != B : B != 1) return GDN2_INVALID_ARGUMENT;
+  if (!width_ok(d_k) || !width_ok(d_v)) return GDN2_UNSUPPORTED;
+  const long tokens = (long)B * T;
+  if (tokens == 0) return GDN2_OK;
+  const void* ptrs[16] = {xq, xk, xv, xg, xb, xw, conv_q, conv_k, conv_v, decay_scale,
+                          q, k, v, log_alpha, b, w};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return GDN2_INVALID_ARGUMENT;
+  if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0)
+    return GDN2_INVALID_ARGUMENT;
+  if (tokens * H > (long)INT_MAX * 8) return GDN2_INVALID_ARGUMENT;
+  gdn2::PrologueArgs a;
+  a.xq = xq; a.xk = xk; a.xv = xv; a.xg = xg; a.xb = xb; a.xw = xw;
+  a.wq = conv_q; a.wk = conv_k; a.wv = conv_v; a.scale = decay_scale; a.b_max = b_max;
+  a.q = q; a.k = k; a.v = v; a.g = log_alpha; a.b = b; a.w = w; a.cu_seqlens = cu_seqlens;
+  a.B = B; a.T = T; a.H = H; a.d_k = d_k; a.d_v = d_v; a.N = N; a.dtype = dtype;
+  a.stream = hip_stream;
+  return status_of(gdn2::launch_prologue(a));
+}
+
+int gdn2_block_epilogue(const void* o, const void* gate, const float* weight, void* y,
+                        long rows, int d_v, int dtype, void* hip_stream) {
+  if (dtype != GDN2_BF16 && dtype != GDN2_F32) return GDN2_INVALID_ARGUMENT;
+  if (rows < 0 || d_v <= 0) return GDN2_INVALID_ARGUMENT;
+  if (!width_ok(d_v)) return GDN2_UNSUPPORTED;
+  if (rows == 0) return GDN2_OK;
+  const void* ptrs[4] = {o, gate, weight, y};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return GDN2_INVALID_ARGUMENT;
+  if (rows > (long)INT_MAX * 16) return GDN2_INVALID_ARGUMENT;
+  gdn2::EpilogueArgs a;
+  a.o = o; a.gate = gate; a.weight = weight; a.y = y; a.rows = rows; a.d_v = d_v;
+  a.dtype = dtype; a.stream = hip_stream;
+  return status_of(gdn2::launch_epilogue(a));
 }
 
 const char* gdn2_status_string(int status) {

@@ -27,6 +27,7 @@ import numpy as np
 
 __all__ = [
     "CONFIGS",
+    "make_block_inputs",
     "round_to_bf16",
     "make_inputs",
     "make_config_inputs",
@@ -155,4 +156,28 @@ def make_decode_inputs(N, H, dk, dv, steps, dtype="bf16", seed=0, s0_std=None):
     if s0_std is not None:
         out["s0"] = (s0_std * rng.standard_normal((N, H, dk, dv))).astype(np.float32)
     out["dtype"] = dtype
+    return out
+
+
+def make_block_inputs(B, T, H, dk, dv, dtype="bf16", seed=0, lengths=None):
+    """Inputs of the block prologue and epilogue around the mixer.
+
+    Projections xq, xk, xg, xb: [B, T, H, d_k] and xv, xw, o, gate: [B, T, H, d_v], all
+    N(0, 1) rounded to the run dtype; conv taps N(0, 1/4) in fp32, [H * d, 4]; decay scale
+    0.1 * U(0.5, 1.5) per key channel (fp32); norm weight 1 + 0.1 * N(0, 1) (fp32, [d_v]).
+    With `lengths`, B must be 1 and T = sum(lengths); cu_seqlens is returned (else None).
+    """
+    rng = np.random.default_rng(seed)
+    if lengths is not None:
+        assert B == 1 and T == int(np.sum(lengths))
+    out = {}
+    for n, d in (("xq", dk), ("xk", dk), ("xv", dv), ("xg", dk), ("xb", dk), ("xw", dv),
+                 ("o", dv), ("gate", dv)):
+        out[n] = _to_dtype(rng.normal(size=(B, T, H, d)), dtype)
+    for n, d in (("conv_q", dk), ("conv_k", dk), ("conv_v", dv)):
+        out[n] = (rng.normal(size=(H * d, 4)) * 0.5).astype(np.float32)
+    out["decay_scale"] = (0.1 * rng.uniform(0.5, 1.5, size=H * dk)).astype(np.float32)
+    out["norm_weight"] = (1.0 + 0.1 * rng.normal(size=dv)).astype(np.float32)
+    out["cu_seqlens"] = (None if lengths is None else
+                         np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32))
     return out

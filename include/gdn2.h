@@ -198,6 +198,45 @@ int gdn2_decode_tokens(const void* q, const void* k, const void* v, const void* 
                        float* step_states, int N, int L, int H, int d_k, int d_v, int P,
                        int dtype, void* hip_stream);
 
+/*
+ * Block prologue: the branches between the block's projections and the mixer (the reading
+ * note's §3 block paragraph: q, k = linear -> conv -> SiLU -> L2 norm; v = linear -> conv ->
+ * SiLU; per-channel decay, erase and write gates from projections of their own). One pass
+ * over the six projected tensors:
+ *     q = l2norm(silu(conv(xq))), k = l2norm(silu(conv(xk))), v = silu(conv(xv)),
+ *     log_alpha = -decay_scale * softplus(xg), b = b_max * sigmoid(xb), w = sigmoid(xw)
+ * with conv the causal depthwise convolution of width 4 over each sequence's tokens
+ * (y[t, c] = sum_j conv[c, j] * x[t - 3 + j, c], zero history at every sequence start) and
+ * l2norm over d_k with eps 1e-6. (Conv width, eps and the gate activations are this
+ * library's readings of what the page leaves open.)
+ *
+ *   xq, xk, xg, xb     : [B, T, H, d_k]   (dtype) projections
+ *   xv, xw             : [B, T, H, d_v]   (dtype)
+ *   conv_q, conv_k     : [H * d_k, 4] fp32 taps;  conv_v : [H * d_v, 4] fp32
+ *   decay_scale        : [H * d_k] fp32 (positive)
+ *   b_max              : 1 nominally, 2 for the widened erase-gate range
+ *   q, k, log_alpha, b : [B, T, H, d_k] (dtype), written;  v, w : [B, T, H, d_v] (dtype)
+ *   cu_seqlens         : as gdn2_chunk_fwd (B = 1 when given; N = B otherwise)
+ * Returns GDN2_OK or an error status.
+ */
+int gdn2_block_prologue(const void* xq, const void* xk, const void* xv, const void* xg,
+                        const void* xb, const void* xw, const float* conv_q,
+                        const float* conv_k, const float* conv_v, const float* decay_scale,
+                        float b_max, void* q, void* k, void* v, void* log_alpha, void* b,
+                        void* w, const int32_t* cu_seqlens, int B, int T, int H, int d_k,
+                        int d_v, int N, int dtype, void* hip_stream);
+
+/*
+ * Block epilogue: the mixer output scaled by an RMSNorm with a SiLU gate (the reading note's
+ * §3 block paragraph): y = o / sqrt(mean_c(o^2) + 1e-6) * weight * silu(gate), the mean over
+ * d_v per (token, head).
+ *
+ *   o, gate, y : [rows, d_v] (dtype), rows = tokens x heads;  weight : [d_v] fp32
+ * Returns GDN2_OK or an error status.
+ */
+int gdn2_block_epilogue(const void* o, const void* gate, const float* weight, void* y,
+                        long rows, int d_v, int dtype, void* hip_stream);
+
 /* Human-readable text for a status code (static storage; never NULL). */
 const char* gdn2_status_string(int status);
 
