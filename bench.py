@@ -246,7 +246,8 @@ def main():
             "kernels": "factor kernel (backward layout) + forward chain + reverse chain + "
                        "local gradients", "calls_timed": KB,
             "algorithmic_bytes": bb, "achieved_GBs": round(bb / (bms * 1e-3) / 1e9, 1),
-            "hbm_frac": round(bb / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            "hbm_frac": round(bb / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("chunk_bwd_layer1p3b_bf16")}
         del bws
 
     if not args.no_block and args.workload == "layer1p3b":
@@ -282,9 +283,11 @@ def main():
             "workload": "block prologue (conv/SiLU/L2 norm branches and gate activations) and "
                         "epilogue (RMSNorm with SiLU gate) on the same tokens, bf16",
             "prologue": {"us_per_call": round(pus, 2), "algorithmic_bytes": pbytes,
+                         "traffic": measured_traffic("block_prologue_layer1p3b_bf16"),
                          "achieved_GBs": round(pbytes / (pus * 1e-6) / 1e9, 1),
                          "hbm_frac": round(pbytes / (pus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
             "epilogue": {"us_per_call": round(eus, 2), "algorithmic_bytes": ebytes,
+                         "traffic": measured_traffic("block_epilogue_layer1p3b_bf16"),
                          "achieved_GBs": round(ebytes / (eus * 1e-6) / 1e9, 1),
                          "hbm_frac": round(ebytes / (eus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}}
         del px, og
@@ -338,6 +341,7 @@ def main():
         out["decode"]["tokens_per_call_L4"] = {
             "us_per_call": round(vus, 2), "tokens_per_s": round(N * Lv / (vus * 1e-6), 1),
             "bytes_per_call": vbytes, "achieved_GBs": round(vbytes / (vus * 1e-6) / 1e9, 1),
+            "traffic": measured_traffic("decode_tokens_n256_l4_h16_bf16"),
             "hbm_frac": round(vbytes / (vus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "vs_four_single_steps": round(4 * res["one_pool"]["us_per_step"] / vus, 3)}
 

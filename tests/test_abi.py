@@ -167,3 +167,34 @@ def test_decode_tokens_error_paths():
     assert call(idx=ctypes.c_void_p(0x100002)) == 1
     assert call(N=0, pool=None) == 0
     assert call(Lt=0, pool=None) == 0
+
+
+def test_block_prologue_epilogue_error_paths():
+    L = _lib.lib()
+
+    def pro(**kw):
+        a = dict(x=FAKE, out=FAKE, cu=None, B=2, T=8, H=2, dk=128, dv=64, N=2, dtype=0, taps=FAKE)
+        a.update(kw)
+        return L.gdn2_block_prologue(a["x"], FAKE, FAKE, FAKE, FAKE, FAKE, a["taps"], FAKE, FAKE,
+                                     FAKE, 1.0, a["out"], FAKE, FAKE, FAKE, FAKE, FAKE, a["cu"],
+                                     a["B"], a["T"], a["H"], a["dk"], a["dv"], a["N"],
+                                     a["dtype"], None)
+    assert pro(dtype=3) == 1
+    assert pro(N=3) == 1                  # N must equal B without cu_seqlens
+    assert pro(cu=FAKE, B=2) == 1         # packed batches have B = 1
+    assert pro(dk=96) == 2
+    assert pro(x=MIS) == 1
+    assert pro(taps=None) == 1
+    assert pro(H=0) == 1
+    assert pro(T=0, x=None) == 0          # no tokens: nothing to do, nothing touched
+
+    def epi(**kw):
+        a = dict(o=FAKE, y=FAKE, rows=16, dv=128, dtype=0)
+        a.update(kw)
+        return L.gdn2_block_epilogue(a["o"], FAKE, FAKE, a["y"], a["rows"], a["dv"], a["dtype"],
+                                     None)
+    assert epi(dtype=2) == 1
+    assert epi(dv=32) == 2
+    assert epi(rows=-1) == 1
+    assert epi(y=MIS) == 1
+    assert epi(rows=0, o=None) == 0
