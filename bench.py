@@ -119,6 +119,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-scalar-gates", action="store_true",
+                    help="skip the scalar-gate forward measurement")
     ap.add_argument("--no-block", action="store_true",
                     help="skip the block prologue / epilogue measurement")
     ap.add_argument("--no-backward", action="store_true")
@@ -265,6 +267,34 @@ def main():
             "hbm_frac": round(bb / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic("chunk_bwd_layer1p3b_bf16")}
         del bws
+
+    if args.workload == "layer1p3b" and not args.no_scalar_gates:
+        # the scalar-gate configuration (one b and one w value per token and head)
+        gen = torch.Generator(device=dev).manual_seed(5)
+        sb = torch.sigmoid(torch.randn(B, T, H, generator=gen, device=dev)).to(t["b"].dtype)
+        sw = torch.sigmoid(torch.randn(B, T, H, generator=gen, device=dev)).to(t["w"].dtype)
+        sg = dict(t, b=sb, w=sw)
+
+        def sstep():
+            return G.chunk_fwd(*(sg[n] for n in NAMES), initial_state=s0, cu_seqlens=cu,
+                               path="fused")
+        for _ in range(3):
+            sstep()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(20)]
+        for a, b2 in evs:
+            a.record()
+            sstep()
+            b2.record()
+        torch.cuda.synchronize()
+        sms = float(np.mean([a.elapsed_time(b2) for a, b2 in evs]))
+        sbytes = B * T * H * ((3 * dk + dv + dv) * 2 + 2 * 2) + N * H * dk * dv * 4
+        out["scalar_gates"] = {
+            "workload": "the same forward with scalar b and w ([B, T, H]), fused path",
+            "ms_per_call": round(sms, 4), "tokens_per_s": round(B * T / (sms * 1e-3), 1),
+            "algorithmic_bytes": sbytes,
+            "hbm_frac": round(sbytes / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
     if not args.no_block and args.workload == "layer1p3b":
         # prologue (projections -> q, k, v, g, b, w) and epilogue (gated RMSNorm) at this shape

@@ -59,6 +59,12 @@ def lib():
         L.gdn2_decode_step.restype = _I
         L.gdn2_decode_tokens.argtypes = [_P] * 11 + [_I] * 7 + [_P]
         L.gdn2_decode_tokens.restype = _I
+        L.gdn2_chunk_fwd_ex.argtypes = [_P] * 10 + [_I] * 8 + [_P, _Z, _P]
+        L.gdn2_chunk_fwd_ex.restype = _I
+        L.gdn2_decode_step_ex.argtypes = [_P] * 8 + [_I] * 6 + [_P]
+        L.gdn2_decode_step_ex.restype = _I
+        L.gdn2_decode_tokens_ex.argtypes = [_P] * 11 + [_I] * 8 + [_P]
+        L.gdn2_decode_tokens_ex.restype = _I
         L.gdn2_block_prologue.argtypes = [_P] * 10 + [ctypes.c_float] + [_P] * 7 + [_I] * 7 + [_P]
         L.gdn2_block_prologue.restype = _I
         L.gdn2_block_epilogue.argtypes = [_P] * 4 + [ctypes.c_long, _I, _I, _P]
@@ -98,6 +104,23 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+GATE_B_SCALAR = 1  # gate layouts (the C header's GDN2_GATE_* bits)
+GATE_W_SCALAR = 2
+
+
+def _gate_layout(b, w, lead, dk, dv, dt, dev):
+    """Gate layout bits from the shapes of b and w: lead + (d,) per channel, lead alone for
+    one value per token and head (broadcast over the channels by the kernels)."""
+    lay = 0
+    for name, t, d, bit in (("b", b, dk, GATE_B_SCALAR), ("w", w, dv, GATE_W_SCALAR)):
+        if tuple(t.shape) == tuple(lead):
+            _check(name, t, tuple(lead), dt, dev)
+            lay |= bit
+        else:
+            _check(name, t, tuple(lead) + (d,), dt, dev)
+    return lay
+
+
 def workspace_bytes(B, T, H, dk, dv, N, dtype=torch.bfloat16):
     """Device workspace the two-phase chunk forward needs (0: that path is not built)."""
     return int(lib().gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, _dtype_code(dtype)))
@@ -114,7 +137,8 @@ def chunk_fwd(q, k, v, g, b, w, initial_state=None, cu_seqlens=None,
     """Gated Delta Rule-2 chunkwise forward.
 
     q, k, g, b: [B, T, H, d_k]; v, w: [B, T, H, d_v] (bf16 or fp32, same dtype, on a HIP
-    device); g = log(alpha) <= 0. initial_state: [N, H, d_k, d_v] fp32 or None.
+    device); g = log(alpha) <= 0. b or w may instead be [B, T, H]: one gate value per token
+    and head, shared by its channels. initial_state: [N, H, d_k, d_v] fp32 or None.
     cu_seqlens: int32 [N+1] on the device (packed batch, B == 1) or None (N = B).
     path: "split" (two-phase: parallel chunk factors into a workspace, then the per-sequence
     recurrence), "fused" (one kernel per sequence, no workspace) or "auto" (split for bf16
@@ -131,9 +155,9 @@ def chunk_fwd(q, k, v, g, b, w, initial_state=None, cu_seqlens=None,
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
     code = _dtype_code(dt)
-    for name, t, d in (("q", q, dk), ("k", k, dk), ("g", g, dk), ("b", b, dk),
-                       ("v", v, dv), ("w", w, dv)):
+    for name, t, d in (("q", q, dk), ("k", k, dk), ("g", g, dk), ("v", v, dv)):
         _check(name, t, (B, T, H, d), dt, dev)
+    layout = _gate_layout(b, w, (B, T, H), dk, dv, dt, dev)
     if cu_seqlens is not None:
         if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != dev or cu_seqlens.dim() != 1:
             raise ValueError("cu_seqlens must be a 1-D int32 tensor on the inputs' device")
@@ -144,6 +168,8 @@ def chunk_fwd(q, k, v, g, b, w, initial_state=None, cu_seqlens=None,
         N = B
     if initial_state is not None:
         _check("initial_state", initial_state, (N, H, dk, dv), torch.float32, dev)
+    if value_slice and layout:
+        raise ValueError("value_slice takes per-channel gates")
     L = lib()
     need = int(L.gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, code))
     if path == "split" and need == 0:
@@ -170,8 +196,8 @@ def chunk_fwd(q, k, v, g, b, w, initial_state=None, cu_seqlens=None,
         fn = "gdn2_chunk_fwd_sliced"
     else:
         wsz = workspace.numel() if workspace is not None else 0
-        st = L.gdn2_chunk_fwd(*args, _ptr(workspace), wsz, _stream(dev))
-        fn = "gdn2_chunk_fwd"
+        st = L.gdn2_chunk_fwd_ex(*args, layout, _ptr(workspace), wsz, _stream(dev))
+        fn = "gdn2_chunk_fwd_ex"
     if st != 0:
         raise Gdn2Error(fn, st)
     return o, sN
@@ -196,6 +222,9 @@ def chunk_bwd(q, k, v, g, b, w, do, initial_state=None, d_final_state=None, cu_s
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
     code = _dtype_code(dt)
+    if b.dim() == 3 or w.dim() == 3:
+        raise ValueError("chunk_bwd takes per-channel gates [B, T, H, d]; scalar gates are "
+                         "supported by the forward and decode calls")
     for name, t, d in (("q", q, dk), ("k", k, dk), ("g", g, dk), ("b", b, dk),
                        ("v", v, dv), ("w", w, dv), ("do", do, dv)):
         _check(name, t, (B, T, H, d), dt, dev)
@@ -235,7 +264,8 @@ def chunk_bwd(q, k, v, g, b, w, do, initial_state=None, d_final_state=None, cu_s
 def decode_step(q, k, v, g, b, w, state):
     """One recurrent decode step; `state` [N, H, d_k, d_v] fp32 is updated in place.
 
-    q, k, g, b: [N, H, d_k]; v, w: [N, H, d_v]. Returns o [N, H, d_v] (input dtype).
+    q, k, g, b: [N, H, d_k]; v, w: [N, H, d_v] (b or w may be [N, H]: one value per head).
+    Returns o [N, H, d_v] (input dtype).
     """
     if q.dim() != 3:
         raise ValueError("q must be [N, H, d_k]")
@@ -243,15 +273,16 @@ def decode_step(q, k, v, g, b, w, state):
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
     code = _dtype_code(dt)
-    for name, t, d in (("q", q, dk), ("k", k, dk), ("g", g, dk), ("b", b, dk),
-                       ("v", v, dv), ("w", w, dv)):
+    for name, t, d in (("q", q, dk), ("k", k, dk), ("g", g, dk), ("v", v, dv)):
         _check(name, t, (N, H, d), dt, dev)
+    layout = _gate_layout(b, w, (N, H), dk, dv, dt, dev)
     _check("state", state, (N, H, dk, dv), torch.float32, dev)
     o = torch.empty((N, H, dv), dtype=dt, device=dev)
-    st = lib().gdn2_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w),
-                                _ptr(state), _ptr(o), N, H, dk, dv, code, _stream(dev))
+    st = lib().gdn2_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w),
+                                   _ptr(state), _ptr(o), N, H, dk, dv, code, layout,
+                                   _stream(dev))
     if st != 0:
-        raise Gdn2Error("gdn2_decode_step", st)
+        raise Gdn2Error("gdn2_decode_step_ex", st)
     return o
 
 
@@ -260,7 +291,8 @@ def decode_tokens(q, k, v, g, b, w, state_pool, state_indices=None, commit_len=N
     """L consecutive tokens per sequence against a pool of fp32 states (decode of several
     tokens, or verification of draft tokens).
 
-    q, k, g, b: [N, L, H, d_k]; v, w: [N, L, H, d_v]; state_pool: [P, H, d_k, d_v] fp32,
+    q, k, g, b: [N, L, H, d_k]; v, w: [N, L, H, d_v] (b or w may be [N, L, H]: one value
+    per token and head); state_pool: [P, H, d_k, d_v] fp32,
     updated in place for the committed prefix; state_indices: int32 [N] (slot per sequence,
     negative to skip) or None (slot n); commit_len: int32 [N] or None (all L tokens).
     Returns (o [N, L, H, d_v], step_states [N, L, H, d_k, d_v] fp32 or None).
@@ -271,9 +303,9 @@ def decode_tokens(q, k, v, g, b, w, state_pool, state_indices=None, commit_len=N
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
     code = _dtype_code(dt)
-    for name, t, d in (("q", q, dk), ("k", k, dk), ("g", g, dk), ("b", b, dk),
-                       ("v", v, dv), ("w", w, dv)):
+    for name, t, d in (("q", q, dk), ("k", k, dk), ("g", g, dk), ("v", v, dv)):
         _check(name, t, (N, L, H, d), dt, dev)
+    layout = _gate_layout(b, w, (N, L, H), dk, dv, dt, dev)
     if state_pool.dim() != 4:
         raise ValueError("state_pool must be [P, H, d_k, d_v]")
     P = state_pool.shape[0]
@@ -284,11 +316,12 @@ def decode_tokens(q, k, v, g, b, w, state_pool, state_indices=None, commit_len=N
     o = torch.empty((N, L, H, dv), dtype=dt, device=dev)
     steps = (torch.empty((N, L, H, dk, dv), dtype=torch.float32, device=dev)
              if return_step_states else None)
-    st = lib().gdn2_decode_tokens(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w),
-                                  _ptr(state_pool), _ptr(state_indices), _ptr(commit_len),
-                                  _ptr(o), _ptr(steps), N, L, H, dk, dv, P, code, _stream(dev))
+    st = lib().gdn2_decode_tokens_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w),
+                                     _ptr(state_pool), _ptr(state_indices), _ptr(commit_len),
+                                     _ptr(o), _ptr(steps), N, L, H, dk, dv, P, code, layout,
+                                     _stream(dev))
     if st != 0:
-        raise Gdn2Error("gdn2_decode_tokens", st)
+        raise Gdn2Error("gdn2_decode_tokens_ex", st)
     return o, steps
 
 

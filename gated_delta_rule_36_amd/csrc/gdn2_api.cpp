@@ -19,6 +19,10 @@ constexpr int kTargetWorkgroups = 256;  // one per compute unit of an MI355X
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool width_ok(int d) { return d == 64 || d == 128; }
 
+constexpr int kGateMask = GDN2_GATE_B_SCALAR | GDN2_GATE_W_SCALAR;
+static_assert(GDN2_GATE_B_SCALAR == gdn2::kGateBScalar && GDN2_GATE_W_SCALAR == gdn2::kGateWScalar,
+              "gate layout bits");
+
 // Widest value slice that still yields about one workgroup per compute unit; wider
 // slices recompute less key-side work per token, narrower ones expose more chains.
 int pick_nv(int dtype, int d_k, int d_v, long chains) {
@@ -52,8 +56,9 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* log_
                    const void* b, const void* w, const float* initial_state, void* o,
                    float* final_state, const int32_t* cu_seqlens, int B, int T, int H, int d_k,
                    int d_v, int N, int dtype, void* workspace, size_t workspace_bytes,
-                   void* hip_stream, int nv) {
+                   void* hip_stream, int nv, int gate_layout) {
   if (dtype != GDN2_BF16 && dtype != GDN2_F32) return GDN2_INVALID_ARGUMENT;
+  if ((gate_layout & ~kGateMask) != 0) return GDN2_INVALID_ARGUMENT;
   if (B < 0 || T < 0 || H <= 0 || N < 0 || d_k <= 0 || d_v <= 0) return GDN2_INVALID_ARGUMENT;
   if (cu_seqlens == nullptr) {
     if (N != B) return GDN2_INVALID_ARGUMENT;
@@ -81,7 +86,7 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* log_
   a.q = q; a.k = k; a.v = v; a.g = log_alpha; a.b = b; a.w = w;
   a.s0 = initial_state; a.o = o; a.sN = final_state; a.cu_seqlens = cu_seqlens;
   a.B = B; a.T = T; a.H = H; a.d_k = d_k; a.d_v = d_v; a.N = N;
-  a.dtype = dtype; a.stream = hip_stream;
+  a.dtype = dtype; a.stream = hip_stream; a.gate_flags = gate_layout;
   a.workspace = split ? workspace : nullptr;
   a.workspace_bytes = split ? workspace_bytes : 0;
   if (split) {
@@ -119,7 +124,17 @@ int gdn2_chunk_fwd(const void* q, const void* k, const void* v, const void* log_
                    int d_k, int d_v, int N, int dtype, void* workspace,
                    size_t workspace_bytes, void* hip_stream) {
   return chunk_fwd_impl(q, k, v, log_alpha, b, w, initial_state, o, final_state, cu_seqlens,
-                        B, T, H, d_k, d_v, N, dtype, workspace, workspace_bytes, hip_stream, 0);
+                        B, T, H, d_k, d_v, N, dtype, workspace, workspace_bytes, hip_stream, 0, 0);
+}
+
+int gdn2_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* log_alpha,
+                      const void* b, const void* w, const float* initial_state, void* o,
+                      float* final_state, const int32_t* cu_seqlens, int B, int T, int H,
+                      int d_k, int d_v, int N, int dtype, int gate_layout, void* workspace,
+                      size_t workspace_bytes, void* hip_stream) {
+  return chunk_fwd_impl(q, k, v, log_alpha, b, w, initial_state, o, final_state, cu_seqlens,
+                        B, T, H, d_k, d_v, N, dtype, workspace, workspace_bytes, hip_stream, 0,
+                        gate_layout);
 }
 
 int gdn2_chunk_fwd_sliced(const void* q, const void* k, const void* v, const void* log_alpha,
@@ -129,7 +144,7 @@ int gdn2_chunk_fwd_sliced(const void* q, const void* k, const void* v, const voi
                           void* hip_stream) {
   if (value_slice < 0) return GDN2_INVALID_ARGUMENT;
   return chunk_fwd_impl(q, k, v, log_alpha, b, w, initial_state, o, final_state, cu_seqlens,
-                        B, T, H, d_k, d_v, N, dtype, nullptr, 0, hip_stream, value_slice);
+                        B, T, H, d_k, d_v, N, dtype, nullptr, 0, hip_stream, value_slice, 0);
 }
 
 size_t gdn2_chunk_bwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int N,
@@ -188,7 +203,15 @@ int gdn2_chunk_bwd(const void* q, const void* k, const void* v, const void* log_
 int gdn2_decode_step(const void* q, const void* k, const void* v, const void* log_alpha,
                      const void* b, const void* w, float* state, void* o, int N, int H,
                      int d_k, int d_v, int dtype, void* hip_stream) {
+  return gdn2_decode_step_ex(q, k, v, log_alpha, b, w, state, o, N, H, d_k, d_v, dtype, 0,
+                             hip_stream);
+}
+
+int gdn2_decode_step_ex(const void* q, const void* k, const void* v, const void* log_alpha,
+                        const void* b, const void* w, float* state, void* o, int N, int H,
+                        int d_k, int d_v, int dtype, int gate_layout, void* hip_stream) {
   if (dtype != GDN2_BF16 && dtype != GDN2_F32) return GDN2_INVALID_ARGUMENT;
+  if ((gate_layout & ~kGateMask) != 0) return GDN2_INVALID_ARGUMENT;
   if (N < 0 || H <= 0 || d_k <= 0 || d_v <= 0) return GDN2_INVALID_ARGUMENT;
   if (!width_ok(d_k) || !width_ok(d_v)) return GDN2_UNSUPPORTED;
   if (N == 0) return GDN2_OK;
@@ -200,7 +223,7 @@ int gdn2_decode_step(const void* q, const void* k, const void* v, const void* lo
   gdn2::DecodeArgs a;
   a.q = q; a.k = k; a.v = v; a.g = log_alpha; a.b = b; a.w = w;
   a.state = state; a.o = o; a.N = N; a.H = H; a.d_k = d_k; a.d_v = d_v;
-  a.dtype = dtype; a.stream = hip_stream;
+  a.dtype = dtype; a.stream = hip_stream; a.gate_flags = gate_layout;
   return status_of(gdn2::launch_decode_step(a));
 }
 
@@ -209,7 +232,17 @@ int gdn2_decode_tokens(const void* q, const void* k, const void* v, const void* 
                        const int32_t* state_indices, const int32_t* commit_len, void* o,
                        float* step_states, int N, int L, int H, int d_k, int d_v, int P,
                        int dtype, void* hip_stream) {
+  return gdn2_decode_tokens_ex(q, k, v, log_alpha, b, w, state_pool, state_indices, commit_len,
+                               o, step_states, N, L, H, d_k, d_v, P, dtype, 0, hip_stream);
+}
+
+int gdn2_decode_tokens_ex(const void* q, const void* k, const void* v, const void* log_alpha,
+                          const void* b, const void* w, float* state_pool,
+                          const int32_t* state_indices, const int32_t* commit_len, void* o,
+                          float* step_states, int N, int L, int H, int d_k, int d_v, int P,
+                          int dtype, int gate_layout, void* hip_stream) {
   if (dtype != GDN2_BF16 && dtype != GDN2_F32) return GDN2_INVALID_ARGUMENT;
+  if ((gate_layout & ~kGateMask) != 0) return GDN2_INVALID_ARGUMENT;
   if (N < 0 || L < 0 || H <= 0 || P < 0 || d_k <= 0 || d_v <= 0) return GDN2_INVALID_ARGUMENT;
   if (!width_ok(d_k) || !width_ok(d_v)) return GDN2_UNSUPPORTED;
   if (N == 0 || L == 0) return GDN2_OK;
@@ -226,7 +259,7 @@ int gdn2_decode_tokens(const void* q, const void* k, const void* v, const void* 
   a.q = q; a.k = k; a.v = v; a.g = log_alpha; a.b = b; a.w = w;
   a.pool = state_pool; a.indices = state_indices; a.commit = commit_len; a.o = o;
   a.step_states = step_states; a.N = N; a.L = L; a.H = H; a.d_k = d_k; a.d_v = d_v; a.P = P;
-  a.dtype = dtype; a.stream = hip_stream;
+  a.dtype = dtype; a.stream = hip_stream; a.gate_flags = gate_layout;
   return status_of(gdn2::launch_decode_tokens(a));
 }
 

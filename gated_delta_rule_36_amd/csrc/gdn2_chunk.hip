@@ -114,7 +114,7 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
                   const T* __restrict__ g, const T* __restrict__ bg, const T* __restrict__ wg,
                   const float* s0, T* __restrict__ o, float* sN,
                   const int* __restrict__ cu_seqlens, int T_len, int H, int DV, int nslices,
-                  int nunits) {
+                  int nunits, int gflags) {
   using Sh = ChunkShape<T, DK, NV>;
   using M = Mma<T>;
   constexpr int C = Sh::C, NW = Sh::NW, NT = Sh::NT, KS = Sh::KS, KPL = Sh::KPL;
@@ -192,6 +192,10 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
   const T* bb = bg + row0 * kstride + (long)h * DK;
   const T* vb = v + row0 * vstride + (long)h * DV + col0;
   const T* wb = wg + row0 * vstride + (long)h * DV + col0;
+  // scalar gates ([rows, H]: one value per token and head, broadcast over the channels)
+  const bool b_scalar = (gflags & kGateBScalar) != 0, w_scalar = (gflags & kGateWScalar) != 0;
+  const T* bsb = bg + row0 * H + h;
+  const T* wsb = wg + row0 * H + h;
   T* ob = o + row0 * vstride + (long)h * DV + col0;
 
   // ---- prep thread mapping
@@ -221,7 +225,7 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
         rq[j].load(qb + off);
         rk[j].load(kb + off);
         rg[j].load(gb + off);
-        rb[j].load(bb + off);
+        if (b_scalar) rb[j].bcast(bsb + (long)(c0 + r) * H); else rb[j].load(bb + off);
       } else {
         rq[j].zero(); rk[j].zero(); rg[j].zero(); rb[j].zero();
       }
@@ -232,7 +236,7 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
       if (r < nvalid) {
         const long off = (long)(c0 + r) * vstride + vcg * 8;
         rv[j].load(vb + off);
-        rw[j].load(wb + off);
+        if (w_scalar) rw[j].bcast(wsb + (long)(c0 + r) * H); else rw[j].load(wb + off);
       } else {
         rv[j].zero(); rw[j].zero();
       }
@@ -625,7 +629,7 @@ static hipError_t launch_chunk(const ChunkArgs& a) {
                      dim3(ChunkShape<T, DK, NV>::NT), 0,
                      (hipStream_t)a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
                      (const T*)a.g, (const T*)a.b, (const T*)a.w, a.s0, (T*)a.o, a.sN,
-                     a.cu_seqlens, a.T, a.H, a.d_v, nslices, a.N * a.H);
+                     a.cu_seqlens, a.T, a.H, a.d_v, nslices, a.N * a.H, a.gate_flags);
   return hipGetLastError();
 }
 

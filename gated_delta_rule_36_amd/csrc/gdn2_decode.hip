@@ -20,7 +20,7 @@ template <typename T, int DK, int DV>
 __global__ void __launch_bounds__(256)
 gdn2_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                    const T* __restrict__ g, const T* __restrict__ bg, const T* __restrict__ wg,
-                   float* __restrict__ state, T* __restrict__ o) {
+                   float* __restrict__ state, T* __restrict__ o, int gflags) {
   constexpr int NT = 256;
   constexpr int CG = DV / 4;        // float4 column groups per row
   constexpr int RG = NT / CG;       // row groups
@@ -43,11 +43,12 @@ gdn2_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   for (int c = tid; c < DK; c += NT) {
     const float kk = to_f(k[unit * DK + c]);
     s_alpha[c] = __expf(to_f(g[unit * DK + c]));
-    s_e[c] = to_f(bg[unit * DK + c]) * kk;
+    s_e[c] = to_f(bg[(gflags & kGateBScalar) ? unit : unit * DK + c]) * kk;
     s_q[c] = to_f(q[unit * DK + c]);
     s_k[c] = kk;
   }
-  for (int c = tid; c < DV; c += NT) s_z[c] = to_f(wg[unit * DV + c]) * to_f(v[unit * DV + c]);
+  for (int c = tid; c < DV; c += NT)
+    s_z[c] = to_f(wg[(gflags & kGateWScalar) ? unit : unit * DV + c]) * to_f(v[unit * DV + c]);
   __syncthreads();
 
   if (tid < 64) {  // q . k by wave 0
@@ -105,7 +106,7 @@ gdn2_decode_tokens_kernel(const T* __restrict__ q, const T* __restrict__ k,
                           const T* __restrict__ bg, const T* __restrict__ wg,
                           float* __restrict__ pool, const int* __restrict__ indices,
                           const int* __restrict__ commit, T* __restrict__ o,
-                          float* __restrict__ step_states, int L, int H, int P) {
+                          float* __restrict__ step_states, int L, int H, int P, int gflags) {
   constexpr int NT = 256;
   constexpr int CG = DV / 4;
   constexpr int RG = NT / CG;
@@ -134,11 +135,12 @@ gdn2_decode_tokens_kernel(const T* __restrict__ q, const T* __restrict__ k,
     for (int c = tid; c < DK; c += NT) {
       const float kk = to_f(k[tk * DK + c]);
       s_alpha[par][c] = __expf(to_f(g[tk * DK + c]));
-      s_e[par][c] = to_f(bg[tk * DK + c]) * kk;
+      s_e[par][c] = to_f(bg[(gflags & kGateBScalar) ? tk : tk * DK + c]) * kk;
       s_q[par][c] = to_f(q[tk * DK + c]);
       s_k[par][c] = kk;
     }
-    for (int c = tid; c < DV; c += NT) s_z[par][c] = to_f(wg[tk * DV + c]) * to_f(v[tk * DV + c]);
+    for (int c = tid; c < DV; c += NT)
+      s_z[par][c] = to_f(wg[(gflags & kGateWScalar) ? tk : tk * DV + c]) * to_f(v[tk * DV + c]);
     __syncthreads();
     if (tid < 64) {
       float p = 0.f;
@@ -189,7 +191,7 @@ template <typename T, int DK, int DV>
 static hipError_t launch_dec(const DecodeArgs& a) {
   hipLaunchKernelGGL((gdn2_decode_kernel<T, DK, DV>), dim3((unsigned)((long)a.N * a.H)), dim3(256),
                      0, (hipStream_t)a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
-                     (const T*)a.g, (const T*)a.b, (const T*)a.w, a.state, (T*)a.o);
+                     (const T*)a.g, (const T*)a.b, (const T*)a.w, a.state, (T*)a.o, a.gate_flags);
   return hipGetLastError();
 }
 
@@ -211,7 +213,7 @@ static hipError_t launch_dec_tokens(const DecodeTokensArgs& a) {
   hipLaunchKernelGGL((gdn2_decode_tokens_kernel<T, DK, DV>), dim3((unsigned)((long)a.N * a.H)),
                      dim3(256), 0, (hipStream_t)a.stream, (const T*)a.q, (const T*)a.k,
                      (const T*)a.v, (const T*)a.g, (const T*)a.b, (const T*)a.w, a.pool,
-                     a.indices, a.commit, (T*)a.o, a.step_states, a.L, a.H, a.P);
+                     a.indices, a.commit, (T*)a.o, a.step_states, a.L, a.H, a.P, a.gate_flags);
   return hipGetLastError();
 }
 

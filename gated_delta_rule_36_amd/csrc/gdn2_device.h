@@ -40,6 +40,12 @@ template <typename T> struct Vec8;
 template <> struct Vec8<bf16> {
   uint4 r;
   __device__ __forceinline__ void load(const bf16* p) { r = *reinterpret_cast<const uint4*>(p); }
+  // one value broadcast to all 8 lanes of the vector (a gate shared by every channel)
+  __device__ __forceinline__ void bcast(const bf16* p) {
+    const uint32_t h = *reinterpret_cast<const unsigned short*>(p);
+    const uint32_t x = h | (h << 16);
+    r = make_uint4(x, x, x, x);
+  }
   __device__ __forceinline__ void zero() { r = make_uint4(0, 0, 0, 0); }
   __device__ __forceinline__ void to_float(float* f) const {
     bf16x8 v = __builtin_bit_cast(bf16x8, r);
@@ -52,6 +58,10 @@ template <> struct Vec8<float> {
   __device__ __forceinline__ void load(const float* p) {
     r0 = reinterpret_cast<const uint4*>(p)[0];
     r1 = reinterpret_cast<const uint4*>(p)[1];
+  }
+  __device__ __forceinline__ void bcast(const float* p) {
+    const uint32_t x = __builtin_bit_cast(uint32_t, *p);
+    r0 = r1 = make_uint4(x, x, x, x);
   }
   __device__ __forceinline__ void zero() { r0 = r1 = make_uint4(0, 0, 0, 0); }
   __device__ __forceinline__ void to_float(float* f) const {

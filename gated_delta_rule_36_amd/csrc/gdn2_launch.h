@@ -6,6 +6,10 @@
 
 namespace gdn2 {
 
+// Gate layouts (bit set: that gate is one value per (token, head), shared by its channels).
+constexpr int kGateBScalar = 1;
+constexpr int kGateWScalar = 2;
+
 struct ChunkArgs {
   const void *q, *k, *v, *g, *b, *w;
   const float* s0;
@@ -18,6 +22,7 @@ struct ChunkArgs {
   void* stream;
   void* workspace;        // two-phase path only: per-chunk factors (see SplitLayout)
   size_t workspace_bytes;
+  int gate_flags = 0;     // kGateBScalar | kGateWScalar
 };
 
 struct DecodeArgs {
@@ -27,6 +32,7 @@ struct DecodeArgs {
   int N, H, d_k, d_v;
   int dtype;
   void* stream;
+  int gate_flags = 0;
 };
 
 struct DecodeTokensArgs {
@@ -39,6 +45,7 @@ struct DecodeTokensArgs {
   int N, L, H, d_k, d_v, P;
   int dtype;
   void* stream;
+  int gate_flags = 0;
 };
 
 // Value-slice widths the chunk kernel is built for, given dtype and d_k.

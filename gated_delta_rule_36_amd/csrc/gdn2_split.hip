@@ -98,7 +98,7 @@ gdn2_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                  const bf16* __restrict__ v, const bf16* __restrict__ g,
                  const bf16* __restrict__ bg, const bf16* __restrict__ wg,
                  char* __restrict__ ws, const int* __restrict__ cu_seqlens, int N, int T_len,
-                 int H, long nunits) {
+                 int H, long nunits, int gflags) {
   typedef bf16 T;
   using Sh = PrepShape<DK, DV>;
   using M = Mma<T>;
@@ -155,7 +155,8 @@ gdn2_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         rq[j].load(q + off);
         rk[j].load(k + off);
         rg[j].load(g + off);
-        rb[j].load(bg + off);
+        if (gflags & kGateBScalar) rb[j].bcast(bg + (cu.row + r) * H + cu.h);
+        else rb[j].load(bg + off);
       } else {
         rq[j].zero(); rk[j].zero(); rg[j].zero(); rb[j].zero();
       }
@@ -167,7 +168,8 @@ gdn2_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       if (r < cu.nvalid) {
         const long off = vb + (long)r * vstride;
         rv[j].load(v + off);
-        rw[j].load(wg + off);
+        if (gflags & kGateWScalar) rw[j].bcast(wg + (cu.row + r) * H + cu.h);
+        else rw[j].load(wg + off);
       } else {
         rv[j].zero(); rw[j].zero();
       }
@@ -764,7 +766,7 @@ static hipError_t launch_split(const ChunkArgs& a) {
     hipLaunchKernelGGL((gdn2_prep_kernel<DK, DV, false>), dim3((unsigned)grid1), dim3(512), 0, st,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.g,
                        (const bf16*)a.b, (const bf16*)a.w, (char*)a.workspace, a.cu_seqlens,
-                       a.N, a.T, a.H, nunits);
+                       a.N, a.T, a.H, nunits, a.gate_flags);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -788,7 +790,7 @@ static hipError_t launch_bwd_forward(const ChunkArgs& a) {
     hipLaunchKernelGGL((gdn2_prep_kernel<DK, DV, true>), dim3((unsigned)grid1), dim3(512), 0, st,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.g,
                        (const bf16*)a.b, (const bf16*)a.w, (char*)a.workspace, a.cu_seqlens,
-                       a.N, a.T, a.H, nunits);
+                       a.N, a.T, a.H, nunits, 0);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

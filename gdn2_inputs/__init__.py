@@ -27,6 +27,7 @@ import numpy as np
 
 __all__ = [
     "CONFIGS",
+    "make_scalar_gate",
     "make_block_inputs",
     "round_to_bf16",
     "make_inputs",
@@ -181,3 +182,10 @@ def make_block_inputs(B, T, H, dk, dv, dtype="bf16", seed=0, lengths=None):
     out["cu_seqlens"] = (None if lengths is None else
                          np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32))
     return out
+
+
+def make_scalar_gate(shape, dtype="bf16", seed=0):
+    """A gate with one value per (token, head): sigmoid(N(0, 1)) of the given leading shape
+    (e.g. [B, T, H]), rounded to the run dtype; its own stream (seed, 2)."""
+    rng = np.random.Generator(np.random.PCG64([seed, 2]))
+    return _to_dtype(_sigmoid(rng.standard_normal(shape)), dtype)

@@ -51,6 +51,15 @@ enum {
 };
 
 /*
+ * Gate layouts for the *_ex entry points (bit set: that gate is one value per token and
+ * head, shared by all of its channels, i.e. b = beta * 1 or w = omega * 1, the scalar-gate
+ * configurations ablated in the reading note's §4). A scalar b is [..., H] in place of
+ * [..., H, d_k]; a scalar w is [..., H] in place of [..., H, d_v]; same dtype, same leading
+ * axes. The result equals the per-channel call with the gate broadcast over its channels.
+ */
+enum { GDN2_GATE_B_SCALAR = 1, GDN2_GATE_W_SCALAR = 2 };
+
+/*
  * Chunkwise-parallel forward over whole sequences (the chunk form of the reading note's
  * §3 chunkwise-training paragraph: a per-channel cumulative decay normalises the state
  * inside a 64-token chunk, the chunk becomes an asymmetric delta recurrence, and the UT
@@ -90,6 +99,18 @@ int gdn2_chunk_fwd(const void* q, const void* k, const void* v, const void* log_
                    float* final_state, const int32_t* cu_seqlens, int B, int T, int H,
                    int d_k, int d_v, int N, int dtype, void* workspace,
                    size_t workspace_bytes, void* hip_stream);
+
+/*
+ * gdn2_chunk_fwd with a gate layout (GDN2_GATE_* bits, 0 = per-channel gates as above):
+ * scalar b and / or w are read as [B, T, H] (one value per token and head). Both the fused
+ * path and the two-phase path (workspace given) support them. Any other bit gives
+ * GDN2_INVALID_ARGUMENT.
+ */
+int gdn2_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* log_alpha,
+                      const void* b, const void* w, const float* initial_state, void* o,
+                      float* final_state, const int32_t* cu_seqlens, int B, int T, int H,
+                      int d_k, int d_v, int N, int dtype, int gate_layout, void* workspace,
+                      size_t workspace_bytes, void* hip_stream);
 
 /*
  * Device workspace, in bytes, that the two-phase path of gdn2_chunk_fwd needs for a call
@@ -170,6 +191,11 @@ int gdn2_decode_step(const void* q, const void* k, const void* v, const void* lo
                      const void* b, const void* w, float* state, void* o, int N, int H,
                      int d_k, int d_v, int dtype, void* hip_stream);
 
+/* gdn2_decode_step with a gate layout: scalar b and / or w are [N, H]. */
+int gdn2_decode_step_ex(const void* q, const void* k, const void* v, const void* log_alpha,
+                        const void* b, const void* w, float* state, void* o, int N, int H,
+                        int d_k, int d_v, int dtype, int gate_layout, void* hip_stream);
+
 /*
  * L consecutive tokens for each of N sequences against a pool of recurrent states: decode
  * of a few tokens at once, or verification of draft tokens in speculative decoding (the
@@ -197,6 +223,13 @@ int gdn2_decode_tokens(const void* q, const void* k, const void* v, const void* 
                        const int32_t* state_indices, const int32_t* commit_len, void* o,
                        float* step_states, int N, int L, int H, int d_k, int d_v, int P,
                        int dtype, void* hip_stream);
+
+/* gdn2_decode_tokens with a gate layout: scalar b and / or w are [N, L, H]. */
+int gdn2_decode_tokens_ex(const void* q, const void* k, const void* v, const void* log_alpha,
+                          const void* b, const void* w, float* state_pool,
+                          const int32_t* state_indices, const int32_t* commit_len, void* o,
+                          float* step_states, int N, int L, int H, int d_k, int d_v, int P,
+                          int dtype, int gate_layout, void* hip_stream);
 
 /*
  * Block prologue: the branches between the block's projections and the mixer (the reading

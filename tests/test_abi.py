@@ -198,3 +198,15 @@ def test_block_prologue_epilogue_error_paths():
     assert epi(rows=-1) == 1
     assert epi(y=MIS) == 1
     assert epi(rows=0, o=None) == 0
+
+
+def test_gate_layout_error_paths():
+    L = _lib.lib()
+    base = [FAKE] * 6 + [None, FAKE, None, None]
+    assert L.gdn2_chunk_fwd_ex(*base, 2, 64, 4, 128, 128, 2, 0, 4, None, 0, None) == 1
+    assert L.gdn2_chunk_fwd_ex(*base, 2, 64, 4, 128, 128, 2, 0, -1, None, 0, None) == 1
+    assert L.gdn2_chunk_fwd_ex(*base, 2, 64, 4, 96, 128, 2, 0, 3, None, 0, None) == 2
+    assert L.gdn2_decode_step_ex(*([FAKE] * 8), 2, 2, 128, 128, 0, 8, None) == 1
+    assert L.gdn2_decode_step_ex(*([FAKE] * 8), 0, 2, 128, 128, 0, 3, None) == 0
+    assert L.gdn2_decode_tokens_ex(*([FAKE] * 7), None, None, FAKE, None, 2, 2, 2, 64, 64, 2,
+                                   0, 5, None) == 1

@@ -1,0 +1,113 @@
+"""GPU parity of the scalar-gate layouts (one erase and / or write gate value per token and
+head, shared by its channels: the scalar-gate configurations of the GDN-2 reading note's §4)
+through gdn2_chunk_fwd_ex, gdn2_decode_step_ex and gdn2_decode_tokens_ex, against the oracle
+run on the same gate broadcast over the channels."""
+import numpy as np
+import pytest
+import torch
+
+from gdn2_inputs import make_decode_inputs, make_inputs, make_scalar_gate, varlen_lengths
+from oracle import gdn2_decode_steps, gdn2_decode_tokens, gdn2_forward
+from tests.gpu_util import TOL, assert_close, dev_tensor, host64, say
+
+pytestmark = pytest.mark.gpu
+NAMES = ("q", "k", "v", "g", "b", "w")
+LAYOUTS = {"b": (True, False), "w": (False, True), "bw": (True, True)}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _scalarise(x, layout, lead, seed):
+    """Replace b and / or w by scalar gates; returns (gates for the GPU, broadcast for the
+    oracle)."""
+    sb, sw = LAYOUTS[layout]
+    gpu = dict(x)
+    ref = dict(x)
+    for name, on, d in (("b", sb, x["q"].shape[-1]), ("w", sw, x["v"].shape[-1])):
+        if on:
+            s = make_scalar_gate(lead, x.get("dtype", "bf16"), seed=seed + (name == "w"))
+            gpu[name] = s
+            ref[name] = np.repeat(s[..., None], d, axis=-1)
+    return gpu, ref
+
+
+@pytest.mark.parametrize("layout", ["b", "w", "bw"])
+@pytest.mark.parametrize("dt,dk,dv,path", [("bf16", 128, 128, "fused"), ("bf16", 64, 128, "fused"),
+                                           ("fp32", 64, 64, "fused"), ("bf16", 128, 64, "split"),
+                                           ("bf16", 128, 128, "split")])
+def test_chunk_forward_scalar_gates(layout, dt, dk, dv, path):
+    import gated_delta_rule_36_amd as G
+    B, T, H = 2, 200, 3
+    x = make_inputs(B, T, H, dk, dv, dt, seed=41 + dk + dv, s0_std=0.05)
+    gx, rx = _scalarise(x, layout, (B, T, H), seed=7)
+    say("chunk_fwd scalar gates", layout, dt, dk, dv, path)
+    t = {n: dev_tensor(gx[n], dt) for n in NAMES}
+    s0 = torch.from_numpy(x["s0"]).cuda()
+    o, sN = G.chunk_fwd(*(t[n] for n in NAMES), initial_state=s0, path=path)
+    torch.cuda.synchronize()
+    o_ref, s_ref = gdn2_forward(*(rx[n] for n in NAMES), s0=x["s0"])
+    assert_close("o", host64(o), o_ref, TOL[dt])
+    assert_close("S_final", host64(sN), s_ref, TOL[dt])
+
+
+@pytest.mark.parametrize("path", ["fused", "split"])
+def test_chunk_forward_scalar_gates_varlen(path):
+    import gated_delta_rule_36_amd as G
+    lens = varlen_lengths(5, 1, 150, seed=3)
+    lens[1] = 64
+    T = int(np.sum(lens))
+    x = make_inputs(1, T, 2, 128, 128, "bf16", seed=5, lengths=lens, s0_std=0.05)
+    gx, rx = _scalarise(x, "bw", (1, T, 2), seed=9)
+    say("chunk_fwd scalar gates varlen", path, list(map(int, lens)))
+    t = {n: dev_tensor(gx[n], "bf16") for n in NAMES}
+    cu = torch.from_numpy(x["cu_seqlens"]).cuda()
+    o, sN = G.chunk_fwd(*(t[n] for n in NAMES), initial_state=torch.from_numpy(x["s0"]).cuda(),
+                        cu_seqlens=cu, path=path)
+    torch.cuda.synchronize()
+    o_ref, s_ref = gdn2_forward(*(rx[n] for n in NAMES), s0=x["s0"], cu_seqlens=x["cu_seqlens"])
+    assert_close("o", host64(o), o_ref, TOL["bf16"])
+    assert_close("S_final", host64(sN), s_ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("layout", ["b", "w", "bw"])
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_decode_step_scalar_gates(layout, dt):
+    import gated_delta_rule_36_amd as G
+    N, H, dk, dv, steps = 5, 3, 128, 64, 4
+    x = make_decode_inputs(N, H, dk, dv, steps, dt, seed=13, s0_std=0.05)
+    # [steps, N, H, d] per-step inputs; scalar gates are [steps, N, H]
+    gx, rx = _scalarise(x, layout, (steps, N, H), seed=17)
+    say("decode_step scalar gates", layout, dt)
+    st = torch.from_numpy(x["s0"]).cuda()
+    outs = []
+    for s in range(steps):
+        outs.append(G.decode_step(*(dev_tensor(gx[n][s], dt) for n in NAMES), st))
+    torch.cuda.synchronize()
+    o_ref, s_ref = gdn2_decode_steps(x["s0"], *(rx[n] for n in NAMES))
+    assert_close("o", host64(torch.stack(outs)), o_ref, TOL[dt])
+    assert_close("state", host64(st), s_ref, TOL[dt])
+
+
+@pytest.mark.parametrize("layout", ["b", "w", "bw"])
+def test_decode_tokens_scalar_gates(layout):
+    import gated_delta_rule_36_amd as G
+    N, L, H, dk, dv, P = 4, 3, 2, 64, 128, 6
+    x = make_decode_inputs(N, H, dk, dv, L, "bf16", seed=19, s0_std=0.05)
+    toks = {n: np.ascontiguousarray(np.swapaxes(x[n], 0, 1)) for n in NAMES}  # [N, L, H, d]
+    toks["dtype"] = "bf16"
+    gx, rx = _scalarise(toks, layout, (N, L, H), seed=23)
+    rng = np.random.default_rng(3)
+    pool = (rng.normal(size=(P, H, dk, dv)) * 0.05).astype(np.float32)
+    idx = np.array([4, 0, 2, 5], np.int32)
+    say("decode_tokens scalar gates", layout)
+    pool_t = torch.from_numpy(pool).cuda()
+    o, _ = G.decode_tokens(*(dev_tensor(gx[n], "bf16") for n in NAMES), pool_t,
+                           state_indices=torch.from_numpy(idx).cuda())
+    torch.cuda.synchronize()
+    o_ref, _, pool_ref = gdn2_decode_tokens(pool, *(rx[n] for n in NAMES), indices=idx)
+    assert_close("o", host64(o), o_ref, TOL["bf16"])
+    assert_close("pool", host64(pool_t), pool_ref, TOL["bf16"])
