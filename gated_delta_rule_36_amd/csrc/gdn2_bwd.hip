@@ -21,8 +21,12 @@
 //   2. gdn2_bwd_chain_kernel: the recurrence, storing dSn and dZ per chunk, and dS0 of the
 //      sequence;
 //   3. gdn2_bwd_local_kernel: every chunk's gradients of q, k, g, b (and v, w = dZ*w, dZ*v).
-// The local kernel forms Khat = K 2^-G, so it needs chunks whose total decay is in the
-// chunk-referenced range (below 83 nats per channel); it flags any chunk outside it.
+// The local kernel references every decay factor to the middle of the chunk's decay
+// range, Gm = Glast / 2 per channel: it forms Khat' = K 2^(Gm - G), Qbar' = Q 2^(G - Gm),
+// Ebar' = E 2^(G - Gm) and the entering state's rows scaled by 2^Gm, so that the products
+// above keep their values up to those per-channel factors (undone in the elementwise
+// chain) while no factor exceeds half the chunk's decay. Chunks whose total decay exceeds
+// twice the forward's chunk-referenced range (166 nats in some channel) are flagged.
 
 #include "gdn2_chunk_common.h"
 #include "gdn2_launch.h"
@@ -398,8 +402,14 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   lds_barrier();
   channel_scan<DK, Sh::TG, Sh::GPB, NT>(sTot, sFac, sFlag, tid);
   lds_barrier();
-  if (tid == 0 && *sFlag != 0 && range_flag != nullptr) *range_flag = 1;
-  // per thread: G (log2) of its tokens; Khat^T = (K 2^-G)^T into LDS (natural token order)
+  (void)sFlag;
+  if (tid < DK && range_flag != nullptr && -sFac[Fac::GL * DK + tid] > 2.f * kFastPathMaxDecay2)
+    *range_flag = 1;
+  // this thread's channels' reference Gm = Glast / 2 (log2)
+  float Gm8[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) Gm8[i] = 0.5f * sFac[Fac::GL * DK + cg * 8 + i];
+  // per thread: G (log2) of its tokens; Khat'^T = (K 2^(Gm-G))^T into LDS (natural order)
   float G2[Sh::TPT][8];
   {
     float run[8];
@@ -415,7 +425,7 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       for (int i = 0; i < 8; ++i) {
         run[i] += fg[i] * kLog2e;
         G2[j][i] = run[i];
-        kh[i].put(j, fk[i] * fast_exp2(-run[i]));
+        kh[i].put(j, fk[i] * fast_exp2(Gm8[i] - run[i]));
       }
     }
     const int sw = tswz(cg * 8);
@@ -478,9 +488,16 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     dKt[Tt] = acc;
   }
   lds_barrier();  // dSn and U are dead
+  {
+    // S0 rows (this lane's channels 16 wave + 4 g4 + i) scaled by 2^Gm
+    const f4 gl = *reinterpret_cast<const f4*>(sFac + Fac::GL * DK + 16 * wave + 4 * g4);
+    f4 rs;
 #pragma unroll
-  for (int ct = 0; ct < NVT; ++ct)
-    store_tile_pairs(sA + (16 * wave) * LDV + 16 * ct, LDV, lane, s0t[ct], ident);
+    for (int i = 0; i < 4; ++i) rs[i] = fast_exp2(0.5f * gl[i]);
+#pragma unroll
+    for (int ct = 0; ct < NVT; ++ct)
+      store_tile_pairs(sA + (16 * wave) * LDV + 16 * ct, LDV, lane, s0t[ct] * rs, ident);
+  }
   lds_barrier();
   // ---- P3: dQbar^T = S0 dO^T + Khat^T M1^T,  dEbar^T = -S0 dZ^T + Khat^T M2^T
   f4 dQb[4], dEb[4];
@@ -517,7 +534,7 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       rb[j].to_float(fb);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float gm = fast_exp2(G2[j][i]);
+        const float gm = fast_exp2(G2[j][i] - Gm8[i]);
         ev[i].put(j, fb[i] * fk[i] * gm);
         qv[i].put(j, fq[i] * gm);
       }
@@ -563,6 +580,7 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // ---- elementwise: lane = token 16*Tt + m16, channels c0 .. c0 + 3 of this wave
   const int c0 = 16 * wave + 4 * g4;
   const f4 gam = *reinterpret_cast<const f4*>(sFac + Fac::GAM * DK + c0);
+  const f4 gl = *reinterpret_cast<const f4*>(sFac + Fac::GL * DK + c0);
   const f4 xc = *reinterpret_cast<const f4*>(sX + c0);
   f4 dgv[4], outq[4], outk[4], outb[4];
   f4 totB = {0.f, 0.f, 0.f, 0.f};
@@ -575,14 +593,17 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     f4 A, Bv;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float gm = fast_exp2(G[i]), ig = fast_exp2(-G[i]);
+      // mid-referenced factors (dQb, dEb, dKh carry the 2^(+-Gm) of their operands)
+      const float gmr = 0.5f * gl[i];
+      const float gm = fast_exp2(G[i] - gmr), ig = fast_exp2(gmr - G[i]);
+      const float kt = fast_exp2(gl[i] - G[i]);  // 2^(Glast - G) <= 1
       const float dE = dEb[Tt][i] * gm;
       outq[Tt][i] = dQb[Tt][i] * gm;
-      outk[Tt][i] = (dKh[Tt][i] + dKt[Tt][i] * gam[i]) * ig + dE * fb[i];
+      outk[Tt][i] = dKh[Tt][i] * ig + dKt[Tt][i] * kt + dE * fb[i];
       outb[Tt][i] = dE * fk[i];
       // dG = dEbar Ebar + dQbar Qbar - dKhat Khat - dKtil Ktil, split as A - B
       A[i] = gm * (dEb[Tt][i] * fb[i] * fk[i] + dQb[Tt][i] * fq[i]) - dKh[Tt][i] * fk[i] * ig;
-      Bv[i] = dKt[Tt][i] * fk[i] * gam[i] * ig;
+      Bv[i] = dKt[Tt][i] * fk[i] * kt;
     }
     dgv[Tt] = A - Bv;
     totB += Bv;

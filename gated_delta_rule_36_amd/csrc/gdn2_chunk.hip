@@ -108,7 +108,9 @@ struct ChunkShape {
 };
 
 
-template <typename T, int DK, int NV>
+// GL: the gate layout this build reads (kGateBScalar | kGateWScalar bits); each layout has
+// its own build, so every load is unconditional in the layout's own form.
+template <typename T, int DK, int NV, int GL>
 __global__ void __launch_bounds__((ChunkShape<T, DK, NV>::NT))
 gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                   const T* __restrict__ g, const T* __restrict__ bg, const T* __restrict__ wg,
@@ -193,8 +195,10 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
   const T* vb = v + row0 * vstride + (long)h * DV + col0;
   const T* wb = wg + row0 * vstride + (long)h * DV + col0;
   // scalar gates ([rows, H]: one value per token and head, broadcast over the channels)
-  const bool b_scalar = (gflags & kGateBScalar) != 0, w_scalar = (gflags & kGateWScalar) != 0;
-  const T* bsb = bg + row0 * H + h;
+  constexpr bool b_scalar = (GL & kGateBScalar) != 0;
+  constexpr bool w_scalar = (GL & kGateWScalar) != 0;
+  (void)gflags;
+  const T* bsb = bg + row0 * H + h;  // a scalar gate: one value per (token, head)
   const T* wsb = wg + row0 * H + h;
   T* ob = o + row0 * vstride + (long)h * DV + col0;
 
@@ -225,7 +229,11 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
         rq[j].load(qb + off);
         rk[j].load(kb + off);
         rg[j].load(gb + off);
-        if (b_scalar) rb[j].bcast(bsb + (long)(c0 + r) * H); else rb[j].load(bb + off);
+        // a scalar gate is read as the aligned 8-element block that holds it (the same
+        // load instruction in both layouts keeps the prefetch's waits precise); its element
+        // is picked out when the chunk is consumed
+        if constexpr (b_scalar) rb[j].load_one(bsb + (long)(c0 + r) * H);
+        else rb[j].load(bb + off);
       } else {
         rq[j].zero(); rk[j].zero(); rg[j].zero(); rb[j].zero();
       }
@@ -236,7 +244,8 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
       if (r < nvalid) {
         const long off = (long)(c0 + r) * vstride + vcg * 8;
         rv[j].load(vb + off);
-        if (w_scalar) rw[j].bcast(wsb + (long)(c0 + r) * H); else rw[j].load(wb + off);
+        if constexpr (w_scalar) rw[j].load_one(wsb + (long)(c0 + r) * H);
+        else rw[j].load(wb + off);
       } else {
         rv[j].zero(); rw[j].zero();
       }
@@ -332,6 +341,7 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
         rg[j].to_float(fg);
         rq[j].to_float(fq);
         rk[j].to_float(fk);
+        if constexpr (b_scalar) rb[j].splat();
         rb[j].to_float(fb);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -376,6 +386,7 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
       for (int j = 0; j < Sh::VTPT; ++j) {
         float fv[8], fw[8];
         rv[j].to_float(fv);
+        if constexpr (w_scalar) rw[j].splat();
         rw[j].to_float(fw);
 #pragma unroll
         for (int i = 0; i < 8; ++i) zv[i].put(j, fv[i] * fw[i]);
@@ -625,7 +636,11 @@ template <typename T, int DK, int NV>
 static hipError_t launch_chunk(const ChunkArgs& a) {
   const int nslices = a.d_v / NV;
   const long grid = (long)a.N * a.H * nslices;
-  hipLaunchKernelGGL((gdn2_chunk_kernel<T, DK, NV>), dim3((unsigned)grid),
+  auto kern = a.gate_flags == 3 ? gdn2_chunk_kernel<T, DK, NV, 3>
+              : a.gate_flags == 2 ? gdn2_chunk_kernel<T, DK, NV, 2>
+              : a.gate_flags == 1 ? gdn2_chunk_kernel<T, DK, NV, 1>
+                                  : gdn2_chunk_kernel<T, DK, NV, 0>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid),
                      dim3(ChunkShape<T, DK, NV>::NT), 0,
                      (hipStream_t)a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
                      (const T*)a.g, (const T*)a.b, (const T*)a.w, a.s0, (T*)a.o, a.sN,

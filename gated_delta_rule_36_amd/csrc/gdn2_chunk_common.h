@@ -22,7 +22,8 @@ struct Fac {
   static constexpr int GAM = 12;  // 2^Glast: the chunk's decay of the state
   static constexpr int OFF = 13;  // 2^(Gs(R) - Ge(I)) for (R, I) = (2,0), (3,0), (3,1)
   static constexpr int GS = 16;   // Gs(R)                  R = 0..3
-  static constexpr int N = 20;
+  static constexpr int GL = 20;   // Glast
+  static constexpr int N = 21;
 };
 
 // Threshold on a chunk's total log2-decay above which the block-referenced path runs:
@@ -176,6 +177,7 @@ __device__ __forceinline__ void channel_scan(float* sTot, float* sFac, int* sFla
       sFac[(Fac::GS + R) * DK + ch] = gs[R];
     }
     sFac[Fac::GAM * DK + ch] = fast_exp2(gn);
+    sFac[Fac::GL * DK + ch] = gn;
     sFac[(Fac::OFF + 0) * DK + ch] = fast_exp2(gs[2] - ge[0]);
     sFac[(Fac::OFF + 1) * DK + ch] = fast_exp2(gs[3] - ge[0]);
     sFac[(Fac::OFF + 2) * DK + ch] = fast_exp2(gs[3] - ge[1]);

@@ -40,9 +40,14 @@ template <typename T> struct Vec8;
 template <> struct Vec8<bf16> {
   uint4 r;
   __device__ __forceinline__ void load(const bf16* p) { r = *reinterpret_cast<const uint4*>(p); }
-  // one value broadcast to all 8 lanes of the vector (a gate shared by every channel)
-  __device__ __forceinline__ void bcast(const bf16* p) {
-    const uint32_t h = *reinterpret_cast<const unsigned short*>(p);
+  // A gate shared by every channel: load_one fetches the one value (nothing waits on it
+  // there, so a prefetch stays in flight); splat broadcasts it to all 8 lanes when the
+  // vector is consumed.
+  __device__ __forceinline__ void load_one(const bf16* p) {
+    r.x = *reinterpret_cast<const unsigned short*>(p);
+  }
+  __device__ __forceinline__ void splat() {
+    const uint32_t h = r.x & 0xffffu;
     const uint32_t x = h | (h << 16);
     r = make_uint4(x, x, x, x);
   }
@@ -59,8 +64,11 @@ template <> struct Vec8<float> {
     r0 = reinterpret_cast<const uint4*>(p)[0];
     r1 = reinterpret_cast<const uint4*>(p)[1];
   }
-  __device__ __forceinline__ void bcast(const float* p) {
-    const uint32_t x = __builtin_bit_cast(uint32_t, *p);
+  __device__ __forceinline__ void load_one(const float* p) {
+    r0.x = *reinterpret_cast<const uint32_t*>(p);
+  }
+  __device__ __forceinline__ void splat() {
+    const uint32_t x = r0.x;
     r0 = r1 = make_uint4(x, x, x, x);
   }
   __device__ __forceinline__ void zero() { r0 = r1 = make_uint4(0, 0, 0, 0); }

@@ -92,13 +92,14 @@ struct PrepPieces {
 
 // BWD: also write the reverse chain's operands (BwdLayout) after the forward factors, and
 // use the backward unit stride.
-template <int DK, int DV, bool BWD>
+template <int DK, int DV, bool BWD, int GL>
 __global__ void __launch_bounds__(512)
 gdn2_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                  const bf16* __restrict__ v, const bf16* __restrict__ g,
                  const bf16* __restrict__ bg, const bf16* __restrict__ wg,
                  char* __restrict__ ws, const int* __restrict__ cu_seqlens, int N, int T_len,
                  int H, long nunits, int gflags) {
+  (void)gflags;  // the layout is the template's GL
   typedef bf16 T;
   using Sh = PrepShape<DK, DV>;
   using M = Mma<T>;
@@ -155,7 +156,9 @@ gdn2_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         rq[j].load(q + off);
         rk[j].load(k + off);
         rg[j].load(g + off);
-        if (gflags & kGateBScalar) rb[j].bcast(bg + (cu.row + r) * H + cu.h);
+        // a scalar gate: the aligned 8-element block holding it (same load either way; its
+        // element is picked out when the unit is consumed)
+        if constexpr ((GL & kGateBScalar) != 0) rb[j].load_one(bg + (cu.row + r) * H + cu.h);
         else rb[j].load(bg + off);
       } else {
         rq[j].zero(); rk[j].zero(); rg[j].zero(); rb[j].zero();
@@ -168,7 +171,7 @@ gdn2_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       if (r < cu.nvalid) {
         const long off = vb + (long)r * vstride;
         rv[j].load(v + off);
-        if (gflags & kGateWScalar) rw[j].bcast(wg + (cu.row + r) * H + cu.h);
+        if constexpr ((GL & kGateWScalar) != 0) rw[j].load_one(wg + (cu.row + r) * H + cu.h);
         else rw[j].load(wg + off);
       } else {
         rv[j].zero(); rw[j].zero();
@@ -250,6 +253,7 @@ gdn2_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         rg[j].to_float(fg);
         rq[j].to_float(fq);
         rk[j].to_float(fk);
+        if constexpr ((GL & kGateBScalar) != 0) rb[j].splat();
         rb[j].to_float(fb);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -294,6 +298,7 @@ gdn2_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       for (int j = 0; j < Sh::VTPT; ++j) {
         float fv[8], fw[8];
         rv[j].to_float(fv);
+        if constexpr ((GL & kGateWScalar) != 0) rw[j].splat();
         rw[j].to_float(fw);
 #pragma unroll
         for (int i = 0; i < 8; ++i) zv[i].put(j, fv[i] * fw[i]);
@@ -763,7 +768,11 @@ static hipError_t launch_split(const ChunkArgs& a) {
   hipStream_t st = (hipStream_t)a.stream;
   if (nunits > 0) {
     const long grid1 = nunits < cu_count() ? nunits : cu_count();
-    hipLaunchKernelGGL((gdn2_prep_kernel<DK, DV, false>), dim3((unsigned)grid1), dim3(512), 0, st,
+    auto prep = a.gate_flags == 3 ? gdn2_prep_kernel<DK, DV, false, 3>
+                : a.gate_flags == 2 ? gdn2_prep_kernel<DK, DV, false, 2>
+                : a.gate_flags == 1 ? gdn2_prep_kernel<DK, DV, false, 1>
+                                    : gdn2_prep_kernel<DK, DV, false, 0>;
+    hipLaunchKernelGGL(prep, dim3((unsigned)grid1), dim3(512), 0, st,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.g,
                        (const bf16*)a.b, (const bf16*)a.w, (char*)a.workspace, a.cu_seqlens,
                        a.N, a.T, a.H, nunits, a.gate_flags);
@@ -787,7 +796,7 @@ static hipError_t launch_bwd_forward(const ChunkArgs& a) {
   hipStream_t st = (hipStream_t)a.stream;
   if (nunits > 0) {
     const long grid1 = nunits < cu_count() ? nunits : cu_count();
-    hipLaunchKernelGGL((gdn2_prep_kernel<DK, DV, true>), dim3((unsigned)grid1), dim3(512), 0, st,
+    hipLaunchKernelGGL((gdn2_prep_kernel<DK, DV, true, 0>), dim3((unsigned)grid1), dim3(512), 0, st,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.g,
                        (const bf16*)a.b, (const bf16*)a.w, (char*)a.workspace, a.cu_seqlens,
                        a.N, a.T, a.H, nunits, 0);

@@ -89,6 +89,30 @@ def test_bwd_gate_cases(case):
     check(x, do, dsn)
 
 
+@pytest.mark.parametrize("nats", [100.0, 150.0])
+def test_bwd_wide_decay_chunk(nats):
+    """A chunk whose total decay is past the chunk-referenced range of the forward (83 nats)
+    but inside the backward's mid-referenced range (166 nats): in every key channel of the
+    second chunk, and in half of the channels of the third."""
+    x = make_inputs(1, 200, 2, 128, 128, "bf16", seed=315, s0_std=0.02)
+    per = float(round_to_bf16(np.array([-nats / 64], np.float32))[0])
+    x["g"][:, 64:128] = per
+    x["g"][:, 128:192, :, ::2] = per
+    do, dsn = _upstream(x, 12)
+    say("bwd wide-decay chunk", nats)
+    check(x, do, dsn)
+
+
+def test_bwd_near_resets():
+    """Near-resets as in the long-context workload (10% of tokens at log-decay -5) plus one
+    chunk with 18 of them (about 95 nats): inside the backward's range."""
+    x = make_inputs(1, 640, 2, 128, 128, "bf16", seed=316, reset_frac=0.1, s0_std=0.02)
+    x["g"][:, 320:338] = -5.0
+    do, dsn = _upstream(x, 13)
+    say("bwd near-resets T640")
+    check(x, do, dsn)
+
+
 def test_bwd_range_flag():
     import gated_delta_rule_36_amd as G
     x = make_inputs(1, 128, 1, 64, 64, "bf16", seed=314)
