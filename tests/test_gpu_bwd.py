@@ -138,3 +138,42 @@ def test_bwd_layer1p3b_full_size_sampled():
         for name, a, r in zip(GRADS, out[:6], ref[:6]):
             assert_close(name, host64(a[n:n + 1, :, h:h + 1]), r, TOL["bf16"])
         assert_close("ds0", host64(out[6][n:n + 1, h:h + 1]), ref[6], TOL["bf16"])
+
+
+def test_bwd_longctx_full_size_sampled():
+    """The long-context workload (B1 H16 T32768, 10% near-resets): heads 15 and 3 each hold
+    a chunk past 83 nats (chunks 13 and 40), inside the backward's mid-referenced range."""
+    from gdn2_inputs import make_config_inputs
+    from oracle import gdn2_backward as ref_bwd
+    x = make_config_inputs("longctx_bf16")
+    do, dsn = _upstream(x, 14)
+    say("bwd longctx B1 H16 T32768 d128 (sampled heads 15, 3)")
+    out = run_bwd(x, do, dsn)
+    for h in (15, 3):
+        sel = {m: x[m][:, :, h:h + 1] for m in NAMES}
+        ref = ref_bwd(*(sel[m] for m in NAMES), do[:, :, h:h + 1], dS_final=dsn[:, h:h + 1])
+        print(f" head {h}", flush=True)
+        for name, a, r in zip(GRADS, out[:6], ref[:6]):
+            assert_close(name, host64(a[:, :, h:h + 1]), r, TOL["bf16"])
+        assert_close("ds0", host64(out[6][:, h:h + 1]), ref[6], TOL["bf16"])
+
+
+def test_bwd_varlen_full_size_sampled():
+    """The packed workload (16 sequences of 512..8192 tokens, nonzero initial states)."""
+    from gdn2_inputs import make_config_inputs
+    from oracle import gdn2_backward as ref_bwd
+    x = make_config_inputs("varlen_bf16")
+    do, dsn = _upstream(x, 15)
+    cu = x["cu_seqlens"]
+    lens = np.diff(cu)
+    say("bwd varlen 16 seqs", int(lens.sum()), "tokens (sampled chains)")
+    out = run_bwd(x, do, dsn)
+    for n, h in ((int(np.argmin(lens)), 2), (5, 13)):
+        sl = slice(int(cu[n]), int(cu[n + 1]))
+        sel = {m: x[m][:, sl, h:h + 1] for m in NAMES}
+        ref = ref_bwd(*(sel[m] for m in NAMES), do[:, sl, h:h + 1],
+                      dS_final=dsn[n:n + 1, h:h + 1], s0=x["s0"][n:n + 1, h:h + 1])
+        print(f" chain (n={n}, h={h})", flush=True)
+        for name, a, r in zip(GRADS, out[:6], ref[:6]):
+            assert_close(name, host64(a[:, sl, h:h + 1]), r, TOL["bf16"])
+        assert_close("ds0", host64(out[6][n:n + 1, h:h + 1]), ref[6], TOL["bf16"])
