@@ -294,7 +294,8 @@ def main():
             "workload": "the same forward with scalar b and w ([B, T, H]), fused path",
             "ms_per_call": round(sms, 4), "tokens_per_s": round(B * T / (sms * 1e-3), 1),
             "algorithmic_bytes": sbytes,
-            "hbm_frac": round(sbytes / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            "hbm_frac": round(sbytes / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("chunk_fwd_scalar_gates_layer1p3b_bf16")}
 
     if not args.no_block and args.workload == "layer1p3b":
         # prologue (projections -> q, k, v, g, b, w) and epilogue (gated RMSNorm) at this shape
