@@ -266,6 +266,37 @@ def main():
             "algorithmic_bytes": bb, "achieved_GBs": round(bb / (bms * 1e-3) / 1e9, 1),
             "hbm_frac": round(bb / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic("chunk_bwd_layer1p3b_bf16")}
+
+        # a training step: forward then backward. Either the fused forward and a backward
+        # that recomputes the forward, or the training forward (keeps the intermediates) and
+        # the backward that reuses them.
+        def pair_recompute():
+            G.chunk_fwd(*(t[n] for n in NAMES), initial_state=s0, cu_seqlens=cu, path="fused")
+            bstep()
+
+        def pair_saved():
+            _, _, sv = G.chunk_fwd_train(*(t[n] for n in NAMES), initial_state=s0, cu_seqlens=cu,
+                                         workspace=bws)
+            G.chunk_bwd(*(t[n] for n in NAMES), do, initial_state=s0, cu_seqlens=cu, saved=sv,
+                        check_range=False)
+        res_t = {}
+        for name, fn in (("recompute", pair_recompute), ("saved", pair_saved)):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            evt = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(KB)]
+            for a, b2 in evt:
+                a.record()
+                fn()
+                b2.record()
+            torch.cuda.synchronize()
+            res_t[name] = round(float(np.mean([a.elapsed_time(b2) for a, b2 in evt])), 4)
+        out["train_step"] = {
+            "workload": "forward + backward on the same workload",
+            "ms_fused_forward_then_recomputing_backward": res_t["recompute"],
+            "ms_training_forward_then_saved_backward": res_t["saved"],
+            "tokens_per_s_saved": round(B * T / (res_t["saved"] * 1e-3), 1)}
         del bws
 
     if args.workload == "layer1p3b" and not args.no_scalar_gates:

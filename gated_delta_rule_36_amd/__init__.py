@@ -9,10 +9,10 @@ several (with slot indexing and committed prefixes, for serving); `block_prologu
 `block_epilogue` are the block's branches around the mixer. Both call libgdn2.so, built in-tree by
 `python -m gated_delta_rule_36_amd.build`.
 """
-from ._lib import (Gdn2Error, Gdn2RangeError, block_epilogue, block_prologue, chunk_bwd,
-                   chunk_fwd, decode_step, decode_tokens, lib, lib_path, uses_split,
-                   workspace_bytes)
+from ._lib import (Gdn2Error, Gdn2RangeError, SavedForBackward, block_epilogue, block_prologue,
+                   chunk_bwd, chunk_fwd, chunk_fwd_train, decode_step, decode_tokens,
+                   gated_delta_rule2, lib, lib_path, uses_split, workspace_bytes)
 
-__all__ = ["chunk_fwd", "chunk_bwd", "decode_step", "decode_tokens", "block_prologue",
+__all__ = ["chunk_fwd", "chunk_fwd_train", "chunk_bwd", "gated_delta_rule2", "SavedForBackward", "decode_step", "decode_tokens", "block_prologue",
            "block_epilogue", "workspace_bytes", "uses_split", "lib", "lib_path", "Gdn2Error",
            "Gdn2RangeError"]

@@ -51,6 +51,10 @@ def lib():
         L.gdn2_chunk_fwd_workspace_bytes.restype = _Z
         L.gdn2_chunk_bwd.argtypes = [_P] * 18 + [_I] * 7 + [_P, _Z, _P]
         L.gdn2_chunk_bwd.restype = _I
+        L.gdn2_chunk_bwd_saved.argtypes = [_P] * 18 + [_I] * 7 + [_P, _Z, _P]
+        L.gdn2_chunk_bwd_saved.restype = _I
+        L.gdn2_chunk_fwd_train.argtypes = [_P] * 10 + [_I] * 7 + [_P, _Z, _P]
+        L.gdn2_chunk_fwd_train.restype = _I
         L.gdn2_chunk_bwd_workspace_bytes.argtypes = [_I] * 7
         L.gdn2_chunk_bwd_workspace_bytes.restype = _Z
         L.gdn2_chunk_fwd_sliced.argtypes = [_P] * 10 + [_I] * 8 + [_P]
@@ -203,18 +207,77 @@ def chunk_fwd(q, k, v, g, b, w, initial_state=None, cu_seqlens=None,
     return o, sN
 
 
+class SavedForBackward:
+    """What chunk_fwd_train keeps for chunk_bwd: the workspace holding the chunk factors,
+    every chunk's entering state and U, and the identity of the inputs it was computed from."""
+
+    def __init__(self, workspace, key):
+        self.workspace = workspace
+        self.key = key
+
+
+def _inputs_key(tensors, cu_seqlens):
+    return tuple((t.data_ptr(), tuple(t.shape)) for t in tensors) + (
+        (None if cu_seqlens is None else (cu_seqlens.data_ptr(), cu_seqlens.numel())),)
+
+
+def chunk_fwd_train(q, k, v, g, b, w, initial_state=None, cu_seqlens=None,
+                    output_final_state=True, workspace=None):
+    """chunk_fwd for training (bf16): the same (o, final_state), plus a SavedForBackward that
+    lets chunk_bwd(..., saved=...) skip its forward recomputation. The saved workspace (about
+    232 KiB per 64-token chunk and head at d = 128) must stay untouched until then."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, d_k]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(dt)
+    for name, t, d in (("q", q, dk), ("k", k, dk), ("g", g, dk), ("b", b, dk),
+                       ("v", v, dv), ("w", w, dv)):
+        _check(name, t, (B, T, H, d), dt, dev)
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != dev or cu_seqlens.dim() != 1:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor on the inputs' device")
+        if B != 1:
+            raise ValueError("packed (cu_seqlens) inputs must have B == 1")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if initial_state is not None:
+        _check("initial_state", initial_state, (N, H, dk, dv), torch.float32, dev)
+    L = lib()
+    need = int(L.gdn2_chunk_bwd_workspace_bytes(B, T, H, dk, dv, N, code))
+    if need == 0:
+        raise ValueError("the training forward is built for bf16 with d_k, d_v in {64, 128}")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    sN = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if output_final_state else None
+    st = L.gdn2_chunk_fwd_train(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w),
+                                _ptr(initial_state), _ptr(o), _ptr(sN), _ptr(cu_seqlens), B, T,
+                                H, dk, dv, N, code, _ptr(workspace), workspace.numel(),
+                                _stream(dev))
+    if st != 0:
+        raise Gdn2Error("gdn2_chunk_fwd_train", st)
+    key = _inputs_key((q, k, v, g, b, w) + ((initial_state,) if initial_state is not None else ()),
+                      cu_seqlens)
+    return o, sN, SavedForBackward(workspace, key)
+
+
 class Gdn2RangeError(RuntimeError):
     """A chunk's total decay exceeded the range of the backward's factors."""
 
 
 def chunk_bwd(q, k, v, g, b, w, do, initial_state=None, d_final_state=None, cu_seqlens=None,
-              workspace=None, check_range=True):
+              workspace=None, check_range=True, saved=None):
     """Gradients of chunk_fwd (bf16).
 
     do: [B, T, H, d_v] gradient of o (input dtype); d_final_state: [N, H, d_k, d_v] fp32 or
     None. Returns (dq, dk, dv, dg, db, dw, d_initial_state): the first six in the input dtype
     and shapes, the last fp32 [N, H, d_k, d_v]. With check_range, synchronises once and
     raises Gdn2RangeError when some chunk's total decay is outside the backward's range.
+    saved: the SavedForBackward of a chunk_fwd_train call on these same tensors; the
+    forward recomputation is then skipped.
     """
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, d_k]")
@@ -243,18 +306,25 @@ def chunk_bwd(q, k, v, g, b, w, do, initial_state=None, d_final_state=None, cu_s
     need = int(L.gdn2_chunk_bwd_workspace_bytes(B, T, H, dk, dv, N, code))
     if need == 0:
         raise ValueError("the backward is built for bf16 with d_k, d_v in {64, 128}")
-    if workspace is None or workspace.numel() < need:
+    fn, call = "gdn2_chunk_bwd", L.gdn2_chunk_bwd
+    if saved is not None:
+        key = _inputs_key((q, k, v, g, b, w) + ((initial_state,) if initial_state is not None
+                                                else ()), cu_seqlens)
+        if key != saved.key:
+            raise ValueError("saved was computed from other tensors than these")
+        workspace = saved.workspace
+        fn, call = "gdn2_chunk_bwd_saved", L.gdn2_chunk_bwd_saved
+    elif workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     grads = [torch.empty_like(x) for x in (q, k, v, g, b, w)]
     ds0 = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     flag = torch.zeros(1, dtype=torch.int32, device=dev)
-    st = L.gdn2_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w),
-                          _ptr(initial_state), _ptr(do), _ptr(d_final_state),
-                          *(_ptr(x) for x in grads), _ptr(ds0), _ptr(flag), _ptr(cu_seqlens),
-                          B, T, H, dk, dv, N, code, _ptr(workspace), workspace.numel(),
-                          _stream(dev))
+    st = call(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w),
+              _ptr(initial_state), _ptr(do), _ptr(d_final_state),
+              *(_ptr(x) for x in grads), _ptr(ds0), _ptr(flag), _ptr(cu_seqlens),
+              B, T, H, dk, dv, N, code, _ptr(workspace), workspace.numel(), _stream(dev))
     if st != 0:
-        raise Gdn2Error("gdn2_chunk_bwd", st)
+        raise Gdn2Error(fn, st)
     if check_range and int(flag.item()) != 0:
         raise Gdn2RangeError("a chunk's total decay exceeds the backward's range "
                              "(about 83 nats over 64 tokens in some key channel)")
@@ -364,3 +434,34 @@ def block_epilogue(o, gate, weight):
     if st != 0:
         raise Gdn2Error("gdn2_block_epilogue", st)
     return y
+
+
+class _GatedDeltaRule2(torch.autograd.Function):
+    """Autograd wrapper: the training forward keeps the backward's intermediates; the
+    backward consumes them (bf16)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, g, b, w, initial_state, cu_seqlens):
+        o, sN, saved = chunk_fwd_train(q, k, v, g, b, w, initial_state=initial_state,
+                                       cu_seqlens=cu_seqlens)
+        ctx.saved = saved
+        ctx.has_s0 = initial_state is not None
+        ctx.save_for_backward(q, k, v, g, b, w, initial_state, cu_seqlens)
+        return o, sN
+
+    @staticmethod
+    def backward(ctx, do, dsN):
+        q, k, v, g, b, w, s0, cu = ctx.saved_tensors
+        do = do.contiguous() if do is not None else torch.zeros_like(v)
+        dsN = None if dsN is None else dsN.contiguous()
+        dq, dk, dv, dg, db, dw, ds0 = chunk_bwd(q, k, v, g, b, w, do, initial_state=s0,
+                                                d_final_state=dsN, cu_seqlens=cu,
+                                                saved=ctx.saved)
+        ctx.saved = None
+        return dq, dk, dv, dg, db, dw, (ds0 if ctx.has_s0 else None), None
+
+
+def gated_delta_rule2(q, k, v, g, b, w, initial_state=None, cu_seqlens=None):
+    """Differentiable GDN-2 mixer (bf16): returns (o, final_state); gradients flow to q, k,
+    v, g, b, w and the initial state through the library's backward."""
+    return _GatedDeltaRule2.apply(q, k, v, g, b, w, initial_state, cu_seqlens)

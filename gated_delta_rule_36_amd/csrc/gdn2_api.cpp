@@ -106,6 +106,52 @@ size_t bwd_workspace_need(bool varlen, int B, int T, int H, int d_k, int d_v, in
   return gdn2::bwd_workspace_bytes(varlen, B, T, H, d_k, d_v, N);
 }
 
+int chunk_bwd_impl(const void* q, const void* k, const void* v, const void* log_alpha,
+                   const void* b, const void* w, const float* initial_state, const void* d_o,
+                   const float* d_final_state, void* dq, void* dk, void* dv, void* dlog_alpha,
+                   void* db, void* dw, float* d_initial_state, int32_t* range_flag,
+                   const int32_t* cu_seqlens, int B, int T, int H, int d_k, int d_v, int N,
+                   int dtype, void* workspace, size_t workspace_bytes, void* hip_stream,
+                   bool saved) {
+  if (dtype != GDN2_BF16 && dtype != GDN2_F32) return GDN2_INVALID_ARGUMENT;
+  if (B < 0 || T < 0 || H <= 0 || N < 0 || d_k <= 0 || d_v <= 0) return GDN2_INVALID_ARGUMENT;
+  if (cu_seqlens == nullptr) {
+    if (N != B) return GDN2_INVALID_ARGUMENT;
+  } else {
+    if (B != 1) return GDN2_INVALID_ARGUMENT;
+  }
+  if (!split_built(dtype, d_k, d_v)) return GDN2_UNSUPPORTED;
+  const long tokens = (long)B * T;
+  if (tokens > 0 && (!q || !k || !v || !log_alpha || !b || !w || !d_o || !dq || !dk || !dv ||
+                     !dlog_alpha || !db || !dw))
+    return GDN2_INVALID_ARGUMENT;
+  const void* ptrs[17] = {q, k, v, log_alpha, b, w, initial_state, d_o, d_final_state, dq,
+                          dk, dv, dlog_alpha, db, dw, d_initial_state, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return GDN2_INVALID_ARGUMENT;
+  if ((cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) ||
+      (range_flag && (reinterpret_cast<uintptr_t>(range_flag) & 3u) != 0))
+    return GDN2_INVALID_ARGUMENT;
+  if (tokens > (long)INT_MAX) return GDN2_INVALID_ARGUMENT;
+  if (workspace == nullptr ||
+      workspace_bytes < bwd_workspace_need(cu_seqlens != nullptr, B, T, H, d_k, d_v, N))
+    return GDN2_WORKSPACE_TOO_SMALL;
+  if (N == 0) return GDN2_OK;
+  if ((long)N * H * (d_v / 64) > (long)INT_MAX) return GDN2_INVALID_ARGUMENT;
+
+  gdn2::BwdArgs a;
+  gdn2::ChunkArgs& f = a.fwd;
+  f.q = q; f.k = k; f.v = v; f.g = log_alpha; f.b = b; f.w = w;
+  f.s0 = initial_state; f.o = nullptr; f.sN = nullptr; f.cu_seqlens = cu_seqlens;
+  f.B = B; f.T = T; f.H = H; f.d_k = d_k; f.d_v = d_v; f.N = N;
+  f.dtype = dtype; f.nv = 64; f.stream = hip_stream;
+  f.workspace = workspace; f.workspace_bytes = workspace_bytes;
+  a.d_o = d_o; a.d_sN = d_final_state;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dlog_alpha; a.db = db; a.dw = dw;
+  a.d_s0 = d_initial_state; a.range_flag = range_flag; a.saved = saved;
+  return status_of(gdn2::launch_chunk_bwd(a));
+}
+
 }  // namespace
 
 extern "C" {
@@ -161,43 +207,53 @@ int gdn2_chunk_bwd(const void* q, const void* k, const void* v, const void* log_
                    void* db, void* dw, float* d_initial_state, int32_t* range_flag,
                    const int32_t* cu_seqlens, int B, int T, int H, int d_k, int d_v, int N,
                    int dtype, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return chunk_bwd_impl(q, k, v, log_alpha, b, w, initial_state, d_o, d_final_state, dq, dk, dv,
+                        dlog_alpha, db, dw, d_initial_state, range_flag, cu_seqlens, B, T, H, d_k,
+                        d_v, N, dtype, workspace, workspace_bytes, hip_stream, false);
+}
+
+int gdn2_chunk_bwd_saved(const void* q, const void* k, const void* v, const void* log_alpha,
+                         const void* b, const void* w, const float* initial_state,
+                         const void* d_o, const float* d_final_state, void* dq, void* dk,
+                         void* dv, void* dlog_alpha, void* db, void* dw,
+                         float* d_initial_state, int32_t* range_flag,
+                         const int32_t* cu_seqlens, int B, int T, int H, int d_k, int d_v,
+                         int N, int dtype, void* workspace, size_t workspace_bytes,
+                         void* hip_stream) {
+  return chunk_bwd_impl(q, k, v, log_alpha, b, w, initial_state, d_o, d_final_state, dq, dk, dv,
+                        dlog_alpha, db, dw, d_initial_state, range_flag, cu_seqlens, B, T, H, d_k,
+                        d_v, N, dtype, workspace, workspace_bytes, hip_stream, true);
+}
+
+int gdn2_chunk_fwd_train(const void* q, const void* k, const void* v, const void* log_alpha,
+                         const void* b, const void* w, const float* initial_state, void* o,
+                         float* final_state, const int32_t* cu_seqlens, int B, int T, int H,
+                         int d_k, int d_v, int N, int dtype, void* workspace,
+                         size_t workspace_bytes, void* hip_stream) {
   if (dtype != GDN2_BF16 && dtype != GDN2_F32) return GDN2_INVALID_ARGUMENT;
   if (B < 0 || T < 0 || H <= 0 || N < 0 || d_k <= 0 || d_v <= 0) return GDN2_INVALID_ARGUMENT;
-  if (cu_seqlens == nullptr) {
-    if (N != B) return GDN2_INVALID_ARGUMENT;
-  } else {
-    if (B != 1) return GDN2_INVALID_ARGUMENT;
-  }
+  if (cu_seqlens == nullptr ? N != B : B != 1) return GDN2_INVALID_ARGUMENT;
   if (!split_built(dtype, d_k, d_v)) return GDN2_UNSUPPORTED;
   const long tokens = (long)B * T;
-  if (tokens > 0 && (!q || !k || !v || !log_alpha || !b || !w || !d_o || !dq || !dk || !dv ||
-                     !dlog_alpha || !db || !dw))
-    return GDN2_INVALID_ARGUMENT;
-  const void* ptrs[17] = {q, k, v, log_alpha, b, w, initial_state, d_o, d_final_state, dq,
-                          dk, dv, dlog_alpha, db, dw, d_initial_state, workspace};
+  if (tokens > 0 && (!q || !k || !v || !log_alpha || !b || !w || !o)) return GDN2_INVALID_ARGUMENT;
+  const void* ptrs[10] = {q, k, v, log_alpha, b, w, o, initial_state, final_state, workspace};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return GDN2_INVALID_ARGUMENT;
-  if ((cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) ||
-      (range_flag && (reinterpret_cast<uintptr_t>(range_flag) & 3u) != 0))
-    return GDN2_INVALID_ARGUMENT;
+  if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return GDN2_INVALID_ARGUMENT;
   if (tokens > (long)INT_MAX) return GDN2_INVALID_ARGUMENT;
   if (workspace == nullptr ||
       workspace_bytes < bwd_workspace_need(cu_seqlens != nullptr, B, T, H, d_k, d_v, N))
     return GDN2_WORKSPACE_TOO_SMALL;
   if (N == 0) return GDN2_OK;
   if ((long)N * H * (d_v / 64) > (long)INT_MAX) return GDN2_INVALID_ARGUMENT;
-
-  gdn2::BwdArgs a;
-  gdn2::ChunkArgs& f = a.fwd;
+  if (o == nullptr) return GDN2_INVALID_ARGUMENT;  // (tokens == 0 with N > 0: o still required)
+  gdn2::ChunkArgs f;
   f.q = q; f.k = k; f.v = v; f.g = log_alpha; f.b = b; f.w = w;
-  f.s0 = initial_state; f.o = nullptr; f.sN = nullptr; f.cu_seqlens = cu_seqlens;
+  f.s0 = initial_state; f.o = o; f.sN = final_state; f.cu_seqlens = cu_seqlens;
   f.B = B; f.T = T; f.H = H; f.d_k = d_k; f.d_v = d_v; f.N = N;
   f.dtype = dtype; f.nv = 64; f.stream = hip_stream;
   f.workspace = workspace; f.workspace_bytes = workspace_bytes;
-  a.d_o = d_o; a.d_sN = d_final_state;
-  a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dlog_alpha; a.db = db; a.dw = dw;
-  a.d_s0 = d_initial_state; a.range_flag = range_flag;
-  return status_of(gdn2::launch_chunk_bwd(a));
+  return status_of(gdn2::launch_bwd_forward_part(f));
 }
 
 int gdn2_decode_step(const void* q, const void* k, const void* v, const void* log_alpha,

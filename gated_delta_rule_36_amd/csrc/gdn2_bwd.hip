@@ -652,8 +652,11 @@ template <int DK, int DV>
 static hipError_t launch_bwd(const BwdArgs& a) {
   const ChunkArgs& f = a.fwd;
   hipStream_t st = (hipStream_t)f.stream;
-  hipError_t e = launch_bwd_forward_part(f);
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (!a.saved) {
+    e = launch_bwd_forward_part(f);
+    if (e != hipSuccess) return e;
+  }
   constexpr int NV = 64 <= DV ? 64 : DV;
   const int nslices = DV / NV;
   hipLaunchKernelGGL((gdn2_bwd_chain_kernel<DK, DV, NV>), dim3((unsigned)(f.N * f.H * nslices)),

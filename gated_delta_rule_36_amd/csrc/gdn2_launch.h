@@ -134,6 +134,8 @@ struct BwdArgs {
   void *dq, *dk, *dv, *dg, *db, *dw;
   float* d_s0;              // [N, H, d_k, d_v] or null
   int* range_flag;          // device int, set to 1 when a chunk is outside the fast range
+  bool saved = false;       // the workspace already holds the forward's factors, entering
+                            // states and U (written by a training forward): skip that part
 };
 
 hipError_t launch_chunk_fwd(const ChunkArgs& a);

@@ -524,14 +524,18 @@ struct StateShape {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-// STORE (backward's forward pass): no output; instead the state entering every chunk and
-// that chunk's U are stored into the backward workspace (BwdLayout::h, ::ub).
-template <int DK, int DV, int NV, bool STORE>
+// MODE 0: the forward (output o). MODE 1 (the backward's own forward pass): no output;
+// instead the state entering every chunk and that chunk's U are stored into the backward
+// workspace (BwdLayout::h, ::ub). MODE 2 (training forward): both, so that a later backward
+// can skip its forward pass.
+template <int DK, int DV, int NV, int MODE>
 __global__ void __launch_bounds__((StateShape<DK, DV, NV>::NT)) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict__ o,
                   float* sN, const int* __restrict__ cu_seqlens, int T_len, int H,
                   int nslices, int nunits) {
   typedef bf16 T;
+  constexpr bool STORE = MODE != 0;  // entering states and U to the backward workspace
+  constexpr bool OUT = MODE != 1;    // the output o
   using Sh = StateShape<DK, DV, NV>;
   using M = Mma<T>;
   constexpr SplitLayout L(DK, DV);
@@ -666,7 +670,7 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
 #pragma unroll
     for (int i = 0; i < 4 * KSK; ++i) fw[i] = frag((int)L.w, i);
     typename M::frag fq[4 * KSK];
-    if constexpr (!STORE) {
+    if constexpr (OUT) {
 #pragma unroll
       for (int i = 0; i < 4 * KSK; ++i) fq[i] = frag((int)L.q, i);
     }
@@ -674,7 +678,7 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
     typename M::frag fk[2 * NMT], fp[6];
 #pragma unroll
     for (int i = 0; i < 2 * NMT; ++i) fk[i] = frag((int)L.kt, i);
-    if constexpr (!STORE) {
+    if constexpr (OUT) {
 #pragma unroll
       for (int i = 0; i < 6; ++i) fp[i] = frag((int)L.p, i < 2 ? 2 * i : i + 2);  // blocks 0,2,4,5,6,7
     }
@@ -687,14 +691,15 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
       for (int s = 0; s < KSK; ++s) U[R] = M::mma(fw[R * KSK + s], sb[s], U[R]);
     // O = Qbar S + P U
     f4 O[4];
-    if constexpr (!STORE) {
+    if constexpr (OUT) {
 #pragma unroll
       for (int R = 0; R < 4; ++R) {
         O[R] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KSK; ++s) O[R] = M::mma(fq[R * KSK + s], sb[s], O[R]);
       }
-    } else {
+    }
+    if constexpr (STORE) {
 #pragma unroll
       for (int R = 0; R < 4; ++R)
         *reinterpret_cast<uint2*>(bunit + LB.ub + ((ctg * 4 + R) * 64 + lane) * 8) =
@@ -711,7 +716,7 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
       for (int s = 0; s < 2; ++s) acc = M::mma(fk[mt * 2 + s], ub[s], acc);
       S[mt] = acc;
     }
-    if constexpr (!STORE) {
+    if constexpr (OUT) {
 #pragma unroll
       for (int R = 0; R < 4; ++R) {
 #pragma unroll
@@ -726,7 +731,7 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
     // at the end of the next chunk then also covers stores a whole chunk old, instead of
     // stores issued after the loads (which the waits cannot tell apart from them).
     if (ci + 1 < nch) stage_store(smem + ((ci + 1) & 1) * Sh::STAGE);
-    if (!STORE && ci > 0) {
+    if (OUT && ci > 0) {
       const int pv = len - (ci - 1) * C;
       out_store(reinterpret_cast<const T*>(smem + Sh::OFF_O + ((ci - 1) & 1) * Sh::SZ_O),
                 (long)(ci - 1) * C, pv < C ? pv : C);
@@ -734,7 +739,7 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
     stage_load(ci + 2 < nch ? ci + 2 : nch - 1);
     lds_barrier();
   }
-  if (!STORE && nch > 0) {
+  if (OUT && nch > 0) {
     const int pv = len - (nch - 1) * C;
     out_store(reinterpret_cast<const T*>(smem + Sh::OFF_O + ((nch - 1) & 1) * Sh::SZ_O),
               (long)(nch - 1) * C, pv < C ? pv : C);
@@ -781,14 +786,15 @@ static hipError_t launch_split(const ChunkArgs& a) {
   }
   const int nslices = DV / NV;
   const long grid2 = (long)a.N * a.H * nslices;
-  hipLaunchKernelGGL((gdn2_state_kernel<DK, DV, NV, false>), dim3((unsigned)grid2),
+  hipLaunchKernelGGL((gdn2_state_kernel<DK, DV, NV, 0>), dim3((unsigned)grid2),
                      dim3(StateShape<DK, DV, NV>::NT), 0, st, (const char*)a.workspace, a.s0,
                      (bf16*)a.o, a.sN, a.cu_seqlens, a.T, a.H, nslices, a.N * a.H);
   return hipGetLastError();
 }
 
 // Backward's forward part: the factors in the backward layout, then the forward chain that
-// stores every chunk's entering state and U (no output).
+// stores every chunk's entering state and U; with a.o set (training forward) the chain
+// also writes the output and, with a.sN, the final state.
 template <int DK, int DV>
 static hipError_t launch_bwd_forward(const ChunkArgs& a) {
   const bool varlen = a.cu_seqlens != nullptr;
@@ -805,9 +811,11 @@ static hipError_t launch_bwd_forward(const ChunkArgs& a) {
   }
   constexpr int NV = 64 <= DV ? 64 : DV;
   const int nslices = DV / NV;
-  hipLaunchKernelGGL((gdn2_state_kernel<DK, DV, NV, true>), dim3((unsigned)(a.N * a.H * nslices)),
+  auto chain = a.o != nullptr ? gdn2_state_kernel<DK, DV, NV, 2> : gdn2_state_kernel<DK, DV, NV, 1>;
+  hipLaunchKernelGGL(chain, dim3((unsigned)(a.N * a.H * nslices)),
                      dim3(StateShape<DK, DV, NV>::NT), 0, st, (const char*)a.workspace, a.s0,
-                     nullptr, nullptr, a.cu_seqlens, a.T, a.H, nslices, a.N * a.H);
+                     (bf16*)a.o, a.o != nullptr ? a.sN : nullptr, a.cu_seqlens, a.T, a.H, nslices,
+                     a.N * a.H);
   return hipGetLastError();
 }
 

@@ -160,6 +160,37 @@ size_t gdn2_chunk_bwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int
                                       int dtype);
 
 /*
+ * Training forward: the same result as gdn2_chunk_fwd (o, and the final state when
+ * final_state is not NULL), computed by the two-phase kernels while the backward's
+ * intermediates (the chunk factors, every chunk's entering state and U) are kept in
+ * `workspace`, so that gdn2_chunk_bwd_saved can skip the forward recomputation that
+ * gdn2_chunk_bwd performs. Same arguments as gdn2_chunk_fwd, except that o is required and
+ * workspace is required, of at least gdn2_chunk_bwd_workspace_bytes(...) bytes; bf16 only
+ * (GDN2_UNSUPPORTED otherwise). The workspace stays owned by the caller and must not be
+ * written until the matching gdn2_chunk_bwd_saved has run.
+ */
+int gdn2_chunk_fwd_train(const void* q, const void* k, const void* v, const void* log_alpha,
+                         const void* b, const void* w, const float* initial_state, void* o,
+                         float* final_state, const int32_t* cu_seqlens, int B, int T, int H,
+                         int d_k, int d_v, int N, int dtype, void* workspace,
+                         size_t workspace_bytes, void* hip_stream);
+
+/*
+ * gdn2_chunk_bwd on a workspace written by gdn2_chunk_fwd_train with the same inputs,
+ * initial state, cu_seqlens and sizes (the forward recomputation is skipped; nothing checks
+ * that the workspace matches, and a mismatched one gives wrong gradients, never an
+ * out-of-bounds access). Same arguments and errors as gdn2_chunk_bwd.
+ */
+int gdn2_chunk_bwd_saved(const void* q, const void* k, const void* v, const void* log_alpha,
+                         const void* b, const void* w, const float* initial_state,
+                         const void* d_o, const float* d_final_state, void* dq, void* dk,
+                         void* dv, void* dlog_alpha, void* db, void* dw,
+                         float* d_initial_state, int32_t* range_flag,
+                         const int32_t* cu_seqlens, int B, int T, int H, int d_k, int d_v,
+                         int N, int dtype, void* workspace, size_t workspace_bytes,
+                         void* hip_stream);
+
+/*
  * The fused single-kernel path of gdn2_chunk_fwd (no workspace) with an explicit
  * value-slice width: each workgroup carries
  * `value_slice` columns of the state (16, 32, 64 or 128; a divisor of d_v; 16 only with
