@@ -51,9 +51,11 @@ def lib():
         L.gdn2_chunk_fwd_workspace_bytes.restype = _Z
         L.gdn2_chunk_bwd.argtypes = [_P] * 18 + [_I] * 7 + [_P, _Z, _P]
         L.gdn2_chunk_bwd.restype = _I
-        L.gdn2_chunk_bwd_saved.argtypes = [_P] * 18 + [_I] * 7 + [_P, _Z, _P]
+        L.gdn2_chunk_bwd_saved.argtypes = [_P] * 18 + [_I] * 8 + [_P, _Z, _P]
         L.gdn2_chunk_bwd_saved.restype = _I
-        L.gdn2_chunk_fwd_train.argtypes = [_P] * 10 + [_I] * 7 + [_P, _Z, _P]
+        L.gdn2_chunk_bwd_ex.argtypes = [_P] * 18 + [_I] * 8 + [_P, _Z, _P]
+        L.gdn2_chunk_bwd_ex.restype = _I
+        L.gdn2_chunk_fwd_train.argtypes = [_P] * 10 + [_I] * 8 + [_P, _Z, _P]
         L.gdn2_chunk_fwd_train.restype = _I
         L.gdn2_chunk_bwd_workspace_bytes.argtypes = [_I] * 7
         L.gdn2_chunk_bwd_workspace_bytes.restype = _Z
@@ -232,9 +234,9 @@ def chunk_fwd_train(q, k, v, g, b, w, initial_state=None, cu_seqlens=None,
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
     code = _dtype_code(dt)
-    for name, t, d in (("q", q, dk), ("k", k, dk), ("g", g, dk), ("b", b, dk),
-                       ("v", v, dv), ("w", w, dv)):
+    for name, t, d in (("q", q, dk), ("k", k, dk), ("g", g, dk), ("v", v, dv)):
         _check(name, t, (B, T, H, d), dt, dev)
+    layout = _gate_layout(b, w, (B, T, H), dk, dv, dt, dev)
     if cu_seqlens is not None:
         if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != dev or cu_seqlens.dim() != 1:
             raise ValueError("cu_seqlens must be a 1-D int32 tensor on the inputs' device")
@@ -255,12 +257,12 @@ def chunk_fwd_train(q, k, v, g, b, w, initial_state=None, cu_seqlens=None,
     sN = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if output_final_state else None
     st = L.gdn2_chunk_fwd_train(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w),
                                 _ptr(initial_state), _ptr(o), _ptr(sN), _ptr(cu_seqlens), B, T,
-                                H, dk, dv, N, code, _ptr(workspace), workspace.numel(),
+                                H, dk, dv, N, code, layout, _ptr(workspace), workspace.numel(),
                                 _stream(dev))
     if st != 0:
         raise Gdn2Error("gdn2_chunk_fwd_train", st)
     key = _inputs_key((q, k, v, g, b, w) + ((initial_state,) if initial_state is not None else ()),
-                      cu_seqlens)
+                      cu_seqlens) + (layout,)
     return o, sN, SavedForBackward(workspace, key)
 
 
@@ -273,8 +275,9 @@ def chunk_bwd(q, k, v, g, b, w, do, initial_state=None, d_final_state=None, cu_s
     """Gradients of chunk_fwd (bf16).
 
     do: [B, T, H, d_v] gradient of o (input dtype); d_final_state: [N, H, d_k, d_v] fp32 or
-    None. Returns (dq, dk, dv, dg, db, dw, d_initial_state): the first six in the input dtype
-    and shapes, the last fp32 [N, H, d_k, d_v]. With check_range, synchronises once and
+    None. b or w may be scalar gates [B, T, H] (their gradients then have that shape: the sum
+    over the channels). Returns (dq, dk, dv, dg, db, dw, d_initial_state): the first six in the
+    input dtype and shapes, the last fp32 [N, H, d_k, d_v]. With check_range, synchronises once and
     raises Gdn2RangeError when some chunk's total decay is outside the backward's range.
     saved: the SavedForBackward of a chunk_fwd_train call on these same tensors; the
     forward recomputation is then skipped.
@@ -285,12 +288,9 @@ def chunk_bwd(q, k, v, g, b, w, do, initial_state=None, d_final_state=None, cu_s
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
     code = _dtype_code(dt)
-    if b.dim() == 3 or w.dim() == 3:
-        raise ValueError("chunk_bwd takes per-channel gates [B, T, H, d]; scalar gates are "
-                         "supported by the forward and decode calls")
-    for name, t, d in (("q", q, dk), ("k", k, dk), ("g", g, dk), ("b", b, dk),
-                       ("v", v, dv), ("w", w, dv), ("do", do, dv)):
+    for name, t, d in (("q", q, dk), ("k", k, dk), ("g", g, dk), ("v", v, dv), ("do", do, dv)):
         _check(name, t, (B, T, H, d), dt, dev)
+    layout = _gate_layout(b, w, (B, T, H), dk, dv, dt, dev)
     if cu_seqlens is not None:
         if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != dev or cu_seqlens.dim() != 1:
             raise ValueError("cu_seqlens must be a 1-D int32 tensor on the inputs' device")
@@ -306,10 +306,10 @@ def chunk_bwd(q, k, v, g, b, w, do, initial_state=None, d_final_state=None, cu_s
     need = int(L.gdn2_chunk_bwd_workspace_bytes(B, T, H, dk, dv, N, code))
     if need == 0:
         raise ValueError("the backward is built for bf16 with d_k, d_v in {64, 128}")
-    fn, call = "gdn2_chunk_bwd", L.gdn2_chunk_bwd
+    fn, call = "gdn2_chunk_bwd_ex", L.gdn2_chunk_bwd_ex
     if saved is not None:
         key = _inputs_key((q, k, v, g, b, w) + ((initial_state,) if initial_state is not None
-                                                else ()), cu_seqlens)
+                                                else ()), cu_seqlens) + (layout,)
         if key != saved.key:
             raise ValueError("saved was computed from other tensors than these")
         workspace = saved.workspace
@@ -322,7 +322,7 @@ def chunk_bwd(q, k, v, g, b, w, do, initial_state=None, d_final_state=None, cu_s
     st = call(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), _ptr(w),
               _ptr(initial_state), _ptr(do), _ptr(d_final_state),
               *(_ptr(x) for x in grads), _ptr(ds0), _ptr(flag), _ptr(cu_seqlens),
-              B, T, H, dk, dv, N, code, _ptr(workspace), workspace.numel(), _stream(dev))
+              B, T, H, dk, dv, N, code, layout, _ptr(workspace), workspace.numel(), _stream(dev))
     if st != 0:
         raise Gdn2Error(fn, st)
     if check_range and int(flag.item()) != 0:

@@ -112,8 +112,9 @@ int chunk_bwd_impl(const void* q, const void* k, const void* v, const void* log_
                    void* db, void* dw, float* d_initial_state, int32_t* range_flag,
                    const int32_t* cu_seqlens, int B, int T, int H, int d_k, int d_v, int N,
                    int dtype, void* workspace, size_t workspace_bytes, void* hip_stream,
-                   bool saved) {
+                   bool saved, int gate_layout) {
   if (dtype != GDN2_BF16 && dtype != GDN2_F32) return GDN2_INVALID_ARGUMENT;
+  if ((gate_layout & ~kGateMask) != 0) return GDN2_INVALID_ARGUMENT;
   if (B < 0 || T < 0 || H <= 0 || N < 0 || d_k <= 0 || d_v <= 0) return GDN2_INVALID_ARGUMENT;
   if (cu_seqlens == nullptr) {
     if (N != B) return GDN2_INVALID_ARGUMENT;
@@ -144,7 +145,7 @@ int chunk_bwd_impl(const void* q, const void* k, const void* v, const void* log_
   f.q = q; f.k = k; f.v = v; f.g = log_alpha; f.b = b; f.w = w;
   f.s0 = initial_state; f.o = nullptr; f.sN = nullptr; f.cu_seqlens = cu_seqlens;
   f.B = B; f.T = T; f.H = H; f.d_k = d_k; f.d_v = d_v; f.N = N;
-  f.dtype = dtype; f.nv = 64; f.stream = hip_stream;
+  f.dtype = dtype; f.nv = 64; f.stream = hip_stream; f.gate_flags = gate_layout;
   f.workspace = workspace; f.workspace_bytes = workspace_bytes;
   a.d_o = d_o; a.d_sN = d_final_state;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dlog_alpha; a.db = db; a.dw = dw;
@@ -209,7 +210,19 @@ int gdn2_chunk_bwd(const void* q, const void* k, const void* v, const void* log_
                    int dtype, void* workspace, size_t workspace_bytes, void* hip_stream) {
   return chunk_bwd_impl(q, k, v, log_alpha, b, w, initial_state, d_o, d_final_state, dq, dk, dv,
                         dlog_alpha, db, dw, d_initial_state, range_flag, cu_seqlens, B, T, H, d_k,
-                        d_v, N, dtype, workspace, workspace_bytes, hip_stream, false);
+                        d_v, N, dtype, workspace, workspace_bytes, hip_stream, false, 0);
+}
+
+int gdn2_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* log_alpha,
+                      const void* b, const void* w, const float* initial_state, const void* d_o,
+                      const float* d_final_state, void* dq, void* dk, void* dv, void* dlog_alpha,
+                      void* db, void* dw, float* d_initial_state, int32_t* range_flag,
+                      const int32_t* cu_seqlens, int B, int T, int H, int d_k, int d_v, int N,
+                      int dtype, int gate_layout, void* workspace, size_t workspace_bytes,
+                      void* hip_stream) {
+  return chunk_bwd_impl(q, k, v, log_alpha, b, w, initial_state, d_o, d_final_state, dq, dk, dv,
+                        dlog_alpha, db, dw, d_initial_state, range_flag, cu_seqlens, B, T, H, d_k,
+                        d_v, N, dtype, workspace, workspace_bytes, hip_stream, false, gate_layout);
 }
 
 int gdn2_chunk_bwd_saved(const void* q, const void* k, const void* v, const void* log_alpha,
@@ -218,19 +231,20 @@ int gdn2_chunk_bwd_saved(const void* q, const void* k, const void* v, const void
                          void* dv, void* dlog_alpha, void* db, void* dw,
                          float* d_initial_state, int32_t* range_flag,
                          const int32_t* cu_seqlens, int B, int T, int H, int d_k, int d_v,
-                         int N, int dtype, void* workspace, size_t workspace_bytes,
-                         void* hip_stream) {
+                         int N, int dtype, int gate_layout, void* workspace,
+                         size_t workspace_bytes, void* hip_stream) {
   return chunk_bwd_impl(q, k, v, log_alpha, b, w, initial_state, d_o, d_final_state, dq, dk, dv,
                         dlog_alpha, db, dw, d_initial_state, range_flag, cu_seqlens, B, T, H, d_k,
-                        d_v, N, dtype, workspace, workspace_bytes, hip_stream, true);
+                        d_v, N, dtype, workspace, workspace_bytes, hip_stream, true, gate_layout);
 }
 
 int gdn2_chunk_fwd_train(const void* q, const void* k, const void* v, const void* log_alpha,
                          const void* b, const void* w, const float* initial_state, void* o,
                          float* final_state, const int32_t* cu_seqlens, int B, int T, int H,
-                         int d_k, int d_v, int N, int dtype, void* workspace,
+                         int d_k, int d_v, int N, int dtype, int gate_layout, void* workspace,
                          size_t workspace_bytes, void* hip_stream) {
   if (dtype != GDN2_BF16 && dtype != GDN2_F32) return GDN2_INVALID_ARGUMENT;
+  if ((gate_layout & ~kGateMask) != 0) return GDN2_INVALID_ARGUMENT;
   if (B < 0 || T < 0 || H <= 0 || N < 0 || d_k <= 0 || d_v <= 0) return GDN2_INVALID_ARGUMENT;
   if (cu_seqlens == nullptr ? N != B : B != 1) return GDN2_INVALID_ARGUMENT;
   if (!split_built(dtype, d_k, d_v)) return GDN2_UNSUPPORTED;
@@ -251,7 +265,7 @@ int gdn2_chunk_fwd_train(const void* q, const void* k, const void* v, const void
   f.q = q; f.k = k; f.v = v; f.g = log_alpha; f.b = b; f.w = w;
   f.s0 = initial_state; f.o = o; f.sN = final_state; f.cu_seqlens = cu_seqlens;
   f.B = B; f.T = T; f.H = H; f.d_k = d_k; f.d_v = d_v; f.N = N;
-  f.dtype = dtype; f.nv = 64; f.stream = hip_stream;
+  f.dtype = dtype; f.nv = 64; f.stream = hip_stream; f.gate_flags = gate_layout;
   f.workspace = workspace; f.workspace_bytes = workspace_bytes;
   return status_of(gdn2::launch_bwd_forward_part(f));
 }

@@ -281,7 +281,9 @@ struct LocalShape {
   static_assert(TPT * TG == C && VTPT * VTG == C, "token mapping");
 };
 
-template <int DK, int DV>
+// GL: gate layout (kGateBScalar / kGateWScalar bits); a scalar gate's gradient is the sum
+// of its per-channel gradients over the channels it is shared by.
+template <int DK, int DV, int GL>
 __global__ void __launch_bounds__((LocalShape<DK, DV>::NT))
 gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                       const bf16* __restrict__ v, const bf16* __restrict__ g,
@@ -294,6 +296,7 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   typedef bf16 T;
   using Sh = LocalShape<DK, DV>;
   using M = Mma<T>;
+  constexpr bool B_S = (GL & kGateBScalar) != 0, W_S = (GL & kGateWScalar) != 0;
   constexpr BwdLayout LB(DK, DV);
   constexpr int C = Sh::C, NT = Sh::NT, LDV = Sh::LDV, LDK = Sh::LDK, LDT = Sh::LDT;
   constexpr int NVT = Sh::NVT;
@@ -333,7 +336,8 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const int r = tg * Sh::TPT + j;
     if (r < cu.nvalid) {
       const long off = kb0 + (long)r * kstride + cg * 8;
-      rq[j].load(q + off); rk[j].load(k + off); rg[j].load(g + off); rb[j].load(bg + off);
+      rq[j].load(q + off); rk[j].load(k + off); rg[j].load(g + off);
+      if constexpr (B_S) rb[j].load_one(bg + (cu.row + r) * H + cu.h); else rb[j].load(bg + off);
     } else {
       rq[j].zero(); rk[j].zero(); rg[j].zero(); rb[j].zero();
     }
@@ -343,7 +347,8 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const int r = vtg * Sh::VTPT + j;
     if (r < cu.nvalid) {
       const long off = vb0 + (long)r * vstride + vcg * 8;
-      rv[j].load(v + off); rw[j].load(wg + off);
+      rv[j].load(v + off);
+      if constexpr (W_S) rw[j].load_one(wg + (cu.row + r) * H + cu.h); else rw[j].load(wg + off);
     } else {
       rv[j].zero(); rw[j].zero();
     }
@@ -441,13 +446,22 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     z.load(sZ + r * LDV + vcg * 8);
     z.to_float(fz);
     rv[j].to_float(fv);
+    if constexpr (W_S) rw[j].splat();
     rw[j].to_float(fw);
 #pragma unroll
     for (int i = 0; i < 8; ++i) { o1[i] = fz[i] * fw[i]; o2[i] = fz[i] * fv[i]; }
     if (r < cu.nvalid) {
       const long off = vb0 + (long)r * vstride + vcg * 8;
       store8(dv + off, o1);
-      store8(dw + off, o2);
+      if constexpr (!W_S) store8(dw + off, o2);
+    }
+    if constexpr (W_S) {  // sum over the token's d_v channels (VCG adjacent lanes)
+      float sw = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sw += o2[i];
+#pragma unroll
+      for (int m = 1; m < Sh::VCG; m <<= 1) sw += __shfl_xor(sw, m, 64);
+      if (vcg == 0 && r < cu.nvalid) dw[(cu.row + r) * H + cu.h] = from_f<T>(sw);
     }
   }
   lds_barrier();  // sTot (in the M buffers) is consumed; Khat^T, dO, dZ, U, dSn are in LDS
@@ -531,6 +545,7 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       float fq[8], fk[8], fb[8];
       rq[j].to_float(fq);
       rk[j].to_float(fk);
+      if constexpr (B_S) rb[j].splat();  // (also what the elementwise step reads back)
       rb[j].to_float(fb);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -641,8 +656,27 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       };
       put4(dq, outq[Tt]);
       put4(dk, outk[Tt]);
-      put4(db, outb[Tt]);
+      if constexpr (!B_S) put4(db, outb[Tt]);
       put4(dg, dgv[Tt]);
+    }
+  }
+  if constexpr (B_S) {
+    // sum over the token's d_k channels: 4 per lane, the 4 lane groups of a wave, then the
+    // NW waves through LDS (the M buffers are dead here)
+    float* sPart = reinterpret_cast<float*>(smem + Sh::OFF_M1);  // [NW][64]
+#pragma unroll
+    for (int Tt = 0; Tt < 4; ++Tt) {
+      float x = outb[Tt][0] + outb[Tt][1] + outb[Tt][2] + outb[Tt][3];
+      x += __shfl_xor(x, 16, 64);
+      x += __shfl_xor(x, 32, 64);
+      if (g4 == 0) sPart[wave * 64 + 16 * Tt + m16] = x;
+    }
+    lds_barrier();
+    if (tid < C) {
+      float x = 0.f;
+#pragma unroll
+      for (int w = 0; w < Sh::NW; ++w) x += sPart[w * 64 + tid];
+      if (tid < cu.nvalid) db[(cu.row + tid) * H + cu.h] = from_f<T>(x);
     }
   }
 }
@@ -667,7 +701,11 @@ static hipError_t launch_bwd(const BwdArgs& a) {
   if (e != hipSuccess) return e;
   const long nunits = split_slots(f.cu_seqlens != nullptr, f.B, f.T, f.N) * f.H;
   if (nunits > 0) {
-    hipLaunchKernelGGL((gdn2_bwd_local_kernel<DK, DV>), dim3((unsigned)nunits),
+    auto local = f.gate_flags == 3 ? gdn2_bwd_local_kernel<DK, DV, 3>
+                 : f.gate_flags == 2 ? gdn2_bwd_local_kernel<DK, DV, 2>
+                 : f.gate_flags == 1 ? gdn2_bwd_local_kernel<DK, DV, 1>
+                                     : gdn2_bwd_local_kernel<DK, DV, 0>;
+    hipLaunchKernelGGL(local, dim3((unsigned)nunits),
                        dim3(LocalShape<DK, DV>::NT), 0, st, (const bf16*)f.q, (const bf16*)f.k,
                        (const bf16*)f.v, (const bf16*)f.g, (const bf16*)f.b, (const bf16*)f.w,
                        (const bf16*)a.d_o, (const char*)f.workspace, (bf16*)a.dq, (bf16*)a.dk,

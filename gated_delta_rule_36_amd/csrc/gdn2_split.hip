@@ -802,7 +802,11 @@ static hipError_t launch_bwd_forward(const ChunkArgs& a) {
   hipStream_t st = (hipStream_t)a.stream;
   if (nunits > 0) {
     const long grid1 = nunits < cu_count() ? nunits : cu_count();
-    hipLaunchKernelGGL((gdn2_prep_kernel<DK, DV, true, 0>), dim3((unsigned)grid1), dim3(512), 0, st,
+    auto prep = a.gate_flags == 3 ? gdn2_prep_kernel<DK, DV, true, 3>
+                : a.gate_flags == 2 ? gdn2_prep_kernel<DK, DV, true, 2>
+                : a.gate_flags == 1 ? gdn2_prep_kernel<DK, DV, true, 1>
+                                    : gdn2_prep_kernel<DK, DV, true, 0>;
+    hipLaunchKernelGGL(prep, dim3((unsigned)grid1), dim3(512), 0, st,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.g,
                        (const bf16*)a.b, (const bf16*)a.w, (char*)a.workspace, a.cu_seqlens,
                        a.N, a.T, a.H, nunits, 0);

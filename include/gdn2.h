@@ -160,26 +160,41 @@ size_t gdn2_chunk_bwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int
                                       int dtype);
 
 /*
+ * gdn2_chunk_bwd with a gate layout (GDN2_GATE_* bits): a scalar b or w is read as
+ * [B, T, H], and its gradient db or dw is written as [B, T, H] (the sum over the channels
+ * of the per-channel gradient, since the one value is shared by all of them).
+ */
+int gdn2_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* log_alpha,
+                      const void* b, const void* w, const float* initial_state, const void* d_o,
+                      const float* d_final_state, void* dq, void* dk, void* dv, void* dlog_alpha,
+                      void* db, void* dw, float* d_initial_state, int32_t* range_flag,
+                      const int32_t* cu_seqlens, int B, int T, int H, int d_k, int d_v, int N,
+                      int dtype, int gate_layout, void* workspace, size_t workspace_bytes,
+                      void* hip_stream);
+
+/*
  * Training forward: the same result as gdn2_chunk_fwd (o, and the final state when
  * final_state is not NULL), computed by the two-phase kernels while the backward's
  * intermediates (the chunk factors, every chunk's entering state and U) are kept in
  * `workspace`, so that gdn2_chunk_bwd_saved can skip the forward recomputation that
  * gdn2_chunk_bwd performs. Same arguments as gdn2_chunk_fwd, except that o is required and
- * workspace is required, of at least gdn2_chunk_bwd_workspace_bytes(...) bytes; bf16 only
+ * workspace is required, of at least gdn2_chunk_bwd_workspace_bytes(...) bytes, and the
+ * gate layout (GDN2_GATE_* bits, as for gdn2_chunk_fwd_ex) is given; bf16 only
  * (GDN2_UNSUPPORTED otherwise). The workspace stays owned by the caller and must not be
  * written until the matching gdn2_chunk_bwd_saved has run.
  */
 int gdn2_chunk_fwd_train(const void* q, const void* k, const void* v, const void* log_alpha,
                          const void* b, const void* w, const float* initial_state, void* o,
                          float* final_state, const int32_t* cu_seqlens, int B, int T, int H,
-                         int d_k, int d_v, int N, int dtype, void* workspace,
+                         int d_k, int d_v, int N, int dtype, int gate_layout, void* workspace,
                          size_t workspace_bytes, void* hip_stream);
 
 /*
  * gdn2_chunk_bwd on a workspace written by gdn2_chunk_fwd_train with the same inputs,
  * initial state, cu_seqlens and sizes (the forward recomputation is skipped; nothing checks
  * that the workspace matches, and a mismatched one gives wrong gradients, never an
- * out-of-bounds access). Same arguments and errors as gdn2_chunk_bwd.
+ * out-of-bounds access). The arguments of gdn2_chunk_bwd_ex, with its errors; the gate layout
+ * must be the training forward's.
  */
 int gdn2_chunk_bwd_saved(const void* q, const void* k, const void* v, const void* log_alpha,
                          const void* b, const void* w, const float* initial_state,
@@ -187,8 +202,8 @@ int gdn2_chunk_bwd_saved(const void* q, const void* k, const void* v, const void
                          void* dv, void* dlog_alpha, void* db, void* dw,
                          float* d_initial_state, int32_t* range_flag,
                          const int32_t* cu_seqlens, int B, int T, int H, int d_k, int d_v,
-                         int N, int dtype, void* workspace, size_t workspace_bytes,
-                         void* hip_stream);
+                         int N, int dtype, int gate_layout, void* workspace,
+                         size_t workspace_bytes, void* hip_stream);
 
 /*
  * The fused single-kernel path of gdn2_chunk_fwd (no workspace) with an explicit

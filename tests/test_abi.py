@@ -216,12 +216,15 @@ def test_train_pair_error_paths():
     L = _lib.lib()
     base = [FAKE] * 6 + [None, FAKE, None, None]
     # no workspace / too small
-    assert L.gdn2_chunk_fwd_train(*base, 2, 64, 4, 128, 128, 2, 0, None, 0, None) == 3
-    assert L.gdn2_chunk_fwd_train(*base, 2, 64, 4, 128, 128, 2, 0, FAKE, 100, None) == 3
-    # fp32 is not built for the training pair; o is required
-    assert L.gdn2_chunk_fwd_train(*base, 2, 64, 4, 128, 128, 2, 1, FAKE, 1 << 40, None) == 2
+    assert L.gdn2_chunk_fwd_train(*base, 2, 64, 4, 128, 128, 2, 0, 0, None, 0, None) == 3
+    assert L.gdn2_chunk_fwd_train(*base, 2, 64, 4, 128, 128, 2, 0, 0, FAKE, 100, None) == 3
+    # fp32 is not built for the training pair; o is required; unknown layout bits
+    assert L.gdn2_chunk_fwd_train(*base, 2, 64, 4, 128, 128, 2, 1, 0, FAKE, 1 << 40, None) == 2
     nob = [FAKE] * 6 + [None, None, None, None]
-    assert L.gdn2_chunk_fwd_train(*nob, 2, 64, 4, 128, 128, 2, 0, FAKE, 1 << 40, None) == 1
+    assert L.gdn2_chunk_fwd_train(*nob, 2, 64, 4, 128, 128, 2, 0, 0, FAKE, 1 << 40, None) == 1
+    assert L.gdn2_chunk_fwd_train(*base, 2, 64, 4, 128, 128, 2, 0, 4, FAKE, 1 << 40, None) == 1
     args = [FAKE] * 6 + [None, FAKE, None] + [FAKE] * 6 + [None, None, None]
-    assert L.gdn2_chunk_bwd_saved(*args, 2, 64, 4, 128, 128, 2, 0, None, 0, None) == 3
-    assert L.gdn2_chunk_bwd_saved(*args, 2, 64, 4, 96, 128, 2, 0, FAKE, 1 << 40, None) == 2
+    assert L.gdn2_chunk_bwd_saved(*args, 2, 64, 4, 128, 128, 2, 0, 0, None, 0, None) == 3
+    assert L.gdn2_chunk_bwd_saved(*args, 2, 64, 4, 96, 128, 2, 0, 0, FAKE, 1 << 40, None) == 2
+    assert L.gdn2_chunk_bwd_ex(*args, 2, 64, 4, 128, 128, 2, 0, 8, FAKE, 1 << 40, None) == 1
+    assert L.gdn2_chunk_bwd_ex(*args, 2, 64, 4, 128, 128, 2, 0, 3, None, 0, None) == 3

@@ -111,3 +111,66 @@ def test_decode_tokens_scalar_gates(layout):
     o_ref, _, pool_ref = gdn2_decode_tokens(pool, *(rx[n] for n in NAMES), indices=idx)
     assert_close("o", host64(o), o_ref, TOL["bf16"])
     assert_close("pool", host64(pool_t), pool_ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("layout", ["b", "w", "bw"])
+@pytest.mark.parametrize("saved", [False, True])
+def test_backward_scalar_gates(layout, saved):
+    """Gradients with scalar gates: a shared gate's gradient is the channel sum of the
+    oracle's per-channel gradient of the broadcast gate; through the recomputing backward
+    and through the training forward / saved backward pair."""
+    import gated_delta_rule_36_amd as G
+    from gdn2_inputs import round_to_bf16
+    from oracle import gdn2_backward
+    B, T, H, dk, dv = 2, 150, 2, 128, 64
+    x = make_inputs(B, T, H, dk, dv, "bf16", seed=61, s0_std=0.02)
+    gx, rx = _scalarise(x, layout, (B, T, H), seed=63)
+    rng = np.random.default_rng(65)
+    do = round_to_bf16(rng.normal(size=(B, T, H, dv)).astype(np.float32))
+    dsn = (rng.normal(size=(B, H, dk, dv)) * 0.1).astype(np.float32)
+    say("backward scalar gates", layout, "saved" if saved else "recompute")
+    t = {n: dev_tensor(gx[n], "bf16") for n in NAMES}
+    s0 = torch.from_numpy(x["s0"]).cuda()
+    do_t, dsn_t = dev_tensor(do, "bf16"), torch.from_numpy(dsn).cuda()
+    sv = None
+    if saved:
+        o, sN, sv = G.chunk_fwd_train(*(t[n] for n in NAMES), initial_state=s0)
+        torch.cuda.synchronize()
+        o_ref, s_ref = gdn2_forward(*(rx[n] for n in NAMES), s0=x["s0"])
+        assert_close("o", host64(o), o_ref, TOL["bf16"])
+        assert_close("S_final", host64(sN), s_ref, TOL["bf16"])
+    grads = G.chunk_bwd(*(t[n] for n in NAMES), do_t, initial_state=s0, d_final_state=dsn_t,
+                        saved=sv)
+    torch.cuda.synchronize()
+    ref = list(gdn2_backward(*(rx[n] for n in NAMES), do, dS_final=dsn, s0=x["s0"]))
+    sb, sw = LAYOUTS[layout]
+    if sb:
+        ref[4] = ref[4].sum(-1)
+    if sw:
+        ref[5] = ref[5].sum(-1)
+    for name, a, r in zip(("dq", "dk", "dv", "dg", "db", "dw", "ds0"), grads, ref):
+        assert tuple(a.shape) == r.shape, name
+        assert_close(name, host64(a), r, TOL["bf16"])
+
+
+def test_backward_scalar_gates_varlen():
+    import gated_delta_rule_36_amd as G
+    from gdn2_inputs import round_to_bf16
+    from oracle import gdn2_backward
+    lens = [1, 64, 0, 100, 33]
+    T = sum(lens)
+    x = make_inputs(1, T, 2, 64, 128, "bf16", seed=71, lengths=lens, s0_std=0.02)
+    gx, rx = _scalarise(x, "bw", (1, T, 2), seed=73)
+    rng = np.random.default_rng(75)
+    do = round_to_bf16(rng.normal(size=(1, T, 2, 128)).astype(np.float32))
+    say("backward scalar gates varlen", lens)
+    t = {n: dev_tensor(gx[n], "bf16") for n in NAMES}
+    cu = torch.from_numpy(x["cu_seqlens"]).cuda()
+    grads = G.chunk_bwd(*(t[n] for n in NAMES), dev_tensor(do, "bf16"),
+                        initial_state=torch.from_numpy(x["s0"]).cuda(), cu_seqlens=cu)
+    torch.cuda.synchronize()
+    ref = list(gdn2_backward(*(rx[n] for n in NAMES), do, s0=x["s0"], cu_seqlens=x["cu_seqlens"]))
+    ref[4] = ref[4].sum(-1)
+    ref[5] = ref[5].sum(-1)
+    for name, a, r in zip(("dq", "dk", "dv", "dg", "db", "dw", "ds0"), grads, ref):
+        assert_close(name, host64(a), r, TOL["bf16"])
