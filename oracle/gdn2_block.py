@@ -10,7 +10,7 @@ normalisation); the decay, erase and write gates have branches of their own, per
 output is scaled by an RMSNorm with a SiLU gate. The linear projections are plain GEMMs and
 are not part of this module.
 
-Readings where the page is silent (stated in the design doc's list of readings):
+Readings where the page is silent:
   * conv: causal depthwise convolution of width 4 over the tokens of each sequence (no bias;
     a sequence starts from zero history, so the convolution never crosses a cu_seqlens
     boundary): y[t, c] = sum_{j=0..3} weight[c, j] * x[t - 3 + j, c].
