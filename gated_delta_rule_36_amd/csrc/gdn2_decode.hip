@@ -9,7 +9,9 @@
 // else (six d-vectors of inputs, one d_v output) is negligible traffic. The kernel is
 // bandwidth-bound: one workgroup of 256 threads per (sequence, head), the state slice is
 // held in registers between the read and the write, float4 accesses make every wave
-// touch whole contiguous rows.
+// touch whole contiguous rows, and the state is streamed with non-temporal loads and
+// stores (read once and written once per step, it would only evict other data from the
+// caches).
 
 #include "gdn2_device.h"
 #include "gdn2_launch.h"
@@ -38,7 +40,7 @@ gdn2_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   f4 s[RPT];
 #pragma unroll
   for (int j = 0; j < RPT; ++j)
-    s[j] = *reinterpret_cast<const f4*>(S + (long)(rg + j * RG) * DV + 4 * cg);
+    s[j] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(S + (long)(rg + j * RG) * DV + 4 * cg));
 
   for (int c = tid; c < DK; c += NT) {
     const float kk = to_f(k[unit * DK + c]);
@@ -88,7 +90,7 @@ gdn2_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
 #pragma unroll
   for (int j = 0; j < RPT; ++j) {
     const int c = rg + j * RG;
-    *reinterpret_cast<f4*>(S + (long)c * DV + 4 * cg) = s[j] + s_k[c] * d;
+    __builtin_nontemporal_store(s[j] + s_k[c] * d, reinterpret_cast<f4*>(S + (long)c * DV + 4 * cg));
   }
 }
 
@@ -127,7 +129,7 @@ gdn2_decode_tokens_kernel(const T* __restrict__ q, const T* __restrict__ k,
   f4 s[RPT];
 #pragma unroll
   for (int j = 0; j < RPT; ++j)
-    s[j] = *reinterpret_cast<const f4*>(S + (long)(rg + j * RG) * DV + 4 * cg);
+    s[j] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(S + (long)(rg + j * RG) * DV + 4 * cg));
 
   for (int t = 0; t < L; ++t) {
     const int par = t & 1;
@@ -178,7 +180,8 @@ gdn2_decode_tokens_kernel(const T* __restrict__ q, const T* __restrict__ k,
     if (step_states != nullptr) {
       float* St = step_states + tk * DK * DV;
 #pragma unroll
-      for (int j = 0; j < RPT; ++j) *reinterpret_cast<f4*>(St + (long)(rg + j * RG) * DV + 4 * cg) = s[j];
+      for (int j = 0; j < RPT; ++j)
+        __builtin_nontemporal_store(s[j], reinterpret_cast<f4*>(St + (long)(rg + j * RG) * DV + 4 * cg));
     }
     if (t + 1 == ncommit) {
 #pragma unroll
