@@ -38,12 +38,21 @@ __device__ __forceinline__ float softplus_f(float x) {
   return fmaxf(x, 0.f) + lp;
 }
 
+// Outputs are written once and never read back by these kernels: non-temporal stores.
 template <typename T>
 __device__ __forceinline__ void store8_t(T* p, const float* f);
 template <>
-__device__ __forceinline__ void store8_t<bf16>(bf16* p, const float* f) { store8(p, f); }
+__device__ __forceinline__ void store8_t<bf16>(bf16* p, const float* f) {
+  bf16x8 v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = static_cast<bf16>(f[i]);
+  __builtin_nontemporal_store(v, reinterpret_cast<bf16x8*>(p));
+}
 template <>
-__device__ __forceinline__ void store8_t<float>(float* p, const float* f) { store8(p, f); }
+__device__ __forceinline__ void store8_t<float>(float* p, const float* f) {
+  __builtin_nontemporal_store(f4{f[0], f[1], f[2], f[3]}, reinterpret_cast<f4*>(p));
+  __builtin_nontemporal_store(f4{f[4], f[5], f[6], f[7]}, reinterpret_cast<f4*>(p) + 1);
+}
 
 // 8 consecutive channels in the storage dtype, as ext-vector registers (arrays of these stay
 // in VGPRs once the loops that index them are unrolled).

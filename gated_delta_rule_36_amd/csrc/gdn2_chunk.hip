@@ -289,7 +289,10 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
     for (int j = 0; j < CPT; ++j) {
       const int idx = tid + j * NT;
       const int r = idx / (NV / EPC), cc = idx % (NV / EPC);
-      if (r < on) *reinterpret_cast<uint4*>(ob + (long)(oc0 + r) * vstride + cc * EPC) = ostage[j];
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      if (r < on)  // o is written once and not read back here: non-temporal
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, ostage[j]),
+                                    reinterpret_cast<u32x4*>(ob + (long)(oc0 + r) * vstride + cc * EPC));
     }
   };
 
