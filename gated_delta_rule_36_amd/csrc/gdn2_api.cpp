@@ -48,8 +48,14 @@ int pick_split_nv(int d_v, long chains) {
   return chains * (d_v / 64) >= kTargetWorkgroups ? 64 : 32;
 }
 
+gdn2::SegPlan seg_plan_for(bool varlen, int T, int H, int d_v, int N) {
+  return gdn2::seg_plan(varlen, T, H, d_v, N, kTargetWorkgroups);
+}
+
 size_t workspace_need(bool varlen, int B, int T, int H, int d_k, int d_v, int N) {
-  return gdn2::split_workspace_bytes(varlen, B, T, H, d_k, d_v, N);
+  const gdn2::SegPlan sp = seg_plan_for(varlen, T, H, d_v, N);
+  return gdn2::split_workspace_bytes(varlen, B, T, H, d_k, d_v, N) +
+         gdn2::seg_buffer_bytes(sp, N, H, d_k, d_v);
 }
 
 int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* log_alpha,
@@ -90,7 +96,11 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* log_
   a.workspace = split ? workspace : nullptr;
   a.workspace_bytes = split ? workspace_bytes : 0;
   if (split) {
-    a.nv = pick_split_nv(d_v, (long)N * H);
+    const gdn2::SegPlan sp = seg_plan_for(cu_seqlens != nullptr, T, H, d_v, N);
+    a.nseg = sp.nseg;
+    a.seg_chunks = sp.seg_chunks;
+    a.nv = pick_split_nv(d_v, (long)N * H * sp.nseg);
+    if ((long)N * H * sp.nseg * ((d_v + d_k) / 64) > (long)INT_MAX) return GDN2_INVALID_ARGUMENT;
     if ((long)N * H * (d_v / a.nv) > (long)INT_MAX) return GDN2_INVALID_ARGUMENT;
     return status_of(gdn2::launch_chunk_fwd_split(a));
   }

@@ -23,6 +23,8 @@ struct ChunkArgs {
   void* workspace;        // two-phase path only: per-chunk factors (see SplitLayout)
   size_t workspace_bytes;
   int gate_flags = 0;     // kGateBScalar | kGateWScalar
+  int nseg = 1;           // two-phase path: segments per sequence (see SegPlan)
+  int seg_chunks = 0;     // chunks per segment when nseg > 1
 };
 
 struct DecodeArgs {
@@ -84,6 +86,32 @@ struct SplitLayout {
 inline long split_slots(bool varlen, int B, int T, int N) {
   const int C = SplitLayout::kChunk;
   return varlen ? (long)T / C + N : (long)B * ((T + C - 1) / C);
+}
+// Segments of long sequences (two-phase path, fixed-length batches): when the recurrence
+// has fewer chains (sequence x head x 64 value columns) than `target` workgroups, each
+// sequence's chunks are cut into nseg segments of seg_chunks (at least 8 chunks each) that
+// run in parallel: a transfer pass per segment, a short scan of segment start states,
+// then the outputs per segment.
+struct SegPlan {
+  int nseg, seg_chunks;
+};
+inline SegPlan seg_plan(bool varlen, int T, int H, int d_v, int N, int target) {
+  const int C = SplitLayout::kChunk;
+  const int nch = T > 0 ? (T + C - 1) / C : 0;
+  const long chains = (long)N * H * (d_v / 64 > 0 ? d_v / 64 : 1);
+  if (varlen || N <= 0 || chains <= 0 || chains >= target || nch < 16) return SegPlan{1, nch};
+  const long want = (target + chains - 1) / chains;
+  const int maxseg = nch / 8;
+  const int p = (int)(want < maxseg ? want : maxseg);
+  if (p <= 1) return SegPlan{1, nch};
+  const int sc = (nch + p - 1) / p;
+  return SegPlan{(nch + sc - 1) / sc, sc};
+}
+// Segment buffers after the factors: end states [N | M] of the transfer pass
+// ([units][d_k][d_v + d_k] fp32) and the segment start states ([units][d_k][d_v] fp32).
+inline size_t seg_buffer_bytes(const SegPlan& sp, int N, int H, int d_k, int d_v) {
+  if (sp.nseg <= 1) return 0;
+  return 256 + (size_t)N * H * sp.nseg * d_k * (size_t)(2 * d_v + d_k) * 4;
 }
 inline size_t split_workspace_bytes(bool varlen, int B, int T, int H, int d_k, int d_v, int N) {
   return (size_t)split_slots(varlen, B, T, N) * H * SplitLayout(d_k, d_v).bytes;

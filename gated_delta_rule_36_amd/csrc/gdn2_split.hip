@@ -527,15 +527,23 @@ struct StateShape {
 // MODE 0: the forward (output o). MODE 1 (the backward's own forward pass): no output;
 // instead the state entering every chunk and that chunk's U are stored into the backward
 // workspace (BwdLayout::h, ::ub). MODE 2 (training forward): both, so that a later backward
-// can skip its forward pass.
+// can skip its forward pass. MODE 3 (segment transfer pass of a long sequence): no output;
+// the columns are [d_v value columns | d_k identity columns]: the value columns run from a
+// zero state, the identity columns from the identity with U~ = 0 (so they carry the
+// segment's product of chunk transitions Diag(gamma) - Kt^T W), and the segment's end
+// state [N | M] is written to ebuf.
+// Segments: a sequence's chunks are cut into nseg runs of seg_chunks (the last may be
+// shorter); a unit is (sequence, head, segment), its start state is s0[unit] (MODE 0; the
+// combine kernel's output when nseg > 1) and only the last segment writes sN.
 template <int DK, int DV, int NV, int MODE>
 __global__ void __launch_bounds__((StateShape<DK, DV, NV>::NT)) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict__ o,
                   float* sN, const int* __restrict__ cu_seqlens, int T_len, int H,
-                  int nslices, int nunits) {
+                  int nslices, int nunits, int nseg, int seg_chunks, float* __restrict__ ebuf) {
   typedef bf16 T;
-  constexpr bool STORE = MODE != 0;  // entering states and U to the backward workspace
-  constexpr bool OUT = MODE != 1;    // the output o
+  constexpr bool XFER = MODE == 3;
+  constexpr bool STORE = MODE == 1 || MODE == 2;  // entering states and U to the backward workspace
+  constexpr bool OUT = MODE == 0 || MODE == 2;    // the output o
   using Sh = StateShape<DK, DV, NV>;
   using M = Mma<T>;
   constexpr SplitLayout L(DK, DV);
@@ -555,10 +563,13 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
   const int gsz = min(8, nunits - grp * 8);
   const int gi = blockIdx.x - grp * 8 * nslices;
   const int slice = gi / gsz;
-  const int nh = grp * 8 + gi % gsz;
+  const int unit_id = grp * 8 + gi % gsz;  // (sequence * H + head) * nseg + segment
+  const int seg = unit_id % nseg;
+  const int nh = unit_id / nseg;
   const int h = nh % H;
   const int n = nh / H;
-  const int col0 = slice * NV;
+  const int col0 = slice * NV;              // MODE 3: within [d_v value | d_k identity] columns
+  const bool ident = XFER && col0 >= DV;    // this slice carries transfer (identity) columns
 
   long row0, slot0;
   int len;
@@ -574,6 +585,13 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
     len = T_len;
     slot0 = (long)n * ((T_len + C - 1) / C);
   }
+  {  // this unit's segment of the sequence
+    const int cbeg = seg * seg_chunks;
+    row0 += (long)cbeg * C;
+    slot0 += cbeg;
+    const int rest = len - cbeg * C;
+    len = rest < 0 ? 0 : (nseg > 1 && rest > seg_chunks * C ? seg_chunks * C : rest);
+  }
   const int nch = (len + C - 1) / C;
   const long vstride = (long)H * DV;
   T* ob = o + row0 * vstride + (long)h * DV + col0;
@@ -581,12 +599,18 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
   // state: tile mt holds key rows [16mt, 16mt+16), column col0 + 16*wave + m16; lane holds
   // rows 16mt + 4*g4 + i
   f4 S[NMT];
-  const long sbase = ((long)n * H + h) * DK * DV + col0 + 16 * wave + m16;
+  const long sbase = ((long)n * H + h) * DK * DV + col0 + 16 * wave + m16;       // sN
+  const long s0base = (long)unit_id * DK * DV + col0 + 16 * wave + m16;           // s0[unit]
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      S[mt][i] = (s0 != nullptr) ? s0[sbase + (long)(16 * mt + 4 * g4 + i) * DV] : 0.f;
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * mt + 4 * g4 + i;
+      if constexpr (XFER)
+        S[mt][i] = (ident && row == col0 - DV + 16 * wave + m16) ? 1.f : 0.f;
+      else
+        S[mt][i] = (s0 != nullptr) ? s0[s0base + (long)row * DV] : 0.f;
+    }
 
   // Staging of the chunk operands: global -> registers -> LDS, one chunk ahead: at the end
   // of chunk c the registers (chunk c+1) go to the LDS buffer that chunk c-1 used and are
@@ -597,7 +621,7 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
   // workspace offset of staged piece p: [-W | Qbar | Kt | P] as is, then this slice's U~
   // tiles, then gamma (selects, no branches)
   static_assert(Sh::OFF_U == (int)L.u, "staged prefix matches the workspace prefix");
-  const int u_shift = slice * Sh::SZ_U;
+  const int u_shift = (XFER && ident ? 0 : slice) * Sh::SZ_U;  // identity slices: unused
   auto piece_src = [&](int p, long chunk) -> const u32x4* {
     const char* unit = ws + ((slot0 + chunk) * H + h) * UNIT;
     const int off = p * 16 + (p >= Sh::OFF_U / 16 && p < Sh::OFF_G / 16 ? u_shift : 0) +
@@ -662,7 +686,7 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
       const bf16x4 ut = *reinterpret_cast<const bf16x4*>(B + Sh::OFF_U + ((wave * 4 + R) * 64 + lane) * 8);
-      U[R] = f4{to_f(ut[0]), to_f(ut[1]), to_f(ut[2]), to_f(ut[3])};
+      U[R] = ident ? f4{0.f, 0.f, 0.f, 0.f} : f4{to_f(ut[0]), to_f(ut[1]), to_f(ut[2]), to_f(ut[3])};
     }
     // Fragments are read from LDS in batches ahead of their products, so that many reads
     // are in flight at once (one wave per SIMD: nothing else hides LDS latency).
@@ -744,11 +768,73 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
     out_store(reinterpret_cast<const T*>(smem + Sh::OFF_O + ((nch - 1) & 1) * Sh::SZ_O),
               (long)(nch - 1) * C, pv < C ? pv : C);
   }
-  if (sN != nullptr) {
+  if constexpr (XFER) {  // the segment's end state [N | M] (rows d_k, d_v + d_k columns)
+    constexpr int LE = DV + DK;
+    float* E = ebuf + (long)unit_id * DK * LE + col0 + 16 * wave + m16;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) E[(long)(16 * mt + 4 * g4 + i) * LE] = S[mt][i];
+  } else if (sN != nullptr && seg == nseg - 1) {
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) sN[sbase + (long)(16 * mt + 4 * g4 + i) * DV] = S[mt][i];
+  }
+}
+
+// Segment start states of a long sequence: S_0 = the sequence's initial state (or 0) and
+// S_{s+1} = M_s S_s + N_s, with [N_s | M_s] the end state of segment s's transfer pass.
+// One workgroup per (sequence, head, 16 value columns); four waves, each owning d_k / 64 of
+// the 16-row tiles; products in fp32 (16x16x4 MFMA), S exchanged through LDS every step.
+template <int DK, int DV>
+__global__ void __launch_bounds__(256)
+gdn2_seg_combine_kernel(const float* __restrict__ ebuf, const float* __restrict__ s0,
+                        float* __restrict__ sbuf, int H, int nseg) {
+  constexpr int LE = DV + DK, NRT = DK / 16, RPW = NRT / 4;  // row tiles, per wave
+  __shared__ float sS[DK][16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m16 = lane & 15, g4 = lane >> 4;
+  const int ct = blockIdx.x % (DV / 16);
+  const int nh = blockIdx.x / (DV / 16);  // sequence * H + head
+  const int c = 16 * ct + m16;            // this lane's value column
+  f4 S[RPW];
+#pragma unroll
+  for (int t = 0; t < RPW; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * (wave * RPW + t) + 4 * g4 + i;
+      S[t][i] = s0 != nullptr ? s0[((long)nh * DK + row) * DV + c] : 0.f;
+    }
+  for (int s = 0; s < nseg; ++s) {
+    const long unit = (long)nh * nseg + s;
+    float* out = sbuf + unit * DK * DV;
+    const float* E = ebuf + unit * DK * LE;
+#pragma unroll
+    for (int t = 0; t < RPW; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * (wave * RPW + t) + 4 * g4 + i;
+        out[(long)row * DV + c] = S[t][i];
+        sS[row][m16] = S[t][i];
+      }
+    __syncthreads();
+    if (s + 1 < nseg) {
+#pragma unroll
+      for (int t = 0; t < RPW; ++t) {
+        const int rt = wave * RPW + t;
+        f4 acc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = E[(long)(16 * rt + 4 * g4 + i) * LE + c];  // N_s
+        for (int k0 = 0; k0 < DK; k0 += 4) {
+          const float a = E[(long)(16 * rt + m16) * LE + DV + k0 + g4];  // M_s[row][k]
+          const float b = sS[k0 + g4][m16];                               // S_s[k][col]
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+        }
+        S[t] = acc;
+      }
+    }
+    __syncthreads();  // sS is rewritten next step
   }
 }
 
@@ -785,10 +871,35 @@ static hipError_t launch_split(const ChunkArgs& a) {
     if (e != hipSuccess) return e;
   }
   const int nslices = DV / NV;
+  if (a.nseg > 1) {
+    // long sequences: transfer pass per segment, start states by a scan, outputs per segment
+    const int nseg = a.nseg;
+    const long units = (long)a.N * a.H * nseg;
+    const size_t base = split_workspace_bytes(false, a.B, a.T, a.H, DK, DV, a.N);
+    float* ebuf = reinterpret_cast<float*>((char*)a.workspace + (base + 255) / 256 * 256);
+    float* sbuf = ebuf + units * DK * (DV + DK);
+    constexpr int NVX = 64;
+    const int xslices = (DV + DK) / NVX;
+    hipLaunchKernelGGL((gdn2_state_kernel<DK, DV, NVX, 3>), dim3((unsigned)(units * xslices)),
+                       dim3(StateShape<DK, DV, NVX>::NT), 0, st, (const char*)a.workspace,
+                       nullptr, nullptr, nullptr, nullptr, a.T, a.H, xslices, (int)units, nseg,
+                       a.seg_chunks, ebuf);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gdn2_seg_combine_kernel<DK, DV>), dim3((unsigned)((long)a.N * a.H * (DV / 16))),
+                       dim3(256), 0, st, ebuf, a.s0, sbuf, a.H, nseg);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gdn2_state_kernel<DK, DV, NV, 0>), dim3((unsigned)(units * nslices)),
+                       dim3(StateShape<DK, DV, NV>::NT), 0, st, (const char*)a.workspace, sbuf,
+                       (bf16*)a.o, a.sN, nullptr, a.T, a.H, nslices, (int)units, nseg,
+                       a.seg_chunks, nullptr);
+    return hipGetLastError();
+  }
   const long grid2 = (long)a.N * a.H * nslices;
   hipLaunchKernelGGL((gdn2_state_kernel<DK, DV, NV, 0>), dim3((unsigned)grid2),
                      dim3(StateShape<DK, DV, NV>::NT), 0, st, (const char*)a.workspace, a.s0,
-                     (bf16*)a.o, a.sN, a.cu_seqlens, a.T, a.H, nslices, a.N * a.H);
+                     (bf16*)a.o, a.sN, a.cu_seqlens, a.T, a.H, nslices, a.N * a.H, 1, 0, nullptr);
   return hipGetLastError();
 }
 
@@ -819,7 +930,7 @@ static hipError_t launch_bwd_forward(const ChunkArgs& a) {
   hipLaunchKernelGGL(chain, dim3((unsigned)(a.N * a.H * nslices)),
                      dim3(StateShape<DK, DV, NV>::NT), 0, st, (const char*)a.workspace, a.s0,
                      (bf16*)a.o, a.o != nullptr ? a.sN : nullptr, a.cu_seqlens, a.T, a.H, nslices,
-                     a.N * a.H);
+                     a.N * a.H, 1, 0, nullptr);
   return hipGetLastError();
 }
 

@@ -81,7 +81,10 @@ def test_workspace_bytes():
     assert unit128 == 74240
     # fixed length: B * ceil(T / 64) slots; packed: floor(T / 64) + N; the larger of the two
     assert L.gdn2_chunk_fwd_workspace_bytes(2, 64, 4, 128, 128, 2, 0) == (2 + 2) * 4 * unit128
-    assert L.gdn2_chunk_fwd_workspace_bytes(1, 2048, 16, 128, 128, 1, 0) == 33 * 16 * unit128
+    # one long sequence with 32 chains (16 heads x 2 value slices) < 256: 4 segments of 8
+    # chunks, whose end states [N | M] and start states follow the factors (fp32)
+    seg = 256 + 1 * 16 * 4 * 128 * (2 * 128 + 128) * 4
+    assert L.gdn2_chunk_fwd_workspace_bytes(1, 2048, 16, 128, 128, 1, 0) == 32 * 16 * unit128 + seg
     assert L.gdn2_chunk_fwd_workspace_bytes(8, 2048, 16, 128, 128, 8, 0) == (256 + 8) * 16 * unit128
     assert L.gdn2_chunk_fwd_workspace_bytes(64, 100, 1, 128, 128, 64, 0) == (100 + 64) * unit128
     unit64 = 4 * 2 * 1024 * 3 + 8 * 1024 + 4 * 4 * 512 + 256

@@ -295,3 +295,28 @@ def test_varlen_full_size_sampled(path):
     longest = int(np.argmax(lens))
     shortest = int(np.argmin(lens))
     _check_chains(x, o, sN, [(longest, 3), (shortest, 9), (5, 15)])
+
+
+
+# ------------------------------------------- long sequences cut into parallel segments
+@pytest.mark.parametrize("B,T,H,dk,dv", [(1, 2048, 2, 128, 128), (2, 1100, 1, 128, 64),
+                                         (1, 1500, 1, 64, 128), (1, 4096, 1, 64, 64)])
+def test_split_segments(B, T, H, dk, dv):
+    """Few long chains: the two-phase path cuts each sequence into segments (transfer pass,
+    start-state scan, outputs per segment); the result is the plain recurrence's."""
+    x = make_inputs(B, T, H, dk, dv, "bf16", seed=900 + T + dk, s0_std=0.05)
+    say("split segments", B, T, H, dk, dv)
+    o, sN = run_gpu(x, path="split")
+    o_ref, s_ref = run_oracle(x)
+    assert_close("o", host64(o), o_ref, TOL["bf16"])
+    assert_close("S_final", host64(sN), s_ref, TOL["bf16"])
+
+
+def test_split_segments_near_resets():
+    """Segments with large decays inside (near-resets), as in the long-context workload."""
+    x = make_inputs(1, 3000, 2, 128, 128, "bf16", seed=907, reset_frac=0.1, s0_std=0.05)
+    say("split segments near-resets T3000 H2")
+    o, sN = run_gpu(x, path="split")
+    o_ref, s_ref = run_oracle(x)
+    assert_close("o", host64(o), o_ref, TOL["bf16"])
+    assert_close("S_final", host64(sN), s_ref, TOL["bf16"])
