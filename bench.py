@@ -119,6 +119,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the long-context forward measurement")
     ap.add_argument("--no-scalar-gates", action="store_true",
                     help="skip the scalar-gate forward measurement")
     ap.add_argument("--no-block", action="store_true",
@@ -298,6 +300,48 @@ def main():
             "ms_training_forward_then_saved_backward": res_t["saved"],
             "tokens_per_s_saved": round(B * T / (res_t["saved"] * 1e-3), 1)}
         del bws
+
+    if args.workload == "layer1p3b" and not args.no_long:
+        # the long-context shape beside the headline (one 32K-token sequence, 16 heads, 10%
+        # near-resets; inputs drawn on the device with the same recipe), with the path
+        # chunk_fwd's "auto" picks for it: the throughput should stay near the headline's
+        gen = torch.Generator(device=dev).manual_seed(3)
+        TL = 32768
+
+        def l2n(t):
+            return t / t.norm(dim=-1, keepdim=True)
+        lq = l2n(torch.randn(1, TL, H, dk, generator=gen, device=dev)).to(torch.bfloat16)
+        lk = l2n(torch.randn(1, TL, H, dk, generator=gen, device=dev)).to(torch.bfloat16)
+        lv = torch.randn(1, TL, H, dv, generator=gen, device=dev).to(torch.bfloat16)
+        lg = -0.1 * torch.nn.functional.softplus(torch.randn(1, TL, H, dk, generator=gen, device=dev))
+        reset = torch.rand(1, TL, H, 1, generator=gen, device=dev) < 0.1
+        lg = torch.where(reset, torch.full_like(lg, -5.0), lg).to(torch.bfloat16)
+        lb = torch.sigmoid(torch.randn(1, TL, H, dk, generator=gen, device=dev)).to(torch.bfloat16)
+        lw = torch.sigmoid(torch.randn(1, TL, H, dv, generator=gen, device=dev)).to(torch.bfloat16)
+        lws = torch.empty(G.workspace_bytes(1, TL, H, dk, dv, 1), dtype=torch.uint8, device=dev)
+
+        def lstep():
+            return G.chunk_fwd(lq, lk, lv, lg, lb, lw, workspace=lws)
+        for _ in range(3):
+            lstep()
+        torch.cuda.synchronize()
+        evl = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(10)]
+        for a, b2 in evl:
+            a.record()
+            lstep()
+            b2.record()
+        torch.cuda.synchronize()
+        lms = float(np.mean([a.elapsed_time(b2) for a, b2 in evl]))
+        lbytes = fwd_bytes(1, TL, H, dk, dv, 1)
+        out["long_context"] = {
+            "workload": "one sequence of 32768 tokens, H=16, d_k=d_v=128, bf16, 10% near-resets "
+                        "(log-alpha=-5); path auto (two-phase, cut into segments)",
+            "ms_per_call": round(lms, 4), "tokens_per_s": round(TL / (lms * 1e-3), 1),
+            "vs_headline_tokens_per_s": round(TL / (lms * 1e-3) / out["value"], 3),
+            "algorithmic_bytes": lbytes,
+            "hbm_frac": round(lbytes / (lms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del lq, lk, lv, lg, lb, lw, lws
 
     if args.workload == "layer1p3b" and not args.no_scalar_gates:
         # the scalar-gate configuration (one b and one w value per token and head)
