@@ -785,15 +785,19 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
 
 // Segment start states of a long sequence: S_0 = the sequence's initial state (or 0) and
 // S_{s+1} = M_s S_s + N_s, with [N_s | M_s] the end state of segment s's transfer pass.
-// One workgroup per (sequence, head, 16 value columns); four waves, each owning d_k / 64 of
-// the 16-row tiles; products in fp32 (16x16x4 MFMA), S exchanged through LDS every step.
+// One workgroup per (sequence, head, 16 value columns); one wave per 16-row tile; M_s is
+// staged in LDS with 16-byte loads, products in fp32 (16x16x4 MFMA), S exchanged through
+// LDS every step.
 template <int DK, int DV>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(DK * 4)
 gdn2_seg_combine_kernel(const float* __restrict__ ebuf, const float* __restrict__ s0,
                         float* __restrict__ sbuf, int H, int nseg) {
-  constexpr int LE = DV + DK, NRT = DK / 16, RPW = NRT / 4;  // row tiles, per wave
+  constexpr int LE = DV + DK, NRT = DK / 16, RPW = 1, NT = 64 * NRT;
+  constexpr int LDM = DK + 4;                                 // padded pitch of M in LDS
   __shared__ float sS[DK][16];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) float sM[DK * LDM];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int m16 = lane & 15, g4 = lane >> 4;
   const int ct = blockIdx.x % (DV / 16);
   const int nh = blockIdx.x / (DV / 16);  // sequence * H + head
@@ -818,23 +822,32 @@ gdn2_seg_combine_kernel(const float* __restrict__ ebuf, const float* __restrict_
         out[(long)row * DV + c] = S[t][i];
         sS[row][m16] = S[t][i];
       }
-    __syncthreads();
     if (s + 1 < nseg) {
-#pragma unroll
-      for (int t = 0; t < RPW; ++t) {
-        const int rt = wave * RPW + t;
-        f4 acc;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = E[(long)(16 * rt + 4 * g4 + i) * LE + c];  // N_s
-        for (int k0 = 0; k0 < DK; k0 += 4) {
-          const float a = E[(long)(16 * rt + m16) * LE + DV + k0 + g4];  // M_s[row][k]
-          const float b = sS[k0 + g4][m16];                               // S_s[k][col]
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
-        }
-        S[t] = acc;
+      // M_s (d_k x d_k, the last d_k columns of E's rows) -> LDS
+      for (int p = tid; p < DK * DK / 4; p += NT) {
+        const int row = p / (DK / 4), c4 = p % (DK / 4);
+        *reinterpret_cast<f4*>(sM + row * LDM + 4 * c4) =
+            *reinterpret_cast<const f4*>(E + (long)row * LE + DV + 4 * c4);
       }
+      f4 acc[RPW];
+#pragma unroll
+      for (int t = 0; t < RPW; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)  // N_s
+          acc[t][i] = E[(long)(16 * (wave * RPW + t) + 4 * g4 + i) * LE + c];
+      __syncthreads();
+#pragma unroll 8
+      for (int k0 = 0; k0 < DK; k0 += 4) {
+        const float b = sS[k0 + g4][m16];  // S_s[k][col]
+#pragma unroll
+        for (int t = 0; t < RPW; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(sM[(16 * (wave * RPW + t) + m16) * LDM + k0 + g4],
+                                                       b, acc[t], 0, 0, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < RPW; ++t) S[t] = acc[t];
     }
-    __syncthreads();  // sS is rewritten next step
+    __syncthreads();  // sS and sM are rewritten next step
   }
 }
 
@@ -887,7 +900,7 @@ static hipError_t launch_split(const ChunkArgs& a) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gdn2_seg_combine_kernel<DK, DV>), dim3((unsigned)((long)a.N * a.H * (DV / 16))),
-                       dim3(256), 0, st, ebuf, a.s0, sbuf, a.H, nseg);
+                       dim3(DK * 4), 0, st, ebuf, a.s0, sbuf, a.H, nseg);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gdn2_state_kernel<DK, DV, NV, 0>), dim3((unsigned)(units * nslices)),
