@@ -83,8 +83,12 @@ enum { GDN2_GATE_B_SCALAR = 1, GDN2_GATE_W_SCALAR = 2 };
  *                        owned by the caller and free for the call's duration on
  *                        `hip_stream`. With a workspace the call runs the two-phase path:
  *                        one kernel computes every chunk's factors in parallel into the
- *                        workspace, a second walks the chunks of each sequence in order.
- *                        Without one, a single fused kernel does both per sequence.
+ *                        workspace, a second walks the chunks of each sequence in order
+ *                        (for fixed-length batches with fewer sequence x head chains than
+ *                        compute units, each sequence is cut into segments that run in
+ *                        parallel: a transfer pass, a scan of segment start states, then
+ *                        the outputs). Without one, a single fused kernel does both per
+ *                        sequence.
  *                        Results agree to rounding. Ignored when
  *                        gdn2_chunk_fwd_workspace_bytes returns 0 for the dtype/widths.
  *   Without cu_seqlens, N must equal B and every sequence has length T.
@@ -115,7 +119,8 @@ int gdn2_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* l
 /*
  * Device workspace, in bytes, that the two-phase path of gdn2_chunk_fwd needs for a call
  * with these sizes, with or without cu_seqlens (about 1.13 KiB per token and head at
- * d_k = d_v = 128, plus one chunk per sequence). 0 when the two-phase path is not built
+ * d_k = d_v = 128, plus one chunk per sequence, plus (2 d_v + d_k) d_k fp32 per segment and
+ * head when long sequences are cut into segments). 0 when the two-phase path is not built
  * for dtype / d_k / d_v (GDN2_BF16 with d_k, d_v in {64, 128} is) or a size is negative.
  */
 size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int N,
@@ -135,9 +140,10 @@ size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int
  *   d_initial_state   : [N, H, d_k, d_v] fp32, or NULL (not written)
  *   range_flag        : NULL, or a device int32 that the call sets to 1 (and otherwise leaves
  *                       alone) when some chunk's total decay, in some key channel, exceeds
- *                       the range of the backward's chunk-referenced factors (about 83 nats
- *                       over 64 tokens); the gradients of such chunks are not valid. The
- *                       caller clears it beforehand and checks it afterwards.
+ *                       the range of the backward's factors (referenced to the middle of
+ *                       each channel's decay over the chunk: about 166 nats over 64 tokens);
+ *                       the gradients of such chunks are not valid. The caller clears it
+ *                       beforehand and checks it afterwards.
  *   workspace         : required, at least gdn2_chunk_bwd_workspace_bytes(...) bytes, 16-byte
  *                       aligned, free for the call's duration on `hip_stream`.
  *   Supported: GDN2_BF16 with d_k, d_v in {64, 128}.
