@@ -329,7 +329,12 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const long kb0 = cu.row * kstride + (long)cu.h * DK;
   const long vb0 = cu.row * vstride + (long)cu.h * DV;
 
-  // ---- loads: key-side inputs (this thread's tokens x 8 channels), value side, dO
+  // ---- loads: every global read of the unit is issued before the first LDS store (one
+  // memory round trip): key-side inputs (this thread's tokens x 8 channels), value side,
+  // dO, and the workspace tiles dZ, U, dSn, S0
+  constexpr int NDO = C * DV / 8 / NT;             // 16-byte pieces of dO per thread
+  constexpr int NZU = Sh::NVT * 4 / Sh::NW;        // dZ and U tiles per wave
+  static_assert(NDO * NT == C * DV / 8 && NZU * Sh::NW == Sh::NVT * 4, "load mapping");
   Vec8<T> rq[Sh::TPT], rk[Sh::TPT], rg[Sh::TPT], rb[Sh::TPT], rv[Sh::VTPT], rw[Sh::VTPT];
 #pragma unroll
   for (int j = 0; j < Sh::TPT; ++j) {
@@ -353,34 +358,51 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       rv[j].zero(); rw[j].zero();
     }
   }
-  for (int p = tid; p < C * DV / 8; p += NT) {  // dO rows -> LDS
-    const int r = p / (DV / 8), cc = p % (DV / 8);
-    uint4 x = make_uint4(0, 0, 0, 0);
-    if (r < cu.nvalid) x = *reinterpret_cast<const uint4*>(d_o + vb0 + (long)r * vstride + cc * 8);
-    *reinterpret_cast<uint4*>(sO + r * LDV + cc * 8) = x;
+  uint4 rdo[NDO];
+#pragma unroll
+  for (int i = 0; i < NDO; ++i) {
+    const int p = tid + i * NT, r = p / (DV / 8), cc = p % (DV / 8);
+    rdo[i] = make_uint4(0, 0, 0, 0);
+    if (r < cu.nvalid) rdo[i] = *reinterpret_cast<const uint4*>(d_o + vb0 + (long)r * vstride + cc * 8);
   }
-  // accumulator tiles (bf16, lane-major) -> row-major LDS arrays
-  auto tile_in = [&](long off, int tile) {
-    const bf16x4 x = *reinterpret_cast<const bf16x4*>(unit + off + (tile * 64 + lane) * 8);
-    return f4{to_f(x[0]), to_f(x[1]), to_f(x[2]), to_f(x[3])};
+  // accumulator tiles (bf16, lane-major, 8 bytes per lane)
+  auto tile_raw = [&](long off, int tile) {
+    return *reinterpret_cast<const bf16x4*>(unit + off + (tile * 64 + lane) * 8);
   };
-  auto ident = [](int c) { return c; };
-  for (int t = wave; t < NVT * 4; t += Sh::NW) {  // dZ, U: tiles (ct, R)
-    const int ct = t / 4, R = t % 4;
-    store_tile_pairs(sZ + (16 * R) * LDV + 16 * ct, LDV, lane, tile_in(LB.zb, t), ident);
-    store_tile_pairs(sU + (16 * R) * LDV + 16 * ct, LDV, lane, tile_in(LB.ub, t), ident);
+  auto tof = [](bf16x4 x) { return f4{to_f(x[0]), to_f(x[1]), to_f(x[2]), to_f(x[3])}; };
+  bf16x4 rz[NZU], ru[NZU], rds[NVT], s0t[NVT];
+#pragma unroll
+  for (int i = 0; i < NZU; ++i) {
+    rz[i] = tile_raw(LB.zb, wave + i * Sh::NW);
+    ru[i] = tile_raw(LB.ub, wave + i * Sh::NW);
   }
-  // dSn -> LDS; S0 stays in registers until dSn is dead; the dg constant
-  // X_c = sum_v dSn[c,v] S0[c,v] (times gamma_c later) from the two tiles' products
-  f4 s0t[NVT];
+#pragma unroll
+  for (int ct = 0; ct < NVT; ++ct) {
+    rds[ct] = tile_raw(LB.db, ct * Sh::NCT + wave);
+    s0t[ct] = tile_raw(LB.h, ct * Sh::NCT + wave);
+  }
+  // ... then into LDS: dO rows, dZ and U (tiles (ct, R)) row-major, dSn; S0 stays in
+  // registers until dSn is dead; the dg constant X_c = sum_v dSn[c,v] S0[c,v] (times gamma_c
+  // later) from the two tiles' products
+#pragma unroll
+  for (int i = 0; i < NDO; ++i) {
+    const int p = tid + i * NT, r = p / (DV / 8), cc = p % (DV / 8);
+    *reinterpret_cast<uint4*>(sO + r * LDV + cc * 8) = rdo[i];
+  }
+  auto ident = [](int c) { return c; };
+#pragma unroll
+  for (int i = 0; i < NZU; ++i) {
+    const int t = wave + i * Sh::NW, ct = t / 4, R = t % 4;
+    store_tile_pairs(sZ + (16 * R) * LDV + 16 * ct, LDV, lane, tof(rz[i]), ident);
+    store_tile_pairs(sU + (16 * R) * LDV + 16 * ct, LDV, lane, tof(ru[i]), ident);
+  }
   {
     f4 xs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ct = 0; ct < NVT; ++ct) {
-      const f4 ds = tile_in(LB.db, ct * Sh::NCT + wave);
-      s0t[ct] = tile_in(LB.h, ct * Sh::NCT + wave);
+      const f4 ds = tof(rds[ct]);
       store_tile_pairs(sA + (16 * wave) * LDV + 16 * ct, LDV, lane, ds, ident);
-      xs += ds * s0t[ct];
+      xs += ds * tof(s0t[ct]);
     }
 #pragma unroll
     for (int m = 1; m < 16; m <<= 1)
@@ -510,7 +532,7 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     for (int i = 0; i < 4; ++i) rs[i] = fast_exp2(0.5f * gl[i]);
 #pragma unroll
     for (int ct = 0; ct < NVT; ++ct)
-      store_tile_pairs(sA + (16 * wave) * LDV + 16 * ct, LDV, lane, s0t[ct] * rs, ident);
+      store_tile_pairs(sA + (16 * wave) * LDV + 16 * ct, LDV, lane, tof(s0t[ct]) * rs, ident);
   }
   lds_barrier();
   // ---- P3: dQbar^T = S0 dO^T + Khat^T M1^T,  dEbar^T = -S0 dZ^T + Khat^T M2^T
