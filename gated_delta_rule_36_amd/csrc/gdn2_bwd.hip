@@ -242,6 +242,18 @@ gdn2_bwd_chain_kernel(char* __restrict__ ws, const bf16* __restrict__ d_o,
 }
 
 // ------------------------------------------------------------------ the local gradients
+// A value that the code below may use only from this point on: the empty asm reads and
+// rewrites the registers, so the wait for a load into them, and the arithmetic on them,
+// cannot be scheduled before it (the compiler otherwise pulls such work up to the first use
+// of any register loaded with it, ahead of unrelated matrix work). `after` is a value the
+// point depends on.
+__device__ __forceinline__ void hold(uint4& x, float after) {
+  asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w) : "v"(after));
+}
+__device__ __forceinline__ void hold(bf16x4& x, float after) {
+  asm volatile("" : "+v"(x) : "v"(after));
+}
+
 template <int DK, int DV>
 struct LocalShape {
   static constexpr int C = 64;
@@ -275,8 +287,8 @@ struct LocalShape {
   static constexpr int OFF_X = OFF_FAC + Fac::N * DK * 4;  // per-channel constant of dg
   static constexpr int OFF_FLAG = OFF_X + DK * 4;
   static constexpr int LDS_BYTES = OFF_FLAG + 16;
-  static constexpr int OFF_TOT = OFF_M1;                   // cumsum scratch in the M buffers
-  static_assert(TG * DK * 4 <= 4 * SZ_M, "cumsum scratch");
+  static constexpr int OFF_TOT = OFF_KH;                   // cumsum scratch in the Khat^T region
+  static_assert(TG * DK * 4 <= DK * LDT * 2, "cumsum scratch");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(TPT * TG == C && VTPT * VTG == C, "token mapping");
 };
@@ -329,41 +341,20 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const long kb0 = cu.row * kstride + (long)cu.h * DK;
   const long vb0 = cu.row * vstride + (long)cu.h * DV;
 
-  // ---- loads: every global read of the unit is issued before the first LDS store (one
-  // memory round trip): key-side inputs (this thread's tokens x 8 channels), value side,
-  // dO, and the workspace tiles dZ, U, dSn, S0
+  // ---- loads: every global read of the unit is issued up front, in the order of use, so
+  // that the matrix work on the workspace tiles (P1, P2) runs while the inputs are still
+  // arriving: dO and the tiles dZ, U, dSn; then g, k; S0; v, w; q, b. Every load is
+  // unconditional (a row past the unit's end reads row 0 and is zeroed where it is first
+  // used), which keeps the waits on the early groups exact.
   constexpr int NDO = C * DV / 8 / NT;             // 16-byte pieces of dO per thread
   constexpr int NZU = Sh::NVT * 4 / Sh::NW;        // dZ and U tiles per wave
   static_assert(NDO * NT == C * DV / 8 && NZU * Sh::NW == Sh::NVT * 4, "load mapping");
-  Vec8<T> rq[Sh::TPT], rk[Sh::TPT], rg[Sh::TPT], rb[Sh::TPT], rv[Sh::VTPT], rw[Sh::VTPT];
-#pragma unroll
-  for (int j = 0; j < Sh::TPT; ++j) {
-    const int r = tg * Sh::TPT + j;
-    if (r < cu.nvalid) {
-      const long off = kb0 + (long)r * kstride + cg * 8;
-      rq[j].load(q + off); rk[j].load(k + off); rg[j].load(g + off);
-      if constexpr (B_S) rb[j].load_one(bg + (cu.row + r) * H + cu.h); else rb[j].load(bg + off);
-    } else {
-      rq[j].zero(); rk[j].zero(); rg[j].zero(); rb[j].zero();
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < Sh::VTPT; ++j) {
-    const int r = vtg * Sh::VTPT + j;
-    if (r < cu.nvalid) {
-      const long off = vb0 + (long)r * vstride + vcg * 8;
-      rv[j].load(v + off);
-      if constexpr (W_S) rw[j].load_one(wg + (cu.row + r) * H + cu.h); else rw[j].load(wg + off);
-    } else {
-      rv[j].zero(); rw[j].zero();
-    }
-  }
+  auto clamp_row = [&](int r) { return r < cu.nvalid ? r : 0; };
   uint4 rdo[NDO];
 #pragma unroll
   for (int i = 0; i < NDO; ++i) {
-    const int p = tid + i * NT, r = p / (DV / 8), cc = p % (DV / 8);
-    rdo[i] = make_uint4(0, 0, 0, 0);
-    if (r < cu.nvalid) rdo[i] = *reinterpret_cast<const uint4*>(d_o + vb0 + (long)r * vstride + cc * 8);
+    const int p = tid + i * NT, r = clamp_row(p / (DV / 8)), cc = p % (DV / 8);
+    rdo[i] = *reinterpret_cast<const uint4*>(d_o + vb0 + (long)r * vstride + cc * 8);
   }
   // accumulator tiles (bf16, lane-major, 8 bytes per lane)
   auto tile_raw = [&](long off, int tile) {
@@ -377,13 +368,37 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     ru[i] = tile_raw(LB.ub, wave + i * Sh::NW);
   }
 #pragma unroll
-  for (int ct = 0; ct < NVT; ++ct) {
-    rds[ct] = tile_raw(LB.db, ct * Sh::NCT + wave);
-    s0t[ct] = tile_raw(LB.h, ct * Sh::NCT + wave);
+  for (int ct = 0; ct < NVT; ++ct) rds[ct] = tile_raw(LB.db, ct * Sh::NCT + wave);
+  __builtin_amdgcn_sched_barrier(0);  // the loads above are issued first
+  Vec8<T> rq[Sh::TPT], rk[Sh::TPT], rg[Sh::TPT], rb[Sh::TPT], rv[Sh::VTPT], rw[Sh::VTPT];
+  bool kvalid[Sh::TPT];
+#pragma unroll
+  for (int j = 0; j < Sh::TPT; ++j) {
+    kvalid[j] = tg * Sh::TPT + j < cu.nvalid;
+    const long off = kb0 + (long)clamp_row(tg * Sh::TPT + j) * kstride + cg * 8;
+    rg[j].load(g + off);
+    rk[j].load(k + off);
   }
-  // ... then into LDS: dO rows, dZ and U (tiles (ct, R)) row-major, dSn; S0 stays in
-  // registers until dSn is dead; the dg constant X_c = sum_v dSn[c,v] S0[c,v] (times gamma_c
-  // later) from the two tiles' products
+#pragma unroll
+  for (int ct = 0; ct < NVT; ++ct) s0t[ct] = tile_raw(LB.h, ct * Sh::NCT + wave);
+#pragma unroll
+  for (int j = 0; j < Sh::VTPT; ++j) {  // rows past the end give outputs that are not stored
+    const int r = clamp_row(vtg * Sh::VTPT + j);
+    rv[j].load(v + vb0 + (long)r * vstride + vcg * 8);
+    if constexpr (W_S) rw[j].load_one(wg + (cu.row + r) * H + cu.h);
+    else rw[j].load(wg + vb0 + (long)r * vstride + vcg * 8);
+  }
+#pragma unroll
+  for (int j = 0; j < Sh::TPT; ++j) {
+    const int r = clamp_row(tg * Sh::TPT + j);
+    rq[j].load(q + kb0 + (long)r * kstride + cg * 8);
+    if constexpr (B_S) rb[j].load_one(bg + (cu.row + r) * H + cu.h);
+    else rb[j].load(bg + kb0 + (long)r * kstride + cg * 8);
+  }
+
+  // ---- dO, dZ and U (tiles (ct, R)) row-major, dSn into LDS. A dO row past the end holds
+  // row 0's values: it reaches only M1's row of that token (zeroed in P1) and dQbar's column
+  // of that token (not stored).
 #pragma unroll
   for (int i = 0; i < NDO; ++i) {
     const int p = tid + i * NT, r = p / (DV / 8), cc = p % (DV / 8);
@@ -396,97 +411,11 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     store_tile_pairs(sZ + (16 * R) * LDV + 16 * ct, LDV, lane, tof(rz[i]), ident);
     store_tile_pairs(sU + (16 * R) * LDV + 16 * ct, LDV, lane, tof(ru[i]), ident);
   }
-  {
-    f4 xs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ct = 0; ct < NVT; ++ct) {
-      const f4 ds = tof(rds[ct]);
-      store_tile_pairs(sA + (16 * wave) * LDV + 16 * ct, LDV, lane, ds, ident);
-      xs += ds * tof(s0t[ct]);
-    }
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xs[i] += __shfl_xor(xs[i], m, 64);
-    if (m16 == 0) *reinterpret_cast<f4*>(sX + 16 * wave + 4 * g4) = xs;
-  }
-
-  // ---- (a), (b): cumulative log2-decay and the chunk factors
-  {
-    float tot8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < Sh::TPT; ++j) {
-      float f[8];
-      rg[j].to_float(f);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) tot8[i] += f[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) tot8[i] *= kLog2e;
-    store8(sTot + tg * DK + cg * 8, tot8);
-  }
+  for (int ct = 0; ct < NVT; ++ct)
+    store_tile_pairs(sA + (16 * wave) * LDV + 16 * ct, LDV, lane, tof(rds[ct]), ident);
   if (tid == 0) *sFlag = 0;
   lds_barrier();
-  channel_scan<DK, Sh::TG, Sh::GPB, NT>(sTot, sFac, sFlag, tid);
-  lds_barrier();
-  (void)sFlag;
-  if (tid < DK && range_flag != nullptr && -sFac[Fac::GL * DK + tid] > 2.f * kFastPathMaxDecay2)
-    *range_flag = 1;
-  // this thread's channels' reference Gm = Glast / 2 (log2)
-  float Gm8[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) Gm8[i] = 0.5f * sFac[Fac::GL * DK + cg * 8 + i];
-  // per thread: G (log2) of its tokens; Khat'^T = (K 2^(Gm-G))^T into LDS (natural order)
-  float G2[Sh::TPT][8];
-  {
-    float run[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) run[i] = sTot[tg * DK + cg * 8 + i];
-    RunBuf<T, Sh::TPT> kh[8];
-#pragma unroll
-    for (int j = 0; j < Sh::TPT; ++j) {
-      float fg[8], fk[8];
-      rg[j].to_float(fg);
-      rk[j].to_float(fk);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        run[i] += fg[i] * kLog2e;
-        G2[j][i] = run[i];
-        kh[i].put(j, fk[i] * fast_exp2(Gm8[i] - run[i]));
-      }
-    }
-    const int sw = tswz(cg * 8);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) kh[i].store_sw(sKh + (cg * 8 + i) * LDT, sw, tg * Sh::TPT);
-  }
-  // dv = dZ * w, dw = dZ * v
-#pragma unroll
-  for (int j = 0; j < Sh::VTPT; ++j) {
-    const int r = vtg * Sh::VTPT + j;
-    float fz[8], fv[8], fw[8], o1[8], o2[8];
-    Vec8<T> z;
-    z.load(sZ + r * LDV + vcg * 8);
-    z.to_float(fz);
-    rv[j].to_float(fv);
-    if constexpr (W_S) rw[j].splat();
-    rw[j].to_float(fw);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) { o1[i] = fz[i] * fw[i]; o2[i] = fz[i] * fv[i]; }
-    if (r < cu.nvalid) {
-      const long off = vb0 + (long)r * vstride + vcg * 8;
-      store8(dv + off, o1);
-      if constexpr (!W_S) store8(dw + off, o2);
-    }
-    if constexpr (W_S) {  // sum over the token's d_v channels (VCG adjacent lanes)
-      float sw = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sw += o2[i];
-#pragma unroll
-      for (int m = 1; m < Sh::VCG; m <<= 1) sw += __shfl_xor(sw, m, 64);
-      if (vcg == 0 && r < cu.nvalid) dw[(cu.row + r) * H + cu.h] = from_f<T>(sw);
-    }
-  }
-  lds_barrier();  // sTot (in the M buffers) is consumed; Khat^T, dO, dZ, U, dSn are in LDS
 
   // ---- P1: M1 = lower_incl(dO U^T), M2 = -strict(dZ U^T); stored row-major and transposed
   for (int t = wave; t < 32; t += Sh::NW) {
@@ -503,7 +432,7 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * g4 + i, c = m16;  // row (token t) within R, column (token i) within I
-      const bool keep = I < R || (which ? c < r : c <= r);
+      const bool keep = (I < R || (which ? c < r : c <= r)) && (which || 16 * R + r < cu.nvalid);
       val[i] = keep ? (which ? -acc[i] : acc[i]) : 0.f;
     }
     T* Mr = which ? sM2 : sM1;
@@ -523,16 +452,113 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                    M::load(sU, LDV, 16 * Tt + m16, 32 * s + 8 * g4), acc);
     dKt[Tt] = acc;
   }
-  lds_barrier();  // dSn and U are dead
+  // ---- (a): per-thread totals of log2-decay (a row past the end decays by nothing) into
+  // sTot, which shares the Khat^T region (written only after the scan's prefixes are read)
+#pragma unroll
+  for (int j = 0; j < Sh::TPT; ++j) {
+    hold(rg[j].r, dKt[3][3]);
+    hold(rk[j].r, dKt[3][3]);
+    if (!kvalid[j]) { rg[j].zero(); rk[j].zero(); }
+  }
   {
-    // S0 rows (this lane's channels 16 wave + 4 g4 + i) scaled by 2^Gm
+    float tot8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < Sh::TPT; ++j) {
+      float f[8];
+      rg[j].to_float(f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) tot8[i] += f[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tot8[i] *= kLog2e;
+    store8(sTot + tg * DK + cg * 8, tot8);
+  }
+  lds_barrier();  // M1, M2 written; the totals complete; dSn and U are dead
+  // ---- (b): the per-channel scan and the chunk factors
+  channel_scan<DK, Sh::TG, Sh::GPB, NT>(sTot, sFac, sFlag, tid);
+  lds_barrier();
+  (void)sFlag;
+  if (tid < DK && range_flag != nullptr && -sFac[Fac::GL * DK + tid] > 2.f * kFastPathMaxDecay2)
+    *range_flag = 1;
+  // this thread's channels' reference Gm = Glast / 2 (log2)
+  float Gm8[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) Gm8[i] = 0.5f * sFac[Fac::GL * DK + cg * 8 + i];
+  // per thread: G (log2) of its tokens; Khat'^T = (K 2^(Gm-G))^T (stored below)
+  float G2[Sh::TPT][8];
+  RunBuf<T, Sh::TPT> kh[8];
+  {
+    float run[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) run[i] = sTot[tg * DK + cg * 8 + i];
+#pragma unroll
+    for (int j = 0; j < Sh::TPT; ++j) {
+      float fg[8], fk[8];
+      rg[j].to_float(fg);
+      rk[j].to_float(fk);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        run[i] += fg[i] * kLog2e;
+        G2[j][i] = run[i];
+        kh[i].put(j, fk[i] * fast_exp2(Gm8[i] - run[i]));
+      }
+    }
+  }
+  {
+    // S0 rows (this lane's channels 16 wave + 4 g4 + i) scaled by 2^Gm into sA (dSn is
+    // dead); the dg constant X_c = sum_v dSn[c,v] S0[c,v] (times gamma_c later)
     const f4 gl = *reinterpret_cast<const f4*>(sFac + Fac::GL * DK + 16 * wave + 4 * g4);
-    f4 rs;
+#pragma unroll
+    for (int ct = 0; ct < NVT; ++ct) hold(s0t[ct], gl[0]);
+    f4 rs, xs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) rs[i] = fast_exp2(0.5f * gl[i]);
 #pragma unroll
-    for (int ct = 0; ct < NVT; ++ct)
-      store_tile_pairs(sA + (16 * wave) * LDV + 16 * ct, LDV, lane, tof(s0t[ct]) * rs, ident);
+    for (int ct = 0; ct < NVT; ++ct) {
+      const f4 s0 = tof(s0t[ct]);
+      store_tile_pairs(sA + (16 * wave) * LDV + 16 * ct, LDV, lane, s0 * rs, ident);
+      xs += tof(rds[ct]) * s0;
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xs[i] += __shfl_xor(xs[i], m, 64);
+    if (m16 == 0) *reinterpret_cast<f4*>(sX + 16 * wave + 4 * g4) = xs;
+  }
+  // dv = dZ * w, dw = dZ * v
+#pragma unroll
+  for (int j = 0; j < Sh::VTPT; ++j) {
+    const int r = vtg * Sh::VTPT + j;
+    float fz[8], fv[8], fw[8], o1[8], o2[8];
+    Vec8<T> z;
+    z.load(sZ + r * LDV + vcg * 8);
+    z.to_float(fz);
+    hold(rv[j].r, fz[0]);
+    hold(rw[j].r, fz[0]);
+    rv[j].to_float(fv);
+    if constexpr (W_S) rw[j].splat();
+    rw[j].to_float(fw);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { o1[i] = fz[i] * fw[i]; o2[i] = fz[i] * fv[i]; }
+    if (r < cu.nvalid) {
+      const long off = vb0 + (long)r * vstride + vcg * 8;
+      store8(dv + off, o1);
+      if constexpr (!W_S) store8(dw + off, o2);
+    }
+    if constexpr (W_S) {  // sum over the token's d_v channels (VCG adjacent lanes)
+      float sw = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sw += o2[i];
+#pragma unroll
+      for (int m = 1; m < Sh::VCG; m <<= 1) sw += __shfl_xor(sw, m, 64);
+      if (vcg == 0 && r < cu.nvalid) dw[(cu.row + r) * H + cu.h] = from_f<T>(sw);
+    }
+  }
+  lds_barrier();  // the prefixes in sTot are read
+  {
+    const int sw = tswz(cg * 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kh[i].store_sw(sKh + (cg * 8 + i) * LDT, sw, tg * Sh::TPT);
   }
   lds_barrier();
   // ---- P3: dQbar^T = S0 dO^T + Khat^T M1^T,  dEbar^T = -S0 dZ^T + Khat^T M2^T
@@ -565,6 +591,9 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
     for (int j = 0; j < Sh::TPT; ++j) {
       float fq[8], fk[8], fb[8];
+      hold(rq[j].r, dQb[3][3]);
+      hold(rb[j].r, dQb[3][3]);
+      if (!kvalid[j]) { rq[j].zero(); rb[j].zero(); }
       rq[j].to_float(fq);
       rk[j].to_float(fk);
       if constexpr (B_S) rb[j].splat();  // (also what the elementwise step reads back)
