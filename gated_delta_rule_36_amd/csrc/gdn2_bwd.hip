@@ -304,7 +304,7 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                       bf16* __restrict__ dq, bf16* __restrict__ dk, bf16* __restrict__ dv,
                       bf16* __restrict__ dg, bf16* __restrict__ db, bf16* __restrict__ dw,
                       int* range_flag, const int* __restrict__ cu_seqlens, int N, int T_len,
-                      int H) {
+                      int H, long nunits) {
   typedef bf16 T;
   using Sh = LocalShape<DK, DV>;
   using M = Mma<T>;
@@ -334,21 +334,55 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int cg = tid % Sh::CG, tg = tid / Sh::CG;
   const int vcg = tid % Sh::VCG, vtg = tid / Sh::VCG;
 
-  const ChunkUnit cu = map_unit(blockIdx.x, H, cu_seqlens, N, T_len, lane);
-  if (cu.nvalid == 0) return;  // an unused slot (uniform)
-  const char* unit = ws + (long)blockIdx.x * LB.bytes;
   const long kstride = (long)H * DK, vstride = (long)H * DV;
-  const long kb0 = cu.row * kstride + (long)cu.h * DK;
-  const long vb0 = cu.row * vstride + (long)cu.h * DV;
-
-  // ---- loads: every global read of the unit is issued up front, in the order of use, so
-  // that the matrix work on the workspace tiles (P1, P2) runs while the inputs are still
-  // arriving: dO and the tiles dZ, U, dSn; then g, k; S0; v, w; q, b. Every load is
-  // unconditional (a row past the unit's end reads row 0 and is zeroed where it is first
-  // used), which keeps the waits on the early groups exact.
+  // The workgroups are persistent (one per compute unit) and walk the units u = blockIdx.x,
+  // + gridDim.x, ... Every global read of a unit is issued before it is needed, in two
+  // groups: the workspace tiles dZ, U, dSn (for the matrix work P1, P2), issued at the end
+  // of the previous unit; then dO; g, k; S0; v, w; q, b, issued at the start of the unit,
+  // the later ones arriving while P1, P2 run. Every load is unconditional (a row
+  // past the unit's end reads row 0 and is zeroed where it is first used; past the last
+  // unit the current one is read again), which keeps the waits on the early groups exact.
   constexpr int NDO = C * DV / 8 / NT;             // 16-byte pieces of dO per thread
   constexpr int NZU = Sh::NVT * 4 / Sh::NW;        // dZ and U tiles per wave
   static_assert(NDO * NT == C * DV / 8 && NZU * Sh::NW == Sh::NVT * 4, "load mapping");
+  // accumulator tiles (bf16, lane-major, 8 bytes per lane)
+  auto tile_raw = [&](const char* un, long off, int tile) {
+    return *reinterpret_cast<const bf16x4*>(un + off + (tile * 64 + lane) * 8);
+  };
+  auto tof = [](bf16x4 x) { return f4{to_f(x[0]), to_f(x[1]), to_f(x[2]), to_f(x[3])}; };
+  bf16x4 rz[NZU], ru[NZU], rds[NVT];
+  auto issue_first = [&](long uu) {
+    const char* un = ws + uu * LB.bytes;
+#pragma unroll
+    for (int i = 0; i < NZU; ++i) {
+      rz[i] = tile_raw(un, LB.zb, wave + i * Sh::NW);
+      ru[i] = tile_raw(un, LB.ub, wave + i * Sh::NW);
+    }
+#pragma unroll
+    for (int ct = 0; ct < NVT; ++ct) rds[ct] = tile_raw(un, LB.db, ct * Sh::NCT + wave);
+  };
+  long u = blockIdx.x;
+  ChunkUnit cu = map_unit(u, H, cu_seqlens, N, T_len, lane);
+  issue_first(u);
+  while (u < nunits) {
+  const long u_next = u + gridDim.x;
+  const long u_pre = u_next < nunits ? u_next : u;  // the unit whose first group is prefetched
+  if (cu.nvalid == 0) {  // an unused slot (uniform)
+    cu = map_unit(u_pre, H, cu_seqlens, N, T_len, lane);
+    issue_first(u_pre);
+    u = u_next;
+    continue;
+  }
+  const char* unit = ws + u * LB.bytes;
+  const long kb0 = cu.row * kstride + (long)cu.h * DK;
+  const long vb0 = cu.row * vstride + (long)cu.h * DV;
+  // the per-lane indices, derived again for every unit from an opaque copy of the thread
+  // index, so that the offsets computed from them are not hoisted out of the unit loop
+  // (where they would hold registers through the whole kernel)
+  int tid_u = threadIdx.x;
+  asm volatile("" : "+v"(tid_u));
+  const int tid = tid_u, lane = tid & 63, m16 = lane & 15, g4 = lane >> 4;
+  const int cg = tid % Sh::CG, tg = tid / Sh::CG, vcg = tid % Sh::VCG, vtg = tid / Sh::VCG;
   auto clamp_row = [&](int r) { return r < cu.nvalid ? r : 0; };
   uint4 rdo[NDO];
 #pragma unroll
@@ -356,20 +390,7 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const int p = tid + i * NT, r = clamp_row(p / (DV / 8)), cc = p % (DV / 8);
     rdo[i] = *reinterpret_cast<const uint4*>(d_o + vb0 + (long)r * vstride + cc * 8);
   }
-  // accumulator tiles (bf16, lane-major, 8 bytes per lane)
-  auto tile_raw = [&](long off, int tile) {
-    return *reinterpret_cast<const bf16x4*>(unit + off + (tile * 64 + lane) * 8);
-  };
-  auto tof = [](bf16x4 x) { return f4{to_f(x[0]), to_f(x[1]), to_f(x[2]), to_f(x[3])}; };
-  bf16x4 rz[NZU], ru[NZU], rds[NVT], s0t[NVT];
-#pragma unroll
-  for (int i = 0; i < NZU; ++i) {
-    rz[i] = tile_raw(LB.zb, wave + i * Sh::NW);
-    ru[i] = tile_raw(LB.ub, wave + i * Sh::NW);
-  }
-#pragma unroll
-  for (int ct = 0; ct < NVT; ++ct) rds[ct] = tile_raw(LB.db, ct * Sh::NCT + wave);
-  __builtin_amdgcn_sched_barrier(0);  // the loads above are issued first
+  bf16x4 s0t[NVT];
   Vec8<T> rq[Sh::TPT], rk[Sh::TPT], rg[Sh::TPT], rb[Sh::TPT], rv[Sh::VTPT], rw[Sh::VTPT];
   bool kvalid[Sh::TPT];
 #pragma unroll
@@ -380,7 +401,7 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     rk[j].load(k + off);
   }
 #pragma unroll
-  for (int ct = 0; ct < NVT; ++ct) s0t[ct] = tile_raw(LB.h, ct * Sh::NCT + wave);
+  for (int ct = 0; ct < NVT; ++ct) s0t[ct] = tile_raw(unit, LB.h, ct * Sh::NCT + wave);
 #pragma unroll
   for (int j = 0; j < Sh::VTPT; ++j) {  // rows past the end give outputs that are not stored
     const int r = clamp_row(vtg * Sh::VTPT + j);
@@ -648,7 +669,13 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const f4 gam = *reinterpret_cast<const f4*>(sFac + Fac::GAM * DK + c0);
   const f4 gl = *reinterpret_cast<const f4*>(sFac + Fac::GL * DK + c0);
   const f4 xc = *reinterpret_cast<const f4*>(sX + c0);
-  f4 dgv[4], outq[4], outk[4], outb[4];
+  // dq, dk and db of a token tile are stored as soon as they are formed; dg waits for the
+  // suffix sums over the chunk
+  auto put4 = [&](bf16* p, long off, f4 x) {
+    *reinterpret_cast<uint2*>(p + off) = make_uint2(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]));
+  };
+  float* sPart = reinterpret_cast<float*>(smem + Sh::OFF_M1);  // scalar db: [NW][64] partials
+  f4 dgv[4];
   f4 totB = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int Tt = 0; Tt < 4; ++Tt) {
@@ -656,7 +683,7 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const f4 G = *reinterpret_cast<const f4*>(sG + t * DK + c0);
     const f4 fq = load4f(sq + t * LDK + c0), fk = load4f(sk + t * LDK + c0);
     const f4 fb = load4f(sb + t * LDK + c0);
-    f4 A, Bv;
+    f4 A, Bv, outq, outk, outb;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       // mid-referenced factors (dQb, dEb, dKh carry the 2^(+-Gm) of their operands)
@@ -664,16 +691,33 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       const float gm = fast_exp2(G[i] - gmr), ig = fast_exp2(gmr - G[i]);
       const float kt = fast_exp2(gl[i] - G[i]);  // 2^(Glast - G) <= 1
       const float dE = dEb[Tt][i] * gm;
-      outq[Tt][i] = dQb[Tt][i] * gm;
-      outk[Tt][i] = dKh[Tt][i] * ig + dKt[Tt][i] * kt + dE * fb[i];
-      outb[Tt][i] = dE * fk[i];
+      outq[i] = dQb[Tt][i] * gm;
+      outk[i] = dKh[Tt][i] * ig + dKt[Tt][i] * kt + dE * fb[i];
+      outb[i] = dE * fk[i];
       // dG = dEbar Ebar + dQbar Qbar - dKhat Khat - dKtil Ktil, split as A - B
       A[i] = gm * (dEb[Tt][i] * fb[i] * fk[i] + dQb[Tt][i] * fq[i]) - dKh[Tt][i] * fk[i] * ig;
       Bv[i] = dKt[Tt][i] * fk[i] * kt;
     }
     dgv[Tt] = A - Bv;
     totB += Bv;
+    if (t < cu.nvalid) {
+      const long off = kb0 + (long)t * kstride + c0;
+      put4(dq, off, outq);
+      put4(dk, off, outk);
+      if constexpr (!B_S) put4(db, off, outb);
+    }
+    if constexpr (B_S) {
+      // a scalar b's gradient sums the token's d_k channels: 4 per lane, the 4 lane groups
+      // of a wave, then the NW waves through LDS (the M buffers are dead here)
+      float x = outb[0] + outb[1] + outb[2] + outb[3];
+      x += __shfl_xor(x, 16, 64);
+      x += __shfl_xor(x, 32, 64);
+      if (g4 == 0) sPart[wave * 64 + t] = x;
+    }
   }
+  // the next unit's first load group, in flight from here on
+  const ChunkUnit cn = map_unit(u_pre, H, cu_seqlens, N, T_len, lane);
+  issue_first(u_pre);
   // dg_t = sum_{t' >= t} (A - B)_{t'} + sum_all B + gamma X   (suffix sums over 64 tokens)
 #pragma unroll
   for (int m = 1; m < 16; m <<= 1)
@@ -694,34 +738,11 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     f4 tile_tot;
 #pragma unroll
     for (int i = 0; i < 4; ++i) tile_tot[i] = __shfl(x[i], lane & ~15, 64);
-    dgv[Tt] = x + carry;
+    const int t = 16 * Tt + m16;
+    if (t < cu.nvalid) put4(dg, kb0 + (long)t * kstride + c0, x + carry);
     carry += tile_tot;
   }
-#pragma unroll
-  for (int Tt = 0; Tt < 4; ++Tt) {
-    const int t = 16 * Tt + m16;
-    if (t < cu.nvalid) {
-      const long off = kb0 + (long)t * kstride + c0;
-      auto put4 = [&](bf16* p, f4 x) {
-        *reinterpret_cast<uint2*>(p + off) = make_uint2(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]));
-      };
-      put4(dq, outq[Tt]);
-      put4(dk, outk[Tt]);
-      if constexpr (!B_S) put4(db, outb[Tt]);
-      put4(dg, dgv[Tt]);
-    }
-  }
   if constexpr (B_S) {
-    // sum over the token's d_k channels: 4 per lane, the 4 lane groups of a wave, then the
-    // NW waves through LDS (the M buffers are dead here)
-    float* sPart = reinterpret_cast<float*>(smem + Sh::OFF_M1);  // [NW][64]
-#pragma unroll
-    for (int Tt = 0; Tt < 4; ++Tt) {
-      float x = outb[Tt][0] + outb[Tt][1] + outb[Tt][2] + outb[Tt][3];
-      x += __shfl_xor(x, 16, 64);
-      x += __shfl_xor(x, 32, 64);
-      if (g4 == 0) sPart[wave * 64 + 16 * Tt + m16] = x;
-    }
     lds_barrier();
     if (tid < C) {
       float x = 0.f;
@@ -729,6 +750,10 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       for (int w = 0; w < Sh::NW; ++w) x += sPart[w * 64 + tid];
       if (tid < cu.nvalid) db[(cu.row + tid) * H + cu.h] = from_f<T>(x);
     }
+  }
+  cu = cn;
+  u = u_next;
+  lds_barrier();  // this unit's readers of LDS are done before the next unit's stores
   }
 }
 
@@ -756,12 +781,13 @@ static hipError_t launch_bwd(const BwdArgs& a) {
                  : f.gate_flags == 2 ? gdn2_bwd_local_kernel<DK, DV, 2>
                  : f.gate_flags == 1 ? gdn2_bwd_local_kernel<DK, DV, 1>
                                      : gdn2_bwd_local_kernel<DK, DV, 0>;
-    hipLaunchKernelGGL(local, dim3((unsigned)nunits),
+    const long grid = nunits < cu_count() ? nunits : cu_count();  // one per compute unit
+    hipLaunchKernelGGL(local, dim3((unsigned)grid),
                        dim3(LocalShape<DK, DV>::NT), 0, st, (const bf16*)f.q, (const bf16*)f.k,
                        (const bf16*)f.v, (const bf16*)f.g, (const bf16*)f.b, (const bf16*)f.w,
                        (const bf16*)a.d_o, (const char*)f.workspace, (bf16*)a.dq, (bf16*)a.dk,
                        (bf16*)a.dv, (bf16*)a.dg, (bf16*)a.db, (bf16*)a.dw, a.range_flag,
-                       f.cu_seqlens, f.N, f.T, f.H);
+                       f.cu_seqlens, f.N, f.T, f.H, nunits);
     e = hipGetLastError();
   }
   return e;
