@@ -61,7 +61,11 @@ struct ChunkShape {
   static constexpr int VCG = NV / 8;      // value-side prep: 8 columns per thread
   static constexpr int VTG = NT / VCG;
   static constexpr int VTPT = C / VTG;
-  static constexpr int PAD = 16 / (int)sizeof(T);  // 16-byte row padding (LDS banks)
+  // Row padding. The LDS has 128 four-byte banks and serves a 16-byte read in two passes of
+  // 32 lanes; a fragment read covers 16 rows x 2 slots per pass, which is free of bank
+  // conflicts when the row pitch is an odd multiple of 8 words (bf16 rows of DK + 16 and
+  // C + 16 elements; with 8 elements of padding every such read took two passes per half).
+  static constexpr int PAD = sizeof(T) == 2 ? 16 : 4;
   static constexpr int LDK = DK + PAD;    // pitch of [64][DK] arrays
   static constexpr int LDT = C + PAD;     // pitch of [x][64] arrays
   static constexpr int KS = Mma<T>::KS;

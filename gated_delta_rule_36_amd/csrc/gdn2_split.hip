@@ -35,7 +35,7 @@ struct PrepShape {
   static constexpr int VCG = DV / 8;      // value-side prep: 8 columns per thread
   static constexpr int VTG = NT / VCG;
   static constexpr int VTPT = C / VTG;
-  static constexpr int PAD = 8;           // 16-byte row padding
+  static constexpr int PAD = 16;          // row padding (odd multiple of 8 words: LDS banks)
   static constexpr int LDK = DK + PAD;
   static constexpr int LDT = C + PAD;
   static constexpr int NCT = DK / 16;     // key-channel tiles
