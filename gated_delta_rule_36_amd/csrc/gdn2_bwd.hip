@@ -266,7 +266,9 @@ struct LocalShape {
   static constexpr int VCG = DV / 8;
   static constexpr int VTG = NT / VCG;
   static constexpr int VTPT = C / VTG;
-  static constexpr int LDV = DV + 8, LDK = DK + 8, LDT = C + 8;
+  // [x][64] arrays: rows of 40 words (an odd multiple of 8: conflict-free fragment reads on
+  // the 128-bank LDS); [x][d] arrays 16 bytes longer (the LDS budget allows no more)
+  static constexpr int LDV = DV + 8, LDK = DK + 8, LDT = C + 16;
   static constexpr int NVT = DV / 16, NCT = DK / 16;
   // LDS regions (bytes)
   static constexpr int SZ_A = DK * LDV * 2;     // dSn, later S0: [DK][DV]
