@@ -123,6 +123,26 @@ def test_bwd_range_flag():
         run_bwd(x, do, None)
 
 
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64)])
+def test_bwd_many_units_sampled(dk, dv):
+    """1024 (chunk, head) units, more than one per workgroup of the persistent local-gradient
+    kernel (which walks units u, u + grid, ...), with a ragged last chunk and an initial
+    state; the sampled chains (sequences 1 and 3) are units of the later iterations."""
+    from oracle import gdn2_backward as ref_bwd
+    x = make_inputs(4, 1000, 16, dk, dv, "bf16", seed=410 + dk + dv, s0_std=0.02)
+    do, dsn = _upstream(x, 12 + dk + dv)
+    say("bwd many units B4 T1000 H16", dk, dv, "(sampled chains)")
+    out = run_bwd(x, do, dsn)
+    for (n, h) in [(3, 5), (1, 14)]:
+        sel = {m: x[m][n:n + 1, :, h:h + 1] for m in NAMES}
+        ref = ref_bwd(*(sel[m] for m in NAMES), do[n:n + 1, :, h:h + 1],
+                      dS_final=dsn[n:n + 1, h:h + 1], s0=x["s0"][n:n + 1, h:h + 1])
+        print(f" chain (n={n}, h={h})", flush=True)
+        for name, a, r in zip(GRADS, out[:6], ref[:6]):
+            assert_close(name, host64(a[n:n + 1, :, h:h + 1]), r, TOL["bf16"])
+        assert_close("ds0", host64(out[6][n:n + 1, h:h + 1]), ref[6], TOL["bf16"])
+
+
 def test_bwd_layer1p3b_full_size_sampled():
     from gdn2_inputs import make_config_inputs
     from oracle import gdn2_backward as ref_bwd

@@ -174,3 +174,33 @@ def test_backward_scalar_gates_varlen():
     ref[5] = ref[5].sum(-1)
     for name, a, r in zip(("dq", "dk", "dv", "dg", "db", "dw", "ds0"), grads, ref):
         assert_close(name, host64(a), r, TOL["bf16"])
+
+
+def test_backward_scalar_gates_many_units_sampled():
+    """Scalar b and w through the saved backward with 1024 (chunk, head) units, more than one
+    per workgroup of the persistent local-gradient kernel (its cross-wave db sum runs once
+    per unit); sampled chains of the later iterations against the oracle."""
+    import gated_delta_rule_36_amd as G
+    from gdn2_inputs import round_to_bf16
+    from oracle import gdn2_backward
+    B, T, H, dk, dv = 4, 1000, 16, 128, 128
+    x = make_inputs(B, T, H, dk, dv, "bf16", seed=81, s0_std=0.02)
+    gx, rx = _scalarise(x, "bw", (B, T, H), seed=83)
+    rng = np.random.default_rng(85)
+    do = round_to_bf16(rng.normal(size=(B, T, H, dv)).astype(np.float32))
+    say("backward scalar gates many units B4 T1000 H16 (sampled chains)")
+    t = {n: dev_tensor(gx[n], "bf16") for n in NAMES}
+    s0 = torch.from_numpy(x["s0"]).cuda()
+    o, sN, sv = G.chunk_fwd_train(*(t[n] for n in NAMES), initial_state=s0)
+    grads = G.chunk_bwd(*(t[n] for n in NAMES), dev_tensor(do, "bf16"), initial_state=s0, saved=sv)
+    torch.cuda.synchronize()
+    for (n, h) in [(3, 11), (2, 0)]:
+        sel = {m: rx[m][n:n + 1, :, h:h + 1] for m in NAMES}
+        ref = list(gdn2_backward(*(sel[m] for m in NAMES), do[n:n + 1, :, h:h + 1],
+                                 s0=x["s0"][n:n + 1, h:h + 1]))
+        ref[4] = ref[4].sum(-1)
+        ref[5] = ref[5].sum(-1)
+        print(f" chain (n={n}, h={h})", flush=True)
+        for name, a, r in zip(("dq", "dk", "dv", "dg", "db", "dw"), grads[:6], ref[:6]):
+            assert_close(name, host64(a[n:n + 1, :, h:h + 1]), r, TOL["bf16"])
+        assert_close("ds0", host64(grads[6][n:n + 1, h:h + 1]), ref[6], TOL["bf16"])
