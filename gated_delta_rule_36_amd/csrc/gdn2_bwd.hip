@@ -329,12 +329,8 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   float* sTot = reinterpret_cast<float*>(smem + Sh::OFF_TOT);
   int* sFlag = reinterpret_cast<int*>(smem + Sh::OFF_FLAG);
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int m16 = lane & 15, g4 = lane >> 4;
-  const int cg = tid % Sh::CG, tg = tid / Sh::CG;
-  const int vcg = tid % Sh::VCG, vtg = tid / Sh::VCG;
+  const int lane = threadIdx.x & 63;  // (the unit loop derives its own per-lane indices)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   const long kstride = (long)H * DK, vstride = (long)H * DV;
   // The workgroups are persistent (one per compute unit) and walk the units u = blockIdx.x,
@@ -367,395 +363,395 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   ChunkUnit cu = map_unit(u, H, cu_seqlens, N, T_len, lane);
   issue_first(u);
   while (u < nunits) {
-  const long u_next = u + gridDim.x;
-  const long u_pre = u_next < nunits ? u_next : u;  // the unit whose first group is prefetched
-  if (cu.nvalid == 0) {  // an unused slot (uniform)
-    cu = map_unit(u_pre, H, cu_seqlens, N, T_len, lane);
-    issue_first(u_pre);
-    u = u_next;
-    continue;
-  }
-  const char* unit = ws + u * LB.bytes;
-  const long kb0 = cu.row * kstride + (long)cu.h * DK;
-  const long vb0 = cu.row * vstride + (long)cu.h * DV;
-  // the per-lane indices, derived again for every unit from an opaque copy of the thread
-  // index, so that the offsets computed from them are not hoisted out of the unit loop
-  // (where they would hold registers through the whole kernel)
-  int tid_u = threadIdx.x;
-  asm volatile("" : "+v"(tid_u));
-  const int tid = tid_u, lane = tid & 63, m16 = lane & 15, g4 = lane >> 4;
-  const int cg = tid % Sh::CG, tg = tid / Sh::CG, vcg = tid % Sh::VCG, vtg = tid / Sh::VCG;
-  auto clamp_row = [&](int r) { return r < cu.nvalid ? r : 0; };
-  uint4 rdo[NDO];
-#pragma unroll
-  for (int i = 0; i < NDO; ++i) {
-    const int p = tid + i * NT, r = clamp_row(p / (DV / 8)), cc = p % (DV / 8);
-    rdo[i] = *reinterpret_cast<const uint4*>(d_o + vb0 + (long)r * vstride + cc * 8);
-  }
-  bf16x4 s0t[NVT];
-  Vec8<T> rq[Sh::TPT], rk[Sh::TPT], rg[Sh::TPT], rb[Sh::TPT], rv[Sh::VTPT], rw[Sh::VTPT];
-  bool kvalid[Sh::TPT];
-#pragma unroll
-  for (int j = 0; j < Sh::TPT; ++j) {
-    kvalid[j] = tg * Sh::TPT + j < cu.nvalid;
-    const long off = kb0 + (long)clamp_row(tg * Sh::TPT + j) * kstride + cg * 8;
-    rg[j].load(g + off);
-    rk[j].load(k + off);
-  }
-#pragma unroll
-  for (int ct = 0; ct < NVT; ++ct) s0t[ct] = tile_raw(unit, LB.h, ct * Sh::NCT + wave);
-#pragma unroll
-  for (int j = 0; j < Sh::VTPT; ++j) {  // rows past the end give outputs that are not stored
-    const int r = clamp_row(vtg * Sh::VTPT + j);
-    rv[j].load(v + vb0 + (long)r * vstride + vcg * 8);
-    if constexpr (W_S) rw[j].load_one(wg + (cu.row + r) * H + cu.h);
-    else rw[j].load(wg + vb0 + (long)r * vstride + vcg * 8);
-  }
-#pragma unroll
-  for (int j = 0; j < Sh::TPT; ++j) {
-    const int r = clamp_row(tg * Sh::TPT + j);
-    rq[j].load(q + kb0 + (long)r * kstride + cg * 8);
-    if constexpr (B_S) rb[j].load_one(bg + (cu.row + r) * H + cu.h);
-    else rb[j].load(bg + kb0 + (long)r * kstride + cg * 8);
-  }
+    const long u_next = u + gridDim.x;
+    const long u_pre = u_next < nunits ? u_next : u;  // the unit whose first group is prefetched
+    if (cu.nvalid == 0) {  // an unused slot (uniform)
+      cu = map_unit(u_pre, H, cu_seqlens, N, T_len, lane);
+      issue_first(u_pre);
+      u = u_next;
+      continue;
+    }
+    const char* unit = ws + u * LB.bytes;
+    const long kb0 = cu.row * kstride + (long)cu.h * DK;
+    const long vb0 = cu.row * vstride + (long)cu.h * DV;
+    // the per-lane indices, derived again for every unit from an opaque copy of the thread
+    // index, so that the offsets computed from them are not hoisted out of the unit loop
+    // (where they would hold registers through the whole kernel)
+    int tid_u = threadIdx.x;
+    asm volatile("" : "+v"(tid_u));
+    const int tid = tid_u, lane = tid & 63, m16 = lane & 15, g4 = lane >> 4;
+    const int cg = tid % Sh::CG, tg = tid / Sh::CG, vcg = tid % Sh::VCG, vtg = tid / Sh::VCG;
+    auto clamp_row = [&](int r) { return r < cu.nvalid ? r : 0; };
+    uint4 rdo[NDO];
+  #pragma unroll
+    for (int i = 0; i < NDO; ++i) {
+      const int p = tid + i * NT, r = clamp_row(p / (DV / 8)), cc = p % (DV / 8);
+      rdo[i] = *reinterpret_cast<const uint4*>(d_o + vb0 + (long)r * vstride + cc * 8);
+    }
+    bf16x4 s0t[NVT];
+    Vec8<T> rq[Sh::TPT], rk[Sh::TPT], rg[Sh::TPT], rb[Sh::TPT], rv[Sh::VTPT], rw[Sh::VTPT];
+    bool kvalid[Sh::TPT];
+  #pragma unroll
+    for (int j = 0; j < Sh::TPT; ++j) {
+      kvalid[j] = tg * Sh::TPT + j < cu.nvalid;
+      const long off = kb0 + (long)clamp_row(tg * Sh::TPT + j) * kstride + cg * 8;
+      rg[j].load(g + off);
+      rk[j].load(k + off);
+    }
+  #pragma unroll
+    for (int ct = 0; ct < NVT; ++ct) s0t[ct] = tile_raw(unit, LB.h, ct * Sh::NCT + wave);
+  #pragma unroll
+    for (int j = 0; j < Sh::VTPT; ++j) {  // rows past the end give outputs that are not stored
+      const int r = clamp_row(vtg * Sh::VTPT + j);
+      rv[j].load(v + vb0 + (long)r * vstride + vcg * 8);
+      if constexpr (W_S) rw[j].load_one(wg + (cu.row + r) * H + cu.h);
+      else rw[j].load(wg + vb0 + (long)r * vstride + vcg * 8);
+    }
+  #pragma unroll
+    for (int j = 0; j < Sh::TPT; ++j) {
+      const int r = clamp_row(tg * Sh::TPT + j);
+      rq[j].load(q + kb0 + (long)r * kstride + cg * 8);
+      if constexpr (B_S) rb[j].load_one(bg + (cu.row + r) * H + cu.h);
+      else rb[j].load(bg + kb0 + (long)r * kstride + cg * 8);
+    }
 
-  // ---- dO, dZ and U (tiles (ct, R)) row-major, dSn into LDS. A dO row past the end holds
-  // row 0's values: it reaches only M1's row of that token (zeroed in P1) and dQbar's column
-  // of that token (not stored).
-#pragma unroll
-  for (int i = 0; i < NDO; ++i) {
-    const int p = tid + i * NT, r = p / (DV / 8), cc = p % (DV / 8);
-    *reinterpret_cast<uint4*>(sO + r * LDV + cc * 8) = rdo[i];
-  }
-  auto ident = [](int c) { return c; };
-#pragma unroll
-  for (int i = 0; i < NZU; ++i) {
-    const int t = wave + i * Sh::NW, ct = t / 4, R = t % 4;
-    store_tile_pairs(sZ + (16 * R) * LDV + 16 * ct, LDV, lane, tof(rz[i]), ident);
-    store_tile_pairs(sU + (16 * R) * LDV + 16 * ct, LDV, lane, tof(ru[i]), ident);
-  }
-#pragma unroll
-  for (int ct = 0; ct < NVT; ++ct)
-    store_tile_pairs(sA + (16 * wave) * LDV + 16 * ct, LDV, lane, tof(rds[ct]), ident);
-  if (tid == 0) *sFlag = 0;
-  lds_barrier();
+    // ---- dO, dZ and U (tiles (ct, R)) row-major, dSn into LDS. A dO row past the end holds
+    // row 0's values: it reaches only M1's row of that token (zeroed in P1) and dQbar's column
+    // of that token (not stored).
+  #pragma unroll
+    for (int i = 0; i < NDO; ++i) {
+      const int p = tid + i * NT, r = p / (DV / 8), cc = p % (DV / 8);
+      *reinterpret_cast<uint4*>(sO + r * LDV + cc * 8) = rdo[i];
+    }
+    auto ident = [](int c) { return c; };
+  #pragma unroll
+    for (int i = 0; i < NZU; ++i) {
+      const int t = wave + i * Sh::NW, ct = t / 4, R = t % 4;
+      store_tile_pairs(sZ + (16 * R) * LDV + 16 * ct, LDV, lane, tof(rz[i]), ident);
+      store_tile_pairs(sU + (16 * R) * LDV + 16 * ct, LDV, lane, tof(ru[i]), ident);
+    }
+  #pragma unroll
+    for (int ct = 0; ct < NVT; ++ct)
+      store_tile_pairs(sA + (16 * wave) * LDV + 16 * ct, LDV, lane, tof(rds[ct]), ident);
+    if (tid == 0) *sFlag = 0;
+    lds_barrier();
 
-  // ---- P1: M1 = lower_incl(dO U^T), M2 = -strict(dZ U^T); stored row-major and transposed
-  for (int t = wave; t < 32; t += Sh::NW) {
-    const int which = t >> 4, R = (t >> 2) & 3, I = t & 3;
-    const T* lhs = which ? sZ : sO;
-    f4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (I <= R) {
-#pragma unroll
+    // ---- P1: M1 = lower_incl(dO U^T), M2 = -strict(dZ U^T); stored row-major and transposed
+    for (int t = wave; t < 32; t += Sh::NW) {
+      const int which = t >> 4, R = (t >> 2) & 3, I = t & 3;
+      const T* lhs = which ? sZ : sO;
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (I <= R) {
+  #pragma unroll
+        for (int s = 0; s < DV / 32; ++s)
+          acc = M::mma(M::load(lhs, LDV, 16 * R + m16, 32 * s + 8 * g4),
+                       M::load(sU, LDV, 16 * I + m16, 32 * s + 8 * g4), acc);
+      }
+      f4 val;
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g4 + i, c = m16;  // row (token t) within R, column (token i) within I
+        const bool keep = (I < R || (which ? c < r : c <= r)) && (which || 16 * R + r < cu.nvalid);
+        val[i] = keep ? (which ? -acc[i] : acc[i]) : 0.f;
+      }
+      T* Mr = which ? sM2 : sM1;
+      T* Mt = which ? sM2t : sM1t;
+      store_tile_pairs(Mr + (16 * R) * LDT + 16 * I, LDT, lane, val, ident);
+      *reinterpret_cast<uint2*>(Mt + (16 * I + m16) * LDT + 16 * R + 4 * g4) =
+          make_uint2(pack_bf16(val[0], val[1]), pack_bf16(val[2], val[3]));
+    }
+    // ---- P2: dKtil^T = dSn U^T   (rows: this wave's channels; columns: tokens)
+    f4 dKt[4];
+  #pragma unroll
+    for (int Tt = 0; Tt < 4; ++Tt) {
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
       for (int s = 0; s < DV / 32; ++s)
-        acc = M::mma(M::load(lhs, LDV, 16 * R + m16, 32 * s + 8 * g4),
-                     M::load(sU, LDV, 16 * I + m16, 32 * s + 8 * g4), acc);
+        acc = M::mma(M::load(sA, LDV, 16 * wave + m16, 32 * s + 8 * g4),
+                     M::load(sU, LDV, 16 * Tt + m16, 32 * s + 8 * g4), acc);
+      dKt[Tt] = acc;
     }
-    f4 val;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * g4 + i, c = m16;  // row (token t) within R, column (token i) within I
-      const bool keep = (I < R || (which ? c < r : c <= r)) && (which || 16 * R + r < cu.nvalid);
-      val[i] = keep ? (which ? -acc[i] : acc[i]) : 0.f;
-    }
-    T* Mr = which ? sM2 : sM1;
-    T* Mt = which ? sM2t : sM1t;
-    store_tile_pairs(Mr + (16 * R) * LDT + 16 * I, LDT, lane, val, ident);
-    *reinterpret_cast<uint2*>(Mt + (16 * I + m16) * LDT + 16 * R + 4 * g4) =
-        make_uint2(pack_bf16(val[0], val[1]), pack_bf16(val[2], val[3]));
-  }
-  // ---- P2: dKtil^T = dSn U^T   (rows: this wave's channels; columns: tokens)
-  f4 dKt[4];
-#pragma unroll
-  for (int Tt = 0; Tt < 4; ++Tt) {
-    f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < DV / 32; ++s)
-      acc = M::mma(M::load(sA, LDV, 16 * wave + m16, 32 * s + 8 * g4),
-                   M::load(sU, LDV, 16 * Tt + m16, 32 * s + 8 * g4), acc);
-    dKt[Tt] = acc;
-  }
-  // ---- (a): per-thread totals of log2-decay (a row past the end decays by nothing) into
-  // sTot, which shares the Khat^T region (written only after the scan's prefixes are read)
-#pragma unroll
-  for (int j = 0; j < Sh::TPT; ++j) {
-    hold(rg[j].r, dKt[3][3]);
-    hold(rk[j].r, dKt[3][3]);
-    if (!kvalid[j]) { rg[j].zero(); rk[j].zero(); }
-  }
-  {
-    float tot8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
+    // ---- (a): per-thread totals of log2-decay (a row past the end decays by nothing) into
+    // sTot, which shares the Khat^T region (written only after the scan's prefixes are read)
+  #pragma unroll
     for (int j = 0; j < Sh::TPT; ++j) {
-      float f[8];
-      rg[j].to_float(f);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) tot8[i] += f[i];
+      hold(rg[j].r, dKt[3][3]);
+      hold(rk[j].r, dKt[3][3]);
+      if (!kvalid[j]) { rg[j].zero(); rk[j].zero(); }
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) tot8[i] *= kLog2e;
-    store8(sTot + tg * DK + cg * 8, tot8);
-  }
-  lds_barrier();  // M1, M2 written; the totals complete; dSn and U are dead
-  // ---- (b): the per-channel scan and the chunk factors
-  channel_scan<DK, Sh::TG, Sh::GPB, NT>(sTot, sFac, sFlag, tid);
-  lds_barrier();
-  (void)sFlag;
-  if (tid < DK && range_flag != nullptr && -sFac[Fac::GL * DK + tid] > 2.f * kFastPathMaxDecay2)
-    *range_flag = 1;
-  // this thread's channels' reference Gm = Glast / 2 (log2)
-  float Gm8[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) Gm8[i] = 0.5f * sFac[Fac::GL * DK + cg * 8 + i];
-  // per thread: G (log2) of its tokens; Khat'^T = (K 2^(Gm-G))^T (stored below)
-  float G2[Sh::TPT][8];
-  RunBuf<T, Sh::TPT> kh[8];
-  {
-    float run[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) run[i] = sTot[tg * DK + cg * 8 + i];
-#pragma unroll
-    for (int j = 0; j < Sh::TPT; ++j) {
-      float fg[8], fk[8];
-      rg[j].to_float(fg);
-      rk[j].to_float(fk);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        run[i] += fg[i] * kLog2e;
-        G2[j][i] = run[i];
-        kh[i].put(j, fk[i] * fast_exp2(Gm8[i] - run[i]));
+    {
+      float tot8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+      for (int j = 0; j < Sh::TPT; ++j) {
+        float f[8];
+        rg[j].to_float(f);
+  #pragma unroll
+        for (int i = 0; i < 8; ++i) tot8[i] += f[i];
+      }
+  #pragma unroll
+      for (int i = 0; i < 8; ++i) tot8[i] *= kLog2e;
+      store8(sTot + tg * DK + cg * 8, tot8);
+    }
+    lds_barrier();  // M1, M2 written; the totals complete; dSn and U are dead
+    // ---- (b): the per-channel scan and the chunk factors
+    channel_scan<DK, Sh::TG, Sh::GPB, NT>(sTot, sFac, sFlag, tid);
+    lds_barrier();
+    (void)sFlag;
+    if (tid < DK && range_flag != nullptr && -sFac[Fac::GL * DK + tid] > 2.f * kFastPathMaxDecay2)
+      *range_flag = 1;
+    // this thread's channels' reference Gm = Glast / 2 (log2)
+    float Gm8[8];
+  #pragma unroll
+    for (int i = 0; i < 8; ++i) Gm8[i] = 0.5f * sFac[Fac::GL * DK + cg * 8 + i];
+    // per thread: G (log2) of its tokens; Khat'^T = (K 2^(Gm-G))^T (stored below)
+    float G2[Sh::TPT][8];
+    RunBuf<T, Sh::TPT> kh[8];
+    {
+      float run[8];
+  #pragma unroll
+      for (int i = 0; i < 8; ++i) run[i] = sTot[tg * DK + cg * 8 + i];
+  #pragma unroll
+      for (int j = 0; j < Sh::TPT; ++j) {
+        float fg[8], fk[8];
+        rg[j].to_float(fg);
+        rk[j].to_float(fk);
+  #pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          run[i] += fg[i] * kLog2e;
+          G2[j][i] = run[i];
+          kh[i].put(j, fk[i] * fast_exp2(Gm8[i] - run[i]));
+        }
       }
     }
-  }
-  {
-    // S0 rows (this lane's channels 16 wave + 4 g4 + i) scaled by 2^Gm into sA (dSn is
-    // dead); the dg constant X_c = sum_v dSn[c,v] S0[c,v] (times gamma_c later)
-    const f4 gl = *reinterpret_cast<const f4*>(sFac + Fac::GL * DK + 16 * wave + 4 * g4);
-#pragma unroll
-    for (int ct = 0; ct < NVT; ++ct) hold(s0t[ct], gl[0]);
-    f4 rs, xs = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) rs[i] = fast_exp2(0.5f * gl[i]);
-#pragma unroll
-    for (int ct = 0; ct < NVT; ++ct) {
-      const f4 s0 = tof(s0t[ct]);
-      store_tile_pairs(sA + (16 * wave) * LDV + 16 * ct, LDV, lane, s0 * rs, ident);
-      xs += tof(rds[ct]) * s0;
+    {
+      // S0 rows (this lane's channels 16 wave + 4 g4 + i) scaled by 2^Gm into sA (dSn is
+      // dead); the dg constant X_c = sum_v dSn[c,v] S0[c,v] (times gamma_c later)
+      const f4 gl = *reinterpret_cast<const f4*>(sFac + Fac::GL * DK + 16 * wave + 4 * g4);
+  #pragma unroll
+      for (int ct = 0; ct < NVT; ++ct) hold(s0t[ct], gl[0]);
+      f4 rs, xs = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) rs[i] = fast_exp2(0.5f * gl[i]);
+  #pragma unroll
+      for (int ct = 0; ct < NVT; ++ct) {
+        const f4 s0 = tof(s0t[ct]);
+        store_tile_pairs(sA + (16 * wave) * LDV + 16 * ct, LDV, lane, s0 * rs, ident);
+        xs += tof(rds[ct]) * s0;
+      }
+  #pragma unroll
+      for (int m = 1; m < 16; m <<= 1)
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) xs[i] += __shfl_xor(xs[i], m, 64);
+      if (m16 == 0) *reinterpret_cast<f4*>(sX + 16 * wave + 4 * g4) = xs;
     }
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xs[i] += __shfl_xor(xs[i], m, 64);
-    if (m16 == 0) *reinterpret_cast<f4*>(sX + 16 * wave + 4 * g4) = xs;
-  }
-  // dv = dZ * w, dw = dZ * v
-#pragma unroll
-  for (int j = 0; j < Sh::VTPT; ++j) {
-    const int r = vtg * Sh::VTPT + j;
-    float fz[8], fv[8], fw[8], o1[8], o2[8];
-    Vec8<T> z;
-    z.load(sZ + r * LDV + vcg * 8);
-    z.to_float(fz);
-    hold(rv[j].r, fz[0]);
-    hold(rw[j].r, fz[0]);
-    rv[j].to_float(fv);
-    if constexpr (W_S) rw[j].splat();
-    rw[j].to_float(fw);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) { o1[i] = fz[i] * fw[i]; o2[i] = fz[i] * fv[i]; }
-    if (r < cu.nvalid) {
-      const long off = vb0 + (long)r * vstride + vcg * 8;
-      store8(dv + off, o1);
-      if constexpr (!W_S) store8(dw + off, o2);
-    }
-    if constexpr (W_S) {  // sum over the token's d_v channels (VCG adjacent lanes)
-      float sw = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sw += o2[i];
-#pragma unroll
-      for (int m = 1; m < Sh::VCG; m <<= 1) sw += __shfl_xor(sw, m, 64);
-      if (vcg == 0 && r < cu.nvalid) dw[(cu.row + r) * H + cu.h] = from_f<T>(sw);
-    }
-  }
-  lds_barrier();  // the prefixes in sTot are read
-  {
-    const int sw = tswz(cg * 8);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) kh[i].store_sw(sKh + (cg * 8 + i) * LDT, sw, tg * Sh::TPT);
-  }
-  lds_barrier();
-  // ---- P3: dQbar^T = S0 dO^T + Khat^T M1^T,  dEbar^T = -S0 dZ^T + Khat^T M2^T
-  f4 dQb[4], dEb[4];
-#pragma unroll
-  for (int Tt = 0; Tt < 4; ++Tt) {
-    f4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < DV / 32; ++s) {
-      const typename M::frag sf = M::load(sA, LDV, 16 * wave + m16, 32 * s + 8 * g4);
-      a1 = M::mma(sf, M::load(sO, LDV, 16 * Tt + m16, 32 * s + 8 * g4), a1);
-      a2 = M::mma(sf, M::load(sZ, LDV, 16 * Tt + m16, 32 * s + 8 * g4), a2);
-    }
-    a2 = -a2;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const typename M::frag kf = M::load_phi_t(sKh, LDT, 16 * wave + m16, s, g4);
-      a1 = M::mma(kf, M::load(sM1, LDT, 16 * Tt + m16, 32 * s + 8 * g4), a1);
-      a2 = M::mma(kf, M::load(sM2, LDT, 16 * Tt + m16, 32 * s + 8 * g4), a2);
-    }
-    dQb[Tt] = a1;
-    dEb[Tt] = a2;
-  }
-  lds_barrier();  // S0, dO, dZ are dead
-  // Ebar^T = (b k 2^G)^T and Qbar^T = (q 2^G)^T, natural token order, into the big region
-  T* sEt = reinterpret_cast<T*>(smem);
-  T* sQt = sEt + DK * LDT;
-  {
-    RunBuf<T, Sh::TPT> ev[8], qv[8];
-#pragma unroll
-    for (int j = 0; j < Sh::TPT; ++j) {
-      float fq[8], fk[8], fb[8];
-      hold(rq[j].r, dQb[3][3]);
-      hold(rb[j].r, dQb[3][3]);
-      if (!kvalid[j]) { rq[j].zero(); rb[j].zero(); }
-      rq[j].to_float(fq);
-      rk[j].to_float(fk);
-      if constexpr (B_S) rb[j].splat();  // (also what the elementwise step reads back)
-      rb[j].to_float(fb);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float gm = fast_exp2(G2[j][i] - Gm8[i]);
-        ev[i].put(j, fb[i] * fk[i] * gm);
-        qv[i].put(j, fq[i] * gm);
+    // dv = dZ * w, dw = dZ * v
+  #pragma unroll
+    for (int j = 0; j < Sh::VTPT; ++j) {
+      const int r = vtg * Sh::VTPT + j;
+      float fz[8], fv[8], fw[8], o1[8], o2[8];
+      Vec8<T> z;
+      z.load(sZ + r * LDV + vcg * 8);
+      z.to_float(fz);
+      hold(rv[j].r, fz[0]);
+      hold(rw[j].r, fz[0]);
+      rv[j].to_float(fv);
+      if constexpr (W_S) rw[j].splat();
+      rw[j].to_float(fw);
+  #pragma unroll
+      for (int i = 0; i < 8; ++i) { o1[i] = fz[i] * fw[i]; o2[i] = fz[i] * fv[i]; }
+      if (r < cu.nvalid) {
+        const long off = vb0 + (long)r * vstride + vcg * 8;
+        store8(dv + off, o1);
+        if constexpr (!W_S) store8(dw + off, o2);
+      }
+      if constexpr (W_S) {  // sum over the token's d_v channels (VCG adjacent lanes)
+        float sw = 0.f;
+  #pragma unroll
+        for (int i = 0; i < 8; ++i) sw += o2[i];
+  #pragma unroll
+        for (int m = 1; m < Sh::VCG; m <<= 1) sw += __shfl_xor(sw, m, 64);
+        if (vcg == 0 && r < cu.nvalid) dw[(cu.row + r) * H + cu.h] = from_f<T>(sw);
       }
     }
-    const int sw = tswz(cg * 8);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ev[i].store_sw(sEt + (cg * 8 + i) * LDT, sw, tg * Sh::TPT);
-      qv[i].store_sw(sQt + (cg * 8 + i) * LDT, sw, tg * Sh::TPT);
+    lds_barrier();  // the prefixes in sTot are read
+    {
+      const int sw = tswz(cg * 8);
+  #pragma unroll
+      for (int i = 0; i < 8; ++i) kh[i].store_sw(sKh + (cg * 8 + i) * LDT, sw, tg * Sh::TPT);
     }
-  }
-  lds_barrier();
-  // ---- P4: dKhat^T = Ebar^T M2 + Qbar^T M1
-  f4 dKh[4];
-#pragma unroll
-  for (int Tt = 0; Tt < 4; ++Tt) {
-    f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      acc = M::mma(M::load_phi_t(sEt, LDT, 16 * wave + m16, s, g4),
-                   M::load(sM2t, LDT, 16 * Tt + m16, 32 * s + 8 * g4), acc);
-      acc = M::mma(M::load_phi_t(sQt, LDT, 16 * wave + m16, s, g4),
-                   M::load(sM1t, LDT, 16 * Tt + m16, 32 * s + 8 * g4), acc);
+    lds_barrier();
+    // ---- P3: dQbar^T = S0 dO^T + Khat^T M1^T,  dEbar^T = -S0 dZ^T + Khat^T M2^T
+    f4 dQb[4], dEb[4];
+  #pragma unroll
+    for (int Tt = 0; Tt < 4; ++Tt) {
+      f4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+      for (int s = 0; s < DV / 32; ++s) {
+        const typename M::frag sf = M::load(sA, LDV, 16 * wave + m16, 32 * s + 8 * g4);
+        a1 = M::mma(sf, M::load(sO, LDV, 16 * Tt + m16, 32 * s + 8 * g4), a1);
+        a2 = M::mma(sf, M::load(sZ, LDV, 16 * Tt + m16, 32 * s + 8 * g4), a2);
+      }
+      a2 = -a2;
+  #pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const typename M::frag kf = M::load_phi_t(sKh, LDT, 16 * wave + m16, s, g4);
+        a1 = M::mma(kf, M::load(sM1, LDT, 16 * Tt + m16, 32 * s + 8 * g4), a1);
+        a2 = M::mma(kf, M::load(sM2, LDT, 16 * Tt + m16, 32 * s + 8 * g4), a2);
+      }
+      dQb[Tt] = a1;
+      dEb[Tt] = a2;
     }
-    dKh[Tt] = acc;
-  }
-  lds_barrier();  // everything but the factors is dead
-  // G (log2, fp32) and q, k, b row-major for the elementwise step
-  float* sG = reinterpret_cast<float*>(smem);
-  T* sq = reinterpret_cast<T*>(smem + C * DK * 4);
-  T* sk = sq + C * LDK;
-  T* sb = sk + C * LDK;
-#pragma unroll
-  for (int j = 0; j < Sh::TPT; ++j) {
-    const int r = tg * Sh::TPT + j;
-    store8(sG + r * DK + cg * 8, G2[j]);
-    *reinterpret_cast<uint4*>(sq + r * LDK + cg * 8) = rq[j].r;
-    *reinterpret_cast<uint4*>(sk + r * LDK + cg * 8) = rk[j].r;
-    *reinterpret_cast<uint4*>(sb + r * LDK + cg * 8) = rb[j].r;
-  }
-  lds_barrier();
+    lds_barrier();  // S0, dO, dZ are dead
+    // Ebar^T = (b k 2^G)^T and Qbar^T = (q 2^G)^T, natural token order, into the big region
+    T* sEt = reinterpret_cast<T*>(smem);
+    T* sQt = sEt + DK * LDT;
+    {
+      RunBuf<T, Sh::TPT> ev[8], qv[8];
+  #pragma unroll
+      for (int j = 0; j < Sh::TPT; ++j) {
+        float fq[8], fk[8], fb[8];
+        hold(rq[j].r, dQb[3][3]);
+        hold(rb[j].r, dQb[3][3]);
+        if (!kvalid[j]) { rq[j].zero(); rb[j].zero(); }
+        rq[j].to_float(fq);
+        rk[j].to_float(fk);
+        if constexpr (B_S) rb[j].splat();  // (also what the elementwise step reads back)
+        rb[j].to_float(fb);
+  #pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float gm = fast_exp2(G2[j][i] - Gm8[i]);
+          ev[i].put(j, fb[i] * fk[i] * gm);
+          qv[i].put(j, fq[i] * gm);
+        }
+      }
+      const int sw = tswz(cg * 8);
+  #pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ev[i].store_sw(sEt + (cg * 8 + i) * LDT, sw, tg * Sh::TPT);
+        qv[i].store_sw(sQt + (cg * 8 + i) * LDT, sw, tg * Sh::TPT);
+      }
+    }
+    lds_barrier();
+    // ---- P4: dKhat^T = Ebar^T M2 + Qbar^T M1
+    f4 dKh[4];
+  #pragma unroll
+    for (int Tt = 0; Tt < 4; ++Tt) {
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        acc = M::mma(M::load_phi_t(sEt, LDT, 16 * wave + m16, s, g4),
+                     M::load(sM2t, LDT, 16 * Tt + m16, 32 * s + 8 * g4), acc);
+        acc = M::mma(M::load_phi_t(sQt, LDT, 16 * wave + m16, s, g4),
+                     M::load(sM1t, LDT, 16 * Tt + m16, 32 * s + 8 * g4), acc);
+      }
+      dKh[Tt] = acc;
+    }
+    lds_barrier();  // everything but the factors is dead
+    // G (log2, fp32) and q, k, b row-major for the elementwise step
+    float* sG = reinterpret_cast<float*>(smem);
+    T* sq = reinterpret_cast<T*>(smem + C * DK * 4);
+    T* sk = sq + C * LDK;
+    T* sb = sk + C * LDK;
+  #pragma unroll
+    for (int j = 0; j < Sh::TPT; ++j) {
+      const int r = tg * Sh::TPT + j;
+      store8(sG + r * DK + cg * 8, G2[j]);
+      *reinterpret_cast<uint4*>(sq + r * LDK + cg * 8) = rq[j].r;
+      *reinterpret_cast<uint4*>(sk + r * LDK + cg * 8) = rk[j].r;
+      *reinterpret_cast<uint4*>(sb + r * LDK + cg * 8) = rb[j].r;
+    }
+    lds_barrier();
 
-  // ---- elementwise: lane = token 16*Tt + m16, channels c0 .. c0 + 3 of this wave
-  const int c0 = 16 * wave + 4 * g4;
-  const f4 gam = *reinterpret_cast<const f4*>(sFac + Fac::GAM * DK + c0);
-  const f4 gl = *reinterpret_cast<const f4*>(sFac + Fac::GL * DK + c0);
-  const f4 xc = *reinterpret_cast<const f4*>(sX + c0);
-  // dq, dk and db of a token tile are stored as soon as they are formed; dg waits for the
-  // suffix sums over the chunk
-  auto put4 = [&](bf16* p, long off, f4 x) {
-    *reinterpret_cast<uint2*>(p + off) = make_uint2(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]));
-  };
-  float* sPart = reinterpret_cast<float*>(smem + Sh::OFF_M1);  // scalar db: [NW][64] partials
-  f4 dgv[4];
-  f4 totB = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int Tt = 0; Tt < 4; ++Tt) {
-    const int t = 16 * Tt + m16;
-    const f4 G = *reinterpret_cast<const f4*>(sG + t * DK + c0);
-    const f4 fq = load4f(sq + t * LDK + c0), fk = load4f(sk + t * LDK + c0);
-    const f4 fb = load4f(sb + t * LDK + c0);
-    f4 A, Bv, outq, outk, outb;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // mid-referenced factors (dQb, dEb, dKh carry the 2^(+-Gm) of their operands)
-      const float gmr = 0.5f * gl[i];
-      const float gm = fast_exp2(G[i] - gmr), ig = fast_exp2(gmr - G[i]);
-      const float kt = fast_exp2(gl[i] - G[i]);  // 2^(Glast - G) <= 1
-      const float dE = dEb[Tt][i] * gm;
-      outq[i] = dQb[Tt][i] * gm;
-      outk[i] = dKh[Tt][i] * ig + dKt[Tt][i] * kt + dE * fb[i];
-      outb[i] = dE * fk[i];
-      // dG = dEbar Ebar + dQbar Qbar - dKhat Khat - dKtil Ktil, split as A - B
-      A[i] = gm * (dEb[Tt][i] * fb[i] * fk[i] + dQb[Tt][i] * fq[i]) - dKh[Tt][i] * fk[i] * ig;
-      Bv[i] = dKt[Tt][i] * fk[i] * kt;
+    // ---- elementwise: lane = token 16*Tt + m16, channels c0 .. c0 + 3 of this wave
+    const int c0 = 16 * wave + 4 * g4;
+    const f4 gam = *reinterpret_cast<const f4*>(sFac + Fac::GAM * DK + c0);
+    const f4 gl = *reinterpret_cast<const f4*>(sFac + Fac::GL * DK + c0);
+    const f4 xc = *reinterpret_cast<const f4*>(sX + c0);
+    // dq, dk and db of a token tile are stored as soon as they are formed; dg waits for the
+    // suffix sums over the chunk
+    auto put4 = [&](bf16* p, long off, f4 x) {
+      *reinterpret_cast<uint2*>(p + off) = make_uint2(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]));
+    };
+    float* sPart = reinterpret_cast<float*>(smem + Sh::OFF_M1);  // scalar db: [NW][64] partials
+    f4 dgv[4];
+    f4 totB = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+    for (int Tt = 0; Tt < 4; ++Tt) {
+      const int t = 16 * Tt + m16;
+      const f4 G = *reinterpret_cast<const f4*>(sG + t * DK + c0);
+      const f4 fq = load4f(sq + t * LDK + c0), fk = load4f(sk + t * LDK + c0);
+      const f4 fb = load4f(sb + t * LDK + c0);
+      f4 A, Bv, outq, outk, outb;
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // mid-referenced factors (dQb, dEb, dKh carry the 2^(+-Gm) of their operands)
+        const float gmr = 0.5f * gl[i];
+        const float gm = fast_exp2(G[i] - gmr), ig = fast_exp2(gmr - G[i]);
+        const float kt = fast_exp2(gl[i] - G[i]);  // 2^(Glast - G) <= 1
+        const float dE = dEb[Tt][i] * gm;
+        outq[i] = dQb[Tt][i] * gm;
+        outk[i] = dKh[Tt][i] * ig + dKt[Tt][i] * kt + dE * fb[i];
+        outb[i] = dE * fk[i];
+        // dG = dEbar Ebar + dQbar Qbar - dKhat Khat - dKtil Ktil, split as A - B
+        A[i] = gm * (dEb[Tt][i] * fb[i] * fk[i] + dQb[Tt][i] * fq[i]) - dKh[Tt][i] * fk[i] * ig;
+        Bv[i] = dKt[Tt][i] * fk[i] * kt;
+      }
+      dgv[Tt] = A - Bv;
+      totB += Bv;
+      if (t < cu.nvalid) {
+        const long off = kb0 + (long)t * kstride + c0;
+        put4(dq, off, outq);
+        put4(dk, off, outk);
+        if constexpr (!B_S) put4(db, off, outb);
+      }
+      if constexpr (B_S) {
+        // a scalar b's gradient sums the token's d_k channels: 4 per lane, the 4 lane groups
+        // of a wave, then the NW waves through LDS (the M buffers are dead here)
+        float x = outb[0] + outb[1] + outb[2] + outb[3];
+        x += __shfl_xor(x, 16, 64);
+        x += __shfl_xor(x, 32, 64);
+        if (g4 == 0) sPart[wave * 64 + t] = x;
+      }
     }
-    dgv[Tt] = A - Bv;
-    totB += Bv;
-    if (t < cu.nvalid) {
-      const long off = kb0 + (long)t * kstride + c0;
-      put4(dq, off, outq);
-      put4(dk, off, outk);
-      if constexpr (!B_S) put4(db, off, outb);
+    // the next unit's first load group, in flight from here on
+    const ChunkUnit cn = map_unit(u_pre, H, cu_seqlens, N, T_len, lane);
+    issue_first(u_pre);
+    // dg_t = sum_{t' >= t} (A - B)_{t'} + sum_all B + gamma X   (suffix sums over 64 tokens)
+  #pragma unroll
+    for (int m = 1; m < 16; m <<= 1)
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) totB[i] += __shfl_xor(totB[i], m, 64);
+    f4 carry = totB + gam * xc;
+  #pragma unroll
+    for (int Tt = 3; Tt >= 0; --Tt) {
+      f4 x = dgv[Tt];
+  #pragma unroll
+      for (int d = 1; d < 16; d <<= 1) {
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float y = __shfl_down(x[i], d, 16);
+          x[i] += (m16 + d < 16) ? y : 0.f;
+        }
+      }
+      f4 tile_tot;
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) tile_tot[i] = __shfl(x[i], lane & ~15, 64);
+      const int t = 16 * Tt + m16;
+      if (t < cu.nvalid) put4(dg, kb0 + (long)t * kstride + c0, x + carry);
+      carry += tile_tot;
     }
     if constexpr (B_S) {
-      // a scalar b's gradient sums the token's d_k channels: 4 per lane, the 4 lane groups
-      // of a wave, then the NW waves through LDS (the M buffers are dead here)
-      float x = outb[0] + outb[1] + outb[2] + outb[3];
-      x += __shfl_xor(x, 16, 64);
-      x += __shfl_xor(x, 32, 64);
-      if (g4 == 0) sPart[wave * 64 + t] = x;
-    }
-  }
-  // the next unit's first load group, in flight from here on
-  const ChunkUnit cn = map_unit(u_pre, H, cu_seqlens, N, T_len, lane);
-  issue_first(u_pre);
-  // dg_t = sum_{t' >= t} (A - B)_{t'} + sum_all B + gamma X   (suffix sums over 64 tokens)
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) totB[i] += __shfl_xor(totB[i], m, 64);
-  f4 carry = totB + gam * xc;
-#pragma unroll
-  for (int Tt = 3; Tt >= 0; --Tt) {
-    f4 x = dgv[Tt];
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float y = __shfl_down(x[i], d, 16);
-        x[i] += (m16 + d < 16) ? y : 0.f;
+      lds_barrier();
+      if (tid < C) {
+        float x = 0.f;
+  #pragma unroll
+        for (int w = 0; w < Sh::NW; ++w) x += sPart[w * 64 + tid];
+        if (tid < cu.nvalid) db[(cu.row + tid) * H + cu.h] = from_f<T>(x);
       }
     }
-    f4 tile_tot;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) tile_tot[i] = __shfl(x[i], lane & ~15, 64);
-    const int t = 16 * Tt + m16;
-    if (t < cu.nvalid) put4(dg, kb0 + (long)t * kstride + c0, x + carry);
-    carry += tile_tot;
-  }
-  if constexpr (B_S) {
-    lds_barrier();
-    if (tid < C) {
-      float x = 0.f;
-#pragma unroll
-      for (int w = 0; w < Sh::NW; ++w) x += sPart[w * 64 + tid];
-      if (tid < cu.nvalid) db[(cu.row + tid) * H + cu.h] = from_f<T>(x);
-    }
-  }
-  cu = cn;
-  u = u_next;
-  lds_barrier();  // this unit's readers of LDS are done before the next unit's stores
+    cu = cn;
+    u = u_next;
+    lds_barrier();  // this unit's readers of LDS are done before the next unit's stores
   }
 }
 
