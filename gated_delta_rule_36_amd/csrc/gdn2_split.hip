@@ -16,6 +16,8 @@
 // the A / P products off the sequential path and computes them once per head instead of
 // once per value slice, at the cost of writing and reading back the factors.
 
+#include <atomic>
+
 #include "gdn2_chunk_common.h"
 #include "gdn2_launch.h"
 
@@ -853,16 +855,17 @@ gdn2_seg_combine_kernel(const float* __restrict__ ebuf, const float* __restrict_
 
 // ------------------------------------------------------------------ launch
 int cu_count() {
-  static int cached[64] = {0};
+  // per device, filled on first use; concurrent first calls store the same value
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 template <int DK, int DV, int NV>
