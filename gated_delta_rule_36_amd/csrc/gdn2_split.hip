@@ -499,7 +499,8 @@ gdn2_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 }
 
 // ------------------------------------------------------------------ phase 2: recurrence
-template <int DK, int DV, int NV>
+// OUTBUF: the two output staging buffers (not needed by the transfer pass, MODE 3)
+template <int DK, int DV, int NV, bool OUTBUF = true>
 struct StateShape {
   static constexpr int C = 64;
   static constexpr int NWV = NV / 16;     // waves: wave w owns state columns [16w, 16w+16)
@@ -521,7 +522,7 @@ struct StateShape {
   static constexpr int OP = NV + 8;                   // output staging pitch
   static constexpr int SZ_O = C * OP * 2;
   static constexpr int OFF_O = 2 * STAGE;             // two output staging buffers
-  static constexpr int LDS_BYTES = OFF_O + 2 * SZ_O;
+  static constexpr int LDS_BYTES = OUTBUF ? OFF_O + 2 * SZ_O : 2 * STAGE;
   static_assert(STAGE % 16 == 0, "stage");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
@@ -538,7 +539,9 @@ struct StateShape {
 // shorter); a unit is (sequence, head, segment), its start state is s0[unit] (MODE 0; the
 // combine kernel's output when nseg > 1) and only the last segment writes sN.
 template <int DK, int DV, int NV, int MODE>
-__global__ void __launch_bounds__((StateShape<DK, DV, NV>::NT)) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__((StateShape<DK, DV, NV, MODE != 3>::NT))
+__attribute__((amdgpu_waves_per_eu(StateShape<DK, DV, NV, MODE != 3>::NT / 256,
+                                   StateShape<DK, DV, NV, MODE != 3>::NT / 256)))
 gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict__ o,
                   float* sN, const int* __restrict__ cu_seqlens, int T_len, int H,
                   int nslices, int nunits, int nseg, int seg_chunks, float* __restrict__ ebuf) {
@@ -546,7 +549,7 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
   constexpr bool XFER = MODE == 3;
   constexpr bool STORE = MODE == 1 || MODE == 2;  // entering states and U to the backward workspace
   constexpr bool OUT = MODE == 0 || MODE == 2;    // the output o
-  using Sh = StateShape<DK, DV, NV>;
+  using Sh = StateShape<DK, DV, NV, !XFER>;
   using M = Mma<T>;
   constexpr SplitLayout L(DK, DV);
   constexpr BwdLayout LB(DK, DV);
@@ -668,7 +671,7 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
     m16 = lane & 15;
     g4 = lane >> 4;
     const char* B = smem + (ci & 1) * Sh::STAGE;
-    T* so = reinterpret_cast<T*>(smem + Sh::OFF_O + (ci & 1) * Sh::SZ_O);
+    T* so = OUT ? reinterpret_cast<T*>(smem + Sh::OFF_O + (ci & 1) * Sh::SZ_O) : nullptr;
     auto frag = [&](int off, int blk) {
       return *reinterpret_cast<const typename M::frag*>(B + off + blk * 1024 + lane * 16);
     };
@@ -894,10 +897,12 @@ static hipError_t launch_split(const ChunkArgs& a) {
     const size_t base = split_workspace_bytes(false, a.B, a.T, a.H, DK, DV, a.N);
     float* ebuf = reinterpret_cast<float*>((char*)a.workspace + (base + 255) / 256 * 256);
     float* sbuf = ebuf + units * DK * (DV + DK);
-    constexpr int NVX = 64;
+    // transfer slices: with d_k = d_v = 128, one of 128 value columns and one of 128
+    // identity columns (8 waves, no output buffers: half the workgroups of 64-wide slices)
+    constexpr int NVX = (DK == 128 && DV == 128) ? 128 : 64;
     const int xslices = (DV + DK) / NVX;
     hipLaunchKernelGGL((gdn2_state_kernel<DK, DV, NVX, 3>), dim3((unsigned)(units * xslices)),
-                       dim3(StateShape<DK, DV, NVX>::NT), 0, st, (const char*)a.workspace,
+                       dim3(StateShape<DK, DV, NVX, false>::NT), 0, st, (const char*)a.workspace,
                        nullptr, nullptr, nullptr, nullptr, a.T, a.H, xslices, (int)units, nseg,
                        a.seg_chunks, ebuf);
     hipError_t e = hipGetLastError();
