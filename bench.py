@@ -121,6 +121,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-long", action="store_true",
                     help="skip the long-context forward measurement")
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip the packed variable-length forward measurement")
     ap.add_argument("--no-scalar-gates", action="store_true",
                     help="skip the scalar-gate forward measurement")
     ap.add_argument("--no-block", action="store_true",
@@ -342,6 +344,50 @@ def main():
             "algorithmic_bytes": lbytes,
             "hbm_frac": round(lbytes / (lms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del lq, lk, lv, lg, lb, lw, lws
+
+    if args.workload == "layer1p3b" and not args.no_varlen:
+        # the packed workload: 16 sequences of 512..8192 tokens, nonzero initial states,
+        # drawn on the device (seeded)
+        lens = np.random.default_rng(7).integers(512, 8193, size=16)
+        cu_v = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev)
+        TV, NV_ = int(lens.sum()), len(lens)
+        gen = torch.Generator(device=dev).manual_seed(7)
+
+        def unit_rows(d):
+            x = torch.randn(1, TV, H, d, generator=gen, device=dev)
+            return x / x.norm(dim=-1, keepdim=True)
+        vq, vk = unit_rows(dk).to(torch.bfloat16), unit_rows(dk).to(torch.bfloat16)
+        vv = torch.randn(1, TV, H, dv, generator=gen, device=dev).to(torch.bfloat16)
+        vg = (-0.1 * torch.nn.functional.softplus(torch.randn(1, TV, H, dk, generator=gen, device=dev))
+              ).to(torch.bfloat16)
+        vb = torch.sigmoid(torch.randn(1, TV, H, dk, generator=gen, device=dev)).to(torch.bfloat16)
+        vw = torch.sigmoid(torch.randn(1, TV, H, dv, generator=gen, device=dev)).to(torch.bfloat16)
+        vs0 = 0.02 * torch.randn(NV_, H, dk, dv, generator=gen, device=dev)
+        vws = torch.empty(G.workspace_bytes(1, TV, H, dk, dv, NV_), dtype=torch.uint8, device=dev)
+
+        def vstep():
+            return G.chunk_fwd(vq, vk, vv, vg, vb, vw, initial_state=vs0, cu_seqlens=cu_v,
+                               workspace=vws)
+        for _ in range(3):
+            vstep()
+        torch.cuda.synchronize()
+        evv = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(10)]
+        for a, b2 in evv:
+            a.record()
+            vstep()
+            b2.record()
+        torch.cuda.synchronize()
+        vms = float(np.mean([a.elapsed_time(b2) for a, b2 in evv]))
+        vbytes = fwd_bytes(1, TV, H, dk, dv, NV_, read_s0=True)
+        out["varlen"] = {
+            "workload": f"{NV_} packed sequences of 512..8192 tokens ({TV} in all), H=16, "
+                        "d_k=d_v=128, bf16, initial states N(0, 0.02^2); path auto (two-phase)",
+            "ms_per_call": round(vms, 4), "tokens_per_s": round(TV / (vms * 1e-3), 1),
+            "vs_headline_tokens_per_s": round(TV / (vms * 1e-3) / out["value"], 3),
+            "algorithmic_bytes": vbytes,
+            "hbm_frac": round(vbytes / (vms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del vq, vk, vv, vg, vb, vw, vs0, vws
 
     if args.workload == "layer1p3b" and not args.no_scalar_gates:
         # the scalar-gate configuration (one b and one w value per token and head)
