@@ -113,7 +113,11 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* log_
 }
 
 size_t bwd_workspace_need(bool varlen, int B, int T, int H, int d_k, int d_v, int N) {
-  return gdn2::bwd_workspace_bytes(varlen, B, T, H, d_k, d_v, N);
+  // the same segment plan (and buffers) as the two-phase forward: the backward's forward
+  // pass and its reverse chain cut long sequences the same way
+  const gdn2::SegPlan sp = seg_plan_for(varlen, T, H, d_v, N);
+  return gdn2::bwd_workspace_bytes(varlen, B, T, H, d_k, d_v, N) +
+         gdn2::seg_buffer_bytes(sp, N, H, d_k, d_v);
 }
 
 int chunk_bwd_impl(const void* q, const void* k, const void* v, const void* log_alpha,
@@ -148,7 +152,8 @@ int chunk_bwd_impl(const void* q, const void* k, const void* v, const void* log_
       workspace_bytes < bwd_workspace_need(cu_seqlens != nullptr, B, T, H, d_k, d_v, N))
     return GDN2_WORKSPACE_TOO_SMALL;
   if (N == 0) return GDN2_OK;
-  if ((long)N * H * (d_v / 64) > (long)INT_MAX) return GDN2_INVALID_ARGUMENT;
+  const gdn2::SegPlan sp = seg_plan_for(cu_seqlens != nullptr, T, H, d_v, N);
+  if ((long)N * H * sp.nseg * ((d_v + d_k) / 64) > (long)INT_MAX) return GDN2_INVALID_ARGUMENT;
 
   gdn2::BwdArgs a;
   gdn2::ChunkArgs& f = a.fwd;
@@ -157,6 +162,7 @@ int chunk_bwd_impl(const void* q, const void* k, const void* v, const void* log_
   f.B = B; f.T = T; f.H = H; f.d_k = d_k; f.d_v = d_v; f.N = N;
   f.dtype = dtype; f.nv = 64; f.stream = hip_stream; f.gate_flags = gate_layout;
   f.workspace = workspace; f.workspace_bytes = workspace_bytes;
+  f.nseg = sp.nseg; f.seg_chunks = sp.seg_chunks;
   a.d_o = d_o; a.d_sN = d_final_state;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dlog_alpha; a.db = db; a.dw = dw;
   a.d_s0 = d_initial_state; a.range_flag = range_flag; a.saved = saved;
@@ -269,7 +275,8 @@ int gdn2_chunk_fwd_train(const void* q, const void* k, const void* v, const void
       workspace_bytes < bwd_workspace_need(cu_seqlens != nullptr, B, T, H, d_k, d_v, N))
     return GDN2_WORKSPACE_TOO_SMALL;
   if (N == 0) return GDN2_OK;
-  if ((long)N * H * (d_v / 64) > (long)INT_MAX) return GDN2_INVALID_ARGUMENT;
+  const gdn2::SegPlan sp = seg_plan_for(cu_seqlens != nullptr, T, H, d_v, N);
+  if ((long)N * H * sp.nseg * ((d_v + d_k) / 64) > (long)INT_MAX) return GDN2_INVALID_ARGUMENT;
   if (o == nullptr) return GDN2_INVALID_ARGUMENT;  // (tokens == 0 with N > 0: o still required)
   gdn2::ChunkArgs f;
   f.q = q; f.k = k; f.v = v; f.g = log_alpha; f.b = b; f.w = w;
@@ -277,6 +284,7 @@ int gdn2_chunk_fwd_train(const void* q, const void* k, const void* v, const void
   f.B = B; f.T = T; f.H = H; f.d_k = d_k; f.d_v = d_v; f.N = N;
   f.dtype = dtype; f.nv = 64; f.stream = hip_stream; f.gate_flags = gate_layout;
   f.workspace = workspace; f.workspace_bytes = workspace_bytes;
+  f.nseg = sp.nseg; f.seg_chunks = sp.seg_chunks;
   return status_of(gdn2::launch_bwd_forward_part(f));
 }
 

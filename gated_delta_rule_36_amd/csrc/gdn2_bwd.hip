@@ -62,12 +62,20 @@ struct ChainShape {
   static_assert(STAGE % 16 == 0 && LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int DK, int DV, int NV>
+// XFER (segment transfer pass of a long sequence): the columns are [d_v value | d_k identity];
+// the value columns run from a zero gradient with dO, the identity columns from the
+// identity with dO = 0 (so they carry the segment's product of the chunks' linear maps of the
+// state gradient), nothing is stored per chunk, and the segment's start value [b | A] is
+// written to ebuf. Segments: a unit is (sequence, head, segment); with nseg > 1 the gradient
+// at a segment's end comes from dbuf[unit] (the reverse combine), and only segment 0
+// writes the initial state's gradient.
+template <int DK, int DV, int NV, bool XFER>
 __global__ void __launch_bounds__((ChainShape<DK, DV, NV>::NT)) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gdn2_bwd_chain_kernel(char* __restrict__ ws, const bf16* __restrict__ d_o,
                       const float* __restrict__ d_sN, float* __restrict__ d_s0,
                       const int* __restrict__ cu_seqlens, int T_len, int H, int nslices,
-                      int nunits) {
+                      int nunits, int nseg, int seg_chunks, float* __restrict__ ebuf,
+                      const float* __restrict__ dbuf) {
   typedef bf16 T;
   using Sh = ChainShape<DK, DV, NV>;
   using M = Mma<T>;
@@ -86,10 +94,13 @@ gdn2_bwd_chain_kernel(char* __restrict__ ws, const bf16* __restrict__ d_o,
   const int gsz = min(8, nunits - grp * 8);
   const int gi = blockIdx.x - grp * 8 * nslices;
   const int slice = gi / gsz;
-  const int nh = grp * 8 + gi % gsz;
+  const int unit_id = grp * 8 + gi % gsz;  // (sequence * H + head) * nseg + segment
+  const int seg = unit_id % nseg;
+  const int nh = unit_id / nseg;
   const int h = nh % H;
   const int n = nh / H;
-  const int col0 = slice * NV;
+  const int col0 = slice * NV;             // XFER: within [d_v value | d_k identity] columns
+  const bool ident = XFER && col0 >= DV;   // this slice carries transfer (identity) columns
   const int ctg = slice * Sh::NWV + wave;  // this wave's column tile within d_v
 
   long row0, slot0;
@@ -106,6 +117,13 @@ gdn2_bwd_chain_kernel(char* __restrict__ ws, const bf16* __restrict__ d_o,
     len = T_len;
     slot0 = (long)n * ((T_len + C - 1) / C);
   }
+  {  // this unit's segment of the sequence
+    const int cbeg = seg * seg_chunks;
+    row0 += (long)cbeg * C;
+    slot0 += cbeg;
+    const int rest = len - cbeg * C;
+    len = rest < 0 ? 0 : (nseg > 1 && rest > seg_chunks * C ? seg_chunks * C : rest);
+  }
   const int nch = (len + C - 1) / C;
   const long vstride = (long)H * DV;
 
@@ -113,11 +131,19 @@ gdn2_bwd_chain_kernel(char* __restrict__ ws, const bf16* __restrict__ d_o,
   // column col0 + 16*wave + m16 (lane rows 4*g4 + i)
   f4 D[NMT];
   const long sbase = ((long)n * H + h) * DK * DV + col0 + 16 * wave + m16;
+  const long dbase = (long)unit_id * DK * DV + col0 + 16 * wave + m16;
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      D[mt][i] = d_sN != nullptr ? d_sN[sbase + (long)(16 * mt + 4 * g4 + i) * DV] : 0.f;
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * mt + 4 * g4 + i;
+      if constexpr (XFER)
+        D[mt][i] = (ident && row == col0 - DV + 16 * wave + m16) ? 1.f : 0.f;
+      else if (nseg > 1)
+        D[mt][i] = dbuf[dbase + (long)row * DV];
+      else
+        D[mt][i] = d_sN != nullptr ? d_sN[sbase + (long)row * DV] : 0.f;
+    }
 
   // staging (one chunk ahead, reverse order): factor pieces and this slice of dO
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -136,6 +162,10 @@ gdn2_bwd_chain_kernel(char* __restrict__ ws, const bf16* __restrict__ d_o,
 #pragma unroll
     for (int j = 0; j < Sh::PPD; ++j) {
       const int p = tid + j * NT, r = p / (NV / 8), cc = p % (NV / 8);
+      if (ident) {  // (uniform) no dO on the identity columns
+        std_[j] = u32x4{0u, 0u, 0u, 0u};
+        continue;
+      }
       const T* src = d_o + (row0 + (long)ci * C + (r < nvalid ? r : 0)) * vstride +
                      (long)h * DV + col0 + cc * 8;
       const u32x4 x = *reinterpret_cast<const u32x4*>(src);
@@ -174,10 +204,12 @@ gdn2_bwd_chain_kernel(char* __restrict__ ws, const bf16* __restrict__ d_o,
     };
     char* unit = unit_of(ci);
     // dSn of this chunk, for the local kernel
+    if constexpr (!XFER) {
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
-      *reinterpret_cast<uint2*>(unit + LB.db + ((ctg * NMT + mt) * 64 + lane) * 8) =
-          make_uint2(pack_bf16(D[mt][0], D[mt][1]), pack_bf16(D[mt][2], D[mt][3]));
+      for (int mt = 0; mt < NMT; ++mt)
+        *reinterpret_cast<uint2*>(unit + LB.db + ((ctg * NMT + mt) * 64 + lane) * 8) =
+            make_uint2(pack_bf16(D[mt][0], D[mt][1]), pack_bf16(D[mt][2], D[mt][3]));
+    }
     typename M::frag db[KSK], dob[2];
 #pragma unroll
     for (int s = 0; s < KSK; ++s) db[s] = M::from_acc(D, s);
@@ -210,10 +242,12 @@ gdn2_bwd_chain_kernel(char* __restrict__ ws, const bf16* __restrict__ d_o,
       dZ[R] = mma16_frag(btf(R, R), Frag16<T>::from_acc(acc), f4{0.f, 0.f, 0.f, 0.f});
       zb[R] = Frag16<T>::from_acc(dZ[R]);
     }
+    if constexpr (!XFER) {
 #pragma unroll
-    for (int R = 0; R < 4; ++R)
-      *reinterpret_cast<uint2*>(unit + LB.zb + ((ctg * 4 + R) * 64 + lane) * 8) =
-          make_uint2(pack_bf16(dZ[R][0], dZ[R][1]), pack_bf16(dZ[R][2], dZ[R][3]));
+      for (int R = 0; R < 4; ++R)
+        *reinterpret_cast<uint2*>(unit + LB.zb + ((ctg * 4 + R) * 64 + lane) * 8) =
+            make_uint2(pack_bf16(dZ[R][0], dZ[R][1]), pack_bf16(dZ[R][2], dZ[R][3]));
+    }
     // dS0 = Diag(gamma) dSn + Qbar^T dO + (-W^T) dU
     typename M::frag ub[2];
 #pragma unroll
@@ -233,7 +267,14 @@ gdn2_bwd_chain_kernel(char* __restrict__ ws, const bf16* __restrict__ d_o,
     stage_load(ci > 1 ? ci - 2 : 0);
     lds_barrier();
   }
-  if (d_s0 != nullptr) {
+  if constexpr (XFER) {  // the segment's start value [b | A] (rows d_k, d_v + d_k columns)
+    constexpr int LE = DV + DK;
+    float* E = ebuf + (long)unit_id * DK * LE + col0 + 16 * wave + m16;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) E[(long)(16 * mt + 4 * g4 + i) * LE] = D[mt][i];
+  } else if (d_s0 != nullptr && seg == 0) {
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
@@ -767,10 +808,34 @@ static hipError_t launch_bwd(const BwdArgs& a) {
   }
   constexpr int NV = 64 <= DV ? 64 : DV;
   const int nslices = DV / NV;
-  hipLaunchKernelGGL((gdn2_bwd_chain_kernel<DK, DV, NV>), dim3((unsigned)(f.N * f.H * nslices)),
-                     dim3(ChainShape<DK, DV, NV>::NT), 0, st, (char*)f.workspace,
-                     (const bf16*)a.d_o, a.d_sN, a.d_s0, f.cu_seqlens, f.T, f.H, nslices,
-                     f.N * f.H);
+  if (f.nseg > 1) {
+    // long sequences: transfer pass per segment, the segments' end gradients by a reverse
+    // scan, then the chain per segment (the buffers after the workspace are free again: the
+    // forward part's are consumed)
+    const int nseg = f.nseg;
+    const long units = (long)f.N * f.H * nseg;
+    float* ebuf = reinterpret_cast<float*>(
+        (char*)f.workspace + (bwd_workspace_bytes(false, f.B, f.T, f.H, DK, DV, f.N) + 255) / 256 * 256);
+    float* dbuf = ebuf + units * DK * (DV + DK);
+    const int xslices = (DV + DK) / NV;
+    hipLaunchKernelGGL((gdn2_bwd_chain_kernel<DK, DV, NV, true>), dim3((unsigned)(units * xslices)),
+                       dim3(ChainShape<DK, DV, NV>::NT), 0, st, (char*)f.workspace,
+                       (const bf16*)a.d_o, nullptr, nullptr, nullptr, f.T, f.H, xslices,
+                       (int)units, nseg, f.seg_chunks, ebuf, nullptr);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_seg_combine(ebuf, a.d_sN, dbuf, f.N, f.H, DK, DV, nseg, true, f.stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gdn2_bwd_chain_kernel<DK, DV, NV, false>), dim3((unsigned)(units * nslices)),
+                       dim3(ChainShape<DK, DV, NV>::NT), 0, st, (char*)f.workspace,
+                       (const bf16*)a.d_o, a.d_sN, a.d_s0, nullptr, f.T, f.H, nslices, (int)units,
+                       nseg, f.seg_chunks, nullptr, dbuf);
+  } else {
+    hipLaunchKernelGGL((gdn2_bwd_chain_kernel<DK, DV, NV, false>), dim3((unsigned)(f.N * f.H * nslices)),
+                       dim3(ChainShape<DK, DV, NV>::NT), 0, st, (char*)f.workspace,
+                       (const bf16*)a.d_o, a.d_sN, a.d_s0, f.cu_seqlens, f.T, f.H, nslices,
+                       f.N * f.H, 1, 0, nullptr, nullptr);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long nunits = split_slots(f.cu_seqlens != nullptr, f.B, f.T, f.N) * f.H;

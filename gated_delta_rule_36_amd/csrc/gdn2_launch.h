@@ -171,6 +171,10 @@ hipError_t launch_chunk_fwd_split(const ChunkArgs& a);
 hipError_t launch_chunk_bwd(const BwdArgs& a);
 // pieces of the backward shared with the two-phase forward (gdn2_split.hip)
 hipError_t launch_bwd_forward_part(const ChunkArgs& a);
+// segment start values by a scan over segments (forward: from s_in = the initial states, in
+// segment order; reverse: from s_in = the final states' gradients, last segment first)
+hipError_t launch_seg_combine(const float* ebuf, const float* s_in, float* sbuf, int N, int H,
+                              int d_k, int d_v, int nseg, bool reverse, void* stream);
 int cu_count();  // compute units of the current device
 hipError_t launch_decode_step(const DecodeArgs& a);
 hipError_t launch_decode_tokens(const DecodeTokensArgs& a);

@@ -530,7 +530,8 @@ struct StateShape {
 // MODE 0: the forward (output o). MODE 1 (the backward's own forward pass): no output;
 // instead the state entering every chunk and that chunk's U are stored into the backward
 // workspace (BwdLayout::h, ::ub). MODE 2 (training forward): both, so that a later backward
-// can skip its forward pass. MODE 3 (segment transfer pass of a long sequence): no output;
+// can skip its forward pass. MODE 3 (segment transfer pass of a long sequence; MODE 4: the
+// same on the backward workspace, whose units start with the same factors): no output;
 // the columns are [d_v value columns | d_k identity columns]: the value columns run from a
 // zero state, the identity columns from the identity with U~ = 0 (so they carry the
 // segment's product of chunk transitions Diag(gamma) - Kt^T W), and the segment's end
@@ -539,21 +540,21 @@ struct StateShape {
 // shorter); a unit is (sequence, head, segment), its start state is s0[unit] (MODE 0; the
 // combine kernel's output when nseg > 1) and only the last segment writes sN.
 template <int DK, int DV, int NV, int MODE>
-__global__ void __launch_bounds__((StateShape<DK, DV, NV, MODE != 3>::NT))
-__attribute__((amdgpu_waves_per_eu(StateShape<DK, DV, NV, MODE != 3>::NT / 256,
-                                   StateShape<DK, DV, NV, MODE != 3>::NT / 256)))
+__global__ void __launch_bounds__((StateShape<DK, DV, NV, (MODE < 3)>::NT))
+__attribute__((amdgpu_waves_per_eu(StateShape<DK, DV, NV, (MODE < 3)>::NT / 256,
+                                   StateShape<DK, DV, NV, (MODE < 3)>::NT / 256)))
 gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict__ o,
                   float* sN, const int* __restrict__ cu_seqlens, int T_len, int H,
                   int nslices, int nunits, int nseg, int seg_chunks, float* __restrict__ ebuf) {
   typedef bf16 T;
-  constexpr bool XFER = MODE == 3;
+  constexpr bool XFER = MODE == 3 || MODE == 4;
   constexpr bool STORE = MODE == 1 || MODE == 2;  // entering states and U to the backward workspace
   constexpr bool OUT = MODE == 0 || MODE == 2;    // the output o
   using Sh = StateShape<DK, DV, NV, !XFER>;
   using M = Mma<T>;
   constexpr SplitLayout L(DK, DV);
   constexpr BwdLayout LB(DK, DV);
-  constexpr long UNIT = STORE ? LB.bytes : L.bytes;
+  constexpr long UNIT = (STORE || MODE == 4) ? LB.bytes : L.bytes;
   constexpr int C = Sh::C, NT = Sh::NT, KSK = Sh::KSK, NMT = Sh::NMT, OP = Sh::OP;
   __shared__ __attribute__((aligned(16))) char smem[Sh::LDS_BYTES];
 
@@ -790,10 +791,13 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
 
 // Segment start states of a long sequence: S_0 = the sequence's initial state (or 0) and
 // S_{s+1} = M_s S_s + N_s, with [N_s | M_s] the end state of segment s's transfer pass.
+// REV (the backward's state gradient, which runs from the last chunk to the first): D at
+// the end of the last segment is the final state's gradient (or 0) and D_{s-1} = A_s D_s + b_s
+// with [b_s | A_s] from segment s's transfer pass; sbuf then holds each segment's end value.
 // One workgroup per (sequence, head, 16 value columns); one wave per 16-row tile; M_s is
 // staged in LDS with 16-byte loads, products in fp32 (16x16x4 MFMA), S exchanged through
 // LDS every step.
-template <int DK, int DV>
+template <int DK, int DV, bool REV>
 __global__ void __launch_bounds__(DK * 4)
 gdn2_seg_combine_kernel(const float* __restrict__ ebuf, const float* __restrict__ s0,
                         float* __restrict__ sbuf, int H, int nseg) {
@@ -815,7 +819,8 @@ gdn2_seg_combine_kernel(const float* __restrict__ ebuf, const float* __restrict_
       const int row = 16 * (wave * RPW + t) + 4 * g4 + i;
       S[t][i] = s0 != nullptr ? s0[((long)nh * DK + row) * DV + c] : 0.f;
     }
-  for (int s = 0; s < nseg; ++s) {
+  for (int step = 0; step < nseg; ++step) {
+    const int s = REV ? nseg - 1 - step : step;
     const long unit = (long)nh * nseg + s;
     float* out = sbuf + unit * DK * DV;
     const float* E = ebuf + unit * DK * LE;
@@ -827,7 +832,7 @@ gdn2_seg_combine_kernel(const float* __restrict__ ebuf, const float* __restrict_
         out[(long)row * DV + c] = S[t][i];
         sS[row][m16] = S[t][i];
       }
-    if (s + 1 < nseg) {
+    if (step + 1 < nseg) {
       // M_s (d_k x d_k, the last d_k columns of E's rows) -> LDS
       for (int p = tid; p < DK * DK / 4; p += NT) {
         const int row = p / (DK / 4), c4 = p % (DK / 4);
@@ -857,6 +862,21 @@ gdn2_seg_combine_kernel(const float* __restrict__ ebuf, const float* __restrict_
 }
 
 // ------------------------------------------------------------------ launch
+hipError_t launch_seg_combine(const float* ebuf, const float* s_in, float* sbuf, int N, int H,
+                              int d_k, int d_v, int nseg, bool reverse, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  const dim3 grid((unsigned)((long)N * H * (d_v / 16)));
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(d_k * 4), 0, st, ebuf, s_in, sbuf, H, nseg);
+    return hipGetLastError();
+  };
+  if (d_k == 64 && d_v == 64) return reverse ? go(gdn2_seg_combine_kernel<64, 64, true>) : go(gdn2_seg_combine_kernel<64, 64, false>);
+  if (d_k == 64 && d_v == 128) return reverse ? go(gdn2_seg_combine_kernel<64, 128, true>) : go(gdn2_seg_combine_kernel<64, 128, false>);
+  if (d_k == 128 && d_v == 64) return reverse ? go(gdn2_seg_combine_kernel<128, 64, true>) : go(gdn2_seg_combine_kernel<128, 64, false>);
+  if (d_k == 128 && d_v == 128) return reverse ? go(gdn2_seg_combine_kernel<128, 128, true>) : go(gdn2_seg_combine_kernel<128, 128, false>);
+  return hipErrorInvalidValue;
+}
+
 int cu_count() {
   // per device, filled on first use; concurrent first calls store the same value
   static std::atomic<int> cached[64];
@@ -907,9 +927,7 @@ static hipError_t launch_split(const ChunkArgs& a) {
                        a.seg_chunks, ebuf);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gdn2_seg_combine_kernel<DK, DV>), dim3((unsigned)((long)a.N * a.H * (DV / 16))),
-                       dim3(DK * 4), 0, st, ebuf, a.s0, sbuf, a.H, nseg);
-    e = hipGetLastError();
+    e = launch_seg_combine(ebuf, a.s0, sbuf, a.N, a.H, DK, DV, nseg, false, a.stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gdn2_state_kernel<DK, DV, NV, 0>), dim3((unsigned)(units * nslices)),
                        dim3(StateShape<DK, DV, NV>::NT), 0, st, (const char*)a.workspace, sbuf,
@@ -948,6 +966,30 @@ static hipError_t launch_bwd_forward(const ChunkArgs& a) {
   constexpr int NV = 64 <= DV ? 64 : DV;
   const int nslices = DV / NV;
   auto chain = a.o != nullptr ? gdn2_state_kernel<DK, DV, NV, 2> : gdn2_state_kernel<DK, DV, NV, 1>;
+  if (a.nseg > 1) {
+    // long sequences: transfer pass per segment (on this workspace), start states by a scan,
+    // then the entering states (and o) per segment, as in the two-phase forward
+    const int nseg = a.nseg;
+    const long units = (long)a.N * a.H * nseg;
+    float* ebuf = reinterpret_cast<float*>(
+        (char*)a.workspace + (bwd_workspace_bytes(false, a.B, a.T, a.H, DK, DV, a.N) + 255) / 256 * 256);
+    float* sbuf = ebuf + units * DK * (DV + DK);
+    constexpr int NVX = (DK == 128 && DV == 128) ? 128 : 64;
+    const int xslices = (DV + DK) / NVX;
+    hipLaunchKernelGGL((gdn2_state_kernel<DK, DV, NVX, 4>), dim3((unsigned)(units * xslices)),
+                       dim3(StateShape<DK, DV, NVX, false>::NT), 0, st, (const char*)a.workspace,
+                       nullptr, nullptr, nullptr, nullptr, a.T, a.H, xslices, (int)units, nseg,
+                       a.seg_chunks, ebuf);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_seg_combine(ebuf, a.s0, sbuf, a.N, a.H, DK, DV, nseg, false, a.stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(chain, dim3((unsigned)(units * nslices)), dim3(StateShape<DK, DV, NV>::NT), 0,
+                       st, (const char*)a.workspace, sbuf, (bf16*)a.o,
+                       a.o != nullptr ? a.sN : nullptr, nullptr, a.T, a.H, nslices, (int)units,
+                       nseg, a.seg_chunks, nullptr);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(chain, dim3((unsigned)(a.N * a.H * nslices)),
                      dim3(StateShape<DK, DV, NV>::NT), 0, st, (const char*)a.workspace, a.s0,
                      (bf16*)a.o, a.o != nullptr ? a.sN : nullptr, a.cu_seqlens, a.T, a.H, nslices,

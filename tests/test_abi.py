@@ -139,6 +139,10 @@ def test_chunk_bwd_error_paths():
     need = 2 * 1 * 4 * 238080  # two sequences x one chunk x 4 heads x the d=128 unit
     assert L.gdn2_chunk_bwd_workspace_bytes(2, 64, 4, 128, 128, 2, 0) == (2 + 2) * 4 * 238080
     assert L.gdn2_chunk_bwd_workspace_bytes(2, 64, 4, 64, 64, 2, 1) == 0      # fp32: not built
+    # a long sequence with few chains is cut into segments (4 of 8 chunks here): the segment
+    # buffers ([units][d_k][2 d_v + d_k] fp32, 256-byte aligned) follow the per-chunk units
+    seg = 256 + 1 * 2 * 4 * 128 * (2 * 128 + 128) * 4
+    assert L.gdn2_chunk_bwd_workspace_bytes(1, 2048, 2, 128, 128, 1, 0) == 32 * 2 * 238080 + seg
     assert _bwd(dtype=1, dk=64, dv=64) == 2
     assert _bwd(dtype=7) == 1
     assert _bwd(dk=96) == 2

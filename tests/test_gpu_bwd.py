@@ -143,6 +143,40 @@ def test_bwd_many_units_sampled(dk, dv):
         assert_close("ds0", host64(out[6][n:n + 1, h:h + 1]), ref[6], TOL["bf16"])
 
 
+# ------------------------------------------- long sequences cut into parallel segments
+@pytest.mark.parametrize("B,T,H,dk,dv", [(1, 2048, 2, 128, 128), (2, 1100, 1, 128, 64),
+                                         (1, 1500, 1, 64, 128), (1, 4096, 1, 64, 64)])
+def test_bwd_segments(B, T, H, dk, dv):
+    """Few long chains: the backward cuts each sequence into segments (the forward pass and
+    the reverse chain each run a transfer pass per segment, a scan over segments, then the
+    segments in parallel); the gradients are the plain reverse loop's."""
+    x = make_inputs(B, T, H, dk, dv, "bf16", seed=930 + T + dk, s0_std=0.05)
+    do, dsn = _upstream(x, 31 + T)
+    say("bwd segments", B, T, H, dk, dv)
+    check(x, do, dsn)
+
+
+def test_bwd_segments_saved_pair():
+    """Segments through the training forward and the saved backward, with near-resets."""
+    import gated_delta_rule_36_amd as G
+    x = make_inputs(1, 3000, 2, 128, 128, "bf16", seed=937, reset_frac=0.1, s0_std=0.05)
+    do, dsn = _upstream(x, 38)
+    say("bwd segments saved pair T3000 H2, near-resets")
+    t = {n: dev_tensor(x[n], "bf16") for n in NAMES}
+    s0 = torch.from_numpy(x["s0"]).cuda()
+    o, sN, sv = G.chunk_fwd_train(*(t[n] for n in NAMES), initial_state=s0)
+    out = G.chunk_bwd(*(t[n] for n in NAMES), dev_tensor(do, "bf16"), initial_state=s0,
+                      d_final_state=torch.from_numpy(dsn).cuda(), saved=sv)
+    torch.cuda.synchronize()
+    from oracle import gdn2_forward
+    o_ref, s_ref = gdn2_forward(*(x[n] for n in NAMES), s0=x["s0"])
+    assert_close("o", host64(o), o_ref, TOL["bf16"])
+    assert_close("S_final", host64(sN), s_ref, TOL["bf16"])
+    ref = gdn2_backward(*(x[n] for n in NAMES), do, dS_final=dsn, s0=x["s0"])
+    for name, a, r in zip(GRADS + ("ds0",), out, ref):
+        assert_close(name, host64(a), r, TOL["bf16"])
+
+
 def test_bwd_layer1p3b_full_size_sampled():
     from gdn2_inputs import make_config_inputs
     from oracle import gdn2_backward as ref_bwd
