@@ -158,9 +158,11 @@ int gdn2_chunk_bwd(const void* q, const void* k, const void* v, const void* log_
                    int dtype, void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
- * Device workspace, in bytes, that gdn2_chunk_bwd needs for these sizes, with or without
- * cu_seqlens (about 3.7 KiB per token and head at d_k = d_v = 128, plus one chunk per
- * sequence); 0 where the backward is not built.
+ * Device workspace, in bytes, that gdn2_chunk_bwd (and gdn2_chunk_fwd_train) needs for these
+ * sizes, with or without cu_seqlens (about 3.7 KiB per token and head at d_k = d_v = 128, plus
+ * one chunk per sequence, plus (2 d_v + d_k) d_k fp32 per segment and head when long
+ * sequences are cut into segments, as for the two-phase forward); 0 where the backward is not
+ * built.
  */
 size_t gdn2_chunk_bwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int N,
                                       int dtype);
