@@ -336,13 +336,34 @@ def main():
         torch.cuda.synchronize()
         lms = float(np.mean([a.elapsed_time(b2) for a, b2 in evl]))
         lbytes = fwd_bytes(1, TL, H, dk, dv, 1)
+        lbwd_ms = None
+        if not args.no_backward:  # the backward on the same sequence (cut into segments too)
+            ldo = torch.randn(1, TL, H, dv, generator=gen, device=dev).to(torch.bfloat16)
+            lbws = torch.empty(int(G.lib().gdn2_chunk_bwd_workspace_bytes(1, TL, H, dk, dv, 1, 0)),
+                               dtype=torch.uint8, device=dev)
+
+            def lbstep(check=False):
+                return G.chunk_bwd(lq, lk, lv, lg, lb, lw, ldo, workspace=lbws, check_range=check)
+            lbstep(check=True)  # (raises if a chunk were outside the backward's decay range)
+            lbstep()
+            torch.cuda.synchronize()
+            evb = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(5)]
+            for a, b2 in evb:
+                a.record()
+                lbstep()
+                b2.record()
+            torch.cuda.synchronize()
+            lbwd_ms = round(float(np.mean([a.elapsed_time(b2) for a, b2 in evb])), 4)
+            del ldo, lbws
         out["long_context"] = {
             "workload": "one sequence of 32768 tokens, H=16, d_k=d_v=128, bf16, 10% near-resets "
                         "(log-alpha=-5); path auto (two-phase, cut into segments)",
             "ms_per_call": round(lms, 4), "tokens_per_s": round(TL / (lms * 1e-3), 1),
             "vs_headline_tokens_per_s": round(TL / (lms * 1e-3) / out["value"], 3),
             "algorithmic_bytes": lbytes,
-            "hbm_frac": round(lbytes / (lms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            "hbm_frac": round(lbytes / (lms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "backward_ms_per_call": lbwd_ms}
         del lq, lk, lv, lg, lb, lw, lws
 
     if args.workload == "layer1p3b" and not args.no_varlen:
