@@ -62,13 +62,14 @@ struct ChainShape {
   static_assert(STAGE % 16 == 0 && LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-// XFER (segment transfer pass of a long sequence): the columns are [d_v value | d_k identity];
-// the value columns run from a zero gradient with dO, the identity columns from the
-// identity with dO = 0 (so they carry the segment's product of the chunks' linear maps of the
-// state gradient), nothing is stored per chunk, and the segment's start value [b | A] is
-// written to ebuf. Segments: a unit is (sequence, head, segment); with nseg > 1 the gradient
-// at a segment's end comes from dbuf[unit] (the reverse combine), and only segment 0
-// writes the initial state's gradient.
+// XFER (segment transfer pass of a long sequence): the chain runs from a zero gradient with
+// dO and writes the segment's start value b (the affine part of its map of the gradient,
+// D_start = A D_end + b) into the value columns of ebuf, nothing being stored per chunk. The
+// linear part A is the transpose of the forward transfer pass's M for the same segment (the
+// gradient of a linear map is its transpose), which that pass left in the other columns of the
+// same buffer. Segments: a unit is (sequence, head, segment); with nseg > 1 the gradient at a
+// segment's end comes from dbuf[unit] (the reverse combine), and only segment 0 writes the
+// initial state's gradient.
 template <int DK, int DV, int NV, bool XFER>
 __global__ void __launch_bounds__((ChainShape<DK, DV, NV>::NT)) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gdn2_bwd_chain_kernel(char* __restrict__ ws, const bf16* __restrict__ d_o,
@@ -99,8 +100,7 @@ gdn2_bwd_chain_kernel(char* __restrict__ ws, const bf16* __restrict__ d_o,
   const int nh = unit_id / nseg;
   const int h = nh % H;
   const int n = nh / H;
-  const int col0 = slice * NV;             // XFER: within [d_v value | d_k identity] columns
-  const bool ident = XFER && col0 >= DV;   // this slice carries transfer (identity) columns
+  const int col0 = slice * NV;
   const int ctg = slice * Sh::NWV + wave;  // this wave's column tile within d_v
 
   long row0, slot0;
@@ -138,7 +138,7 @@ gdn2_bwd_chain_kernel(char* __restrict__ ws, const bf16* __restrict__ d_o,
     for (int i = 0; i < 4; ++i) {
       const int row = 16 * mt + 4 * g4 + i;
       if constexpr (XFER)
-        D[mt][i] = (ident && row == col0 - DV + 16 * wave + m16) ? 1.f : 0.f;
+        D[mt][i] = 0.f;
       else if (nseg > 1)
         D[mt][i] = dbuf[dbase + (long)row * DV];
       else
@@ -162,10 +162,6 @@ gdn2_bwd_chain_kernel(char* __restrict__ ws, const bf16* __restrict__ d_o,
 #pragma unroll
     for (int j = 0; j < Sh::PPD; ++j) {
       const int p = tid + j * NT, r = p / (NV / 8), cc = p % (NV / 8);
-      if (ident) {  // (uniform) no dO on the identity columns
-        std_[j] = u32x4{0u, 0u, 0u, 0u};
-        continue;
-      }
       const T* src = d_o + (row0 + (long)ci * C + (r < nvalid ? r : 0)) * vstride +
                      (long)h * DV + col0 + cc * 8;
       const u32x4 x = *reinterpret_cast<const u32x4*>(src);
@@ -267,7 +263,7 @@ gdn2_bwd_chain_kernel(char* __restrict__ ws, const bf16* __restrict__ d_o,
     stage_load(ci > 1 ? ci - 2 : 0);
     lds_barrier();
   }
-  if constexpr (XFER) {  // the segment's start value [b | A] (rows d_k, d_v + d_k columns)
+  if constexpr (XFER) {  // b into the value columns of the segment's [b | M] (rows d_k, d_v + d_k columns)
     constexpr int LE = DV + DK;
     float* E = ebuf + (long)unit_id * DK * LE + col0 + 16 * wave + m16;
 #pragma unroll
@@ -809,18 +805,17 @@ static hipError_t launch_bwd(const BwdArgs& a) {
   constexpr int NV = 64 <= DV ? 64 : DV;
   const int nslices = DV / NV;
   if (f.nseg > 1) {
-    // long sequences: transfer pass per segment, the segments' end gradients by a reverse
-    // scan, then the chain per segment (the buffers after the workspace are free again: the
-    // forward part's are consumed)
+    // long sequences: transfer pass per segment (b; A = M^T is in the buffer from the forward
+    // part's transfer pass, run here or by the training forward), the segments' end
+    // gradients by a reverse scan, then the chain per segment
     const int nseg = f.nseg;
     const long units = (long)f.N * f.H * nseg;
     float* ebuf = reinterpret_cast<float*>(
         (char*)f.workspace + (bwd_workspace_bytes(false, f.B, f.T, f.H, DK, DV, f.N) + 255) / 256 * 256);
     float* dbuf = ebuf + units * DK * (DV + DK);
-    const int xslices = (DV + DK) / NV;
-    hipLaunchKernelGGL((gdn2_bwd_chain_kernel<DK, DV, NV, true>), dim3((unsigned)(units * xslices)),
+    hipLaunchKernelGGL((gdn2_bwd_chain_kernel<DK, DV, NV, true>), dim3((unsigned)(units * nslices)),
                        dim3(ChainShape<DK, DV, NV>::NT), 0, st, (char*)f.workspace,
-                       (const bf16*)a.d_o, nullptr, nullptr, nullptr, f.T, f.H, xslices,
+                       (const bf16*)a.d_o, nullptr, nullptr, nullptr, f.T, f.H, nslices,
                        (int)units, nseg, f.seg_chunks, ebuf, nullptr);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -793,7 +793,8 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
 // S_{s+1} = M_s S_s + N_s, with [N_s | M_s] the end state of segment s's transfer pass.
 // REV (the backward's state gradient, which runs from the last chunk to the first): D at
 // the end of the last segment is the final state's gradient (or 0) and D_{s-1} = A_s D_s + b_s
-// with [b_s | A_s] from segment s's transfer pass; sbuf then holds each segment's end value.
+// with b_s from the reverse chain's transfer pass and A_s = M_s^T (the buffer holds
+// [b_s | M_s]); sbuf then holds each segment's end value.
 // One workgroup per (sequence, head, 16 value columns); one wave per 16-row tile; M_s is
 // staged in LDS with 16-byte loads, products in fp32 (16x16x4 MFMA), S exchanged through
 // LDS every step.
@@ -850,9 +851,11 @@ gdn2_seg_combine_kernel(const float* __restrict__ ebuf, const float* __restrict_
       for (int k0 = 0; k0 < DK; k0 += 4) {
         const float b = sS[k0 + g4][m16];  // S_s[k][col]
 #pragma unroll
-        for (int t = 0; t < RPW; ++t)
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(sM[(16 * (wave * RPW + t) + m16) * LDM + k0 + g4],
-                                                       b, acc[t], 0, 0, 0);
+        for (int t = 0; t < RPW; ++t) {
+          const int row = 16 * (wave * RPW + t) + m16, k = k0 + g4;
+          const float a = REV ? sM[k * LDM + row] : sM[row * LDM + k];  // A = M^T, or M
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[t], 0, 0, 0);
+        }
       }
 #pragma unroll
       for (int t = 0; t < RPW; ++t) S[t] = acc[t];

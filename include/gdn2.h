@@ -183,7 +183,8 @@ int gdn2_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* l
 /*
  * Training forward: the same result as gdn2_chunk_fwd (o, and the final state when
  * final_state is not NULL), computed by the two-phase kernels while the backward's
- * intermediates (the chunk factors, every chunk's entering state and U) are kept in
+ * intermediates (the chunk factors, every chunk's entering state and U, and for a sequence
+ * cut into segments each segment's linear map of the state) are kept in
  * `workspace`, so that gdn2_chunk_bwd_saved can skip the forward recomputation that
  * gdn2_chunk_bwd performs. Same arguments as gdn2_chunk_fwd, except that o is required and
  * workspace is required, of at least gdn2_chunk_bwd_workspace_bytes(...) bytes, and the
