@@ -515,10 +515,7 @@ struct StateShape {
   static constexpr int OFF_U = SZ_A;
   static constexpr int OFF_G = OFF_U + SZ_U;
   static constexpr int NPIECE = (OFF_G + DK * 4) / 16;  // 16-byte pieces per chunk
-  static constexpr int PPT = (NPIECE + NT - 1) / NT;    // pieces per thread
-  // every thread moves PPT pieces (the tail ones re-read the last piece into padding),
-  // so the staging code has no branches and its registers stay registers
-  static constexpr int STAGE = PPT * NT * 16;
+  static constexpr int STAGE = NPIECE * 16;
   static constexpr int OP = NV + 8;                   // output staging pitch
   static constexpr int SZ_O = C * OP * 2;
   static constexpr int OFF_O = 2 * STAGE;             // two output staging buffers
@@ -623,27 +620,37 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
   // refilled with chunk c+2. (A plain vector type: an array of HIP's uint4 struct of this
   // length is kept in scratch memory.)
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 stg[Sh::PPT];
-  // workspace offset of staged piece p: [-W | Qbar | Kt | P] as is, then this slice's U~
-  // tiles, then gamma (selects, no branches)
+  // Without an output, Qbar and P are not staged (they feed only o): the staged pieces are
+  // [-W | Kt | U~ | gamma], each at its usual place in the stage, whose layout is the
+  // workspace's prefix [-W | Qbar | Kt | P], then this slice's U~ tiles, then gamma.
   static_assert(Sh::OFF_U == (int)L.u, "staged prefix matches the workspace prefix");
+  constexpr int SKIP_Q = OUT ? 0 : (int)(L.kt - L.q);
+  constexpr int SKIP_P = OUT ? 0 : (int)(L.u - L.p);
+  constexpr int NPC = Sh::NPIECE - (SKIP_Q + SKIP_P) / 16;  // pieces staged per chunk
+  constexpr int PPC = (NPC + NT - 1) / NT;                  // ... per thread
+  u32x4 stg[PPC];
+  // stage offset of staged piece p (the tail pieces repeat the last one, same data to the
+  // same place, so the staging code has no branches); selects only
+  auto piece_off = [&](int p) {
+    int off = (p < NPC ? p : NPC - 1) * 16;
+    off += off >= (int)L.q ? SKIP_Q : 0;
+    off += off >= (int)L.p ? SKIP_P : 0;
+    return off;
+  };
   const int u_shift = (XFER && ident ? 0 : slice) * Sh::SZ_U;  // identity slices: unused
-  auto piece_src = [&](int p, long chunk) -> const u32x4* {
+  auto piece_src = [&](int off, long chunk) -> const u32x4* {
     const char* unit = ws + ((slot0 + chunk) * H + h) * UNIT;
-    const int off = p * 16 + (p >= Sh::OFF_U / 16 && p < Sh::OFF_G / 16 ? u_shift : 0) +
-                    (p >= Sh::OFF_G / 16 ? (int)L.g - Sh::OFF_G : 0);
+    off += (off >= Sh::OFF_U && off < Sh::OFF_G ? u_shift : 0) +
+           (off >= Sh::OFF_G ? (int)L.g - Sh::OFF_G : 0);
     return reinterpret_cast<const u32x4*>(unit + off);
   };
   auto stage_load = [&](long chunk) {
 #pragma unroll
-    for (int j = 0; j < Sh::PPT; ++j) {
-      const int p = tid + j * NT;
-      stg[j] = *piece_src(p < Sh::NPIECE ? p : Sh::NPIECE - 1, chunk);
-    }
+    for (int j = 0; j < PPC; ++j) stg[j] = *piece_src(piece_off(tid + j * NT), chunk);
   };
   auto stage_store = [&](char* buf) {
 #pragma unroll
-    for (int j = 0; j < Sh::PPT; ++j) *reinterpret_cast<u32x4*>(buf + (tid + j * NT) * 16) = stg[j];
+    for (int j = 0; j < PPC; ++j) *reinterpret_cast<u32x4*>(buf + piece_off(tid + j * NT)) = stg[j];
   };
   // output rows of the previous chunk: staging buffer -> HBM (16-byte pieces)
   constexpr int OPR = NV / 8;  // pieces per row

@@ -175,6 +175,22 @@ def test_bwd_segments_saved_pair():
     ref = gdn2_backward(*(x[n] for n in NAMES), do, dS_final=dsn, s0=x["s0"])
     for name, a, r in zip(GRADS + ("ds0",), out, ref):
         assert_close(name, host64(a), r, TOL["bf16"])
+    # A second backward on the same saved workspace (the first overwrote only what it may:
+    # the segments' linear maps, kept by the training forward, are read again), with the
+    # upstream gradients scaled by -2 (exact in bf16 and fp32), so the reference gradients
+    # are the oracle's scaled by -2.
+    out2 = G.chunk_bwd(*(t[n] for n in NAMES), dev_tensor(-2.0 * do, "bf16"), initial_state=s0,
+                       d_final_state=torch.from_numpy(-2.0 * dsn).cuda(), saved=sv)
+    torch.cuda.synchronize()
+    for name, a2, r in zip(GRADS + ("ds0",), out2, ref):
+        assert_close(name + " (second call)", host64(a2), -2.0 * r, TOL["bf16"])
+    # a third with the first call's upstream gradients repeats the first bit for bit
+    out3 = G.chunk_bwd(*(t[n] for n in NAMES), dev_tensor(do, "bf16"), initial_state=s0,
+                       d_final_state=torch.from_numpy(dsn).cuda(), saved=sv)
+    torch.cuda.synchronize()
+    for name, a, a3 in zip(GRADS + ("ds0",), out, out3):
+        assert torch.equal(a, a3), f"{name}: third call differs from the first"
+
 
 
 def test_bwd_layer1p3b_full_size_sampled():
