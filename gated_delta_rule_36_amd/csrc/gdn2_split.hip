@@ -93,15 +93,15 @@ struct PrepPieces {
 };
 
 // BWD: also write the reverse chain's operands (BwdLayout) after the forward factors, and
-// use the backward unit stride.
+// use the backward unit stride. out_factors = 0 leaves out Qbar and P, which only the output
+// o needs (the backward's own forward pass writes none).
 template <int DK, int DV, bool BWD, int GL>
 __global__ void __launch_bounds__(512)
 gdn2_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                  const bf16* __restrict__ v, const bf16* __restrict__ g,
                  const bf16* __restrict__ bg, const bf16* __restrict__ wg,
                  char* __restrict__ ws, const int* __restrict__ cu_seqlens, int N, int T_len,
-                 int H, long nunits, int gflags) {
-  (void)gflags;  // the layout is the template's GL
+                 int H, long nunits, int out_factors) {
   typedef bf16 T;
   using Sh = PrepShape<DK, DV>;
   using M = Mma<T>;
@@ -192,13 +192,13 @@ gdn2_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
     for (int q = 0; q < Op::NW_; ++q) {
       *reinterpret_cast<u32x4*>(prev_out + L.w + (tid + q * NT) * 16) = ost[Op::J_W + q];
-      *reinterpret_cast<u32x4*>(prev_out + L.q + (tid + q * NT) * 16) = ost[Op::J_Q + q];
+      if (out_factors) *reinterpret_cast<u32x4*>(prev_out + L.q + (tid + q * NT) * 16) = ost[Op::J_Q + q];
     }
 #pragma unroll
     for (int q = 0; q < Op::NK_; ++q)
       *reinterpret_cast<u32x4*>(prev_out + L.kt + (tid + q * NT) * 16) = ost[Op::J_K + q];
     const int pb = tid >> 6;  // P blocks (0,1) and (1,1) are never read
-    if (pb != 1 && pb != 3) *reinterpret_cast<u32x4*>(prev_out + L.p + tid * 16) = ost[Op::J_P];
+    if (out_factors && pb != 1 && pb != 3) *reinterpret_cast<u32x4*>(prev_out + L.p + tid * 16) = ost[Op::J_P];
 #pragma unroll
     for (int q = 0; q < Op::NU_; ++q)
       *reinterpret_cast<u32x4*>(prev_out + L.u + (tid + q * NT) * 16) = ost[Op::J_U + q];
@@ -915,7 +915,7 @@ static hipError_t launch_split(const ChunkArgs& a) {
     hipLaunchKernelGGL(prep, dim3((unsigned)grid1), dim3(512), 0, st,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.g,
                        (const bf16*)a.b, (const bf16*)a.w, (char*)a.workspace, a.cu_seqlens,
-                       a.N, a.T, a.H, nunits, a.gate_flags);
+                       a.N, a.T, a.H, nunits, 1);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -969,7 +969,7 @@ static hipError_t launch_bwd_forward(const ChunkArgs& a) {
     hipLaunchKernelGGL(prep, dim3((unsigned)grid1), dim3(512), 0, st,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.g,
                        (const bf16*)a.b, (const bf16*)a.w, (char*)a.workspace, a.cu_seqlens,
-                       a.N, a.T, a.H, nunits, 0);
+                       a.N, a.T, a.H, nunits, a.o != nullptr ? 1 : 0);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
