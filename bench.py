@@ -203,7 +203,8 @@ def main():
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
     if use_split:
         kernel = (f"gdn2_prep_kernel<{dk},{dv}> + gdn2_state_kernel<{dk},{dv},NV> "
-                  "(the two launches of one call)")
+                  "(the launches of one call; a sequence cut into segments adds the "
+                  "transfer pass and the combine kernel between them)")
         tkey = f"chunk_fwd_split_{cfg}"
     else:
         kernel = f"gdn2_chunk_kernel<bf16,{dk},NV>"
@@ -237,7 +238,7 @@ def main():
                  "frac": round(flops / (kern_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
     }
 
-    if not args.no_backward and args.workload == "layer1p3b":
+    if not args.no_backward:
         rng = np.random.default_rng(7)
         do = torch.from_numpy(rng.normal(size=(B, T, H, dv)).astype(np.float32)).to(dev)
         do = do.to(torch.bfloat16)
@@ -269,11 +270,12 @@ def main():
                        "local gradients", "calls_timed": KB,
             "algorithmic_bytes": bb, "achieved_GBs": round(bb / (bms * 1e-3) / 1e9, 1),
             "hbm_frac": round(bb / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic("chunk_bwd_layer1p3b_bf16")}
+            "traffic": (measured_traffic("chunk_bwd_layer1p3b_bf16")
+                        if args.workload == "layer1p3b" else None)}
 
-        # a training step: forward then backward. Either the fused forward and a backward
-        # that recomputes the forward, or the training forward (keeps the intermediates) and
-        # the backward that reuses them.
+        # a training step (on the headline workload): forward then backward. Either the fused
+        # forward and a backward that recomputes the forward, or the training forward (keeps
+        # the intermediates) and the backward that reuses them.
         def pair_recompute():
             G.chunk_fwd(*(t[n] for n in NAMES), initial_state=s0, cu_seqlens=cu, path="fused")
             bstep()
@@ -284,7 +286,8 @@ def main():
             G.chunk_bwd(*(t[n] for n in NAMES), do, initial_state=s0, cu_seqlens=cu, saved=sv,
                         check_range=False)
         res_t = {}
-        for name, fn in (("recompute", pair_recompute), ("saved", pair_saved)):
+        pairs = (("recompute", pair_recompute), ("saved", pair_saved))
+        for name, fn in (pairs if args.workload == "layer1p3b" else ()):
             for _ in range(3):
                 fn()
             torch.cuda.synchronize()
@@ -296,11 +299,12 @@ def main():
                 b2.record()
             torch.cuda.synchronize()
             res_t[name] = round(float(np.mean([a.elapsed_time(b2) for a, b2 in evt])), 4)
-        out["train_step"] = {
-            "workload": "forward + backward on the same workload",
-            "ms_fused_forward_then_recomputing_backward": res_t["recompute"],
-            "ms_training_forward_then_saved_backward": res_t["saved"],
-            "tokens_per_s_saved": round(B * T / (res_t["saved"] * 1e-3), 1)}
+        if res_t:
+            out["train_step"] = {
+                "workload": "forward + backward on the same workload",
+                "ms_fused_forward_then_recomputing_backward": res_t["recompute"],
+                "ms_training_forward_then_saved_backward": res_t["saved"],
+                "tokens_per_s_saved": round(B * T / (res_t["saved"] * 1e-3), 1)}
         del bws
 
     if args.workload == "layer1p3b" and not args.no_long:
