@@ -142,9 +142,9 @@ def main():
                          "(3 times) so hardware byte counters can be calibrated against it")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU (got --gpus {args.gpus}); the "
-              "chunk forward shards by sequence/head/value-column with no exchange, but "
-              "multi-GPU runs are not part of it.", file=sys.stderr)
+        print(f"bench.py: runs on exactly one GPU (got --gpus {args.gpus}); the chunk "
+              "forward shards by sequence/head/value-column with no exchange, but multi-GPU "
+              "runs are not implemented.", file=sys.stderr)
         sys.exit(2)
 
     import torch
