@@ -412,11 +412,12 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
     fresh_prep();
 
     // ---- (d) A (stored negated) and P, and the diagonal blocks of (I + A)^{-1}.
-    // Chunk path: the last wave (TDW) forms the four diagonal A tiles itself and goes
-    // straight on to their inverses (fp32 forward substitution, one block per 16-lane group,
-    // one column per lane), with no barrier in between; the other waves form the other 16
-    // tiles and then their partial Q exp(G) S products.
-    constexpr int TDW = NW - 1;  // wave that forms the diagonal inverse blocks
+    // Chunk path: the wave(s) that invert form their diagonal A tiles themselves and go
+    // straight on to the inverse blocks (fp32 forward substitution, one block per 16-lane
+    // group, one column per lane), with no barrier in between: with 8 waves the last two
+    // take two blocks each, otherwise the last wave all four. The other waves form the
+    // other tiles and then their partial Q exp(G) S products.
+    constexpr int TDW = NW - 1;  // (last) wave that forms diagonal inverse blocks
     typename M::frag sb[KSH];    // this wave's state rows as B operands
 #pragma unroll
     for (int s = 0; s < KSH; ++s) sb[s] = M::from_acc(S, s);
@@ -439,7 +440,25 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
     constexpr int DIAG = 0x225;     // (0,0) (1,1) (2,2) (3,3)
     constexpr int OFFD = 0x1DA;     // off-diagonal pairs
     if (!block_path) {
-      if (wave == TDW) {
+      if constexpr (NW >= 8) {
+        if (wave >= TDW - 1) {
+          if (wave == TDW) ap_tiles<T, DK, LDK, LDT, 0x005, 0>(sE, sQ, sK, sAm, sP, sAd, m16, g4);
+          else ap_tiles<T, DK, LDK, LDT, 0x220, 0>(sE, sQ, sK, sAm, sP, sAd, m16, g4);
+          // reads only what this wave just wrote: no barrier needed
+          diag_inverse_pair<T, LDT, ADB, ADP>(sAd, sT, m16, g4, wave == TDW ? 0 : 2);
+        } else {
+          switch (wave) {
+            case 0: ap_tiles<T, DK, LDK, LDT, 0x0C0, 0>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
+            case 1: ap_tiles<T, DK, LDK, LDT, 0x118, 0>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
+            case 2: ap_tiles<T, DK, LDK, LDT, 0x002, 0x003>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
+            case 3: ap_tiles<T, DK, LDK, LDT, 0, 0x0C0>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
+            case 4: ap_tiles<T, DK, LDK, LDT, 0, 0x304>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
+            case 5: ap_tiles<T, DK, LDK, LDT, 0, 0x038>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
+            default: break;
+          }
+          o_partial();
+        }
+      } else if (wave == TDW) {
         if constexpr (NW == 1) {
           ap_tiles<T, DK, LDK, LDT, 0x3FF, 0x3FF>(sE, sQ, sK, sAm, sP, sAd, m16, g4);
         } else if constexpr (NW == 2) {
@@ -449,18 +468,7 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
         }
         tdiag();  // reads only what this wave just wrote: no barrier needed
       } else {
-        if constexpr (NW >= 8) {
-          switch (wave) {
-            case 0: ap_tiles<T, DK, LDK, LDT, 0x0C0, 0>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
-            case 1: ap_tiles<T, DK, LDK, LDT, 0x118, 0>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
-            case 2: ap_tiles<T, DK, LDK, LDT, 0x002, 0x001>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
-            case 3: ap_tiles<T, DK, LDK, LDT, 0, 0x0C0>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
-            case 4: ap_tiles<T, DK, LDK, LDT, 0, 0x300>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
-            case 5: ap_tiles<T, DK, LDK, LDT, 0, 0x038>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
-            case 6: ap_tiles<T, DK, LDK, LDT, 0, 0x006>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
-            default: break;
-          }
-        } else if constexpr (NW >= 4) {
+        if constexpr (NW >= 4) {
           switch (wave) {
             case 0: ap_tiles<T, DK, LDK, LDT, OFFD, 0>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
             case 1: ap_tiles<T, DK, LDK, LDT, 0, 0x3C1>(sE, sQ, sK, sAm, sP, sAd, m16, g4); break;
@@ -545,7 +553,7 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
 #pragma unroll
       for (int R = 0; R < 4; ++R) U[R] = (RS == 1 || whw == 0) ? X[NE][R] : f4{0.f, 0.f, 0.f, 0.f};
     }
-    if (wave == TDW && !block_path) o_partial();
+    if ((wave == TDW || (NW >= 8 && wave == TDW - 1)) && !block_path) o_partial();
     lds_barrier();
     fresh_prep();
 

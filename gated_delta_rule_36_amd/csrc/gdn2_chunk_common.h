@@ -215,6 +215,36 @@ __device__ __forceinline__ void diag_inverse(const float* sAd, T* sT, int m16, i
   for (int r = 0; r < 16; ++r) sT[(16 * jb + r) * LDT + 16 * jb + c] = from_f<T>(x[r]);
 }
 
+// Two of the four diagonal blocks, jb0 and jb0 + 1 (lane groups 0 and 1; groups 2 and 3
+// repeat them and do not write).
+template <typename T, int LDT, int ADB, int ADP>
+__device__ __forceinline__ void diag_inverse_pair(const float* sAd, T* sT, int m16, int g4, int jb0) {
+  const int jb = jb0 + (g4 & 1), c = m16;
+  const float* Ab = sAd + jb * ADB;
+  float am[16][16];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) {
+#pragma unroll
+    for (int i4 = 0; i4 < r; i4 += 4) {
+      const f4 v = *reinterpret_cast<const f4*>(Ab + r * ADP + i4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) am[r][i4 + j] = v[j];
+    }
+  }
+  float x[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+#pragma unroll
+    for (int r = i + 1; r < 16; ++r) x[r] += am[r][i] * x[i];
+  }
+  if (g4 < 2) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sT[(16 * jb + r) * LDT + 16 * jb + c] = from_f<T>(x[r]);
+  }
+}
+
 // Block-referenced A and P tiles (chunks whose total decay is too large for the chunk-
 // referenced factors): rows of block R against Kn of block I; off-diagonal tiles scale Kn
 // by 2^(Ge(I)-Gs(I)) and, two or more blocks apart, the left operand by 2^(Gs(R)-Ge(I)).
