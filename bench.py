@@ -154,6 +154,18 @@ def main():
     from gdn2_inputs import CONFIGS, make_config_inputs, make_decode_inputs
 
     dev = torch.device("cuda:0")
+
+    def settle(fn, seconds=0.1):
+        """Untimed calls of fn (at least 3) for about `seconds` of wall time, so that the
+        timed calls after them run at the GPU's settled clocks."""
+        n, t_end = 0, time.perf_counter() + seconds
+        while n < 3 or time.perf_counter() < t_end:
+            fn()
+            n += 1
+            if n % 4 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+
     cfg = args.workload + "_bf16"
     x = make_config_inputs(cfg)
     B, T, H, dk = x["q"].shape
@@ -251,9 +263,7 @@ def main():
             return G.chunk_bwd(*(t[n] for n in NAMES), do, initial_state=s0, cu_seqlens=cu,
                                workspace=bws, check_range=check)
         bstep(check=True)
-        for _ in range(3):
-            bstep()
-        torch.cuda.synchronize()
+        settle(bstep)
         KB = max(5, K // 5)
         evb = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(KB)]
@@ -290,9 +300,7 @@ def main():
         res_t = {}
         pairs = (("recompute", pair_recompute), ("saved", pair_saved))
         for name, fn in (pairs if args.workload == "layer1p3b" else ()):
-            for _ in range(3):
-                fn()
-            torch.cuda.synchronize()
+            settle(fn)
             evt = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(KB)]
             for a, b2 in evt:
@@ -330,9 +338,7 @@ def main():
 
         def lstep():
             return G.chunk_fwd(lq, lk, lv, lg, lb, lw, workspace=lws)
-        for _ in range(3):
-            lstep()
-        torch.cuda.synchronize()
+        settle(lstep)
         evl = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(10)]
         for a, b2 in evl:
@@ -351,8 +357,7 @@ def main():
             def lbstep(check=False):
                 return G.chunk_bwd(lq, lk, lv, lg, lb, lw, ldo, workspace=lbws, check_range=check)
             lbstep(check=True)  # (raises if a chunk were outside the backward's decay range)
-            lbstep()
-            torch.cuda.synchronize()
+            settle(lbstep)
             evb = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(5)]
             for a, b2 in evb:
@@ -395,9 +400,7 @@ def main():
         def vstep():
             return G.chunk_fwd(vq, vk, vv, vg, vb, vw, initial_state=vs0, cu_seqlens=cu_v,
                                workspace=vws)
-        for _ in range(3):
-            vstep()
-        torch.cuda.synchronize()
+        settle(vstep)
         evv = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(10)]
         for a, b2 in evv:
@@ -426,9 +429,7 @@ def main():
         def sstep():
             return G.chunk_fwd(*(sg[n] for n in NAMES), initial_state=s0, cu_seqlens=cu,
                                path="fused")
-        for _ in range(3):
-            sstep()
-        torch.cuda.synchronize()
+        settle(sstep)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(20)]
         for a, b2 in evs:
@@ -458,9 +459,7 @@ def main():
         nw = torch.ones(dv, device=dev)
 
         def timed(fn, reps=20):
-            for _ in range(3):
-                fn()
-            torch.cuda.synchronize()
+            settle(fn)
             ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                   for _ in range(reps)]
             for a, b2 in ev:
@@ -469,8 +468,10 @@ def main():
                 b2.record()
             torch.cuda.synchronize()
             return float(np.mean([a.elapsed_time(b2) for a, b2 in ev])) * 1e3
-        pus = timed(lambda: G.block_prologue(*px.values(), *taps, dsc))
-        eus = timed(lambda: G.block_epilogue(og[0], og[1], nw))
+        pout = [torch.empty_like(x) for x in px.values()]  # outputs allocated once, outside
+        yout = torch.empty_like(og[0])                       # the timed calls
+        pus = timed(lambda: G.block_prologue(*px.values(), *taps, dsc, out=pout))
+        eus = timed(lambda: G.block_epilogue(og[0], og[1], nw, out=yout))
         rows = B * T * H
         pbytes = rows * (4 * dk + 2 * dv) * 2 * 2  # each projection read once, each input written
         ebytes = rows * dv * 2 * 3
@@ -485,7 +486,7 @@ def main():
                          "traffic": measured_traffic("block_epilogue_layer1p3b_bf16"),
                          "achieved_GBs": round(ebytes / (eus * 1e-6) / 1e9, 1),
                          "hbm_frac": round(ebytes / (eus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}}
-        del px, og
+        del px, og, pout, yout
 
     if not args.no_decode and args.workload == "layer1p3b":
         cd = CONFIGS["decode_bf16"]
@@ -497,9 +498,7 @@ def main():
         res = {}
         for mode in ("one_pool", "two_pools"):
             st = states[0]
-            for s in range(5):
-                G.decode_step(*(td[n][s % pool] for n in NAMES), st)
-            torch.cuda.synchronize()
+            settle(lambda: G.decode_step(*(td[n][0] for n in NAMES), st))
             evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(cd["steps"])]
             for s in range(cd["steps"]):
@@ -521,9 +520,7 @@ def main():
         vt = {n: torch.stack([td[n][s % pool] for s in range(Lv)], dim=1).contiguous()
               for n in NAMES}
         vstate = states[0]
-        for _ in range(5):
-            G.decode_tokens(*(vt[n] for n in NAMES), vstate)
-        torch.cuda.synchronize()
+        settle(lambda: G.decode_tokens(*(vt[n] for n in NAMES), vstate))
         evv = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(50)]
         for a, b2 in evv:

@@ -396,10 +396,11 @@ def decode_tokens(q, k, v, g, b, w, state_pool, state_indices=None, commit_len=N
 
 
 def block_prologue(xq, xk, xv, xg, xb, xw, conv_q, conv_k, conv_v, decay_scale, b_max=1.0,
-                   cu_seqlens=None):
+                   cu_seqlens=None, out=None):
     """Projections -> mixer inputs (q, k, v, g, b, w): conv/SiLU/L2-norm branches and gate
     activations in one pass. xq, xk, xg, xb: [B, T, H, d_k]; xv, xw: [B, T, H, d_v];
-    conv_*: fp32 [H * d, 4]; decay_scale: fp32 [H * d_k]."""
+    conv_*: fp32 [H * d, 4]; decay_scale: fp32 [H * d_k]. out: optional six preallocated
+    outputs shaped like xq, xk, xv, xg, xb, xw (written and returned)."""
     B, T, H, dk = xq.shape
     dv = xv.shape[-1]
     dev, dt = xq.device, xq.dtype
@@ -411,7 +412,15 @@ def block_prologue(xq, xk, xv, xg, xb, xw, conv_q, conv_k, conv_v, decay_scale, 
                            ("conv_v", conv_v, (H * dv, 4)), ("decay_scale", decay_scale, (H * dk,))):
         _check(name, t, shape, torch.float32, dev)
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
-    outs = [torch.empty_like(x) for x in (xq, xk, xv, xg, xb, xw)]
+    ins = (xq, xk, xv, xg, xb, xw)
+    if out is None:
+        outs = [torch.empty_like(x) for x in ins]
+    else:
+        outs = list(out)
+        if len(outs) != 6:
+            raise ValueError("out must hold six tensors (q, k, v, log_alpha, b, w)")
+        for name, t, x in zip(("q", "k", "v", "log_alpha", "b", "w"), outs, ins):
+            _check(name, t, tuple(x.shape), dt, dev)
     st = lib().gdn2_block_prologue(*(_ptr(x) for x in (xq, xk, xv, xg, xb, xw)), _ptr(conv_q),
                                    _ptr(conv_k), _ptr(conv_v), _ptr(decay_scale), float(b_max),
                                    *(_ptr(x) for x in outs), _ptr(cu_seqlens), B, T, H, dk, dv,
@@ -421,14 +430,19 @@ def block_prologue(xq, xk, xv, xg, xb, xw, conv_q, conv_k, conv_v, decay_scale, 
     return tuple(outs)
 
 
-def block_epilogue(o, gate, weight):
-    """y = RMSNorm(o) * weight * SiLU(gate) over the last axis (d_v); weight fp32 [d_v]."""
+def block_epilogue(o, gate, weight, out=None):
+    """y = RMSNorm(o) * weight * SiLU(gate) over the last axis (d_v); weight fp32 [d_v].
+    out: optional preallocated y shaped like o (written and returned)."""
     dv = o.shape[-1]
     _check("gate", gate, tuple(o.shape), o.dtype, o.device)
     _check("weight", weight, (dv,), torch.float32, o.device)
     if not o.is_contiguous():
         raise ValueError("o must be contiguous")
-    y = torch.empty_like(o)
+    if out is None:
+        y = torch.empty_like(o)
+    else:
+        _check("out", out, tuple(o.shape), o.dtype, o.device)
+        y = out
     st = lib().gdn2_block_epilogue(_ptr(o), _ptr(gate), _ptr(weight), _ptr(y), o.numel() // dv,
                                    dv, _dtype_code(o.dtype), _stream(o.device))
     if st != 0:

@@ -113,3 +113,29 @@ def test_full_size_prologue_epilogue_sampled():
             assert_close(f"{n}[{bi},{ti}]", host64(g_[bi, ti]), r_[0, -1], TOL["bf16"])
     ry = ref_epilogue(x["o"][:, ::97], x["gate"][:, ::97], x["norm_weight"])
     assert_close("y sampled", host64(y[:, ::97]), ry, TOL["bf16"])
+
+
+def test_preallocated_outputs():
+    """out= writes the same values into the caller's tensors as the allocating calls."""
+    import gated_delta_rule_36_amd as G
+    x = make_block_inputs(2, 70, 3, 128, 64, "bf16", seed=77)
+    say("block out= B2 T70 H3 dk128 dv64")
+    t = {n: dev_tensor(x[n], "bf16") for n in PROJ}
+    args = [t[n] for n in PROJ] + [_f32(x["conv_q"]), _f32(x["conv_k"]), _f32(x["conv_v"]),
+                                   _f32(x["decay_scale"])]
+    ref = G.block_prologue(*args, b_max=1.5)
+    out = [torch.full_like(r, float("nan")) for r in ref]
+    got = G.block_prologue(*args, b_max=1.5, out=out)
+    o, gate = dev_tensor(x["o"], "bf16"), dev_tensor(x["gate"], "bf16")
+    y_ref = G.block_epilogue(o, gate, _f32(x["norm_weight"]))
+    y = torch.full_like(y_ref, float("nan"))
+    y_got = G.block_epilogue(o, gate, _f32(x["norm_weight"]), out=y)
+    torch.cuda.synchronize()
+    assert all(g is o_ for g, o_ in zip(got, out)) and y_got is y
+    for name, a, b in zip(OUTS, got, ref):
+        assert torch.equal(a, b), name
+    assert torch.equal(y, y_ref)
+    with pytest.raises(ValueError):
+        G.block_prologue(*args, out=out[:5])
+    with pytest.raises(ValueError):
+        G.block_epilogue(o, gate, _f32(x["norm_weight"]), out=y[:1])
