@@ -113,22 +113,24 @@ def test_decode_tokens_scalar_gates(layout):
     assert_close("pool", host64(pool_t), pool_ref, TOL["bf16"])
 
 
+@pytest.mark.parametrize("T", [150, 1100])
 @pytest.mark.parametrize("layout", ["b", "w", "bw"])
 @pytest.mark.parametrize("saved", [False, True])
-def test_backward_scalar_gates(layout, saved):
+def test_backward_scalar_gates(layout, saved, T):
     """Gradients with scalar gates: a shared gate's gradient is the channel sum of the
     oracle's per-channel gradient of the broadcast gate; through the recomputing backward
-    and through the training forward / saved backward pair."""
+    and through the training forward / saved backward pair. At 1100 tokens (18 chunks, four
+    chains) both passes cut each sequence into segments."""
     import gated_delta_rule_36_amd as G
     from gdn2_inputs import round_to_bf16
     from oracle import gdn2_backward
-    B, T, H, dk, dv = 2, 150, 2, 128, 64
+    B, H, dk, dv = 2, 2, 128, 64
     x = make_inputs(B, T, H, dk, dv, "bf16", seed=61, s0_std=0.02)
     gx, rx = _scalarise(x, layout, (B, T, H), seed=63)
     rng = np.random.default_rng(65)
     do = round_to_bf16(rng.normal(size=(B, T, H, dv)).astype(np.float32))
     dsn = (rng.normal(size=(B, H, dk, dv)) * 0.1).astype(np.float32)
-    say("backward scalar gates", layout, "saved" if saved else "recompute")
+    say("backward scalar gates", layout, "saved" if saved else "recompute", "T", T)
     t = {n: dev_tensor(gx[n], "bf16") for n in NAMES}
     s0 = torch.from_numpy(x["s0"]).cuda()
     do_t, dsn_t = dev_tensor(do, "bf16"), torch.from_numpy(dsn).cuda()
