@@ -206,3 +206,21 @@ def test_backward_scalar_gates_many_units_sampled():
         for name, a, r in zip(("dq", "dk", "dv", "dg", "db", "dw"), grads[:6], ref[:6]):
             assert_close(name, host64(a[n:n + 1, :, h:h + 1]), r, TOL["bf16"])
         assert_close("ds0", host64(grads[6][n:n + 1, h:h + 1]), ref[6], TOL["bf16"])
+
+
+@pytest.mark.parametrize("layout", ["b", "bw"])
+def test_chunk_forward_scalar_gates_segments(layout):
+    """The two-phase forward with scalar gates at a length it cuts into segments (1100
+    tokens: 18 chunks, six chains of 64 value columns), against the token loop."""
+    import gated_delta_rule_36_amd as G
+    B, T, H = 1, 1100, 3
+    x = make_inputs(B, T, H, 128, 128, "bf16", seed=43, s0_std=0.05, reset_frac=0.05)
+    gx, rx = _scalarise(x, layout, (B, T, H), seed=11)
+    say("chunk_fwd scalar gates, segments", layout)
+    t = {n: dev_tensor(gx[n], "bf16") for n in NAMES}
+    s0 = torch.from_numpy(x["s0"]).cuda()
+    o, sN = G.chunk_fwd(*(t[n] for n in NAMES), initial_state=s0, path="split")
+    torch.cuda.synchronize()
+    o_ref, s_ref = gdn2_forward(*(rx[n] for n in NAMES), s0=x["s0"])
+    assert_close("o", host64(o), o_ref, TOL["bf16"])
+    assert_close("S_final", host64(sN), s_ref, TOL["bf16"])
