@@ -185,13 +185,12 @@ __device__ __forceinline__ void channel_scan(float* sTot, float* sFac, int* sFla
   }
 }
 
-// The four 16x16 diagonal blocks of (I + A)^{-1} by fp32 forward substitution, one block
-// per 16-lane group and one column per lane, from the fp32 copy of the diagonal blocks of
-// -A (block jb, row r, column i at sAd[jb * ADB + r * ADP + i]); written to the diagonal
-// blocks of sT ([64][LDT]).
+// One 16x16 diagonal block jb of (I + A)^{-1} by fp32 forward substitution, column c per lane,
+// from the fp32 copy of the diagonal blocks of -A (block jb, row r, column i at
+// sAd[jb * ADB + r * ADP + i]); written to block jb of sT ([64][LDT]) when `write`.
 template <typename T, int LDT, int ADB, int ADP>
-__device__ __forceinline__ void diag_inverse(const float* sAd, T* sT, int m16, int g4) {
-  const int jb = g4, c = m16;
+__device__ __forceinline__ void diag_inverse_block(const float* sAd, T* sT, int jb, int c,
+                                                   bool write) {
   const float* Ab = sAd + jb * ADB;
   float am[16][16];
 #pragma unroll
@@ -211,38 +210,23 @@ __device__ __forceinline__ void diag_inverse(const float* sAd, T* sT, int m16, i
 #pragma unroll
     for (int r = i + 1; r < 16; ++r) x[r] += am[r][i] * x[i];  // am holds -A
   }
-#pragma unroll
-  for (int r = 0; r < 16; ++r) sT[(16 * jb + r) * LDT + 16 * jb + c] = from_f<T>(x[r]);
-}
-
-// Two of the four diagonal blocks, jb0 and jb0 + 1 (lane groups 0 and 1; groups 2 and 3
-// repeat them and do not write).
-template <typename T, int LDT, int ADB, int ADP>
-__device__ __forceinline__ void diag_inverse_pair(const float* sAd, T* sT, int m16, int g4, int jb0) {
-  const int jb = jb0 + (g4 & 1), c = m16;
-  const float* Ab = sAd + jb * ADB;
-  float am[16][16];
-#pragma unroll
-  for (int r = 1; r < 16; ++r) {
-#pragma unroll
-    for (int i4 = 0; i4 < r; i4 += 4) {
-      const f4 v = *reinterpret_cast<const f4*>(Ab + r * ADP + i4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) am[r][i4 + j] = v[j];
-    }
-  }
-  float x[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-#pragma unroll
-    for (int r = i + 1; r < 16; ++r) x[r] += am[r][i] * x[i];
-  }
-  if (g4 < 2) {
+  if (write) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) sT[(16 * jb + r) * LDT + 16 * jb + c] = from_f<T>(x[r]);
   }
+}
+
+// All four diagonal blocks, one per 16-lane group.
+template <typename T, int LDT, int ADB, int ADP>
+__device__ __forceinline__ void diag_inverse(const float* sAd, T* sT, int m16, int g4) {
+  diag_inverse_block<T, LDT, ADB, ADP>(sAd, sT, g4, m16, true);
+}
+
+// Two of them, jb0 and jb0 + 1, on lane groups 0 and 1 (groups 2 and 3 repeat them and do
+// not write).
+template <typename T, int LDT, int ADB, int ADP>
+__device__ __forceinline__ void diag_inverse_pair(const float* sAd, T* sT, int m16, int g4, int jb0) {
+  diag_inverse_block<T, LDT, ADB, ADP>(sAd, sT, jb0 + (g4 & 1), m16, g4 < 2);
 }
 
 // Block-referenced A and P tiles (chunks whose total decay is too large for the chunk-
