@@ -81,13 +81,25 @@ def decode_bytes(N, H, dk, dv, elt=2):
 
 
 def _oracle_shard(arrays):
-    """One worker's share of the CPU baseline: the oracle over a block of sequences x heads."""
+    """One worker's share of the CPU baseline: the oracle over a block of sequences x heads.
+    Returns the token-heads it covered (a shard holds only some of the heads of its tokens,
+    so tokens are counted by dividing the sum over shards by H)."""
     from oracle import gdn2_forward
     gdn2_forward(*arrays)
-    return arrays[0].shape[0] * arrays[0].shape[1]
+    return arrays[0].shape[0] * arrays[0].shape[1] * arrays[0].shape[2]
 
 
-def cpu_baseline(x, workers=None):
+def _oracle_shard_errors(args):
+    """Parity of one shard: the oracle over it against the GPU's o and final state for the
+    same (sequence, heads); returns (max|o - ref|, max|ref o|, max|S - ref|, max|ref S|)."""
+    from oracle import gdn2_forward
+    arrays, o_gpu, s_gpu = args
+    o_ref, s_ref = gdn2_forward(*arrays)
+    return (float(np.max(np.abs(o_gpu - o_ref))), float(np.max(np.abs(o_ref))),
+            float(np.max(np.abs(s_gpu - s_ref))), float(np.max(np.abs(s_ref))))
+
+
+def cpu_baseline(x, workers=None, gpu_out=None):
     """The float64 oracle (gdn2_forward, unchanged) over the whole forward workload, sharded
     by (sequence, block of heads) over a process pool of up to 16 host cores; the pool is
     started and warmed before the timed region."""
@@ -102,14 +114,46 @@ def cpu_baseline(x, workers=None):
     with ctx.Pool(min(workers, len(shards))) as pool:
         pool.map(_oracle_shard, [tuple(a[:, :4] for a in sh) for sh in shards])  # warm-up
         t0 = time.perf_counter()
-        done = sum(pool.map(_oracle_shard, shards))
+        token_heads = sum(pool.map(_oracle_shard, shards))
         dt = time.perf_counter() - t0
         used = min(workers, len(shards))
-    return {"value": round(done / dt, 1), "unit": "tokens/s", "cores": used, "kind": "oracle",
+        parity = None
+        if gpu_out is not None:  # untimed: the same shards again, against the GPU's results
+            o_gpu, s_gpu = gpu_out
+            jobs = [(sh, o_gpu[bi:bi + 1, :, h0:h0 + hb], s_gpu[bi:bi + 1, h0:h0 + hb])
+                    for sh, (bi, h0) in zip(shards, [(bi, h0) for bi in range(B)
+                                                     for h0 in range(0, H, hb)])]
+            errs = pool.map(_oracle_shard_errors, jobs)
+            parity = {"max_rel_err_o": max(e[0] for e in errs) / max(e[1] for e in errs),
+                      "max_rel_err_S": max(e[2] for e in errs) / max(e[3] for e in errs)}
+    done = token_heads / H  # tokens: every shard holds hb of the H heads of its tokens
+    res = {"value": round(done / dt, 1), "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "tokens": int(round(done)), "seconds": round(dt, 3),
             "sample": f"the whole workload ({B} sequences x {T} tokens x {H} heads) in "
                       f"{len(shards)} shards of {hb} heads (float64 token loop, {dt:.1f} s "
                       f"wall on {used} processes)",
             "cpu": platform.processor() or platform.machine()}
+    return res, parity
+
+
+def provenance():
+    """The git commit when the tree is a checkout (None otherwise) and a digest of the
+    library's sources and header, which identifies the build either way."""
+    import hashlib
+    import subprocess
+    try:
+        sha = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True,
+                             text=True, timeout=10).stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        sha = None
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_delta_rule_36_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    with open(os.path.join(ROOT, "include", "gdn2.h"), "rb") as f:
+        h.update(f.read())
+    return {"git_sha": sha, "source_sha256": h.hexdigest()[:16]}
 
 
 def main():
@@ -538,7 +582,15 @@ def main():
             "vs_four_single_steps": round(4 * res["one_pool"]["us_per_step"] / vus, 3)}
 
     if not args.no_cpu and args.workload == "layer1p3b":
-        out["cpu_baseline"] = cpu_baseline(x)
+        o_last, s_last = step()  # one more call: its outputs are checked against the oracle
+        torch.cuda.synchronize()
+        gpu_out = (o_last.float().cpu().numpy().astype(np.float64),
+                   s_last.cpu().numpy().astype(np.float64))
+        out["cpu_baseline"], parity = cpu_baseline(x, gpu_out=gpu_out)
+        out["parity"] = {**{k: float(f"{v:.3e}") for k, v in parity.items()},
+                         "tolerance": 2e-2, "norm": "normwise: max|x - ref| / max|ref| over "
+                         "the whole call's o and final states, float64 oracle"}
+    out["provenance"] = provenance()
     print(json.dumps(out), flush=True)
 
 
