@@ -67,6 +67,10 @@ def lib():
         L.gdn2_decode_tokens.restype = _I
         L.gdn2_chunk_fwd_ex.argtypes = [_P] * 10 + [_I] * 8 + [_P, _Z, _P]
         L.gdn2_chunk_fwd_ex.restype = _I
+        L.gdn2_chunk_fwd_noalloc.argtypes = [_P] * 10 + [_I] * 8 + [_P]
+        L.gdn2_chunk_fwd_noalloc.restype = _I
+        L.gdn2_noalloc_scratch_bytes.argtypes = []
+        L.gdn2_noalloc_scratch_bytes.restype = _Z
         L.gdn2_decode_step_ex.argtypes = [_P] * 8 + [_I] * 6 + [_P]
         L.gdn2_decode_step_ex.restype = _I
         L.gdn2_decode_tokens_ex.argtypes = [_P] * 11 + [_I] * 8 + [_P]

@@ -190,6 +190,32 @@ int gdn2_chunk_fwd(const void* q, const void* k, const void* v, const void* log_
                         B, T, H, d_k, d_v, N, dtype, workspace, workspace_bytes, hip_stream, 0, 0);
 }
 
+int gdn2_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* log_alpha,
+                           const void* b, const void* w, const float* initial_state, void* o,
+                           float* final_state, const int32_t* cu_seqlens, int B, int T, int H,
+                           int d_k, int d_v, int N, int dtype, int gate_layout,
+                           void* hip_stream) {
+  if (dtype != GDN2_BF16 && dtype != GDN2_F32) return GDN2_INVALID_ARGUMENT;
+  if (B < 0 || T < 0 || H <= 0 || N < 0 || d_k <= 0 || d_v <= 0) return GDN2_INVALID_ARGUMENT;
+  if (!split_built(dtype, d_k, d_v)) return GDN2_UNSUPPORTED;
+  const size_t need = workspace_need(cu_seqlens != nullptr, B, T, H, d_k, d_v, N);
+  if (need > gdn2::scratch_capacity()) return GDN2_WORKSPACE_TOO_SMALL;
+  int dev = -1;
+  if (hip_stream != nullptr) {
+    if (hipStreamGetDevice((hipStream_t)hip_stream, &dev) != hipSuccess)
+      return GDN2_INVALID_ARGUMENT;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return GDN2_LAUNCH_FAILED;
+  }
+  void* scratch = nullptr;
+  if (gdn2::scratch_for_device(dev, &scratch) != hipSuccess) return GDN2_LAUNCH_FAILED;
+  return chunk_fwd_impl(q, k, v, log_alpha, b, w, initial_state, o, final_state, cu_seqlens,
+                        B, T, H, d_k, d_v, N, dtype, scratch, gdn2::scratch_capacity(),
+                        hip_stream, 0, gate_layout);
+}
+
+size_t gdn2_noalloc_scratch_bytes(void) { return gdn2::scratch_capacity(); }
+
 int gdn2_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* log_alpha,
                       const void* b, const void* w, const float* initial_state, void* o,
                       float* final_state, const int32_t* cu_seqlens, int B, int T, int H,
@@ -400,7 +426,9 @@ const char* gdn2_status_string(int status) {
     case GDN2_OK: return "ok";
     case GDN2_INVALID_ARGUMENT: return "invalid argument";
     case GDN2_UNSUPPORTED: return "unsupported head width, dtype or value slice";
-    case GDN2_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case GDN2_WORKSPACE_TOO_SMALL:
+      return "workspace too small (for gdn2_chunk_fwd_noalloc: the call needs more than the "
+             "library-held scratch, gdn2_noalloc_scratch_bytes())";
     case GDN2_LAUNCH_FAILED: return "kernel launch failed";
     default: return "unknown status";
   }

@@ -176,6 +176,9 @@ hipError_t launch_bwd_forward_part(const ChunkArgs& a);
 hipError_t launch_seg_combine(const float* ebuf, const float* s_in, float* sbuf, int N, int H,
                               int d_k, int d_v, int nseg, bool reverse, void* stream);
 int cu_count();  // compute units of the current device
+// Library-held scratch (gdn2_noalloc.hip): bytes per device, and this device's address.
+size_t scratch_capacity();
+hipError_t scratch_for_device(int device, void** ptr);
 hipError_t launch_decode_step(const DecodeArgs& a);
 hipError_t launch_decode_tokens(const DecodeTokensArgs& a);
 

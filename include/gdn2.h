@@ -117,6 +117,34 @@ int gdn2_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* l
                       size_t workspace_bytes, void* hip_stream);
 
 /*
+ * For callers that cannot allocate device memory (work under HIP stream capture, tight
+ * serving loops, harnesses that forbid hipMalloc): gdn2_chunk_fwd_ex's two-phase path with
+ * its workspace taken from a scratch array that the library holds on each device (a static
+ * device array of gdn2_noalloc_scratch_bytes() = 128 MiB, resident from the library's load
+ * on that device until the process ends). The call allocates and frees nothing; on its
+ * first use on a device it looks up that device's scratch address (hipGetSymbolAddress).
+ * The caller still passes every input and output, as for gdn2_chunk_fwd_ex (same
+ * arguments without the workspace). Results equal gdn2_chunk_fwd_ex with a workspace.
+ *   - Every call on one device shares that device's scratch: calls that may overlap on one
+ *     device (different streams, or threads) race and must be serialised by the caller.
+ *     The scratch keeps the last call's contents; nothing in it needs to start at zero.
+ *   - Sizes whose workspace (gdn2_chunk_fwd_workspace_bytes for the same arguments,
+ *     with or without cu_seqlens as given) exceeds the scratch give
+ *     GDN2_WORKSPACE_TOO_SMALL and launch nothing; about 1.1 K tokens x heads fit per MiB
+ *     at d_k = d_v = 128 (e.g. 4096 tokens x 16 heads in one sequence).
+ *   - Built where the two-phase path is: GDN2_BF16 with d_k, d_v in {64, 128}
+ *     (GDN2_UNSUPPORTED otherwise; the fused path of gdn2_chunk_fwd needs no workspace).
+ */
+int gdn2_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* log_alpha,
+                           const void* b, const void* w, const float* initial_state, void* o,
+                           float* final_state, const int32_t* cu_seqlens, int B, int T, int H,
+                           int d_k, int d_v, int N, int dtype, int gate_layout,
+                           void* hip_stream);
+
+/* Bytes of the per-device scratch array that gdn2_chunk_fwd_noalloc uses. */
+size_t gdn2_noalloc_scratch_bytes(void);
+
+/*
  * Device workspace, in bytes, that the two-phase path of gdn2_chunk_fwd needs for a call
  * with these sizes, with or without cu_seqlens (about 1.13 KiB per token and head at
  * d_k = d_v = 128, plus one chunk per sequence, plus (2 d_v + d_k) d_k fp32 per segment and

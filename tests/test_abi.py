@@ -235,3 +235,18 @@ def test_train_pair_error_paths():
     assert L.gdn2_chunk_bwd_saved(*args, 2, 64, 4, 96, 128, 2, 0, 0, FAKE, 1 << 40, None) == 2
     assert L.gdn2_chunk_bwd_ex(*args, 2, 64, 4, 128, 128, 2, 0, 8, FAKE, 1 << 40, None) == 1
     assert L.gdn2_chunk_bwd_ex(*args, 2, 64, 4, 128, 128, 2, 0, 3, None, 0, None) == 3
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch():
+    """A call whose two-phase workspace exceeds the library-held scratch is refused on the
+    host (status 3, nothing launched); fp32 has no two-phase path (status 2)."""
+    L = _lib.lib()
+    cap = int(L.gdn2_noalloc_scratch_bytes())
+    assert cap == 128 << 20
+    T = 1 << 20
+    assert int(L.gdn2_chunk_fwd_workspace_bytes(1, T, 16, 128, 128, 1, 0)) > cap
+    args = [FAKE] * 6 + [None, FAKE, None, None]
+    assert L.gdn2_chunk_fwd_noalloc(*args, 1, T, 16, 128, 128, 1, 0, 0, None) == 3
+    assert b"scratch" in L.gdn2_status_string(3)
+    assert L.gdn2_chunk_fwd_noalloc(*args, 1, 64, 2, 64, 64, 1, 1, 0, None) == 2
+    assert L.gdn2_chunk_fwd_noalloc(*args, 1, 64, 0, 64, 64, 1, 0, 0, None) == 1
