@@ -104,6 +104,11 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* log_
     if ((long)N * H * (d_v / a.nv) > (long)INT_MAX) return GDN2_INVALID_ARGUMENT;
     return status_of(gdn2::launch_chunk_fwd_split(a));
   }
+  if (nv == 0 && gdn2::fwd_pipelined_supported(dtype, d_k, d_v)) {
+    if ((long)N * H * (d_v / 64) > (long)INT_MAX) return GDN2_INVALID_ARGUMENT;
+    a.nv = 64;
+    return status_of(gdn2::launch_fwd_pipelined(a));
+  }
   if (nv == 0) nv = pick_nv(dtype, d_k, d_v, (long)N * H);
   if (!gdn2::chunk_nv_supported(dtype, d_k, d_v, nv)) return GDN2_UNSUPPORTED;
   const long grid = (long)N * H * (d_v / nv);

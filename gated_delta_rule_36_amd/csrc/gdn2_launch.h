@@ -167,6 +167,10 @@ struct BwdArgs {
 };
 
 hipError_t launch_chunk_fwd(const ChunkArgs& a);
+// The pipelined fused forward (gdn2_fwd.hip): bf16, d_k and d_v in {64, 128}, 64-column
+// value slices.
+bool fwd_pipelined_supported(int dtype, int d_k, int d_v);
+hipError_t launch_fwd_pipelined(const ChunkArgs& a);
 hipError_t launch_chunk_fwd_split(const ChunkArgs& a);
 hipError_t launch_chunk_bwd(const BwdArgs& a);
 // pieces of the backward shared with the two-phase forward (gdn2_split.hip)
