@@ -88,6 +88,20 @@ __device__ __forceinline__ f4 mma16(bf16x4 a, bf16x4 b, f4 c) {
                                                    __builtin_bit_cast(short4v, b), c, 0, 0, 0);
 }
 
+// Element offset of (row r, phi-ordered column col) in a [64][DK] operand array. With d_k =
+// 128 the rows are 256 bytes (the LDS's 128 four-byte banks hold two of them) and the 16-byte
+// chunk index of a column is XORed with f(r) = 4 ((r >> 1) & 3) + 2 ((r >> 3) & 1). Both ways
+// the kernel reads these arrays then hit every bank once per 32-lane pass: 16-byte row
+// fragments (16 consecutive rows x two chunks; rows of one parity need distinct f >> 1) and
+// transposing reads (8 consecutive rows x four chunks of one 64-byte group; rows of one
+// parity among eight need distinct f >> 2). The 8-byte pieces and runs of 4 channels the
+// kernel addresses never straddle a chunk.
+template <int LDK, bool SWZ>
+__device__ __forceinline__ int kx(int r, int col) {
+  if constexpr (SWZ) return r * LDK + (col ^ ((4 * ((r >> 1) & 3) + 2 * ((r >> 3) & 1)) << 3));
+  else return r * LDK + col;
+}
+
 // Tile slots of the causal 16x16 pairs (R, I), I <= R: (0,0) (1,0) (1,1) (2,0) (2,1) (2,2)
 // (3,0) (3,1) (3,2) (3,3); and of the six strictly-lower pairs of A.
 __device__ __forceinline__ constexpr int pair_slot(int R, int I) { return R * (R + 1) / 2 + I; }
@@ -109,7 +123,10 @@ struct FwdShape {
   static constexpr int VTPT = 2;        // value side (waves 0-3): 2 tokens x 8 columns
   static constexpr int NCT = DK / 16;   // key-channel tiles
   static constexpr int KS = DK / 32;    // 32-wide K steps over the channels
-  static constexpr int LDK = DK + 8;    // pitches (elements) of the bf16 arrays
+  // [64][DK] operand arrays: with d_k = 128, unpadded rows whose 16-byte chunks are
+  // XOR-swizzled by the row (see kx); with d_k = 64, rows padded by 8 elements
+  static constexpr bool SWZ = DK == 128;
+  static constexpr int LDK = SWZ ? DK : DK + 8;  // pitches (elements) of the bf16 arrays
   static constexpr int LDZ = NV + 8;
   static constexpr int LDW = C + 8;
   static constexpr int LDTT = 24;       // column-major 16x16 T blocks
@@ -260,6 +277,7 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   using Sh = FwdShape<DK>;
   constexpr int C = Sh::C, CG = Sh::CG, TPT = Sh::TPT, NCT = Sh::NCT, KS = Sh::KS;
   constexpr int LDK = Sh::LDK, LDZ = Sh::LDZ, LDW = Sh::LDW, LDTT = Sh::LDTT, LDD = Sh::LDD;
+  auto KX = [](int r, int col) __attribute__((always_inline)) { return kx<Sh::LDK, Sh::SWZ>(r, col); };
   constexpr int NFAC = Sh::NFAC;
   constexpr bool b_scalar = (GL & kGateBScalar) != 0;
   constexpr bool w_scalar = (GL & kGateWScalar) != 0;
@@ -344,8 +362,8 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      bf16x8 a = *reinterpret_cast<const bf16x8*>(kg + (16 * I + m16) * LDK + 32 * s + 8 * g4);
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(X + (16 * R + m16) * LDK + 32 * s + 8 * g4);
+      bf16x8 a = *reinterpret_cast<const bf16x8*>(kg + KX(16 * I + m16, 32 * s + 8 * g4));
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(X + KX(16 * R + m16, 32 * s + 8 * g4));
       if (scale) {  // the fragment's channels: 32s + 4g4 + (0..3), 32s + 16 + 4g4 + (0..3)
         const f4 lo = *reinterpret_cast<const f4*>(fr + 32 * s + 4 * g4);
         const f4 hi = *reinterpret_cast<const f4*>(fr + 32 * s + 16 + 4 * g4);
@@ -386,7 +404,7 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
     for (int j = 0; j < CPT / 4; ++j) {
       const int ch = CPT * m + 4 * j;
-      const int o = r * LDK + Mma<bf16>::phi(ch);
+      const int o = KX(r, Mma<bf16>::phi(ch));
       f4 sx, sy;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -412,7 +430,7 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       f4 acc;
       if (key) {
         const int pcol = 32 * (ct >> 1) + 8 * (m16 & 3) + 4 * (ct & 1);  // phi of 16ct + 4(m16&3)
-        acc = from_bf4(ds_tr4(sEg + (16 * R + 4 * g4 + (m16 >> 2)) * LDK + pcol));
+        acc = from_bf4(ds_tr4(sEg + KX(16 * R + 4 * g4 + (m16 >> 2), pcol)));
       } else {
         acc = from_bf4(ds_tr4(sZ + (16 * R + 4 * g4 + (m16 >> 2)) * LDZ + 16 * ct + 4 * (m16 & 3)));
       }
@@ -501,14 +519,17 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       const int nvalid = nvalid_of(c);
       const bool more = c + 1 < nchunks;
       const bool gen = flag(p);
-      // ---- phase 1: A / P tiles
+      // ---- phase 1: one A / P tile, diagonal A tile w and its inverse block
       if (!gen) {
         switch (w) {
-          case 0: put_p(3, 3, tile(p, 3, 3, true, false)); put_p(3, 2, tile(p, 3, 2, true, false)); put_off_a(3, 2, tile(p, 3, 2, false, false)); break;
-          case 1: put_p(3, 1, tile(p, 3, 1, true, false)); put_p(3, 0, tile(p, 3, 0, true, false)); put_off_a(3, 1, tile(p, 3, 1, false, false)); break;
-          case 2: put_p(2, 2, tile(p, 2, 2, true, false)); put_p(2, 1, tile(p, 2, 1, true, false)); put_off_a(3, 0, tile(p, 3, 0, false, false)); break;
-          default: put_p(2, 0, tile(p, 2, 0, true, false)); put_off_a(2, 1, tile(p, 2, 1, false, false)); put_off_a(2, 0, tile(p, 2, 0, false, false)); break;
+          case 0: put_p(0, 0, tile(p, 0, 0, true, false)); break;
+          case 1: put_p(1, 1, tile(p, 1, 1, true, false)); break;
+          case 2: put_p(1, 0, tile(p, 1, 0, true, false)); break;
+          default: put_off_a(1, 0, tile(p, 1, 0, false, false)); break;
         }
+        put_diag_a(w, tile(p, w, w, false, false));
+        // reads only what this wave just wrote: no barrier needed
+        tinv_block<LDD, LDTT>(sAd + w * 16 * LDD, sT + w * 16 * LDTT, lane);
       } else {
         switch (w) {
           case 0: put_p(3, 2, tile(p, 3, 2, true, true)); put_off_a(3, 2, tile(p, 3, 2, false, true)); break;
@@ -518,7 +539,8 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         }
         diag_tiles_exact<DK, b_scalar>(qb, kb, gb, bb, bsb, kstride, H, c0, nvalid, tid, sAd, sP);
         lds_barrier();
-      fresh();
+        fresh();
+        tinv_block<LDD, LDTT>(sAd + w * 16 * LDD, sT + w * 16 * LDTT, lane);
         rescale(p);
       }
       lds_barrier();
@@ -562,7 +584,7 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           f4 Ot = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < KS; ++s)
-            Ot = mma32(Sb[s], *reinterpret_cast<const bf16x8*>(qg + (16 * R + m16) * LDK + 32 * s + 8 * g4), Ot);
+            Ot = mma32(Sb[s], *reinterpret_cast<const bf16x8*>(qg + KX(16 * R + m16, 32 * s + 8 * g4)), Ot);
 #pragma unroll
           for (int s2 = 0; 2 * s2 <= R; ++s2) {
             const bf16x4 p0 = *reinterpret_cast<const bf16x4*>(sP + pair_slot(R, 2 * s2) * 256 + lane * 4);
@@ -588,7 +610,8 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           f4 acc = gen ? S[mt] * gam : S[mt];
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2) {
-            const bf16* k0 = kg + (32 * s2 + 4 * g4 + (m16 >> 2)) * LDK + pcol;
+            // rows r and r + 16 share the swizzle
+            const bf16* k0 = kg + KX(32 * s2 + 4 * g4 + (m16 >> 2), pcol);
             acc = mma32(cat8(ds_tr4(k0), ds_tr4(k0 + 16 * LDK)), Ub32[s2], acc);
           }
           S[mt] = gen ? acc : acc * gam;
@@ -703,7 +726,7 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
       for (int j = 0; j < TPT; ++j) {
         const int r = tg * TPT + j;
-        if (r >= nv) { rq[j].zero(); rk[j].zero(); rb[j].zero(); }
+        if (nv < C && r >= nv) { rq[j].zero(); rk[j].zero(); rb[j].zero(); }
         if constexpr (b_scalar) rb[j].splat();
         float fg[8];
         gk[j].to_float(fg);
@@ -717,7 +740,9 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int ci = 4 * hf + i;
-            run[ci] += fmaxf(fg[ci] * kLog2e, kMinTokenDecay2);
+            // (on the fast path no token's decay reaches the clamp: the chunk's total is
+            // within kFwdFastDecay2)
+            run[ci] = GEN ? run[ci] + fmaxf(fg[ci] * kLog2e, kMinTokenDecay2) : fmaf(fg[ci], kLog2e, run[ci]);
             const float G = run[ci];
             const float xe = fast_exp2(GEN ? G - ox[ci] : G);
             const float ye = fast_exp2(GEN ? oy[ci] - G : -G);
@@ -726,7 +751,7 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
             q1[i] = fq * xe;
             k1[i] = fk * ye;
           }
-          const int o = r * LDK + Mma<bf16>::phi(cg * 8) + 8 * hf;
+          const int o = KX(r, Mma<bf16>::phi(cg * 8) + 8 * hf);
           *reinterpret_cast<bf16x4*>(sEg + o) = to_bf4(e1);
           *reinterpret_cast<bf16x4*>(qg + o) = to_bf4(q1);
           *reinterpret_cast<bf16x4*>(kg + o) = to_bf4(k1);
@@ -762,17 +787,14 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       const bool more = c + 1 < nchunks;
       const bool gen = flag(p);
       const int R4 = wave - 4;
-      // ---- phase 1: one A / P tile, a diagonal A tile and its inverse block; next totals
+      // ---- phase 1: three A / P tiles; next totals
       if (!gen) {
         switch (R4) {
-          case 0: put_p(1, 1, tile(p, 1, 1, true, false)); break;
-          case 1: put_p(1, 0, tile(p, 1, 0, true, false)); break;
-          case 2: put_p(0, 0, tile(p, 0, 0, true, false)); break;
-          default: put_off_a(1, 0, tile(p, 1, 0, false, false)); break;
+          case 0: put_p(3, 3, tile(p, 3, 3, true, false)); put_p(3, 2, tile(p, 3, 2, true, false)); put_off_a(3, 2, tile(p, 3, 2, false, false)); break;
+          case 1: put_p(3, 1, tile(p, 3, 1, true, false)); put_p(3, 0, tile(p, 3, 0, true, false)); put_off_a(3, 1, tile(p, 3, 1, false, false)); break;
+          case 2: put_p(2, 2, tile(p, 2, 2, true, false)); put_p(2, 1, tile(p, 2, 1, true, false)); put_off_a(3, 0, tile(p, 3, 0, false, false)); break;
+          default: put_p(2, 0, tile(p, 2, 0, true, false)); put_off_a(2, 1, tile(p, 2, 1, false, false)); put_off_a(2, 0, tile(p, 2, 0, false, false)); break;
         }
-        put_diag_a(R4, tile(p, R4, R4, false, false));
-        // reads only what this wave just wrote: no barrier needed
-        tinv_block<LDD, LDTT>(sAd + R4 * 16 * LDD, sT + R4 * 16 * LDTT, lane);
       } else {
         switch (R4) {
           case 0: put_p(2, 0, tile(p, 2, 0, true, true)); put_off_a(2, 0, tile(p, 2, 0, false, true)); break;
@@ -781,8 +803,7 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         }
         diag_tiles_exact<DK, b_scalar>(qb, kb, gb, bb, bsb, kstride, H, c0, nvalid, tid, sAd, sP);
         lds_barrier();
-      fresh();
-        tinv_block<LDD, LDTT>(sAd + R4 * 16 * LDD, sT + R4 * 16 * LDTT, lane);
+        fresh();
         rescale(p);
       }
       if (more) {
