@@ -331,7 +331,7 @@ def chunk_bwd(q, k, v, g, b, w, do, initial_state=None, d_final_state=None, cu_s
         raise Gdn2Error(fn, st)
     if check_range and int(flag.item()) != 0:
         raise Gdn2RangeError("a chunk's total decay exceeds the backward's range "
-                             "(about 83 nats over 64 tokens in some key channel)")
+                             "(about 166 nats over 64 tokens in some key channel)")
     return (*grads, ds0)
 
 

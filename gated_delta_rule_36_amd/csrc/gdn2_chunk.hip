@@ -78,7 +78,7 @@ struct ChunkShape {
   static constexpr int SZ_K = C * LDK * (int)sizeof(T);
   static constexpr int OFF_E = 0;                  // E exp(G) (or Ea); later -W
   static constexpr int OFF_Q = OFF_E + SZ_K;       // Q exp(G) (or Qa, rescaled in (e))
-  static constexpr int OFF_K = OFF_Q + SZ_K;       // K exp(-G) (or Kn)
+  static constexpr int OFF_K = OFF_Q + SZ_K;       // K exp(-G) (or K exp(Ge(block) - G))
   static constexpr int SZ_T = DK * LDT * (int)sizeof(T);
   static constexpr int OFF_ET = OFF_K + SZ_K;      // (E exp(G))^T        [DK][64]
   static constexpr int OFF_KT = OFF_ET + SZ_T;     // (K exp(Gl - G))^T   [DK][64]
@@ -341,8 +341,10 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
 #pragma unroll
       for (int i = 0; i < 8; ++i) run[i] = sTot[tg * DK + cg * 8 + i];
       RunBuf<T, Sh::TPT> ev[8], kv[8];  // E exp(G) and K exp(Glast - G), per channel
-      // one token of this thread: x = G (chunk path) or G - Gs(block) (block path)
-      auto token = [&](int j, const float* sub, const float* fA, const float* fB, bool scaled) {
+      // one token of this thread: x = G (chunk path) or G - Gs(block) (block path, where K
+      // takes Ge(block) - G)
+      auto token = [&](int j, const float* sub, const float* subk, const float* fA,
+                       const float* fB, bool scaled) {
         const int r = tg * Sh::TPT + j;
         float fg[8], fq[8], fk[8], fb[8], e1[8], q1[8], k1[8];
         rg[j].to_float(fg);
@@ -354,7 +356,7 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
         for (int i = 0; i < 8; ++i) {
           run[i] += fg[i] * kLog2e;
           const float x = scaled ? run[i] - sub[i] : run[i];
-          const float xe = fast_exp2(x), xk = fast_exp2(-x);
+          const float xe = fast_exp2(x), xk = fast_exp2(scaled ? subk[i] - run[i] : -run[i]);
           e1[i] = fb[i] * fk[i] * xe;
           q1[i] = fq[i] * xe;
           k1[i] = fk[i] * xk;
@@ -370,17 +372,19 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
 #pragma unroll
         for (int i = 0; i < 8; ++i) gam[i] = sFac[Fac::GAM * DK + cg * 8 + i];
 #pragma unroll
-        for (int j = 0; j < Sh::TPT; ++j) token(j, nullptr, nullptr, gam, false);
+        for (int j = 0; j < Sh::TPT; ++j) token(j, nullptr, nullptr, nullptr, gam, false);
       } else {
-        float fA[8], fB[8], sub[8];
+        // E, Q times 2^(G - Gs(block)); K times 2^(Ge(block) - G); every factor <= 1
+        float fA[8], fB[8], sub[8], subk[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           fA[i] = sFac[(Fac::ES + blk) * DK + cg * 8 + i];
-          fB[i] = sFac[(Fac::KNB + blk) * DK + cg * 8 + i];
+          fB[i] = sFac[(Fac::KE + blk) * DK + cg * 8 + i];
           sub[i] = sFac[(Fac::GS + blk) * DK + cg * 8 + i];
+          subk[i] = sFac[(Fac::GS + blk + 1) * DK + cg * 8 + i];
         }
 #pragma unroll
-        for (int j = 0; j < Sh::TPT; ++j) token(j, sub, fA, fB, true);
+        for (int j = 0; j < Sh::TPT; ++j) token(j, sub, subk, fA, fB, true);
       }
       const int sw = tswz(cg * 8);  // same for the thread's 8 channels
 #pragma unroll
@@ -481,7 +485,10 @@ gdn2_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
         o_partial();
       }
     } else {
-      ap_tiles_block<T, DK, LDK, LDT, ADB, ADP, NW>(sE, sQ, sK, sAm, sP, sAd, sFac, wave, lane);
+      ap_tiles_block<T, DK, LDK, LDT, NW>(sE, sQ, sK, sAm, sP, sFac, wave, lane);
+      diag_tiles_pairwise<T, DK, LDT, ADB, ADP, NT, b_scalar>(
+          qb + (long)c0 * kstride, kb + (long)c0 * kstride, gb + (long)c0 * kstride,
+          bb + (long)c0 * kstride, bsb + (long)c0 * H, kstride, H, nvalid, tid, sAd, sP);
     }
     zero_p_upper<T, LDT, NT>(sP, tid);
     lds_barrier();

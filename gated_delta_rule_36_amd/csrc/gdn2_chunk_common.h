@@ -17,14 +17,14 @@ namespace gdn2 {
 // by the block-referenced path.
 struct Fac {
   static constexpr int ES = 0;    // 2^Gs(R)                R = 0..3
-  static constexpr int KB = 4;    // 2^(Ge(R) - Gs(R))      R = 0..3
-  static constexpr int KNB = 8;   // 2^(Glast - Gs(R))      R = 0..3
-  static constexpr int GAM = 12;  // 2^Glast: the chunk's decay of the state
-  static constexpr int OFF = 13;  // 2^(Gs(R) - Ge(I)) for (R, I) = (2,0), (3,0), (3,1)
-  static constexpr int GS = 16;   // Gs(R)                  R = 0..3
-  static constexpr int GL = 20;   // Glast
-  static constexpr int N = 21;
+  static constexpr int KE = 4;    // 2^(Glast - Ge(R))      R = 0..3
+  static constexpr int GAM = 8;   // 2^Glast: the chunk's decay of the state
+  static constexpr int OFF = 9;   // 2^(Gs(R) - Ge(I)) for (R, I) = (2,0), (3,0), (3,1)
+  static constexpr int GS = 12;   // Gs(R)                  R = 0..3
+  static constexpr int GL = 16;   // Glast (= Ge(3): row GS + R + 1 holds Ge(R) for every R)
+  static constexpr int N = 17;
 };
+static_assert(Fac::GL == Fac::GS + 4, "Ge(R) is read as row GS + R + 1");
 
 // Threshold on a chunk's total log2-decay above which the block-referenced path runs:
 // 120 log2 units = 83 nats, so exp(-G) <= 1.3e36 stays finite in fp32 and bf16.
@@ -172,8 +172,7 @@ __device__ __forceinline__ void channel_scan(float* sTot, float* sFac, int* sFla
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
       sFac[(Fac::ES + R) * DK + ch] = fast_exp2(gs[R]);
-      sFac[(Fac::KB + R) * DK + ch] = fast_exp2(ge[R] - gs[R]);
-      sFac[(Fac::KNB + R) * DK + ch] = fast_exp2(gn - gs[R]);
+      sFac[(Fac::KE + R) * DK + ch] = fast_exp2(gn - ge[R]);
       sFac[(Fac::GS + R) * DK + ch] = gs[R];
     }
     sFac[Fac::GAM * DK + ch] = fast_exp2(gn);
@@ -229,19 +228,21 @@ __device__ __forceinline__ void diag_inverse_pair(const float* sAd, T* sT, int m
   diag_inverse_block<T, LDT, ADB, ADP>(sAd, sT, jb0 + (g4 & 1), m16, g4 < 2);
 }
 
-// Block-referenced A and P tiles (chunks whose total decay is too large for the chunk-
-// referenced factors): rows of block R against Kn of block I; off-diagonal tiles scale Kn
-// by 2^(Ge(I)-Gs(I)) and, two or more blocks apart, the left operand by 2^(Gs(R)-Ge(I)).
-// The 20 tiles are dealt round-robin to the NW waves.
-template <typename T, int DK, int LDK, int LDT, int ADB, int ADP, int NW>
+// Block-referenced off-diagonal A and P tiles (chunks whose total decay is too large for
+// the chunk-referenced factors): rows of block R (E or Q times 2^(G - Gs(R)), each factor
+// <= 1) against the rows of block I (K times 2^(Ge(I) - G), <= 1); two or more blocks apart
+// the left operand is also scaled by 2^(Gs(R) - Ge(I)) <= 1, so no factor can overflow. The
+// 12 tiles are dealt round-robin to the NW waves; the diagonal tiles come from
+// diag_tiles_pairwise.
+template <typename T, int DK, int LDK, int LDT, int NW>
 __device__ __forceinline__ void ap_tiles_block(const T* sE, const T* sQ, const T* sK, T* sAm,
-                                               T* sP, float* sAd, const float* sFac, int wave,
-                                               int lane) {
+                                               T* sP, const float* sFac, int wave, int lane) {
   using M = Mma<T>;
   constexpr int KS = M::KS, KPL = M::KPL;
+  constexpr int kOffPairs[6] = {1, 3, 4, 6, 7, 8};  // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
   const int m16 = lane & 15, g4 = lane >> 4;
-  for (int job = wave; job < 20; job += NW) {
-    const int pair = job >> 1;
+  for (int job = wave; job < 12; job += NW) {
+    const int pair = kOffPairs[job >> 1];
     const bool isP = job & 1;
     const int R = pair_R(pair), I = pair_I(pair);
     const T* lhs = isP ? sQ : sE;
@@ -249,29 +250,100 @@ __device__ __forceinline__ void ap_tiles_block(const T* sE, const T* sQ, const T
     f4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < DK / KS; ++s) {
       const int kk = s * KS + KPL * g4;  // physical (phi-ordered) K position
-      float fa[KPL], fb[KPL];
+      typename M::frag a;
+      if (off >= 0) {
+        float fa[KPL];
 #pragma unroll
-      for (int i = 0; i < KPL; ++i) {
-        const int ch = M::phi_inv(kk + i);  // logical key channel of that position
-        fa[i] = off >= 0 ? sFac[(Fac::OFF + off) * DK + ch] : 1.f;
-        fb[i] = I != R ? sFac[(Fac::KB + I) * DK + ch] : 1.f;
+        for (int i = 0; i < KPL; ++i) fa[i] = sFac[(Fac::OFF + off) * DK + M::phi_inv(kk + i)];
+        a = M::load_scaled(lhs, LDK, 16 * R + m16, kk, fa);
+      } else {
+        a = M::load(lhs, LDK, 16 * R + m16, kk);
       }
-      const typename M::frag a = M::load_scaled(lhs, LDK, 16 * R + m16, kk, fa);
-      const typename M::frag b = M::load_scaled(sK, LDK, 16 * I + m16, kk, fb);
-      acc = M::mma(a, b, acc);
-    }
-    f4 val;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * g4 + i, c = m16;
-      const bool keep = (I < R) || (isP ? (c <= r) : (c < r));
-      val[i] = keep ? (isP ? acc[i] : -acc[i]) : 0.f;
-      if (!isP && sizeof(T) == 2 && I == R) sAd[R * ADB + r * ADP + c] = val[i];
+      acc = M::mma(a, M::load(sK, LDK, 16 * I + m16, kk), acc);
     }
     if (isP)
-      store_tile_pairs(sP + (16 * R) * LDT, LDT, lane, val, [&](int c) { return M::phi(16 * I + c); });
+      store_tile_pairs(sP + (16 * R) * LDT, LDT, lane, acc, [&](int c) { return M::phi(16 * I + c); });
     else
-      store_tile_pairs(sAm + (16 * R) * LDT + 16 * I, LDT, lane, val, [](int c) { return c; });
+      store_tile_pairs(sAm + (16 * R) * LDT + 16 * I, LDT, lane, -acc, [](int c) { return c; });
+  }
+}
+
+// The diagonal 16x16 tiles of A (negated, fp32: block R, row r, column i at
+// sAd[R * ADB + r * ADP + i], zero for i >= r) and of P (sP, phi-ordered columns, zero above
+// the diagonal), computed from the raw inputs of the chunk with the exact pairwise decay
+// 2^(G[r] - G[i]) = prod_{i < j <= r} alpha_j (a running product, each factor <= 1), so any
+// decay in (0, 1] is represented. Rows (R, r) x 8-channel groups are dealt to the NT
+// threads; the NCG = d_k / 8 lanes of one row are adjacent and reduce by lane exchange.
+// qb, kb, gb, bb: the chunk's first token of this head ([tokens][kstride] rows); bsb the
+// scalar b of that token (BS: one b per token and head, H apart).
+template <typename T, int DK, int LDT, int ADB, int ADP, int NT, bool BS>
+__device__ __forceinline__ void diag_tiles_pairwise(const T* qb, const T* kb, const T* gb,
+                                                    const T* bb, const T* bsb, long kstride,
+                                                    int H, int nvalid, int tid, float* sAd,
+                                                    T* sP) {
+  constexpr int NCG = DK / 8;
+  static_assert(64 % NCG == 0 && NT % 64 == 0, "a row's channel groups share one wave");
+  for (int idx = tid; idx < 64 * NCG; idx += NT) {
+    const int cq = idx % NCG, item = idx / NCG;
+    const int R = item >> 4, r = item & 15, tr = 16 * R + r;
+    float er[8], qr[8], f[8];
+    {
+      Vec8<T> vq, vk, vb;
+      if (tr < nvalid) {
+        const long off = (long)tr * kstride + cq * 8;
+        vq.load(qb + off);
+        vk.load(kb + off);
+        if constexpr (BS) { vb.load_one(bsb + (long)tr * H); vb.splat(); }
+        else vb.load(bb + off);
+      } else {
+        vq.zero(); vk.zero(); vb.zero();
+      }
+      float fk[8], fb[8];
+      vq.to_float(qr); vk.to_float(fk); vb.to_float(fb);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) { er[c] = fb[c] * fk[c]; f[c] = 1.f; }
+    }
+    float* arow = sAd + R * ADB + r * ADP;
+    T* prow = sP + tr * LDT;
+    for (int i = r; i >= 0; --i) {
+      const int ti = 16 * R + i;
+      float ki[8], gi[8];
+      {
+        Vec8<T> vk, vg;
+        if (ti < nvalid) {
+          const long off = (long)ti * kstride + cq * 8;
+          vk.load(kb + off);
+          vg.load(gb + off);
+        } else {
+          vk.zero(); vg.zero();
+        }
+        vk.to_float(ki);
+        vg.to_float(gi);
+      }
+      float a = 0.f, p = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float kf = ki[c] * f[c];
+        a += er[c] * kf;
+        p += qr[c] * kf;
+        f[c] *= fast_exp2(gi[c] * kLog2e);  // alpha_i: the product now spans tokens i..r
+      }
+#pragma unroll
+      for (int m = 1; m < NCG; m <<= 1) {
+        a += __shfl_xor(a, m, 64);
+        p += __shfl_xor(p, m, 64);
+      }
+      if (cq == 0) {
+        arow[i] = i < r ? -a : 0.f;
+        prow[Mma<T>::phi(16 * R + i)] = from_f<T>(p);
+      }
+    }
+    if (cq == 0) {
+      for (int i = r + 1; i < 16; ++i) {
+        arow[i] = 0.f;
+        prow[Mma<T>::phi(16 * R + i)] = from_f<T>(0.f);
+      }
+    }
   }
 }
 

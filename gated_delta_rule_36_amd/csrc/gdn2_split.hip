@@ -48,7 +48,7 @@ struct PrepShape {
   static constexpr int SZ_K = C * LDK * 2;
   static constexpr int OFF_E = 0;                  // E 2^G (or Ea); later -W
   static constexpr int OFF_Q = OFF_E + SZ_K;       // Q 2^G (or Qa, rescaled)
-  static constexpr int OFF_K = OFF_Q + SZ_K;       // K 2^-G (or Kn)
+  static constexpr int OFF_K = OFF_Q + SZ_K;       // K 2^-G (or K 2^(Ge(block) - G))
   static constexpr int SZ_T = DK * LDT * 2;
   static constexpr int OFF_ET = OFF_K + SZ_K;      // (E 2^G)^T          [DK][64]
   static constexpr int OFF_KT = OFF_ET + SZ_T;     // (K 2^(Gl - G))^T   [DK][64]
@@ -249,7 +249,8 @@ gdn2_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
       for (int i = 0; i < 8; ++i) run[i] = sTot[tg * DK + cg * 8 + i];
       RunBuf<T, Sh::TPT> ev[8], kv[8];  // E 2^G and K 2^(Glast - G), per channel
-      auto token = [&](int j, const float* sub, const float* fA, const float* fB, bool scaled) {
+      auto token = [&](int j, const float* sub, const float* subk, const float* fA,
+                       const float* fB, bool scaled) {
         const int r = tg * Sh::TPT + j;
         float fg[8], fq[8], fk[8], fb[8], e1[8], q1[8], k1[8];
         rg[j].to_float(fg);
@@ -261,7 +262,7 @@ gdn2_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         for (int i = 0; i < 8; ++i) {
           run[i] += fg[i] * kLog2e;
           const float x = scaled ? run[i] - sub[i] : run[i];
-          const float xe = fast_exp2(x), xk = fast_exp2(-x);
+          const float xe = fast_exp2(x), xk = fast_exp2(scaled ? subk[i] - run[i] : -run[i]);
           e1[i] = fb[i] * fk[i] * xe;
           q1[i] = fq[i] * xe;
           k1[i] = fk[i] * xk;
@@ -277,17 +278,19 @@ gdn2_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
         for (int i = 0; i < 8; ++i) gam[i] = sFac[Fac::GAM * DK + cg * 8 + i];
 #pragma unroll
-        for (int j = 0; j < Sh::TPT; ++j) token(j, nullptr, nullptr, gam, false);
+        for (int j = 0; j < Sh::TPT; ++j) token(j, nullptr, nullptr, nullptr, gam, false);
       } else {
-        float fA[8], fB[8], sub[8];
+        // E, Q times 2^(G - Gs(block)); K times 2^(Ge(block) - G); every factor <= 1
+        float fA[8], fB[8], sub[8], subk[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           fA[i] = sFac[(Fac::ES + blk) * DK + cg * 8 + i];
-          fB[i] = sFac[(Fac::KNB + blk) * DK + cg * 8 + i];
+          fB[i] = sFac[(Fac::KE + blk) * DK + cg * 8 + i];
           sub[i] = sFac[(Fac::GS + blk) * DK + cg * 8 + i];
+          subk[i] = sFac[(Fac::GS + blk + 1) * DK + cg * 8 + i];
         }
 #pragma unroll
-        for (int j = 0; j < Sh::TPT; ++j) token(j, sub, fA, fB, true);
+        for (int j = 0; j < Sh::TPT; ++j) token(j, sub, subk, fA, fB, true);
       }
       const int sw = tswz(cg * 8);
 #pragma unroll
@@ -335,7 +338,11 @@ gdn2_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           break;
       }
     } else {
-      ap_tiles_block<T, DK, LDK, LDT, ADB, ADP, NW>(sE, sQ, sK, sAm, sP, sAd, sFac, wave, lane);
+      ap_tiles_block<T, DK, LDK, LDT, NW>(sE, sQ, sK, sAm, sP, sFac, wave, lane);
+      const long base = cur.row * kstride + (long)cur.h * DK;
+      diag_tiles_pairwise<T, DK, LDT, ADB, ADP, NT, (GL & kGateBScalar) != 0>(
+          q + base, k + base, g + base, bg + base, bg + cur.row * H + cur.h, kstride, H,
+          cur.nvalid, tid, sAd, sP);
     }
     zero_p_upper<T, LDT, NT>(sP, tid);
     lds_barrier();

@@ -26,9 +26,10 @@
  *     launched and an error status is returned. Gate VALUES are not checked: b and w
  *     outside [0, 1] are computed as given.
  *   - Device faults surface at the caller's next synchronisation.
- *   - Numeric range of the chunked forward: the per-channel decay accumulated over any
- *     aligned 16-token block of a chunk must stay above -80 (log space), i.e. alpha
- *     averaged over 16 tokens >= exp(-5). The decode step has no such limit.
+ *   - Numeric range: every forward entry point (chunked, training, decode) accepts any
+ *     log_alpha <= 0, i.e. alpha anywhere in (0, 1], however strong the decay of a chunk
+ *     or of a 16-token block; alpha below fp32 range acts as 0 (a full reset). The
+ *     chunked backward has a limit of its own (see gdn2_chunk_bwd).
  */
 #ifndef GDN2_H_
 #define GDN2_H_

@@ -103,6 +103,17 @@ def test_bwd_wide_decay_chunk(nats):
     check(x, do, dsn)
 
 
+def test_bwd_decay_concentrated_in_one_block():
+    """100 nats over one chunk with 90 of them inside one aligned 16-token block: past any
+    per-block referencing of the forward factors, inside the backward's per-chunk range."""
+    x = make_inputs(1, 200, 2, 128, 128, "bf16", seed=317, s0_std=0.02)
+    x["g"][:, 64:128] = float(round_to_bf16(np.array([-10.0 / 48], np.float32))[0])
+    x["g"][:, 80:96] = float(round_to_bf16(np.array([-90.0 / 16], np.float32))[0])
+    do, dsn = _upstream(x, 14)
+    say("bwd decay concentrated in one block")
+    check(x, do, dsn)
+
+
 def test_bwd_near_resets():
     """Near-resets as in the long-context workload (10% of tokens at log-decay -5) plus one
     chunk with 18 of them (about 95 nats): inside the backward's range."""

@@ -1,10 +1,14 @@
-"""GPU parity of the pipelined fused forward (gdn2_chunk_fwd without a workspace, bf16)
-against the float64 oracle: every width pair on ragged lengths with an initial state, long
-sequences (many chunks through the double-buffered pipeline), and the whole decay domain
-that alpha in (0, 1] allows (reading note §1 gate domains, §2 Diag(alpha_t)): strong decay
-on every token of one chunk, on one aligned 16-token block, on every token of a sequence,
-single near-total resets, and decays far below fp32 range (alpha that underflows).
-Tolerance: normwise max relative error 2e-2 on o and on the final state."""
+"""GPU parity of the chunk forwards against the float64 oracle over the whole decay domain
+that alpha in (0, 1] allows (reading note §1 gate domains, §2 Diag(alpha_t)).
+
+The pipelined fused forward (gdn2_chunk_fwd without a workspace, bf16): every width pair
+on ragged lengths with an initial state, long sequences (many chunks through the double-
+buffered pipeline), and strong decay on every token of one chunk, on one aligned 16-token
+block, on every token of a sequence, single near-total resets, and decays far below fp32
+range (alpha that underflows). The same decay cases also run through every other forward:
+the two-phase path (with a workspace), the training forward, the value-sliced fused kernel
+and its fp32 build.
+Tolerance: normwise max relative error 2e-2 on o and on the final state (1e-4 in fp32)."""
 import numpy as np
 import pytest
 import torch
@@ -24,6 +28,8 @@ def _need_gpu():
 
 
 def _run(x, path="fused", scalar_b=None, scalar_w=None):
+    """path: "fused" or "split" (chunk_fwd), "train" (chunk_fwd_train) or "sliced"
+    (chunk_fwd with 32-wide value slices)."""
     import gated_delta_rule_36_amd as G
     t = {n: dev_tensor(x[n], x["dtype"]) for n in NAMES}
     if scalar_b is not None:
@@ -32,7 +38,13 @@ def _run(x, path="fused", scalar_b=None, scalar_w=None):
         t["w"] = dev_tensor(scalar_w, x["dtype"])
     s0 = None if x["s0"] is None else torch.from_numpy(np.ascontiguousarray(x["s0"])).cuda()
     cu = None if x["cu_seqlens"] is None else torch.from_numpy(x["cu_seqlens"]).cuda()
-    o, sN = G.chunk_fwd(*(t[n] for n in NAMES), initial_state=s0, cu_seqlens=cu, path=path)
+    args = [t[n] for n in NAMES]
+    if path == "train":
+        o, sN, _ = G.chunk_fwd_train(*args, initial_state=s0, cu_seqlens=cu)
+    elif path == "sliced":
+        o, sN = G.chunk_fwd(*args, initial_state=s0, cu_seqlens=cu, path="fused", value_slice=32)
+    else:
+        o, sN = G.chunk_fwd(*args, initial_state=s0, cu_seqlens=cu, path=path)
     torch.cuda.synchronize()
     return host64(o), host64(sN)
 
@@ -45,8 +57,8 @@ def _check(x, path="fused", scalar_b=None, scalar_w=None):
     if scalar_w is not None:
         xr["w"] = np.repeat(scalar_w[..., None], x["v"].shape[-1], axis=-1)
     o_ref, s_ref = gdn2_forward(*(xr[n] for n in NAMES), s0=x["s0"], cu_seqlens=x["cu_seqlens"])
-    assert_close("o", o, o_ref, TOL["bf16"])
-    assert_close("S", sN, s_ref, TOL["bf16"])
+    assert_close("o", o, o_ref, TOL[x["dtype"]])
+    assert_close("S", sN, s_ref, TOL[x["dtype"]])
 
 
 @pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
@@ -100,3 +112,33 @@ def test_decay_range_varlen_and_scalar_gates():
     _check(x)
     _check(x, scalar_b=sb)
     _check(x, scalar_b=sb, scalar_w=sw)
+
+
+@pytest.mark.parametrize("case", list(RANGE_CASES))
+@pytest.mark.parametrize("dk", [64, 128])
+@pytest.mark.parametrize("path", ["split", "train", "sliced"])
+def test_decay_range_other_paths(path, case, dk):
+    tokens, gn = RANGE_CASES[case]
+    x = _with_decay(make_inputs(2, 300, 2, dk, 128, "bf16", seed=313 + dk, s0_std=0.05),
+                    tokens, gn)
+    say("fwd range", path, case, "dk", dk)
+    _check(x, path)
+
+
+@pytest.mark.parametrize("case", list(RANGE_CASES))
+def test_decay_range_fp32(case):
+    tokens, gn = RANGE_CASES[case]
+    x = _with_decay(make_inputs(2, 300, 2, 64, 64, "fp32", seed=323, s0_std=0.05), tokens, gn)
+    say("fwd range fp32", case)
+    _check(x)
+
+
+@pytest.mark.parametrize("path", ["split", "train"])
+def test_decay_range_other_paths_varlen_scalar_gates(path):
+    lens = [70, 1, 130, 0, 99]
+    x = make_inputs(1, sum(lens), 2, 128, 64, "bf16", seed=414, lengths=lens, s0_std=0.05)
+    x = _with_decay(x, slice(16, 48), -9.0)
+    x = _with_decay(x, slice(100, 140), -7.0)
+    sb = make_scalar_gate(x["q"].shape[:3], seed=414)
+    say("fwd range varlen + scalar b", path)
+    _check(x, path, scalar_b=sb)
