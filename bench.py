@@ -32,21 +32,28 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 NAMES = ("q", "k", "v", "g", "b", "w")
 
 
-def measured_traffic(key):
-    """HBM bytes per call from the committed rocprofv3 counter summary (summed over the
-    call's kernels), or None when a kernel's sources changed since the counters were taken
-    (digest mismatch) or no record exists."""
+def measured_record(key):
+    """The committed rocprofv3 counter record of a workload (profiles/counters.json), or None
+    when a kernel's sources changed since the counters were taken (digest mismatch) or no
+    record exists."""
     import hashlib
     try:
         with open(os.path.join(ROOT, "profiles", "counters.json")) as f:
             rec = json.load(f)[key]
-    except (OSError, KeyError, ValueError):
+    except (OSError, KeyError, ValueError, TypeError):
         return None
     h = hashlib.sha256()
     for name in rec["sources"]:
         with open(os.path.join(ROOT, "gated_delta_rule_36_amd", "csrc", name), "rb") as f:
             h.update(f.read())
-    return rec["traffic_bytes"] if h.hexdigest() == rec["source_sha256"] else None
+    return rec if h.hexdigest() == rec["source_sha256"] else None
+
+
+def measured_traffic(key):
+    """HBM bytes per call from the committed counter record (summed over the call's
+    kernels), or None (see measured_record)."""
+    rec = measured_record(key)
+    return None if rec is None else rec["traffic_bytes"]
 
 
 def fwd_bytes(B, T, H, dk, dv, N, elt=2, read_s0=False):
@@ -264,8 +271,11 @@ def main():
                   "(the launches of one call; a sequence cut into segments adds the "
                   "transfer pass and the combine kernel between them)")
         tkey = f"chunk_fwd_split_{cfg}"
+    elif args.value_slice:
+        kernel = f"gdn2_chunk_kernel<bf16,{dk},{args.value_slice},0>"
+        tkey = None
     else:
-        kernel = f"gdn2_chunk_kernel<bf16,{dk},NV>"
+        kernel = f"gdn2_fwd_kernel<{dk},0>"
         tkey = f"chunk_fwd_{cfg}"
     workloads = {
         "layer1p3b": "GDN-2 chunk forward, 1.3B-layer shape: B=8 H=16 T=2048 d_k=d_v=128 "
@@ -295,6 +305,12 @@ def main():
                  "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
                  "frac": round(flops / (kern_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
     }
+    rec = measured_record(tkey)
+    if rec is not None and "derived" in rec:
+        # rocprofv3 counters of the same kernel (profiles/): SQ_VALU_MFMA_BUSY_CYCLES over
+        # the GRBM active cycles of the 1024 SIMDs, and the MFMA work the hardware executed
+        out["mfma"]["counter_busy_frac"] = round(rec["derived"]["mfma_busy_frac"], 4)
+        out["mfma"]["counter_executed_flops_per_launch"] = rec["derived"]["mfma_bf16_flops_executed"]
 
     if not args.no_backward:
         rng = np.random.default_rng(7)

@@ -29,35 +29,36 @@ def run_steps(x, steps, state):
     return torch.stack(outs)
 
 
-def test_decode_1000_steps_subset():
-    """1000 consecutive steps of the decode workload's recurrence (bf16 inputs, fp32 state),
-    on a subset of 8 sequences x 16 heads that the oracle runs in seconds."""
+def test_decode_1000_steps_16x16():
+    """1000 consecutive steps of the decode workload's recurrence (bf16 inputs, fp32 state)
+    on 16 sequences x 16 heads; every state and output against the oracle."""
+    from tests.oracle_pool import decode_errors
     c = CONFIGS["decode_bf16"]
     steps = c["steps"]
-    x = make_decode_inputs(8, c["H"], c["dk"], c["dv"], steps, "bf16", seed=c["seed"],
+    x = make_decode_inputs(16, c["H"], c["dk"], c["dv"], steps, "bf16", seed=c["seed"],
                            s0_std=0.02)
-    say("decode 1000 steps N8 H16 d128 bf16")
+    say("decode 1000 steps N16 H16 d128 bf16")
     state = torch.from_numpy(x["s0"]).cuda()
     o = run_steps(x, steps, state)
-    o_ref, s_ref = gdn2_decode_steps(x["s0"], *(x[n] for n in NAMES))
-    assert_close("o", host64(o), o_ref, TOL["bf16"])
-    assert_close("S", host64(state), s_ref, TOL["bf16"])
+    e = decode_errors(x["s0"], x, host64(o), host64(state), seqs_per_shard=1)
+    print(f"  all states: o {e['o']:.3e}  S {e['S']:.3e}", flush=True)
+    assert e["o"] <= TOL["bf16"] and e["S"] <= TOL["bf16"], e
 
 
-def test_decode_full_batch_sampled():
-    """The decode workload's full batch (256 sequences x 16 heads), a few steps, with
-    sampled (sequence, head) pairs checked against the oracle."""
+def test_decode_full_batch_all_states():
+    """The decode workload's full batch (256 sequences x 16 heads) over 12 steps; every one
+    of the 4096 states and every output against the oracle."""
+    from tests.oracle_pool import decode_errors
     c = CONFIGS["decode_bf16"]
-    x = make_decode_inputs(c["N"], c["H"], c["dk"], c["dv"], 3, "bf16", seed=c["seed"] + 7,
+    x = make_decode_inputs(c["N"], c["H"], c["dk"], c["dv"], 12, "bf16", seed=c["seed"] + 7,
                            s0_std=0.02)
-    say("decode full batch N256 H16, 3 steps")
+    say("decode full batch N256 H16, 12 steps")
     state = torch.from_numpy(x["s0"]).cuda()
-    o = run_steps(x, 3, state)
-    for (n, h) in [(0, 0), (100, 5), (255, 15)]:
-        sel = {m: x[m][:, n:n + 1, h:h + 1] for m in NAMES}
-        o_ref, s_ref = gdn2_decode_steps(x["s0"][n:n + 1, h:h + 1], *(sel[m] for m in NAMES))
-        assert_close(f"o[{n},{h}]", host64(o[:, n:n + 1, h:h + 1]), o_ref, TOL["bf16"])
-        assert_close(f"S[{n},{h}]", host64(state[n:n + 1, h:h + 1]), s_ref, TOL["bf16"])
+    o = run_steps(x, 12, state)
+    e = decode_errors(x["s0"], x, host64(o), host64(state), seqs_per_shard=8)
+    print(f"  all 4096 states: o {e['o']:.3e}  S {e['S']:.3e}", flush=True)
+    assert np.all(np.isfinite(host64(state)))
+    assert e["o"] <= TOL["bf16"] and e["S"] <= TOL["bf16"], e
 
 
 @pytest.mark.parametrize("dt", ["fp32", "bf16"])
