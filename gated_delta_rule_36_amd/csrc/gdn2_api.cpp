@@ -104,7 +104,9 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* log_
     if ((long)N * H * (d_v / a.nv) > (long)INT_MAX) return GDN2_INVALID_ARGUMENT;
     return status_of(gdn2::launch_chunk_fwd_split(a));
   }
-  if (nv == 0 && gdn2::fwd_pipelined_supported(dtype, d_k, d_v)) {
+  // (the pipelined kernel addresses a chunk's value rows through 32-bit buffer offsets)
+  if (nv == 0 && gdn2::fwd_pipelined_supported(dtype, d_k, d_v) &&
+      (long)H * d_v * kChunk * 2 <= (long)INT_MAX) {
     if ((long)N * H * (d_v / 64) > (long)INT_MAX) return GDN2_INVALID_ARGUMENT;
     a.nv = 64;
     return status_of(gdn2::launch_fwd_pipelined(a));

@@ -57,6 +57,20 @@ constexpr float kFwdFastDecay2 = 100.f;  // log2 units
 constexpr float kMinTokenDecay2 = -256.f;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Buffer resource over `bytes` bytes from p (raw buffer, dword data format): loads at offsets
+// at or past the end return zeros, so a chunk's rows past the end of its sequence need
+// neither clamped addresses nor masking.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t bload2(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
 
 // 4 bf16 from the transposing LDS read (see the file comment for the lane mapping).
 __device__ __forceinline__ bf16x4 ds_tr4(const bf16* p) {
@@ -149,7 +163,8 @@ struct FwdShape {
   static constexpr int OFF_TOT = OFF_AD + 4 * 16 * LDD * 4; // decay totals / prefixes
   static constexpr int OFF_FAC = OFF_TOT + TG * DK * 4;     // factor rows (two)
   static constexpr int OFF_FLAG = OFF_FAC + 2 * NFAC * DK * 4;
-  static constexpr int LDS_BYTES = OFF_FLAG + 16;
+  static constexpr int OFF_ID = OFF_FLAG + 16;              // 16x16 identity, fp32, pitch LDD
+  static constexpr int LDS_BYTES = OFF_ID + 16 * LDD * 4;
 
   static_assert(TPT >= 1 && 16 % TPT == 0, "token groups tile 16-token blocks");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -235,10 +250,10 @@ __device__ __forceinline__ void diag_tiles_exact(const bf16* qb, const bf16* kb,
 // One 16x16 diagonal block of T = (I + A)^-1 by fp32 forward substitution, column c per lane
 // (lanes 0..15 write; the other lane groups repeat the work). sAdb: the -A block stored
 // column-major (column i at sAdb + i * LDD, rows r > i used), read in full before the
-// substitution so that its 15 dependent steps wait on the LDS once; sTb: the block of T,
-// column-major.
+// substitution so that its 15 dependent steps wait on the LDS once; sId: the 16x16 identity
+// (row c at sId + c * LDD), which starts column c; sTb: the block of T, column-major.
 template <int LDD, int LDTT>
-__device__ __forceinline__ void tinv_block(const float* sAdb, bf16* sTb, int lane) {
+__device__ __forceinline__ void tinv_block(const float* sAdb, const float* sId, bf16* sTb, int lane) {
   const int c = lane & 15;
   float col[15][16];
 #pragma unroll
@@ -252,7 +267,11 @@ __device__ __forceinline__ void tinv_block(const float* sAdb, bf16* sTb, int lan
   }
   float x[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
+  for (int r4 = 0; r4 < 16; r4 += 4) {
+    const f4 v = *reinterpret_cast<const f4*>(sId + c * LDD + r4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[r4 + j] = v[j];
+  }
 #pragma unroll
   for (int i = 0; i < 15; ++i) {
 #pragma unroll
@@ -289,6 +308,7 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   bf16* const sP = reinterpret_cast<bf16*>(smem + Sh::OFF_P);
   bf16* const sT = reinterpret_cast<bf16*>(smem + Sh::OFF_T);
   float* const sAd = reinterpret_cast<float*>(smem + Sh::OFF_AD);
+  float* const sId = reinterpret_cast<float*>(smem + Sh::OFF_ID);
   float* const sTot = reinterpret_cast<float*>(smem + Sh::OFF_TOT);
   int* const sFlag = reinterpret_cast<int*>(smem + Sh::OFF_FLAG);
   auto sQg = [&](int p) __attribute__((always_inline)) {
@@ -477,37 +497,41 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // the last chunk) and tokens past a chunk's end are zeroed where the values are used: the
     // compiler can then count the loads in flight exactly and wait for only the ones it needs.
     auto load_vw = [&](int c) __attribute__((always_inline)) {
-      const int c0 = min(c, nchunks - 1) * C;
+      const int cc = min(c, nchunks - 1) * C;
+      const int rows = c < nchunks ? nvalid_of(c) : 0;  // past the last chunk: zeros, no traffic
+      const auto rv_ = rsrc(vb + (long)cc * vstride, rows * (int)vstride * 2);
+      const auto rw_ = rsrc(w_scalar ? wsb + (long)cc * H : wb + (long)cc * vstride,
+                            w_scalar ? rows * H * 2 : rows * (int)vstride * 2);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int r = min(c0 + 2 * vtk + j, len - 1);
-        rv[j].load(vb + (long)r * vstride + vcg * 8);
-        if constexpr (w_scalar) rw[j].load_one(wsb + (long)r * H);
-        else rw[j].load(wb + (long)r * vstride + vcg * 8);
+        const int r = 2 * vtk + j;
+        rv[j].r = bload16(rv_, r * (int)vstride * 2 + vcg * 16);
+        if constexpr (w_scalar) rw[j].r.x = bload2(rw_, r * H * 2);
+        else rw[j].r = bload16(rw_, r * (int)vstride * 2 + vcg * 16);
       }
     };
-    auto make_z = [&](int nv) __attribute__((always_inline)) {
+    auto make_z = [&]() __attribute__((always_inline)) {  // rows past the end load as 0
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         float fv[8], fw[8], z[8];
         rv[j].to_float(fv);
         if constexpr (w_scalar) rw[j].splat();
         rw[j].to_float(fw);
-        const bool ok = 2 * vtk + j < nv;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) z[i] = ok ? fv[i] * fw[i] : 0.f;
+        for (int i = 0; i < 8; ++i) z[i] = fv[i] * fw[i];
         store8(sZ + (2 * vtk + j) * LDZ + vcg * 8, z);
       }
     };
     f4 Ut[4];  // U~ of this wave's value tile, from phase 2 to phase 3
 
+    if (tid < 256) sId[(tid >> 4) * LDD + (tid & 15)] = (tid >> 4) == (tid & 15) ? 1.f : 0.f;
     if (nchunks > 0) {  // prologue: chunk 0's operands (three barriers, as the other waves)
       load_vw(0);
       lds_barrier();
       fresh();
       lds_barrier();
       fresh();
-      make_z(nvalid_of(0));
+      make_z();
       load_vw(1);
       lds_barrier();
       fresh();
@@ -529,7 +553,7 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         }
         put_diag_a(w, tile(p, w, w, false, false));
         // reads only what this wave just wrote: no barrier needed
-        tinv_block<LDD, LDTT>(sAd + w * 16 * LDD, sT + w * 16 * LDTT, lane);
+        tinv_block<LDD, LDTT>(sAd + w * 16 * LDD, sId, sT + w * 16 * LDTT, lane);
       } else {
         switch (w) {
           case 0: put_p(3, 2, tile(p, 3, 2, true, true)); put_off_a(3, 2, tile(p, 3, 2, false, true)); break;
@@ -540,7 +564,7 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         diag_tiles_exact<DK, b_scalar>(qb, kb, gb, bb, bsb, kstride, H, c0, nvalid, tid, sAd, sP);
         lds_barrier();
         fresh();
-        tinv_block<LDD, LDTT>(sAd + w * 16 * LDD, sT + w * 16 * LDTT, lane);
+        tinv_block<LDD, LDTT>(sAd + w * 16 * LDD, sId, sT + w * 16 * LDTT, lane);
         rescale(p);
       }
       lds_barrier();
@@ -553,9 +577,10 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       column(false, w, Ut);
       lds_barrier();
       fresh();
-      // ---- phase 3: the next chunk's Z (its loads were issued a chunk ago and nothing has
-      // been issued since), then U = U~ - W S, O, state update
-      if (more) make_z(nvalid_of(c + 1));
+      // ---- phase 3: the next chunk's Z (its loads were issued a chunk ago) and the loads
+      // for the chunk after it (in flight during the products), then U = U~ - W S, O, state
+      // update
+      if (more) make_z();
       {
         const bf16* qg = sQg(p);
         const bf16* kg = sKg(p);
@@ -595,7 +620,6 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           }
           const int r = 16 * R + m16;
           if (r < nvalid) {
-            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
             const uint2 pk = make_uint2(pack_bf16(Ot[0], Ot[1]), pack_bf16(Ot[2], Ot[3]));
             __builtin_nontemporal_store(__builtin_bit_cast(u32x2, pk),
                                         reinterpret_cast<u32x2*>(ob + (long)(c0 + r) * vstride + 16 * w + 4 * g4));
@@ -642,24 +666,27 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     Vec8<bf16> rq[TPT], rk[TPT], rb[TPT], rg[TPT], gk[TPT];
     // unconditional prefetch loads (see load_vw): clamped rows, zeroed at use
     auto load_g = [&](int c) __attribute__((always_inline)) {
-      const int c0 = min(c, nchunks - 1) * C;
+      const int cc = min(c, nchunks - 1) * C;
 #pragma unroll
       for (int j = 0; j < TPT; ++j) {
-        const int r = min(c0 + tg * TPT + j, len - 1);
-        rg[j].load(gb + (long)r * kstride + cg * 8);
+        const int r = min(tg * TPT + j, len - 1 - cc);
+        rg[j].load(gb + (long)cc * kstride + (unsigned)(r * (int)kstride + cg * 8));
       }
     };
+    // token j of chunk c; issued token by token as X.c frees the registers, so that the
+    // chunk's loads reach the memory pipeline spread over X.c's arithmetic, not as one burst
+    auto load_qkb_tok = [&](int c, int j) __attribute__((always_inline)) {
+      const int cc = min(c, nchunks - 1) * C;
+      const int r = min(tg * TPT + j, len - 1 - cc);
+      const unsigned off = (unsigned)(r * (int)kstride + cg * 8);
+      rq[j].load(qb + (long)cc * kstride + off);
+      rk[j].load(kb + (long)cc * kstride + off);
+      if constexpr (b_scalar) rb[j].load_one(bsb + (long)cc * H + (unsigned)(r * H));
+      else rb[j].load(bb + (long)cc * kstride + off);
+    };
     auto load_qkb = [&](int c) __attribute__((always_inline)) {
-      const int c0 = min(c, nchunks - 1) * C;
 #pragma unroll
-      for (int j = 0; j < TPT; ++j) {
-        const int r = min(c0 + tg * TPT + j, len - 1);
-        const long off = (long)r * kstride + cg * 8;
-        rq[j].load(qb + off);
-        rk[j].load(kb + off);
-        if constexpr (b_scalar) rb[j].load_one(bsb + (long)r * H);
-        else rb[j].load(bb + off);
-      }
+      for (int j = 0; j < TPT; ++j) load_qkb_tok(c, j);
     };
     // X.a: this thread's decay total into sTot[tg][channel]; the raw decays are kept (gk)
     // for X.c, since rg is refilled with the chunk after next
@@ -702,8 +729,10 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       }
     };
     // X.c: gated operands of the chunk into Eg, Qg[p], Kg[p] (fast: chunk-referenced;
-    // general: block-referenced)
-    auto xc_impl = [&](int p, int nv, auto gen_c) __attribute__((always_inline)) {
+    // general: block-referenced); then the loads of chunk cn into the freed registers. Tokens
+    // past the chunk's end get K = 0 (so E = 0 too): their rows of Kg, Eg, W and U are then
+    // zero and add nothing to the state; their Qg rows only reach outputs that are not stored.
+    auto xc_impl = [&](int p, int nv, int cn, auto gen_c) __attribute__((always_inline)) {
       constexpr bool GEN = decltype(gen_c)::value;
       const float* fac = sFac(p);
       float run[8], ox[8], oy[8];
@@ -726,7 +755,7 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
       for (int j = 0; j < TPT; ++j) {
         const int r = tg * TPT + j;
-        if (nv < C && r >= nv) { rq[j].zero(); rk[j].zero(); rb[j].zero(); }
+        if (nv < C && r >= nv) rk[j].zero();
         if constexpr (b_scalar) rb[j].splat();
         float fg[8];
         gk[j].to_float(fg);
@@ -756,11 +785,12 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           *reinterpret_cast<bf16x4*>(qg + o) = to_bf4(q1);
           *reinterpret_cast<bf16x4*>(kg + o) = to_bf4(k1);
         }
+        load_qkb_tok(cn, j);
       }
     };
-    auto xc = [&](int p, int nv) __attribute__((always_inline)) {
-      if (flag(p)) xc_impl(p, nv, std::true_type{});
-      else xc_impl(p, nv, std::false_type{});
+    auto xc = [&](int p, int nv, int cn) __attribute__((always_inline)) {
+      if (flag(p)) xc_impl(p, nv, cn, std::true_type{});
+      else xc_impl(p, nv, cn, std::false_type{});
     };
 
     if (nchunks > 0) {  // prologue: chunk 0's operands
@@ -774,8 +804,7 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       xb(0);
       lds_barrier();
       fresh();
-      xc(0, nvalid_of(0));
-      load_qkb(1);
+      xc(0, nvalid_of(0), 1);
       lds_barrier();
       fresh();
     }
@@ -821,9 +850,9 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       if (more) xb(pn);
       lds_barrier();
       fresh();
-      // ---- phase 3: the next chunk's operands, then its loads
-      if (more) xc(pn, nvalid_of(c + 1));
-      load_qkb(c + 2);
+      // ---- phase 3: the next chunk's operands, and the loads of the chunk after it
+      if (more) xc(pn, nvalid_of(c + 1), c + 2);
+      else load_qkb(c + 2);
       lds_barrier();
       fresh();
     }
