@@ -532,7 +532,6 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       lds_barrier();
       fresh();
       make_z();
-      load_vw(1);
       lds_barrier();
       fresh();
     }
@@ -543,6 +542,7 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       const int nvalid = nvalid_of(c);
       const bool more = c + 1 < nchunks;
       const bool gen = flag(p);
+      load_vw(c + 1);  // the next chunk's values, for its Z in phase 3
       // ---- phase 1: one A / P tile, diagonal A tile w and its inverse block
       if (!gen) {
         switch (w) {
@@ -577,9 +577,8 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       column(false, w, Ut);
       lds_barrier();
       fresh();
-      // ---- phase 3: the next chunk's Z (its loads were issued a chunk ago) and the loads
-      // for the chunk after it (in flight during the products), then U = U~ - W S, O, state
-      // update
+      // ---- phase 3: the next chunk's Z (its loads were issued in phase 1), then
+      // U = U~ - W S, O, state update
       if (more) make_z();
       {
         const bf16* qg = sQg(p);
@@ -641,7 +640,6 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           S[mt] = gen ? acc : acc * gam;
         }
       }
-      load_vw(c + 2);
       lds_barrier();
       fresh();
     }
@@ -673,20 +671,42 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         rg[j].load(gb + (long)cc * kstride + (unsigned)(r * (int)kstride + cg * 8));
       }
     };
-    // token j of chunk c; issued token by token as X.c frees the registers, so that the
-    // chunk's loads reach the memory pipeline spread over X.c's arithmetic, not as one burst
-    auto load_qkb_tok = [&](int c, int j) __attribute__((always_inline)) {
-      const int cc = min(c, nchunks - 1) * C;
+    // The loads of a chunk are spread over the three phases, so that the vector memory
+    // path of the compute unit never holds one phase's worth of every array in flight at
+    // once (measured: loads issued as one burst stall on the L1's pending misses): q and b
+    // of the next chunk at the starts of phases 1 and 2, k of the chunk after next token by
+    // token inside X.c as it frees the registers, g of the chunk after next at the end of
+    // phase 1, and the value side (waves 0-3) at the start of phase 1.
+    auto key_off = [&](int c, int j, int& cc) __attribute__((always_inline)) {
+      cc = min(c, nchunks - 1) * C;
       const int r = min(tg * TPT + j, len - 1 - cc);
-      const unsigned off = (unsigned)(r * (int)kstride + cg * 8);
-      rq[j].load(qb + (long)cc * kstride + off);
-      rk[j].load(kb + (long)cc * kstride + off);
-      if constexpr (b_scalar) rb[j].load_one(bsb + (long)cc * H + (unsigned)(r * H));
-      else rb[j].load(bb + (long)cc * kstride + off);
+      return (unsigned)(r * (int)kstride + cg * 8);
     };
-    auto load_qkb = [&](int c) __attribute__((always_inline)) {
+    auto load_q = [&](int c) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < TPT; ++j) load_qkb_tok(c, j);
+      for (int j = 0; j < TPT; ++j) {
+        int cc;
+        const unsigned off = key_off(c, j, cc);
+        rq[j].load(qb + (long)cc * kstride + off);
+      }
+    };
+    auto load_b = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < TPT; ++j) {
+        int cc;
+        const unsigned off = key_off(c, j, cc);
+        if constexpr (b_scalar) {
+          const int r = min(tg * TPT + j, len - 1 - cc);
+          rb[j].load_one(bsb + (long)cc * H + (unsigned)(r * H));
+        } else {
+          rb[j].load(bb + (long)cc * kstride + off);
+        }
+      }
+    };
+    auto load_k_tok = [&](int c, int j) __attribute__((always_inline)) {
+      int cc;
+      const unsigned off = key_off(c, j, cc);
+      rk[j].load(kb + (long)cc * kstride + off);
     };
     // X.a: this thread's decay total into sTot[tg][channel]; the raw decays are kept (gk)
     // for X.c, since rg is refilled with the chunk after next
@@ -729,7 +749,7 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       }
     };
     // X.c: gated operands of the chunk into Eg, Qg[p], Kg[p] (fast: chunk-referenced;
-    // general: block-referenced); then the loads of chunk cn into the freed registers. Tokens
+    // general: block-referenced); then the k loads of chunk cn into the freed registers. Tokens
     // past the chunk's end get K = 0 (so E = 0 too): their rows of Kg, Eg, W and U are then
     // zero and add nothing to the state; their Qg rows only reach outputs that are not stored.
     auto xc_impl = [&](int p, int nv, int cn, auto gen_c) __attribute__((always_inline)) {
@@ -785,7 +805,7 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           *reinterpret_cast<bf16x4*>(qg + o) = to_bf4(q1);
           *reinterpret_cast<bf16x4*>(kg + o) = to_bf4(k1);
         }
-        load_qkb_tok(cn, j);
+        load_k_tok(cn, j);
       }
     };
     auto xc = [&](int p, int nv, int cn) __attribute__((always_inline)) {
@@ -795,7 +815,10 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
     if (nchunks > 0) {  // prologue: chunk 0's operands
       load_g(0);
-      load_qkb(0);
+      load_q(0);
+      load_b(0);
+#pragma unroll
+      for (int j = 0; j < TPT; ++j) load_k_tok(0, j);
       if (tid == 256) sFlag[0] = 0;
       xa(nvalid_of(0));
       load_g(1);
@@ -816,6 +839,7 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       const bool more = c + 1 < nchunks;
       const bool gen = flag(p);
       const int R4 = wave - 4;
+      load_q(c + 1);
       // ---- phase 1: three A / P tiles; next totals
       if (!gen) {
         switch (R4) {
@@ -843,6 +867,7 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       lds_barrier();
       fresh();
       // ---- phase 2: a key tile; the next chunk's decay scan
+      load_b(c + 1);
       {
         f4 X[4];
         column(true, NCT == 8 ? wave : R4, X);
@@ -850,9 +875,15 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       if (more) xb(pn);
       lds_barrier();
       fresh();
-      // ---- phase 3: the next chunk's operands, and the loads of the chunk after it
-      if (more) xc(pn, nvalid_of(c + 1), c + 2);
-      else load_qkb(c + 2);
+      // ---- phase 3: the next chunk's operands (and the k loads of the chunk after it; issued
+      // on the last chunk too, so that every iteration leaves the same loads in flight and
+      // the compiler's waits stay exact)
+      if (more) {
+        xc(pn, nvalid_of(c + 1), c + 2);
+      } else {
+#pragma unroll
+        for (int j = 0; j < TPT; ++j) load_k_tok(c + 2, j);
+      }
       lds_barrier();
       fresh();
     }
