@@ -14,7 +14,7 @@ BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["gdn2_api.cpp", "gdn2_chunk.hip", "gdn2_split.hip", "gdn2_bwd.hip", "gdn2_decode.hip",
            "gdn2_block.hip", "gdn2_noalloc.hip",
-           "gdn2_fwd.hip"]
+           "gdn2_fwd.hip", "gdn2_recurrent.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU forms are kept out of generated code on purpose

@@ -72,7 +72,8 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* log_
     if (B != 1) return GDN2_INVALID_ARGUMENT;
   }
   if (!width_ok(d_k) || !width_ok(d_v)) return GDN2_UNSUPPORTED;
-  if (dtype == GDN2_F32 && d_k != 64) return GDN2_UNSUPPORTED;
+  // fp32 with d_k = 128 runs the token-recurrent kernel, which has no value-slice choice
+  if (nv != 0 && gdn2::fwd_recurrent_used(dtype, d_k, d_v)) return GDN2_UNSUPPORTED;
   const long tokens = (long)B * T;
   if (tokens > 0 && (!q || !k || !v || !log_alpha || !b || !w || !o))
     return GDN2_INVALID_ARGUMENT;
@@ -103,6 +104,10 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* log_
     if ((long)N * H * sp.nseg * ((d_v + d_k) / 64) > (long)INT_MAX) return GDN2_INVALID_ARGUMENT;
     if ((long)N * H * (d_v / a.nv) > (long)INT_MAX) return GDN2_INVALID_ARGUMENT;
     return status_of(gdn2::launch_chunk_fwd_split(a));
+  }
+  if (gdn2::fwd_recurrent_used(dtype, d_k, d_v)) {
+    if ((long)N * H * (d_v / 64) > (long)INT_MAX) return GDN2_INVALID_ARGUMENT;
+    return status_of(gdn2::launch_fwd_recurrent(a));
   }
   // (the pipelined kernel addresses a chunk's value rows through 32-bit buffer offsets)
   if (nv == 0 && gdn2::fwd_pipelined_supported(dtype, d_k, d_v) &&

@@ -171,6 +171,10 @@ hipError_t launch_chunk_fwd(const ChunkArgs& a);
 // value slices.
 bool fwd_pipelined_supported(int dtype, int d_k, int d_v);
 hipError_t launch_fwd_pipelined(const ChunkArgs& a);
+// Token-recurrent forward (gdn2_recurrent.hip): fp32 with d_k = 128, where the chunk
+// kernels' fp32 operands do not fit the LDS.
+bool fwd_recurrent_used(int dtype, int d_k, int d_v);
+hipError_t launch_fwd_recurrent(const ChunkArgs& a);
 hipError_t launch_chunk_fwd_split(const ChunkArgs& a);
 hipError_t launch_chunk_bwd(const BwdArgs& a);
 // pieces of the backward shared with the two-phase forward (gdn2_split.hip)

@@ -89,13 +89,16 @@ enum { GDN2_GATE_B_SCALAR = 1, GDN2_GATE_W_SCALAR = 2 };
  *                        compute units, each sequence is cut into segments that run in
  *                        parallel: a transfer pass, a scan of segment start states, then
  *                        the outputs). Without one, a single fused kernel does both per
- *                        sequence.
+ *                        sequence (for bf16 a kernel that prepares the next chunk's
+ *                        operands while it finishes the current one).
  *                        Results agree to rounding. Ignored when
  *                        gdn2_chunk_fwd_workspace_bytes returns 0 for the dtype/widths.
  *   Without cu_seqlens, N must equal B and every sequence has length T.
- *   Supported: GDN2_BF16 with d_k, d_v in {64, 128}; GDN2_F32 with d_k = 64 and
- *   d_v in {64, 128} (fused path only). T = 0 or N = 0 is a no-op (apart from
- *   final_state = initial).
+ *   Supported: d_k, d_v in {64, 128} for both dtypes. GDN2_F32 runs without a workspace
+ *   only: the chunk kernel for d_k = 64, and for d_k = 128, whose fp32 chunk operands do
+ *   not fit the 160 KB of LDS, the token recurrence itself (one token at a time, fp32
+ *   state in registers; exact to fp32 rounding, not chunk-parallel). T = 0 or N = 0 is a
+ *   no-op (apart from final_state = initial).
  * Returns GDN2_OK or an error status (GDN2_WORKSPACE_TOO_SMALL when workspace_bytes is
  * below the requirement).
  */
@@ -247,9 +250,9 @@ int gdn2_chunk_bwd_saved(const void* q, const void* k, const void* v, const void
  * The fused single-kernel path of gdn2_chunk_fwd (no workspace) with an explicit
  * value-slice width: each workgroup carries
  * `value_slice` columns of the state (16, 32, 64 or 128; a divisor of d_v; 16 only with
- * d_k = 64; at most 64 for GDN2_F32). 0 selects the width automatically, exactly as
- * gdn2_chunk_fwd does. Results do not depend on the width beyond rounding. Returns
- * GDN2_UNSUPPORTED for a width that is not built.
+ * d_k = 64; at most 64 for GDN2_F32, whose d_k = 128 form has no slices). 0 selects the
+ * width automatically, exactly as gdn2_chunk_fwd does. Results do not depend on the width
+ * beyond rounding. Returns GDN2_UNSUPPORTED for a width that is not built.
  */
 int gdn2_chunk_fwd_sliced(const void* q, const void* k, const void* v, const void* log_alpha,
                           const void* b, const void* w, const float* initial_state, void* o,

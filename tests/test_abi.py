@@ -57,7 +57,6 @@ def test_chunk_fwd_error_paths():
     assert _chunk(T=-1) == 1
     assert _chunk(dk=96) == 2
     assert _chunk(dv=256) == 2
-    assert _chunk(dtype=1, dk=128) == 2     # fp32 path is built for d_k = 64
     assert _chunk(q=None) == 1
     assert _chunk(o=None) == 1
     assert _chunk(k=MIS) == 1               # misaligned
@@ -106,6 +105,7 @@ def test_chunk_fwd_sliced_error_paths():
     assert call(256) == 2
     assert call(128, dk=64, dv=64) == 2     # wider than d_v
     assert call(128, dk=64, dv=128, dtype=1) == 2
+    assert call(64, dk=128, dv=128, dtype=1) == 2  # fp32, d_k = 128: token-recurrent, no slices
 
 
 def test_decode_error_paths():

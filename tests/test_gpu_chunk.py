@@ -60,6 +60,24 @@ def slices_for(dt, dk, dv):
 
 
 # ------------------------------------------------------------------ small, full oracle
+@pytest.mark.parametrize("dv", [64, 128])
+@pytest.mark.parametrize("varlen", [False, True])
+def test_fp32_dk128(dv, varlen):
+    """fp32 with d_k = 128 (the token-recurrent kernel): ragged lengths spanning several
+    16-token blocks, an initial state, fp32 tolerance."""
+    if varlen:
+        lens = [37, 0, 150, 1, 64]
+        x = make_inputs(1, sum(lens), 3, 128, dv, "fp32", seed=61 + dv, lengths=lens, s0_std=0.05)
+    else:
+        x = make_inputs(2, 130, 3, 128, dv, "fp32", seed=71 + dv, s0_std=0.05)
+    say("fp32 d_k=128", "dv", dv, "varlen", varlen)
+    o, sN = run_gpu(x, 0)
+    o_ref, s_ref = run_oracle(x)
+    assert_close("o", host64(o), o_ref, TOL["fp32"])
+    assert_close("S", host64(sN), s_ref, TOL["fp32"])
+
+
+
 @pytest.mark.parametrize("nv", [16, 32, 64])
 def test_tiny_fp32_config(nv):
     x = make_config_inputs("tiny_fp32")

@@ -6,8 +6,8 @@ on ragged lengths with an initial state, long sequences (many chunks through the
 buffered pipeline), and strong decay on every token of one chunk, on one aligned 16-token
 block, on every token of a sequence, single near-total resets, and decays far below fp32
 range (alpha that underflows). The same decay cases also run through every other forward:
-the two-phase path (with a workspace), the training forward, the value-sliced fused kernel
-and its fp32 build.
+the two-phase path (with a workspace), the training forward, the value-sliced fused kernel,
+its fp32 build (d_k = 64) and the fp32 token-recurrent kernel (d_k = 128).
 Tolerance: normwise max relative error 2e-2 on o and on the final state (1e-4 in fp32)."""
 import numpy as np
 import pytest
@@ -126,10 +126,11 @@ def test_decay_range_other_paths(path, case, dk):
 
 
 @pytest.mark.parametrize("case", list(RANGE_CASES))
-def test_decay_range_fp32(case):
+@pytest.mark.parametrize("dk", [64, 128])
+def test_decay_range_fp32(case, dk):
     tokens, gn = RANGE_CASES[case]
-    x = _with_decay(make_inputs(2, 300, 2, 64, 64, "fp32", seed=323, s0_std=0.05), tokens, gn)
-    say("fwd range fp32", case)
+    x = _with_decay(make_inputs(2, 300, 2, dk, 64, "fp32", seed=323 + dk, s0_std=0.05), tokens, gn)
+    say("fwd range fp32", case, "dk", dk)
     _check(x)
 
 

@@ -37,7 +37,8 @@ def _scalarise(x, layout, lead, seed):
 
 @pytest.mark.parametrize("layout", ["b", "w", "bw"])
 @pytest.mark.parametrize("dt,dk,dv,path", [("bf16", 128, 128, "fused"), ("bf16", 64, 128, "fused"),
-                                           ("fp32", 64, 64, "fused"), ("bf16", 128, 64, "split"),
+                                           ("fp32", 64, 64, "fused"), ("fp32", 128, 64, "fused"),
+                                           ("bf16", 128, 64, "split"),
                                            ("bf16", 128, 128, "split")])
 def test_chunk_forward_scalar_gates(layout, dt, dk, dv, path):
     import gated_delta_rule_36_amd as G
