@@ -319,10 +319,10 @@ def main():
         bws = torch.empty(int(G.lib().gdn2_chunk_bwd_workspace_bytes(B, T, H, dk, dv, N, 0)),
                           dtype=torch.uint8, device=dev)
 
-        def bstep(check=False):
+        def bstep():
             return G.chunk_bwd(*(t[n] for n in NAMES), do, initial_state=s0, cu_seqlens=cu,
-                               workspace=bws, check_range=check)
-        bstep(check=True)
+                               workspace=bws)
+        bstep()
         settle(bstep)
         KB = max(5, K // 5)
         evb = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -355,8 +355,7 @@ def main():
         def pair_saved():
             _, _, sv = G.chunk_fwd_train(*(t[n] for n in NAMES), initial_state=s0, cu_seqlens=cu,
                                          workspace=bws)
-            G.chunk_bwd(*(t[n] for n in NAMES), do, initial_state=s0, cu_seqlens=cu, saved=sv,
-                        check_range=False)
+            G.chunk_bwd(*(t[n] for n in NAMES), do, initial_state=s0, cu_seqlens=cu, saved=sv)
         res_t = {}
         pairs = (("recompute", pair_recompute), ("saved", pair_saved))
         for name, fn in (pairs if args.workload == "layer1p3b" else ()):
@@ -414,9 +413,9 @@ def main():
             lbws = torch.empty(int(G.lib().gdn2_chunk_bwd_workspace_bytes(1, TL, H, dk, dv, 1, 0)),
                                dtype=torch.uint8, device=dev)
 
-            def lbstep(check=False):
-                return G.chunk_bwd(lq, lk, lv, lg, lb, lw, ldo, workspace=lbws, check_range=check)
-            lbstep(check=True)  # (raises if a chunk were outside the backward's decay range)
+            def lbstep():
+                return G.chunk_bwd(lq, lk, lv, lg, lb, lw, ldo, workspace=lbws)
+            lbstep()
             settle(lbstep)
             evb = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(5)]

@@ -270,19 +270,15 @@ def chunk_fwd_train(q, k, v, g, b, w, initial_state=None, cu_seqlens=None,
     return o, sN, SavedForBackward(workspace, key)
 
 
-class Gdn2RangeError(RuntimeError):
-    """A chunk's total decay exceeded the range of the backward's factors."""
-
-
 def chunk_bwd(q, k, v, g, b, w, do, initial_state=None, d_final_state=None, cu_seqlens=None,
-              workspace=None, check_range=True, saved=None):
+              workspace=None, saved=None):
     """Gradients of chunk_fwd (bf16).
 
     do: [B, T, H, d_v] gradient of o (input dtype); d_final_state: [N, H, d_k, d_v] fp32 or
     None. b or w may be scalar gates [B, T, H] (their gradients then have that shape: the sum
     over the channels). Returns (dq, dk, dv, dg, db, dw, d_initial_state): the first six in the
-    input dtype and shapes, the last fp32 [N, H, d_k, d_v]. With check_range, synchronises once and
-    raises Gdn2RangeError when some chunk's total decay is outside the backward's range.
+    input dtype and shapes, the last fp32 [N, H, d_k, d_v]. Exact for any decay: chunks past the
+    local-gradient kernel's factor range are recomputed by the library's exact kernel.
     saved: the SavedForBackward of a chunk_fwd_train call on these same tensors; the
     forward recomputation is then skipped.
     """
@@ -329,9 +325,6 @@ def chunk_bwd(q, k, v, g, b, w, do, initial_state=None, d_final_state=None, cu_s
               B, T, H, dk, dv, N, code, layout, _ptr(workspace), workspace.numel(), _stream(dev))
     if st != 0:
         raise Gdn2Error(fn, st)
-    if check_range and int(flag.item()) != 0:
-        raise Gdn2RangeError("a chunk's total decay exceeds the backward's range "
-                             "(about 166 nats over 64 tokens in some key channel)")
     return (*grads, ds0)
 
 

@@ -792,6 +792,224 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   }
 }
 
+// ------------------------------------------------------------------ exact local gradients
+// The local kernel references its decay factors to the middle of each chunk's decay, which
+// keeps them finite for chunks of up to 2 x kFastPathMaxDecay2 log2 units per channel. This
+// kernel recomputes dq, dk, db and dg of the (chunk, head) units past a slightly lower
+// bound (every unit the local kernel may have left invalid; dv and dw carry no decay and
+// stay as it wrote them), with the pairwise factors 2^(G_r - G_i) <= 1 (r >= i) evaluated
+// directly, so any decay in (0, 1] is exact: the same chunk-form formulas as the local
+// kernel, term by term, in fp32 and without matrix cores (a rare path).
+//   M1 = lower_incl(dO U^T), M2 = -strict(dZ U^T), dOS = dO S0^T, dZS = dZ S0^T,
+//   dKt = U dSn^T, X = rowsum(dSn * S0);
+//   dq_t = 2^G_t dOS_t + sum_{i<=t} M1[t,i] k_i 2^(G_t-G_i)
+//   de_t = -2^G_t dZS_t + sum_{i<t} M2[t,i] k_i 2^(G_t-G_i)
+//   dkh_t = sum_{r>=t} (M2[r,t] e_r + M1[r,t] q_r) 2^(G_r-G_t)
+//   dk_t = dkh_t + dKt_t 2^(Gl-G_t) + de_t b_t,  db_t = de_t k_t
+//   dg_t = sum_{t'>=t} (A - B)_{t'} + sum_t B_t + 2^Gl X,
+//   A_t = de_t b_t k_t + dq_t q_t - dkh_t k_t,  B_t = dKt_t k_t 2^(Gl-G_t).
+// One 256-thread workgroup per unit (persistent over units); thread = (key channel c, half
+// of the chunk's tokens). Launched after the local kernel; with a range flag that the local
+// kernel left at 0 (no unit out of its range) every workgroup returns at once.
+template <int DK, int DV, int GL>
+__global__ void __launch_bounds__(256)
+gdn2_bwd_exact_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                      const bf16* __restrict__ g, const bf16* __restrict__ bg,
+                      const bf16* __restrict__ d_o, const char* __restrict__ ws,
+                      bf16* __restrict__ dq, bf16* __restrict__ dk, bf16* __restrict__ dg,
+                      bf16* __restrict__ db, const int* range_flag,
+                      const int* __restrict__ cu_seqlens, int N, int T_len, int H, long nunits) {
+  static_assert(DK * 2 == 256 || DK * 4 == 256, "thread mapping");
+  constexpr int C = 64, NT = 256;
+  constexpr int NH = NT / DK;         // token groups per channel (2 for d_k = 128, 4 for 64)
+  constexpr int TPH = C / NH;         // tokens per thread
+  constexpr int LDV = DV + 8;         // bf16 rows of the value-side arrays
+  constexpr int LDM = C + 1;          // fp32 rows of M1, M2
+  constexpr bool B_S = (GL & kGateBScalar) != 0;
+  constexpr BwdLayout LB(DK, DV);
+  // stage 1: S0, dSn [DK][LDV], U, dO, dZ [C][LDV] (bf16); stage 2 reuses the space for
+  // G [C][DK] (fp32) and q, k, b [C][DK] (bf16)
+  constexpr int SZ1 = (2 * DK + 3 * C) * LDV * 2;
+  constexpr int SZ2 = C * DK * 4 + 3 * C * DK * 2;
+  constexpr int SZ12 = SZ1 > SZ2 ? SZ1 : SZ2;
+  __shared__ __attribute__((aligned(16))) char smem[SZ12 + 2 * C * LDM * 4 + (NH + 2) * DK * 4 + C * 4];
+  bf16* sS0 = reinterpret_cast<bf16*>(smem);
+  bf16* sdS = sS0 + DK * LDV;
+  bf16* sU = sdS + DK * LDV;
+  bf16* sO = sU + C * LDV;
+  bf16* sZ = sO + C * LDV;
+  float* sG = reinterpret_cast<float*>(smem);
+  bf16* sq = reinterpret_cast<bf16*>(smem + C * DK * 4);
+  bf16* sk = sq + C * DK;
+  bf16* sb = sk + C * DK;
+  float* sM1 = reinterpret_cast<float*>(smem + SZ12);
+  float* sM2 = sM1 + C * LDM;
+  float* sPart = sM2 + C * LDM;       // [NH][DK] per-group totals (decay, then dg suffix)
+  float* sTB = sPart + NH * DK;       // [DK] sum of B over the chunk
+  float* sMx = sTB + DK;              // [DK] largest decay total (range test)
+  float* sDb = sMx + DK;              // [C] scalar b: channel sums
+
+  if (range_flag != nullptr && __builtin_amdgcn_readfirstlane(*range_flag) == 0) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int c = tid % DK, hg = tid / DK, t0 = hg * TPH;
+  const long kstride = (long)H * DK, vstride = (long)H * (long)DV;
+
+  for (long u = blockIdx.x; u < nunits; u += gridDim.x) {
+    const ChunkUnit cu = map_unit(u, H, cu_seqlens, N, T_len, lane);
+    if (cu.nvalid == 0) continue;  // (uniform)
+    const long kb0 = cu.row * kstride + (long)cu.h * DK;
+    const long vb0 = cu.row * vstride + (long)cu.h * DV;
+    // ---- range test: this channel's decay over the chunk (log2), against a bound a little
+    // below the local kernel's, so that every unit it may have left invalid is redone
+    float tot = 0.f;
+    for (int t = t0; t < t0 + TPH; ++t)
+      if (t < cu.nvalid) tot += static_cast<float>(g[kb0 + (long)t * kstride + c]) * kLog2e;
+    sPart[hg * DK + c] = tot;
+    __syncthreads();
+    if (tid < DK) {
+      float x = 0.f;
+      for (int h2 = 0; h2 < NH; ++h2) x += sPart[h2 * DK + tid];
+      sMx[tid] = -x;
+    }
+    __syncthreads();
+    float mx = 0.f;
+    for (int i = 0; i < DK; ++i) mx = fmaxf(mx, sMx[i]);
+    if (!(mx > 2.f * kFastPathMaxDecay2 - 10.f)) {  // (uniform; a NaN total is redone too)
+      __syncthreads();
+      continue;
+    }
+    // ---- stage 1: dense products
+    const char* un = ws + u * LB.bytes;
+    for (int x = tid; x < (DV / 16) * (DK / 16) * 64; x += NT) {  // S0, dSn tiles (ct, channel tile)
+      const int tile = x / 64, ln = x % 64, ct = tile / (DK / 16), w = tile % (DK / 16);
+      const bf16x4 a = *reinterpret_cast<const bf16x4*>(un + LB.h + (tile * 64 + ln) * 8);
+      const bf16x4 d = *reinterpret_cast<const bf16x4*>(un + LB.db + (tile * 64 + ln) * 8);
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * w + 4 * (ln >> 4) + i, col = 16 * ct + (ln & 15);
+        sS0[row * LDV + col] = a[i];
+        sdS[row * LDV + col] = d[i];
+      }
+    }
+    for (int x = tid; x < (DV / 16) * 4 * 64; x += NT) {  // U, dZ tiles (ct, token block)
+      const int tile = x / 64, ln = x % 64, ct = tile / 4, R = tile % 4;
+      const bf16x4 a = *reinterpret_cast<const bf16x4*>(un + LB.ub + (tile * 64 + ln) * 8);
+      const bf16x4 d = *reinterpret_cast<const bf16x4*>(un + LB.zb + (tile * 64 + ln) * 8);
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * R + 4 * (ln >> 4) + i, col = 16 * ct + (ln & 15);
+        const bool ok = row < cu.nvalid;
+        sU[row * LDV + col] = ok ? a[i] : static_cast<bf16>(0.f);
+        sZ[row * LDV + col] = ok ? d[i] : static_cast<bf16>(0.f);
+      }
+    }
+    for (int x = tid; x < C * DV; x += NT) {
+      const int t = x / DV, v = x % DV;
+      sO[t * LDV + v] = t < cu.nvalid ? d_o[vb0 + (long)t * vstride + v] : static_cast<bf16>(0.f);
+    }
+    __syncthreads();
+    float dOS[TPH], dZS[TPH], dKt[TPH], X = 0.f;
+    for (int j = 0; j < TPH; ++j) dOS[j] = dZS[j] = dKt[j] = 0.f;
+    for (int v = 0; v < DV; ++v) {
+      const float s0 = static_cast<float>(sS0[c * LDV + v]), ds = static_cast<float>(sdS[c * LDV + v]);
+      X += ds * s0;
+      for (int j = 0; j < TPH; ++j) {
+        const int t = t0 + j;
+        dOS[j] += s0 * static_cast<float>(sO[t * LDV + v]);
+        dZS[j] += s0 * static_cast<float>(sZ[t * LDV + v]);
+        dKt[j] += ds * static_cast<float>(sU[t * LDV + v]);
+      }
+    }
+    for (int e = tid; e < C * C; e += NT) {
+      const int r = e / C, i = e % C;
+      float m1 = 0.f, m2 = 0.f;
+      if (i <= r) {
+        for (int v = 0; v < DV; ++v) {
+          const float uu = static_cast<float>(sU[i * LDV + v]);
+          m1 += static_cast<float>(sO[r * LDV + v]) * uu;
+          m2 += static_cast<float>(sZ[r * LDV + v]) * uu;
+        }
+      }
+      sM1[r * LDM + i] = m1;
+      sM2[r * LDM + i] = i < r ? -m2 : 0.f;
+    }
+    __syncthreads();
+    // ---- stage 2: q, k, b and the clamped cumulative decay G (log2) of every token
+    float gs[TPH];
+    float run = 0.f;
+    for (int j = 0; j < TPH; ++j) {
+      const int t = t0 + j;
+      const bool ok = t < cu.nvalid;
+      const long off = kb0 + (long)t * kstride + c;
+      sq[t * DK + c] = ok ? q[off] : static_cast<bf16>(0.f);
+      sk[t * DK + c] = ok ? k[off] : static_cast<bf16>(0.f);
+      if constexpr (B_S) sb[t * DK + c] = ok ? bg[(cu.row + t) * H + cu.h] : static_cast<bf16>(0.f);
+      else sb[t * DK + c] = ok ? bg[off] : static_cast<bf16>(0.f);
+      run += ok ? fmaxf(static_cast<float>(g[off]) * kLog2e, -256.f) : 0.f;
+      gs[j] = run;
+    }
+    sPart[hg * DK + c] = run;
+    if (tid < C) sDb[tid] = 0.f;
+    __syncthreads();
+    float pre = 0.f;
+    for (int h2 = 0; h2 < hg; ++h2) pre += sPart[h2 * DK + c];
+    for (int j = 0; j < TPH; ++j) sG[(t0 + j) * DK + c] = gs[j] + pre;
+    __syncthreads();
+    // ---- stage 3: pairwise sums, dq, dk, db and the terms of dg
+    const float Gl = sG[(C - 1) * DK + c];
+    float amb[TPH], totB = 0.f;
+    for (int j = 0; j < TPH; ++j) {
+      const int t = t0 + j;
+      const float Gt = sG[t * DK + c];
+      const float pt = fast_exp2(Gt);
+      float dqv = pt * dOS[j], de = -pt * dZS[j];
+      for (int i = 0; i <= t; ++i) {
+        const float kw = static_cast<float>(sk[i * DK + c]) * fast_exp2(Gt - sG[i * DK + c]);
+        dqv += sM1[t * LDM + i] * kw;
+        de += sM2[t * LDM + i] * kw;  // (zero at i = t)
+      }
+      float dkh = 0.f;
+      for (int r = t; r < C; ++r) {
+        const float w = fast_exp2(sG[r * DK + c] - Gt);
+        const float er = static_cast<float>(sb[r * DK + c]) * static_cast<float>(sk[r * DK + c]);
+        dkh += (sM2[r * LDM + t] * er + sM1[r * LDM + t] * static_cast<float>(sq[r * DK + c])) * w;
+      }
+      const float qt = static_cast<float>(sq[t * DK + c]), kt = static_cast<float>(sk[t * DK + c]);
+      const float bt = static_cast<float>(sb[t * DK + c]);
+      const float sf = fast_exp2(Gl - Gt);
+      const float dkv = dkh + dKt[j] * sf + de * bt;
+      const float dbv = de * kt;
+      amb[j] = de * bt * kt + dqv * qt - dkh * kt - dKt[j] * kt * sf;
+      totB += dKt[j] * kt * sf;
+      if (t < cu.nvalid) {
+        const long off = kb0 + (long)t * kstride + c;
+        dq[off] = from_f<bf16>(dqv);
+        dk[off] = from_f<bf16>(dkv);
+        if constexpr (!B_S) db[off] = from_f<bf16>(dbv);
+      }
+      if constexpr (B_S) atomicAdd(&sDb[t], dbv);
+    }
+    // ---- stage 4: dg by suffix sums over the chunk
+    float suf = 0.f;
+    for (int j = TPH - 1; j >= 0; --j) { suf += amb[j]; amb[j] = suf; }
+    __syncthreads();  // (sPart's decay totals are read)
+    sPart[hg * DK + c] = suf;
+    if (hg == 0) sTB[c] = 0.f;
+    __syncthreads();
+    atomicAdd(&sTB[c], totB);
+    __syncthreads();
+    float after = 0.f;
+    for (int h2 = hg + 1; h2 < NH; ++h2) after += sPart[h2 * DK + c];
+    const float base = sTB[c] + fast_exp2(Gl) * X + after;
+    for (int j = 0; j < TPH; ++j) {
+      const int t = t0 + j;
+      if (t < cu.nvalid) dg[kb0 + (long)t * kstride + c] = from_f<bf16>(amb[j] + base);
+    }
+    if constexpr (B_S) {
+      if (tid < cu.nvalid) db[(cu.row + tid) * H + cu.h] = from_f<bf16>(sDb[tid]);
+    }
+    __syncthreads();  // this unit's LDS readers are done
+  }
+}
+
 // ------------------------------------------------------------------ launch
 template <int DK, int DV>
 static hipError_t launch_bwd(const BwdArgs& a) {
@@ -846,6 +1064,15 @@ static hipError_t launch_bwd(const BwdArgs& a) {
                        (const bf16*)a.d_o, (const char*)f.workspace, (bf16*)a.dq, (bf16*)a.dk,
                        (bf16*)a.dv, (bf16*)a.dg, (bf16*)a.db, (bf16*)a.dw, a.range_flag,
                        f.cu_seqlens, f.N, f.T, f.H, nunits);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // units past the local kernel's decay range (rare): exact recomputation
+    auto exact = f.gate_flags & kGateBScalar ? gdn2_bwd_exact_kernel<DK, DV, kGateBScalar>
+                                             : gdn2_bwd_exact_kernel<DK, DV, 0>;
+    hipLaunchKernelGGL(exact, dim3((unsigned)grid), dim3(256), 0, st, (const bf16*)f.q,
+                       (const bf16*)f.k, (const bf16*)f.g, (const bf16*)f.b, (const bf16*)a.d_o,
+                       (const char*)f.workspace, (bf16*)a.dq, (bf16*)a.dk, (bf16*)a.dg,
+                       (bf16*)a.db, a.range_flag, f.cu_seqlens, f.N, f.T, f.H, nunits);
     e = hipGetLastError();
   }
   return e;

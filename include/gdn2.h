@@ -170,12 +170,14 @@ size_t gdn2_chunk_fwd_workspace_bytes(int B, int T, int H, int d_k, int d_v, int
  *   dq, dk, dlog_alpha, db : [B, T, H, d_k] (dtype), written
  *   dv, dw            : [B, T, H, d_v] (dtype), written
  *   d_initial_state   : [N, H, d_k, d_v] fp32, or NULL (not written)
- *   range_flag        : NULL, or a device int32 that the call sets to 1 (and otherwise leaves
- *                       alone) when some chunk's total decay, in some key channel, exceeds
- *                       the range of the backward's factors (referenced to the middle of
- *                       each channel's decay over the chunk: about 166 nats over 64 tokens);
- *                       the gradients of such chunks are not valid. The caller clears it
- *                       beforehand and checks it afterwards.
+ *   range_flag        : NULL, or a device int32 that the caller clears beforehand. The call
+ *                       sets it to 1 when some chunk's total decay, in some key channel,
+ *                       exceeds the range of the local-gradient kernel's factors (referenced
+ *                       to the middle of each channel's decay over the chunk: about 166 nats
+ *                       over 64 tokens); a second kernel then recomputes those chunks'
+ *                       gradients with exact pairwise decay factors, so the result is valid
+ *                       for any decay either way. The second kernel reads the flag to skip
+ *                       its scan when no chunk is out of range (with NULL it always scans).
  *   workspace         : required, at least gdn2_chunk_bwd_workspace_bytes(...) bytes, 16-byte
  *                       aligned, free for the call's duration on `hip_stream`.
  *   Supported: GDN2_BF16 with d_k, d_v in {64, 128}.

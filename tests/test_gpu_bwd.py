@@ -124,14 +124,36 @@ def test_bwd_near_resets():
     check(x, do, dsn)
 
 
-def test_bwd_range_flag():
-    import gated_delta_rule_36_amd as G
-    x = make_inputs(1, 128, 1, 64, 64, "bf16", seed=314)
-    x["g"][:, 64:] = -5.0  # the second chunk decays by 320 nats
-    do, _ = _upstream(x, 10, with_dsn=False)
-    say("bwd range flag")
-    with pytest.raises(G.Gdn2RangeError):
-        run_bwd(x, do, None)
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128)])
+@pytest.mark.parametrize("case", ["chunk_g-5", "chunk_g-8", "block_g-8", "token_g-300"])
+def test_bwd_past_local_range(case, dk, dv):
+    """Chunks past the local-gradient kernel's factor range (166 nats per channel over 64
+    tokens), recomputed by the exact kernel: g = -5 or -8 on every token of the second chunk
+    (320 or 512 nats), g = -8 on one aligned 16-token block plus -3 on the rest of its chunk
+    (224 nats), two tokens at -300 (alpha underflows fp32); a ragged last chunk and an
+    initial state."""
+    x = make_inputs(1, 200, 2, dk, dv, "bf16", seed=318 + dk, s0_std=0.02)
+    if case == "chunk_g-5":
+        x["g"][:, 64:128] = -5.0
+    elif case == "chunk_g-8":
+        x["g"][:, 64:128] = -8.0
+    elif case == "block_g-8":
+        x["g"][:, 64:128] = -3.0
+        x["g"][:, 80:96] = -8.0
+    else:
+        x["g"][:, 100:102] = -300.0
+    do, dsn = _upstream(x, 15)
+    say("bwd past the local range", case, dk, dv)
+    check(x, do, dsn)
+
+
+def test_bwd_past_local_range_varlen():
+    lens = [70, 1, 130, 0, 99]
+    x = make_inputs(1, sum(lens), 2, 128, 64, "bf16", seed=319, lengths=lens, s0_std=0.02)
+    x["g"][:, 80:140] = -6.0  # spans the third sequence's first chunk
+    do, dsn = _upstream(x, 16)
+    say("bwd past the local range, varlen")
+    check(x, do, dsn)
 
 
 @pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64)])

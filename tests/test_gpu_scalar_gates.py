@@ -156,13 +156,19 @@ def test_backward_scalar_gates(layout, saved, T):
         assert_close(name, host64(a), r, TOL["bf16"])
 
 
-def test_backward_scalar_gates_varlen():
+@pytest.mark.parametrize("strong_decay", [False, True])
+def test_backward_scalar_gates_varlen(strong_decay):
+    """Packed sequences with both gates scalar; with strong_decay, g = -6 on 70 tokens that
+    span the fourth sequence's first chunk (past the local-gradient kernel's factor range,
+    so its gradients come from the exact kernel and its scalar-b channel sums)."""
     import gated_delta_rule_36_amd as G
     from gdn2_inputs import round_to_bf16
     from oracle import gdn2_backward
     lens = [1, 64, 0, 100, 33]
     T = sum(lens)
     x = make_inputs(1, T, 2, 64, 128, "bf16", seed=71, lengths=lens, s0_std=0.02)
+    if strong_decay:
+        x["g"][:, 65:135] = -6.0
     gx, rx = _scalarise(x, "bw", (1, T, 2), seed=73)
     rng = np.random.default_rng(75)
     do = round_to_bf16(rng.normal(size=(1, T, 2, 128)).astype(np.float32))
