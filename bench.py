@@ -237,7 +237,8 @@ def main():
         del src, dst
 
     ws_bytes = G.workspace_bytes(B, T, H, dk, dv, N)
-    use_split = G.uses_split(B, T, N, ws_bytes, args.path, args.value_slice)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    use_split = G.uses_split(B, T, N, H, dv, ws_bytes, args.path, args.value_slice, cus)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if use_split else None
 
     def step():
@@ -471,7 +472,9 @@ def main():
         vbytes = fwd_bytes(1, TV, H, dk, dv, NV_, read_s0=True)
         out["varlen"] = {
             "workload": f"{NV_} packed sequences of 512..8192 tokens ({TV} in all), H=16, "
-                        "d_k=d_v=128, bf16, initial states N(0, 0.02^2); path auto (two-phase)",
+                        "d_k=d_v=128, bf16, initial states N(0, 0.02^2); path auto ("
+                        + ("two-phase" if G.uses_split(1, TV, NV_, H, dv, 1, "auto", 0, cus)
+                           else "fused, longest sequences first") + ")",
             "ms_per_call": round(vms, 4), "tokens_per_s": round(TV / (vms * 1e-3), 1),
             "vs_headline_tokens_per_s": round(TV / (vms * 1e-3) / out["value"], 3),
             "algorithmic_bytes": vbytes,

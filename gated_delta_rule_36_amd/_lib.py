@@ -21,7 +21,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
-_SPLIT_MIN_AVG_TOKENS = 40 * 64  # "auto" picks the two-phase path from this average length
+_SPLIT_MIN_AVG_TOKENS = 1024  # "auto" takes the two-phase path only past this average length
 _Z = ctypes.c_size_t
 
 
@@ -136,10 +136,29 @@ def workspace_bytes(B, T, H, dk, dv, N, dtype=torch.bfloat16):
     return int(lib().gdn2_chunk_fwd_workspace_bytes(B, T, H, dk, dv, N, _dtype_code(dtype)))
 
 
-def uses_split(B, T, N, need, path="auto", value_slice=0):
-    """Whether chunk_fwd runs the two-phase path (`need`: its workspace bytes, 0 if unbuilt)."""
-    long_seqs = N > 0 and B * T >= N * _SPLIT_MIN_AVG_TOKENS
-    return need > 0 and not value_slice and (path == "split" or (path == "auto" and long_seqs))
+def uses_split(B, T, N, H, dv, need, path="auto", value_slice=0, cus=256):
+    """Whether chunk_fwd runs the two-phase path (`need`: its workspace bytes, 0 if unbuilt;
+    `cus`: compute units of the device).
+
+    "auto" takes it when the fused kernel would leave most of the GPU idle: its workgroups
+    (one per sequence, head and 64 value columns) number at most a third of the compute
+    units, and the sequences average more than 1024 tokens (shorter ones run as fast fused).
+    Measured on MI355X (H = 16, d = 128): 64 workgroups (2 x 8192 tokens) 0.33 ms two-phase
+    against 0.54 ms fused; 96 (3 x 4096) 0.34 against 0.27; 512 (16 packed sequences,
+    79,750 tokens) 1.35 against 0.83."""
+    chains = N * H * max(1, dv // 64)
+    few_long = N > 0 and 3 * chains <= cus and B * T > N * _SPLIT_MIN_AVG_TOKENS
+    return need > 0 and not value_slice and (path == "split" or (path == "auto" and few_long))
+
+
+_CUS = {}
+
+
+def _cu_count(dev) -> int:
+    i = dev.index if dev.index is not None else torch.cuda.current_device()
+    if i not in _CUS:
+        _CUS[i] = torch.cuda.get_device_properties(i).multi_processor_count
+    return _CUS[i]
 
 
 def chunk_fwd(q, k, v, g, b, w, initial_state=None, cu_seqlens=None,
@@ -152,7 +171,8 @@ def chunk_fwd(q, k, v, g, b, w, initial_state=None, cu_seqlens=None,
     cu_seqlens: int32 [N+1] on the device (packed batch, B == 1) or None (N = B).
     path: "split" (two-phase: parallel chunk factors into a workspace, then the per-sequence
     recurrence), "fused" (one kernel per sequence, no workspace) or "auto" (split for bf16
-    when sequences average at least 2560 tokens, else fused). value_slice selects the fused
+    when the fused kernel's workgroups would number at most a third of the compute units
+    and sequences average more than 1024 tokens, else fused). value_slice selects the fused
     kernel's value-slice width.
     workspace: optional uint8 device tensor reused across calls (allocated when None).
     Returns (o [B, T, H, d_v] in the input dtype, final_state [N, H, d_k, d_v] fp32 or None).
@@ -186,10 +206,10 @@ def chunk_fwd(q, k, v, g, b, w, initial_state=None, cu_seqlens=None,
         raise ValueError("the two-phase path is built for bf16 with d_k, d_v in {64, 128}")
     if value_slice and path == "split":
         raise ValueError("value_slice applies to the fused path")
-    # auto: the two-phase path pays where sequences are long (its recurrence kernel has the
-    # shorter sequential step); with many short sequences the fused kernel is as fast and
-    # moves less data (measured crossover: about 40 chunks of 64 tokens per sequence)
-    use_split = uses_split(B, T, N, need, path, value_slice)
+    # auto: the two-phase path pays where a few long sequences would leave most CUs idle
+    # under the fused kernel (its segments run in parallel); otherwise the fused kernel is
+    # faster and moves less data
+    use_split = uses_split(B, T, N, H, dv, need, path, value_slice, _cu_count(dev))
     if use_split:
         if workspace is None or workspace.numel() < need:
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)

@@ -285,6 +285,9 @@ __device__ __forceinline__ void tinv_block(const float* sAdb, const float* sId, 
   }
 }
 
+// Packed batches of up to this many sequences are started longest first.
+constexpr int kOrderMaxSeqs = 1024;
+
 template <int DK, int GL>
 __global__ void __launch_bounds__(512)
 gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
@@ -343,7 +346,34 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int slice = gi / gsz;
   const int nh = grp * 8 + gi % gsz;
   const int h = nh % H;
-  const int n = nh / H;
+  int n = nh / H;
+  if (cu_seqlens != nullptr && nunits / H <= kOrderMaxSeqs) {
+    // Packed batch: workgroups start in id order, so ids go to sequences longest first (ties
+    // by index) and the longest chains do not wait for a second round of workgroups. The
+    // rank of each sequence is counted in LDS, which the chunk loop has not used yet.
+    static_assert(Sh::LDS_BYTES >= 4 * (kOrderMaxSeqs + 1), "sequence order table");
+    const int nseq = nunits / H;
+    int* const sLen = reinterpret_cast<int*>(smem);
+    for (int i = tid; i < nseq; i += 512) {
+      int a = cu_seqlens[i], b = cu_seqlens[i + 1];
+      a = a < 0 ? 0 : (a > T_len ? T_len : a);
+      b = b < a ? a : (b > T_len ? T_len : b);
+      sLen[i] = b - a;
+    }
+    __syncthreads();
+    for (int i = tid; i < nseq; i += 512) {
+      const int li = sLen[i];
+      int r = 0;
+      for (int j = 0; j < nseq; ++j) {
+        const int lj = sLen[j];
+        r += (lj > li || (lj == li && j < i)) ? 1 : 0;
+      }
+      if (r == n) sLen[nseq] = i;  // ranks are a permutation: exactly one sequence matches
+    }
+    __syncthreads();
+    n = __builtin_amdgcn_readfirstlane(sLen[nseq]);
+    __syncthreads();
+  }
   const int col0 = slice * Sh::NV;
 
   long row0;

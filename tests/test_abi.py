@@ -250,3 +250,21 @@ def test_noalloc_rejects_sizes_beyond_its_scratch():
     assert b"scratch" in L.gdn2_status_string(3)
     assert L.gdn2_chunk_fwd_noalloc(*args, 1, 64, 2, 64, 64, 1, 1, 0, None) == 2
     assert L.gdn2_chunk_fwd_noalloc(*args, 1, 64, 0, 64, 64, 1, 0, 0, None) == 1
+
+
+def test_auto_path_rule():
+    # "auto" takes the two-phase path only where the fused kernel's workgroups (sequence x
+    # head x 64 value columns) number at most a third of the CUs and sequences are long
+    from gated_delta_rule_36_amd import uses_split
+    need = 1
+    assert uses_split(1, 32768, 1, 16, 128, need)            # 32 workgroups
+    assert uses_split(2, 8192, 2, 16, 128, need)             # 64
+    assert not uses_split(3, 4096, 3, 16, 128, need)         # 96
+    assert not uses_split(8, 2048, 8, 16, 128, need)         # the 1.3B-layer batch
+    assert not uses_split(1, 79750, 16, 16, 128, need)       # 16 packed sequences
+    assert not uses_split(1, 1024, 1, 16, 128, need)         # short
+    assert uses_split(1, 4096, 1, 16, 64, need, cus=48)      # 16 workgroups on 48 CUs
+    assert not uses_split(1, 32768, 1, 16, 128, 0)           # two-phase path not built
+    assert not uses_split(1, 32768, 1, 16, 128, need, value_slice=64)
+    assert uses_split(8, 2048, 8, 16, 128, need, path="split")
+    assert not uses_split(1, 32768, 1, 16, 128, need, path="fused")
