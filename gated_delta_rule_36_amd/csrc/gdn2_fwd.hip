@@ -286,7 +286,7 @@ __device__ __forceinline__ void tinv_block(const float* sAdb, const float* sId, 
 }
 
 // Packed batches of up to this many sequences are started longest first.
-constexpr int kOrderMaxSeqs = 1024;
+constexpr int kOrderMaxSeqs = 256;
 
 template <int DK, int GL>
 __global__ void __launch_bounds__(512)
@@ -349,29 +349,42 @@ gdn2_fwd_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   int n = nh / H;
   if (cu_seqlens != nullptr && nunits / H <= kOrderMaxSeqs) {
     // Packed batch: workgroups start in id order, so ids go to sequences longest first (ties
-    // by index) and the longest chains do not wait for a second round of workgroups. The
-    // rank of each sequence is counted in LDS, which the chunk loop has not used yet.
-    static_assert(Sh::LDS_BYTES >= 4 * (kOrderMaxSeqs + 1), "sequence order table");
+    // by index) and the longest chains do not wait for a second round of workgroups. Each
+    // sequence's rank is counted in LDS (which the chunk loop has not used yet) by two lanes,
+    // each over half of the length table (padded with -1, shorter than any sequence).
+    static_assert(Sh::LDS_BYTES >= 4 * (kOrderMaxSeqs + 1) && kOrderMaxSeqs * 2 <= 512,
+                  "sequence order table");
     const int nseq = nunits / H;
+    const int npad = (nseq + 7) & ~7;
     int* const sLen = reinterpret_cast<int*>(smem);
-    for (int i = tid; i < nseq; i += 512) {
-      int a = cu_seqlens[i], b = cu_seqlens[i + 1];
-      a = a < 0 ? 0 : (a > T_len ? T_len : a);
-      b = b < a ? a : (b > T_len ? T_len : b);
-      sLen[i] = b - a;
-    }
-    __syncthreads();
-    for (int i = tid; i < nseq; i += 512) {
-      const int li = sLen[i];
-      int r = 0;
-      for (int j = 0; j < nseq; ++j) {
-        const int lj = sLen[j];
-        r += (lj > li || (lj == li && j < i)) ? 1 : 0;
+    if (tid < npad) {
+      int l = -1;
+      if (tid < nseq) {
+        int a = cu_seqlens[tid], b = cu_seqlens[tid + 1];
+        a = a < 0 ? 0 : (a > T_len ? T_len : a);
+        b = b < a ? a : (b > T_len ? T_len : b);
+        l = b - a;
       }
-      if (r == n) sLen[nseq] = i;  // ranks are a permutation: exactly one sequence matches
+      sLen[tid] = l;
     }
     __syncthreads();
-    n = __builtin_amdgcn_readfirstlane(sLen[nseq]);
+    const int i = tid >> 1, part = tid & 1;
+    int r = 0;
+    if (i < nseq) {
+      const int li = sLen[i];
+      const int j0 = part * (npad / 2);
+      const int4* row = reinterpret_cast<const int4*>(sLen + j0);
+      for (int x = 0; x < npad / 8; ++x) {
+        const int4 v = row[x];
+        const int j = j0 + 4 * x;
+        r += (v.x > li || (v.x == li && j < i)) + (v.y > li || (v.y == li && j + 1 < i)) +
+             (v.z > li || (v.z == li && j + 2 < i)) + (v.w > li || (v.w == li && j + 3 < i));
+      }
+    }
+    r += __shfl_xor(r, 1, 64);
+    if (i < nseq && part == 0 && r == n) sLen[npad] = i;  // ranks are a permutation
+    __syncthreads();
+    n = __builtin_amdgcn_readfirstlane(sLen[npad]);
     __syncthreads();
   }
   const int col0 = slice * Sh::NV;
