@@ -33,6 +33,15 @@
 
 namespace gdn2 {
 
+// 16 bytes at byte offset `off` from `base` (uniform), non-temporal (the `nt` policy bit):
+// for data one workgroup reads once, so that it streams through the caches instead of
+// displacing what neighbouring workgroups share in L2.
+__device__ __forceinline__ uint4 load16_nt(const void* base, int off) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7ffffff0, 0x00020000);
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
+
 // ------------------------------------------------------------------ the recurrence
 template <int DK, int DV, int NV>
 struct ChainShape {
@@ -162,9 +171,12 @@ gdn2_bwd_chain_kernel(char* __restrict__ ws, const bf16* __restrict__ d_o,
 #pragma unroll
     for (int j = 0; j < Sh::PPD; ++j) {
       const int p = tid + j * NT, r = p / (NV / 8), cc = p % (NV / 8);
-      const T* src = d_o + (row0 + (long)ci * C + (r < nvalid ? r : 0)) * vstride +
-                     (long)h * DV + col0 + cc * 8;
-      const u32x4 x = *reinterpret_cast<const u32x4*>(src);
+      // this slice's dO columns are read by this workgroup alone: non-temporal (measured
+      // 0.790 -> 0.766 ms per backward call on the 1.3B-layer workload), while the factor
+      // pieces, which the head's other slice reads too, stay cached
+      const T* src0 = d_o + (row0 + (long)ci * C) * vstride + (long)h * DV + col0;
+      const u32x4 x = __builtin_bit_cast(
+          u32x4, load16_nt(src0, (int)(((r < nvalid ? r : 0) * vstride + cc * 8) * 2)));
       std_[j] = r < nvalid ? x : u32x4{0u, 0u, 0u, 0u};
     }
   };
