@@ -303,6 +303,23 @@ __device__ __forceinline__ void hold(bf16x4& x, float after) {
   asm volatile("" : "+v"(x) : "v"(after));
 }
 
+// Sums along the 16-lane rows of a wave (lanes 16r .. 16r + 15) with DPP row operations, in
+// registers: row_suffix gives lane i the sum over lanes i .. 15 of its row (lanes shifted in
+// from past the row's end read 0), row_first the value of its row's lane 0.
+template <int N>
+__device__ __forceinline__ float row_shl(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x100 + N, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float row_suffix(float x) {
+  x += row_shl<1>(x);
+  x += row_shl<2>(x);
+  x += row_shl<4>(x);
+  x += row_shl<8>(x);
+  return x;
+}
+__device__ __forceinline__ float row_first(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150, 0xf, 0xf, false));
+}
 template <int DK, int DV>
 struct LocalShape {
   static constexpr int C = 64;
@@ -588,9 +605,7 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         xs += tof(rds[ct]) * s0;
       }
   #pragma unroll
-      for (int m = 1; m < 16; m <<= 1)
-  #pragma unroll
-        for (int i = 0; i < 4; ++i) xs[i] += __shfl_xor(xs[i], m, 64);
+      for (int i = 0; i < 4; ++i) xs[i] = row_suffix(xs[i]);  // lane 0 of the row: the row's sum
       if (m16 == 0) *reinterpret_cast<f4*>(sX + 16 * wave + 4 * g4) = xs;
     }
     // dv = dZ * w, dw = dZ * v
@@ -767,24 +782,17 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     issue_first(u_pre);
     // dg_t = sum_{t' >= t} (A - B)_{t'} + sum_all B + gamma X   (suffix sums over 64 tokens)
   #pragma unroll
-    for (int m = 1; m < 16; m <<= 1)
-  #pragma unroll
-      for (int i = 0; i < 4; ++i) totB[i] += __shfl_xor(totB[i], m, 64);
+    for (int i = 0; i < 4; ++i) totB[i] = row_first(row_suffix(totB[i]));
     f4 carry = totB + gam * xc;
   #pragma unroll
     for (int Tt = 3; Tt >= 0; --Tt) {
       f4 x = dgv[Tt];
-  #pragma unroll
-      for (int d = 1; d < 16; d <<= 1) {
-  #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float y = __shfl_down(x[i], d, 16);
-          x[i] += (m16 + d < 16) ? y : 0.f;
-        }
-      }
       f4 tile_tot;
   #pragma unroll
-      for (int i = 0; i < 4; ++i) tile_tot[i] = __shfl(x[i], lane & ~15, 64);
+      for (int i = 0; i < 4; ++i) {
+        x[i] = row_suffix(x[i]);
+        tile_tot[i] = row_first(x[i]);
+      }
       const int t = 16 * Tt + m16;
       if (t < cu.nvalid) put4(dg, kb0 + (long)t * kstride + c0, x + carry);
       carry += tile_tot;
