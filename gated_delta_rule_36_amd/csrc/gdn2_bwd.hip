@@ -377,6 +377,7 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   using Sh = LocalShape<DK, DV>;
   using M = Mma<T>;
   constexpr bool B_S = (GL & kGateBScalar) != 0, W_S = (GL & kGateWScalar) != 0;
+  constexpr bool early_dsn = !(B_S && W_S);  // see the elementwise step
   constexpr BwdLayout LB(DK, DV);
   constexpr int C = Sh::C, NT = Sh::NT, LDV = Sh::LDV, LDK = Sh::LDK, LDT = Sh::LDT;
   constexpr int NVT = Sh::NVT;
@@ -401,8 +402,10 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const long kstride = (long)H * DK, vstride = (long)H * DV;
   // The workgroups are persistent (one per compute unit) and walk the units u = blockIdx.x,
   // + gridDim.x, ... Every global read of a unit is issued before it is needed, in two
-  // groups: the workspace tiles dZ, U, dSn (for the matrix work P1, P2), issued at the end
-  // of the previous unit; then dO; g, k; S0; v, w; q, b, issued at the start of the unit,
+  // groups: the workspace tiles dZ, U, dSn (for the matrix work P1, P2), issued during the
+  // previous unit (dSn before its elementwise step, dZ and U after its gradient stores, so
+  // that they do not queue behind them); then dO; g, k; S0; v, w; q, b, issued at the start
+  // of the unit,
   // the later ones arriving while P1, P2 run. Every load is unconditional (a row
   // past the unit's end reads row 0 and is zeroed where it is first used; past the last
   // unit the current one is read again), which keeps the waits on the early groups exact.
@@ -415,15 +418,22 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   };
   auto tof = [](bf16x4 x) { return f4{to_f(x[0]), to_f(x[1]), to_f(x[2]), to_f(x[3])}; };
   bf16x4 rz[NZU], ru[NZU], rds[NVT];
-  auto issue_first = [&](long uu) {
+  auto issue_first_a = [&](long uu) {  // dSn
+    const char* un = ws + uu * LB.bytes;
+#pragma unroll
+    for (int ct = 0; ct < NVT; ++ct) rds[ct] = tile_raw(un, LB.db, ct * Sh::NCT + wave);
+  };
+  auto issue_first_b = [&](long uu) {  // dZ and U
     const char* un = ws + uu * LB.bytes;
 #pragma unroll
     for (int i = 0; i < NZU; ++i) {
       rz[i] = tile_raw(un, LB.zb, wave + i * Sh::NW);
       ru[i] = tile_raw(un, LB.ub, wave + i * Sh::NW);
     }
-#pragma unroll
-    for (int ct = 0; ct < NVT; ++ct) rds[ct] = tile_raw(un, LB.db, ct * Sh::NCT + wave);
+  };
+  auto issue_first = [&](long uu) {
+    issue_first_b(uu);
+    issue_first_a(uu);
   };
   long u = blockIdx.x;
   ChunkUnit cu = map_unit(u, H, cu_seqlens, N, T_len, lane);
@@ -726,6 +736,9 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }
     lds_barrier();
 
+    // the next unit's dSn tiles (this unit's are consumed); with both gates scalar the
+    // registers are short here, and they are issued with dZ and U after the stores
+    if constexpr (early_dsn) issue_first_a(u_pre);
     // ---- elementwise: lane = token 16*Tt + m16, channels c0 .. c0 + 3 of this wave
     const int c0 = 16 * wave + 4 * g4;
     const f4 gam = *reinterpret_cast<const f4*>(sFac + Fac::GAM * DK + c0);
@@ -779,7 +792,8 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }
     // the next unit's first load group, in flight from here on
     const ChunkUnit cn = map_unit(u_pre, H, cu_seqlens, N, T_len, lane);
-    issue_first(u_pre);
+    if constexpr (early_dsn) issue_first_b(u_pre);
+    else issue_first(u_pre);
     // dg_t = sum_{t' >= t} (A - B)_{t'} + sum_all B + gamma X   (suffix sums over 64 tokens)
   #pragma unroll
     for (int i = 0; i < 4; ++i) totB[i] = row_first(row_suffix(totB[i]));
