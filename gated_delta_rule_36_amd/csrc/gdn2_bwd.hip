@@ -340,7 +340,8 @@ struct LocalShape {
   static constexpr int SZ_A = DK * LDV * 2;     // dSn, later S0: [DK][DV]
   static constexpr int SZ_R = C * LDV * 2;      // dO, dZ, U: [64][DV]
   static constexpr int SZ_ET = 2 * DK * LDT * 2;  // Ebar^T, Qbar^T
-  static constexpr int SZ_EL = C * DK * 4 + 3 * C * LDK * 2;  // G (fp32), q, k, b
+  static constexpr int LDG = DK + 16;  // G rows: 16 words of padding (conflict-free row reads)
+  static constexpr int SZ_EL = C * LDG * 4 + 3 * C * LDK * 2;  // G (fp32), q, k, b
   static constexpr int SZ_BIG0 = SZ_A + 3 * SZ_R;
   static constexpr int SZ_BIG = SZ_BIG0 > SZ_EL ? (SZ_BIG0 > SZ_ET ? SZ_BIG0 : SZ_ET)
                                                 : (SZ_EL > SZ_ET ? SZ_EL : SZ_ET);
@@ -723,13 +724,13 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     lds_barrier();  // everything but the factors is dead
     // G (log2, fp32) and q, k, b row-major for the elementwise step
     float* sG = reinterpret_cast<float*>(smem);
-    T* sq = reinterpret_cast<T*>(smem + C * DK * 4);
+    T* sq = reinterpret_cast<T*>(smem + C * Sh::LDG * 4);
     T* sk = sq + C * LDK;
     T* sb = sk + C * LDK;
   #pragma unroll
     for (int j = 0; j < Sh::TPT; ++j) {
       const int r = tg * Sh::TPT + j;
-      store8(sG + r * DK + cg * 8, G2[j]);
+      store8(sG + r * Sh::LDG + cg * 8, G2[j]);
       *reinterpret_cast<uint4*>(sq + r * LDK + cg * 8) = rq[j].r;
       *reinterpret_cast<uint4*>(sk + r * LDK + cg * 8) = rk[j].r;
       *reinterpret_cast<uint4*>(sb + r * LDK + cg * 8) = rb[j].r;
@@ -755,7 +756,7 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   #pragma unroll
     for (int Tt = 0; Tt < 4; ++Tt) {
       const int t = 16 * Tt + m16;
-      const f4 G = *reinterpret_cast<const f4*>(sG + t * DK + c0);
+      const f4 G = *reinterpret_cast<const f4*>(sG + t * Sh::LDG + c0);
       const f4 fq = load4f(sq + t * LDK + c0), fk = load4f(sk + t * LDK + c0);
       const f4 fb = load4f(sb + t * LDK + c0);
       f4 A, Bv, outq, outk, outb;
