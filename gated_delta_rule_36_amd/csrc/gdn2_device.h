@@ -231,6 +231,12 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v{a, b}), bf16x2));
 }
 
+// The value held by the neighbouring lane (lane ^ 1), by a DPP quad permutation [1,0,3,2]
+// (a register operation, no LDS round trip).
+__device__ __forceinline__ float lane_swap1(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xf, 0xf, false));
+}
+
 // Store a 16x16 D tile (lane: column l%16, rows 4g..4g+3) into a row-major [row][col]
 // array with 2-element stores: neighbouring lanes swap two rows so that each lane writes
 // (row, cols 2j..2j+1) pairs; no two lanes share an LDS dword. `colmap` maps the tile's
@@ -243,7 +249,7 @@ __device__ __forceinline__ void store_tile_pairs(T* base, int ld, int lane, f4 v
   // even lane keeps rows 4g, 4g+1 and receives them from the odd neighbour;
   // odd lane keeps rows 4g+2, 4g+3 and receives them from the even neighbour
   const float s0 = odd ? v[0] : v[2], s1 = odd ? v[1] : v[3];
-  const float r0 = __shfl_xor(s0, 1, 64), r1 = __shfl_xor(s1, 1, 64);
+  const float r0 = lane_swap1(s0), r1 = lane_swap1(s1);
   const int c0 = colmap(n & ~1);
   const int ra = 4 * g + (odd ? 2 : 0);
   float a0, a1, b0, b1;  // (row ra: col c0, c0+1), (row ra+1: col c0, c0+1)
