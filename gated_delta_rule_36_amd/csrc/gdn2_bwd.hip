@@ -154,49 +154,57 @@ gdn2_bwd_chain_kernel(char* __restrict__ ws, const bf16* __restrict__ d_o,
         D[mt][i] = d_sN != nullptr ? d_sN[sbase + (long)row * DV] : 0.f;
     }
 
-  // staging (one chunk ahead, reverse order): factor pieces and this slice of dO
+  // staging, one chunk ahead (reverse order): the factor pieces go straight from global
+  // memory into the stage buffer (direct-to-LDS loads, no registers), this slice of dO
+  // through registers (transposed on the way in)
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 stf[Sh::PPF], std_[Sh::PPD];
+  u32x4 std_[Sh::PPD];
   auto unit_of = [&](int ci) { return ws + ((slot0 + ci) * H + h) * LB.bytes; };
-  auto stage_load = [&](int ci) {
+  auto stage_factors = [&](int ci, char* buf) {
     const char* unit = unit_of(ci);
 #pragma unroll
     for (int j = 0; j < Sh::PPF; ++j) {
       int p = tid + j * NT;
-      p = p < Sh::NPF ? p : Sh::NPF - 1;
+      p = p < Sh::NPF ? p : Sh::NPF - 1;  // the tail re-reads the last piece
       const long off = p < Sh::SZ_F / 16 ? LB.kr + p * 16 : LB.f.g + (p * 16 - Sh::SZ_F);
-      stf[j] = *reinterpret_cast<const u32x4*>(unit + off);
+      // lane l of the wave lands at buf + (64 wave + j NT + l) * 16
+      __builtin_amdgcn_global_load_lds(unit + off,
+                                       (__attribute__((address_space(3))) void*)(buf + (64 * wave + j * NT) * 16),
+                                       16, 0, 0);
     }
+  };
+  auto load_do = [&](int ci) {
     const int nvalid = min(C, len - ci * C);
 #pragma unroll
     for (int j = 0; j < Sh::PPD; ++j) {
       const int p = tid + j * NT, r = p / (NV / 8), cc = p % (NV / 8);
-      // this slice's dO columns are read by this workgroup alone: non-temporal (measured
-      // 0.790 -> 0.766 ms per backward call on the 1.3B-layer workload), while the factor
-      // pieces, which the head's other slice reads too, stay cached
+      // this slice's dO columns are read by this workgroup alone: non-temporal
       const T* src0 = d_o + (row0 + (long)ci * C) * vstride + (long)h * DV + col0;
       const u32x4 x = __builtin_bit_cast(
           u32x4, load16_nt(src0, (int)(((r < nvalid ? r : 0) * vstride + cc * 8) * 2)));
-      std_[j] = r < nvalid ? x : u32x4{0u, 0u, 0u, 0u};
+      std_[j] = x;  // rows past the end (row 0's values) are zeroed when stored
     }
   };
-  auto stage_store = [&](char* buf) {
-#pragma unroll
-    for (int j = 0; j < Sh::PPF; ++j) *reinterpret_cast<u32x4*>(buf + (tid + j * NT) * 16) = stf[j];
+  auto store_do = [&](char* buf, int ci) {
+    const int nvalid = min(C, len - ci * C);
     T* dot = reinterpret_cast<T*>(buf + Sh::OFF_DO);
 #pragma unroll
     for (int j = 0; j < Sh::PPD; ++j) {  // transpose: [column][token]
       const int p = tid + j * NT, r = p / (NV / 8), cc = p % (NV / 8);
-      const bf16x8 x = __builtin_bit_cast(bf16x8, std_[j]);
+      const bf16x8 x = __builtin_bit_cast(bf16x8, r < nvalid ? std_[j] : u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
       for (int e = 0; e < 8; ++e) dot[(cc * 8 + e) * Sh::LDO + r] = x[e];
     }
   };
+  // the direct loads of a stage are complete (s_waitcnt vmcnt(0)); before the barrier that
+  // publishes the stage
+  auto wait_stage = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
   if (nch > 0) {
-    stage_load(nch - 1);
-    stage_store(smem);
-    stage_load(nch > 1 ? nch - 2 : 0);
+    stage_factors(nch - 1, smem);
+    load_do(nch - 1);
+    store_do(smem, nch - 1);
+    wait_stage();
   }
   lds_barrier();
 
@@ -211,6 +219,10 @@ gdn2_bwd_chain_kernel(char* __restrict__ ws, const bf16* __restrict__ d_o,
       return *reinterpret_cast<const typename M::frag*>(B + off + blk * 1024 + lane * 16);
     };
     char* unit = unit_of(ci);
+    if (ci > 0) {  // the next chunk's operands, arriving while this one is computed
+      stage_factors(ci - 1, smem + ((k + 1) & 1) * Sh::STAGE);
+      load_do(ci - 1);
+    }
     // dSn of this chunk, for the local kernel
     if constexpr (!XFER) {
 #pragma unroll
@@ -270,9 +282,10 @@ gdn2_bwd_chain_kernel(char* __restrict__ ws, const bf16* __restrict__ d_o,
       for (int s = 0; s < 2; ++s) acc = M::mma(frag(Sh::OFF_WT, mt * 2 + s), ub[s], acc);
       D[mt] = acc;
     }
-    // next chunk (ci - 1) into the other buffer; then the loads for ci - 2
-    if (ci > 0) stage_store(smem + ((k + 1) & 1) * Sh::STAGE);
-    stage_load(ci > 1 ? ci - 2 : 0);
+    // the next chunk (ci - 1): its dO slice into the other buffer, whose factor pieces were
+    // issued at the start of this chunk
+    if (ci > 0) store_do(smem + ((k + 1) & 1) * Sh::STAGE, ci - 1);
+    wait_stage();
     lds_barrier();
   }
   if constexpr (XFER) {  // b into the value columns of the segment's [b | M] (rows d_k, d_v + d_k columns)
