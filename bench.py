@@ -133,6 +133,8 @@ def cpu_baseline(x, workers=None, gpu_out=None):
             errs = pool.map(_oracle_shard_errors, jobs)
             parity = {"max_rel_err_o": max(e[0] for e in errs) / max(e[1] for e in errs),
                       "max_rel_err_S": max(e[2] for e in errs) / max(e[3] for e in errs)}
+        pool.close()  # the workers exit on their own (no SIGTERM from the context's exit)
+        pool.join()
     done = token_heads / H  # tokens: every shard holds hb of the H heads of its tokens
     res = {"value": round(done / dt, 1), "unit": "tokens/s", "cores": used, "kind": "oracle",
             "tokens": int(round(done)), "seconds": round(dt, 3),
