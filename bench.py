@@ -2,7 +2,7 @@
 
 A step is one gdn2_chunk_fwd call over the 1.3B-layer workload (B=8, H=16, T=2048,
 d_k = d_v = 128, bf16 inputs, fp32 state, zero initial state), inputs resident in HBM;
-with the path chunk_fwd's "auto" picks (the fused kernel at this shape; where the two-phase
+with the path chunk_fwd's "auto" picks (the pipelined kernel at this shape; where the two-phase
 path is picked, its two launches are timed together as one call).
 Prints ONE JSON line. Also reports (as extra fields) the recurrent decode step on the
 decode workload (256 sequences x 16 heads, fp32 128x128 states) and a CPU baseline: the
@@ -251,6 +251,11 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # then untimed calls for at least 100 ms of sustained work, whatever W is: a few warm-up
+    # calls leave the clocks still ramping (5 of them timed the forward about 30% slower)
+    t_settle = time.perf_counter()
+    settle(step)
+    settle_s = time.perf_counter() - t_settle
     K = args.steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(K)]
@@ -280,6 +285,8 @@ def main():
     else:
         kernel = f"gdn2_fwd_kernel<{dk},0>"
         tkey = f"chunk_fwd_{cfg}"
+    path_name = ("two-phase" if use_split else
+                 "fused (value slice %d)" % args.value_slice if args.value_slice else "pipelined")
     workloads = {
         "layer1p3b": "GDN-2 chunk forward, 1.3B-layer shape: B=8 H=16 T=2048 d_k=d_v=128 "
                      "C=64, bf16 in/out, fp32 state, zero S0",
@@ -295,8 +302,9 @@ def main():
         "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), "
                 "log-alpha=-0.1*softplus(N(0,1)), b,w=sigmoid(N(0,1)))",
         "config": {"workload": workloads[args.workload], "global_batch": B, "seq_len": T,
-                   "sequences": N, "path": "split" if use_split else "fused",
+                   "sequences": N, "path": path_name,
                    "parallelism": "single GPU"},
+        "clock_settle_s": round(settle_s, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(tkey),
@@ -337,7 +345,7 @@ def main():
         sms = float(np.mean([a.elapsed_time(b2) for a, b2 in evs]))
         sbytes = B * T * H * ((3 * dk + dv + dv) * 2 + 2 * 2) + N * H * dk * dv * 4
         out["scalar_gates"] = {
-            "workload": "the same forward with scalar b and w ([B, T, H]), fused path",
+            "workload": "the same forward with scalar b and w ([B, T, H]), pipelined kernel",
             "ms_per_call": round(sms, 4), "tokens_per_s": round(B * T / (sms * 1e-3), 1),
             "algorithmic_bytes": sbytes,
             "hbm_frac": round(sbytes / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
