@@ -415,14 +415,17 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   const long kstride = (long)H * DK, vstride = (long)H * DV;
   // The workgroups are persistent (one per compute unit) and walk the units u = blockIdx.x,
-  // + gridDim.x, ... Every global read of a unit is issued before it is needed, in two
-  // groups: the workspace tiles dZ, U, dSn (for the matrix work P1, P2), issued during the
-  // previous unit (dSn before its elementwise step, dZ and U after its gradient stores, so
-  // that they do not queue behind them); then dO; g, k; S0; v, w; q, b, issued at the start
-  // of the unit,
-  // the later ones arriving while P1, P2 run. Every load is unconditional (a row
-  // past the unit's end reads row 0 and is zeroed where it is first used; past the last
-  // unit the current one is read again), which keeps the waits on the early groups exact.
+  // + gridDim.x, ... Every global read of a unit is issued before it is needed: the workspace
+  // tiles dZ, U, dSn (for the matrix work P1, P2) during the previous unit (dSn before its
+  // elementwise step, dZ and U after its gradient stores, so that they do not queue behind
+  // them); dO and S0 at the start of the unit; g, k once dO is in LDS; v, w after P1; q, b
+  // after P2. Every compute unit starts its units at about the same time, so what is issued
+  // at a unit's start competes for HBM with dO, which P1 waits for: issuing the rest at
+  // these later points (each a step ahead of its first use) took the backward from 736 to
+  // 700 us on the 1.3B-layer workload, against issuing every late load at the unit's start.
+  // Every load is unconditional (a row past the unit's end reads row 0 and is zeroed where
+  // it is first used; past the last unit the current one is read again), which keeps the
+  // waits on the early groups exact.
   constexpr int NDO = C * DV / 8 / NT;             // 16-byte pieces of dO per thread
   constexpr int NZU = Sh::NVT * 4 / Sh::NW;        // dZ and U tiles per wave
   static_assert(NDO * NT == C * DV / 8 && NZU * Sh::NW == Sh::NVT * 4, "load mapping");
@@ -482,28 +485,7 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     Vec8<T> rq[Sh::TPT], rk[Sh::TPT], rg[Sh::TPT], rb[Sh::TPT], rv[Sh::VTPT], rw[Sh::VTPT];
     bool kvalid[Sh::TPT];
   #pragma unroll
-    for (int j = 0; j < Sh::TPT; ++j) {
-      kvalid[j] = tg * Sh::TPT + j < cu.nvalid;
-      const long off = kb0 + (long)clamp_row(tg * Sh::TPT + j) * kstride + cg * 8;
-      rg[j].load(g + off);
-      rk[j].load(k + off);
-    }
-  #pragma unroll
     for (int ct = 0; ct < NVT; ++ct) s0t[ct] = tile_raw(unit, LB.h, ct * Sh::NCT + wave);
-  #pragma unroll
-    for (int j = 0; j < Sh::VTPT; ++j) {  // rows past the end give outputs that are not stored
-      const int r = clamp_row(vtg * Sh::VTPT + j);
-      rv[j].load(v + vb0 + (long)r * vstride + vcg * 8);
-      if constexpr (W_S) rw[j].load_one(wg + (cu.row + r) * H + cu.h);
-      else rw[j].load(wg + vb0 + (long)r * vstride + vcg * 8);
-    }
-  #pragma unroll
-    for (int j = 0; j < Sh::TPT; ++j) {
-      const int r = clamp_row(tg * Sh::TPT + j);
-      rq[j].load(q + kb0 + (long)r * kstride + cg * 8);
-      if constexpr (B_S) rb[j].load_one(bg + (cu.row + r) * H + cu.h);
-      else rb[j].load(bg + kb0 + (long)r * kstride + cg * 8);
-    }
 
     // ---- dO, dZ and U (tiles (ct, R)) row-major, dSn into LDS. A dO row past the end holds
     // row 0's values: it reaches only M1's row of that token (zeroed in P1) and dQbar's column
@@ -523,6 +505,13 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   #pragma unroll
     for (int ct = 0; ct < NVT; ++ct)
       store_tile_pairs(sA + (16 * wave) * LDV + 16 * ct, LDV, lane, tof(rds[ct]), ident);
+  #pragma unroll
+    for (int j = 0; j < Sh::TPT; ++j) {
+      kvalid[j] = tg * Sh::TPT + j < cu.nvalid;
+      const long off = kb0 + (long)clamp_row(tg * Sh::TPT + j) * kstride + cg * 8;
+      rg[j].load(g + off);
+      rk[j].load(k + off);
+    }
     if (tid == 0) *sFlag = 0;
     lds_barrier();
 
@@ -550,6 +539,13 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       *reinterpret_cast<uint2*>(Mt + (16 * I + m16) * LDT + 16 * R + 4 * g4) =
           make_uint2(pack_bf16(val[0], val[1]), pack_bf16(val[2], val[3]));
     }
+  #pragma unroll
+    for (int j = 0; j < Sh::VTPT; ++j) {  // rows past the end give outputs that are not stored
+      const int r = clamp_row(vtg * Sh::VTPT + j);
+      rv[j].load(v + vb0 + (long)r * vstride + vcg * 8);
+      if constexpr (W_S) rw[j].load_one(wg + (cu.row + r) * H + cu.h);
+      else rw[j].load(wg + vb0 + (long)r * vstride + vcg * 8);
+    }
     // ---- P2: dKtil^T = dSn U^T   (rows: this wave's channels; columns: tokens)
     f4 dKt[4];
   #pragma unroll
@@ -560,6 +556,13 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         acc = M::mma(M::load(sA, LDV, 16 * wave + m16, 32 * s + 8 * g4),
                      M::load(sU, LDV, 16 * Tt + m16, 32 * s + 8 * g4), acc);
       dKt[Tt] = acc;
+    }
+  #pragma unroll
+    for (int j = 0; j < Sh::TPT; ++j) {
+      const int r = clamp_row(tg * Sh::TPT + j);
+      rq[j].load(q + kb0 + (long)r * kstride + cg * 8);
+      if constexpr (B_S) rb[j].load_one(bg + (cu.row + r) * H + cu.h);
+      else rb[j].load(bg + kb0 + (long)r * kstride + cg * 8);
     }
     // ---- (a): per-thread totals of log2-decay (a row past the end decays by nothing) into
     // sTot, which shares the Khat^T region (written only after the scan's prefixes are read)
