@@ -148,7 +148,7 @@ gdn2_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   Vec8<T> rq[Sh::TPT], rk[Sh::TPT], rg[Sh::TPT], rb[Sh::TPT];
   Vec8<T> rv[Sh::VTPT], rw[Sh::VTPT];
-  auto load_raw = [&](const ChunkUnit& cu) {
+  auto load_key = [&](const ChunkUnit& cu) {
     const long kb = cu.row * kstride + (long)cu.h * DK + cg * 8;
 #pragma unroll
     for (int j = 0; j < Sh::TPT; ++j) {
@@ -166,6 +166,8 @@ gdn2_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         rq[j].zero(); rk[j].zero(); rg[j].zero(); rb[j].zero();
       }
     }
+  };
+  auto load_val = [&](const ChunkUnit& cu) {
     const long vb = cu.row * vstride + (long)cu.h * DV + vcg * 8;
 #pragma unroll
     for (int j = 0; j < Sh::VTPT; ++j) {
@@ -179,6 +181,10 @@ gdn2_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         rv[j].zero(); rw[j].zero();
       }
     }
+  };
+  auto load_raw = [&](const ChunkUnit& cu) {
+    load_key(cu);
+    load_val(cu);
   };
 
   // this thread's pieces of the previous unit's factors (see (g)) and their destination
@@ -312,11 +318,12 @@ gdn2_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
       for (int i = 0; i < 8; ++i) zv[i].store_sw(sZt + (vcg * 8 + i) * LDT, zsw, vtg * Sh::VTPT);
     }
-    // the previous unit's factors to the workspace, then the next unit's prefetch: the
-    // wait for these loads (next unit's (a)) then covers stores issued before them rather
-    // than after (the waits cannot tell late stores from the loads)
+    // the previous unit's factors to the workspace, then the next unit's key-side prefetch:
+    // the wait for these loads (next unit's (a)) then covers stores issued before them
+    // rather than after (the waits cannot tell late stores from the loads). The value side
+    // follows after (d), so the two bursts do not queue together behind the stores.
     flush();
-    load_raw(nxt);
+    load_key(nxt);
     lds_barrier();
     fresh();
 
@@ -359,6 +366,7 @@ gdn2_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       fresh();
     }
 
+    load_val(nxt);
     // ---- (f) [W | U~] = (I + A)^{-1} [E 2^G | Z] by block forward substitution:
     //   X_R = T_RR (RHS_R - sum_{J<R} A_RJ X_J)
     // Column tiles (key tiles, then value tiles) are dealt round-robin to the waves.
