@@ -41,6 +41,12 @@
 extern "C" {
 #endif
 
+/*
+ * Element type of q, k, v, the gates and o. Entry points take it as a plain int holding a
+ * gdn2_dtype value, so that any other value is well defined on both sides of the boundary
+ * and is rejected with GDN2_INVALID_ARGUMENT (an enum parameter may be assumed by the
+ * compiler to hold only its enumerators, which would let it drop that check).
+ */
 typedef enum { GDN2_BF16 = 0, GDN2_F32 = 1 } gdn2_dtype;
 
 enum {
