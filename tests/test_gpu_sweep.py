@@ -1,0 +1,117 @@
+"""Seeded sweep of the forward and backward over mixed small shapes, each call checked in full
+against the float64 oracle (normwise max relative error, 2e-2 for bf16 and 1e-4 for fp32).
+
+Each case draws its own combination of element type, head widths, gate layout (per-channel or
+scalar b and / or w), fixed-length or packed batch (empty sequences allowed), ragged lengths,
+head count, initial state, near-resets and forward path, so that combinations the targeted
+tests do not pair up still meet the oracle. The draw uses its own generator and holds none of
+the method's arithmetic.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gdn2_inputs import make_inputs, make_scalar_gate, round_to_bf16
+from oracle import gdn2_backward, gdn2_forward
+from tests.gpu_util import TOL, assert_close, dev_tensor, host64, say
+
+pytestmark = pytest.mark.gpu
+NAMES = ("q", "k", "v", "g", "b", "w")
+GRADS = ("dq", "dk", "dv", "dg", "db", "dw")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _draw_case(i, backward):
+    rng = np.random.default_rng([20261204, i, int(backward)])
+    dt = "bf16" if backward else str(rng.choice(["bf16", "bf16", "bf16", "fp32"]))
+    dk = int(rng.choice([64, 128]))
+    dv = int(rng.choice([64, 128]))
+    layout = str(rng.choice(["", "b", "w", "bw"]))
+    H = int(rng.integers(1, 4))
+    lengths = None
+    if rng.random() < 0.4:
+        n = int(rng.integers(1, 6))
+        lengths = rng.integers(0, 200, size=n)
+        lengths[rng.random(n) < 0.2] = 0  # empty sequences
+        if lengths.sum() == 0:
+            lengths[0] = int(rng.integers(1, 130))
+        B, T = 1, int(lengths.sum())
+    else:
+        B = int(rng.integers(1, 4))
+        T = int(rng.integers(1, 261))
+    s0 = bool(rng.random() < 0.5)
+    reset = float(rng.choice([0.0, 0.0, 0.1]))
+    if dt == "fp32":
+        path = str(rng.choice(["auto", "fused"]))
+    else:
+        path = "-" if backward else str(rng.choice(["auto", "fused", "split"]))
+    return dict(dt=dt, dk=dk, dv=dv, layout=layout, H=H, B=B, T=T, lengths=lengths, s0=s0,
+                reset=reset, path=path, seed=1000 + i)
+
+
+def _inputs(c):
+    x = make_inputs(c["B"], c["T"], c["H"], c["dk"], c["dv"], c["dt"], seed=c["seed"],
+                    reset_frac=c["reset"], lengths=c["lengths"],
+                    s0_std=0.05 if c["s0"] else None)
+    gpu, ref = dict(x), dict(x)
+    lead = (c["B"], c["T"], c["H"])
+    for name, d in (("b", c["dk"]), ("w", c["dv"])):
+        if name in c["layout"]:
+            s = make_scalar_gate(lead, c["dt"], seed=c["seed"] + (name == "w"))
+            gpu[name] = s
+            ref[name] = np.repeat(s[..., None], d, axis=-1)
+    return x, gpu, ref
+
+
+def _describe(c):
+    kind = "packed %s" % list(map(int, c["lengths"])) if c["lengths"] is not None else \
+        "B%d T%d" % (c["B"], c["T"])
+    return (f"{c['dt']} dk{c['dk']} dv{c['dv']} H{c['H']} {kind} gates[{c['layout'] or 'channel'}]"
+            f" s0={c['s0']} reset={c['reset']} path={c['path']}")
+
+
+@pytest.mark.parametrize("i", range(36))
+def test_forward_sweep(i):
+    import gated_delta_rule_36_amd as G
+    c = _draw_case(i, backward=False)
+    x, gx, rx = _inputs(c)
+    say("forward sweep", i, _describe(c))
+    t = {n: dev_tensor(gx[n], c["dt"]) for n in NAMES}
+    s0 = None if x["s0"] is None else torch.from_numpy(x["s0"]).cuda()
+    cu = None if x["cu_seqlens"] is None else torch.from_numpy(x["cu_seqlens"]).cuda()
+    o, sN = G.chunk_fwd(*(t[n] for n in NAMES), initial_state=s0, cu_seqlens=cu, path=c["path"])
+    torch.cuda.synchronize()
+    o_ref, s_ref = gdn2_forward(*(rx[n] for n in NAMES), s0=x["s0"], cu_seqlens=x["cu_seqlens"])
+    assert_close("o", host64(o), o_ref, TOL[c["dt"]])
+    assert_close("S_final", host64(sN), s_ref, TOL[c["dt"]])
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_backward_sweep(i):
+    import gated_delta_rule_36_amd as G
+    c = _draw_case(i, backward=True)
+    x, gx, rx = _inputs(c)
+    rng = np.random.default_rng([20261204, i, 7])
+    N = c["B"] if x["cu_seqlens"] is None else len(x["cu_seqlens"]) - 1
+    do = round_to_bf16(rng.normal(size=(c["B"], c["T"], c["H"], c["dv"])).astype(np.float32))
+    dsn = (0.1 * rng.normal(size=(N, c["H"], c["dk"], c["dv"]))).astype(np.float32)
+    say("backward sweep", i, _describe(c))
+    t = {n: dev_tensor(gx[n], "bf16") for n in NAMES}
+    s0 = None if x["s0"] is None else torch.from_numpy(x["s0"]).cuda()
+    cu = None if x["cu_seqlens"] is None else torch.from_numpy(x["cu_seqlens"]).cuda()
+    out = G.chunk_bwd(*(t[n] for n in NAMES), dev_tensor(do, "bf16"), initial_state=s0,
+                      d_final_state=torch.from_numpy(dsn).cuda(), cu_seqlens=cu)
+    torch.cuda.synchronize()
+    ref = list(gdn2_backward(*(rx[n] for n in NAMES), do, dS_final=dsn, s0=x["s0"],
+                             cu_seqlens=x["cu_seqlens"]))
+    # a scalar gate's gradient is the sum over the channels of the broadcast gate's
+    for name, idx in (("b", 4), ("w", 5)):
+        if name in c["layout"]:
+            ref[idx] = ref[idx].sum(axis=-1)
+    for name, a, r in zip(GRADS + ("ds0",), out, ref):
+        assert_close(name, host64(a), r, TOL["bf16"])
