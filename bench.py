@@ -146,23 +146,31 @@ def cpu_baseline(x, workers=None, gpu_out=None):
 
 
 def provenance():
-    """The git commit when the tree is a checkout (None otherwise) and a digest of the
-    library's sources and header, which identifies the build either way."""
-    import hashlib
+    """The git commit of the tree, and a digest of the library's sources and header, which
+    identifies the build either way. Where the tree is not a checkout (a copy without its git
+    metadata), the commit is the one the library was built from, taken only while that build
+    record's source digest still matches the sources."""
     import subprocess
+    from gated_delta_rule_36_amd.build import BUILD_INFO, source_digest
+    digest = source_digest()
     try:
-        sha = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True,
-                             text=True, timeout=10).stdout.strip() or None
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True,
+                           text=True, timeout=10)
+        sha = r.stdout.strip() if r.returncode == 0 else None
     except (OSError, subprocess.SubprocessError):
         sha = None
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "gated_delta_rule_36_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
-    with open(os.path.join(ROOT, "include", "gdn2.h"), "rb") as f:
-        h.update(f.read())
-    return {"git_sha": sha, "source_sha256": h.hexdigest()[:16]}
+    out = {"git_sha": sha or None, "source_sha256": digest}
+    if not sha:
+        try:
+            with open(BUILD_INFO) as f:
+                info = json.load(f)
+        except (OSError, ValueError):
+            info = None
+        if info and info.get("source_sha256") == digest and info.get("git_sha"):
+            out["git_sha"] = info["git_sha"]
+            out["git_sha_from"] = "build record"
+            out["library_sources_committed"] = info.get("library_sources_committed")
+    return out
 
 
 def main():
