@@ -29,3 +29,30 @@ def test_cpu_baseline_counts_each_token_once():
     assert parity is None
     assert r["tokens"] == B * T
     assert r["cores"] == 2
+
+
+def test_provenance_without_git_metadata(monkeypatch, tmp_path):
+    """Without git (the tree copied without .git), the commit comes from the build record, and
+    only while the record's source digest matches the sources."""
+    import json
+    import subprocess as sp
+    sys.path.insert(0, ROOT)
+    import bench
+    from gated_delta_rule_36_amd import build as b
+
+    def no_git(cmd, *a, **k):
+        if cmd and cmd[0] == "git":
+            raise OSError("no git here")
+        return sp.run(cmd, *a, **k)
+
+    monkeypatch.setattr(sp, "run", no_git)
+    rec = tmp_path / "build_info.json"
+    monkeypatch.setattr(b, "BUILD_INFO", str(rec))
+    assert bench.provenance()["git_sha"] is None  # no record
+    rec.write_text(json.dumps({"git_sha": "abc123", "library_sources_committed": True,
+                               "source_sha256": b.source_digest()}))
+    p = bench.provenance()
+    assert p["git_sha"] == "abc123" and p["git_sha_from"] == "build record"
+    rec.write_text(json.dumps({"git_sha": "abc123", "library_sources_committed": True,
+                               "source_sha256": "0" * 16}))
+    assert bench.provenance()["git_sha"] is None  # sources changed since that build
