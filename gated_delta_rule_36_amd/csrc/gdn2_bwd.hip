@@ -370,6 +370,14 @@ struct LocalShape {
   static constexpr int OFF_FLAG = OFF_X + DK * 4;
   static constexpr int LDS_BYTES = OFF_FLAG + 16;
   static constexpr int OFF_TOT = OFF_KH;                   // cumsum scratch in the Khat^T region
+  // staging of the elementwise step's row-major outputs (dq, dk, db) in the Khat^T and M
+  // regions, dead by then; dg's in the region of the elementwise inputs. Rows padded by 8
+  // elements (conflict-free 8-byte writes of 16 rows x 32 bytes)
+  static constexpr int LDSG = DK + 8;
+  static constexpr int OFF_SG = OFF_KH;
+  static_assert(OFF_SG + 3 * C * LDSG * 2 <= OFF_FAC, "staging of dq, dk, db");
+  static_assert(C * LDSG * 2 <= SZ_BIG, "staging of dg");
+  static_assert(2 * C * LDSG * 2 + (DK / 16) * 64 * 4 <= OFF_FAC - OFF_SG, "scalar-db partials");
   static_assert(TG * DK * 4 <= DK * LDT * 2, "cumsum scratch");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(TPT * TG == C && VTPT * VTG == C, "token mapping");
@@ -761,12 +769,22 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const f4 gam = *reinterpret_cast<const f4*>(sFac + Fac::GAM * DK + c0);
     const f4 gl = *reinterpret_cast<const f4*>(sFac + Fac::GL * DK + c0);
     const f4 xc = *reinterpret_cast<const f4*>(sX + c0);
-    // dq, dk and db of a token tile are stored as soon as they are formed; dg waits for the
-    // suffix sums over the chunk
-    auto put4 = [&](bf16* p, long off, f4 x) {
-      *reinterpret_cast<uint2*>(p + off) = make_uint2(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]));
+    // dq, dk and db of a token tile go to row-major staging tiles in LDS as soon as they are
+    // formed (the Khat and M regions are dead here), dg once the suffix sums over the chunk are
+    // done (into the region of the elementwise inputs, after they are read); the rows are then
+    // stored whole, 16 bytes per lane. A wave's own results are 32 bytes of each row: stored
+    // directly, each store instruction addressed 16 row pieces, and the vector memory path
+    // carried four times the requests.
+    constexpr int LDS_ = Sh::LDSG;
+    T* sSq = reinterpret_cast<T*>(smem + Sh::OFF_SG);
+    T* sSk = sSq + C * LDS_;
+    T* sSb = sSk + C * LDS_;
+    T* sSg = reinterpret_cast<T*>(smem);
+    auto put4 = [&](T* p, int t, f4 x) {
+      *reinterpret_cast<uint2*>(p + t * LDS_ + c0) =
+          make_uint2(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]));
     };
-    float* sPart = reinterpret_cast<float*>(smem + Sh::OFF_M1);  // scalar db: [NW][64] partials
+    float* sPart = reinterpret_cast<float*>(sSb);  // scalar db: [NW][64] partials
     f4 dgv[4];
     f4 totB = {0.f, 0.f, 0.f, 0.f};
   #pragma unroll
@@ -792,15 +810,13 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       }
       dgv[Tt] = A - Bv;
       totB += Bv;
-      if (t < cu.nvalid) {
-        const long off = kb0 + (long)t * kstride + c0;
-        put4(dq, off, outq);
-        put4(dk, off, outk);
-        if constexpr (!B_S) put4(db, off, outb);
-      }
-      if constexpr (B_S) {
+      put4(sSq, t, outq);
+      put4(sSk, t, outk);
+      if constexpr (!B_S) {
+        put4(sSb, t, outb);
+      } else {
         // a scalar b's gradient sums the token's d_k channels: 4 per lane, the 4 lane groups
-        // of a wave, then the NW waves through LDS (the M buffers are dead here)
+        // of a wave, then the NW waves through LDS
         float x = outb[0] + outb[1] + outb[2] + outb[3];
         x += __shfl_xor(x, 16, 64);
         x += __shfl_xor(x, 32, 64);
@@ -815,6 +831,7 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   #pragma unroll
     for (int i = 0; i < 4; ++i) totB[i] = row_first(row_suffix(totB[i]));
     f4 carry = totB + gam * xc;
+    lds_barrier();  // every wave is done with G, q, k and b: their region takes dg
   #pragma unroll
     for (int Tt = 3; Tt >= 0; --Tt) {
       f4 x = dgv[Tt];
@@ -824,12 +841,25 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         x[i] = row_suffix(x[i]);
         tile_tot[i] = row_first(x[i]);
       }
-      const int t = 16 * Tt + m16;
-      if (t < cu.nvalid) put4(dg, kb0 + (long)t * kstride + c0, x + carry);
+      put4(sSg, 16 * Tt + m16, x + carry);
       carry += tile_tot;
     }
+    lds_barrier();  // the staged rows are complete
+    // whole rows, 16-byte pieces (DK / 8 per row), rows past the unit's end not stored
+    auto store_rows = [&](T* dst, const T* src) {
+  #pragma unroll
+      for (int j = 0; j < C * DK / 8 / NT; ++j) {
+        const int pc = tid + j * NT, r = pc / (DK / 8), c8 = pc % (DK / 8);
+        if (r < cu.nvalid)
+          *reinterpret_cast<uint4*>(dst + kb0 + (long)r * kstride + c8 * 8) =
+              *reinterpret_cast<const uint4*>(src + r * LDS_ + c8 * 8);
+      }
+    };
+    store_rows(dq, sSq);
+    store_rows(dk, sSk);
+    if constexpr (!B_S) store_rows(db, sSb);
+    store_rows(dg, sSg);
     if constexpr (B_S) {
-      lds_barrier();
       if (tid < C) {
         float x = 0.f;
   #pragma unroll
