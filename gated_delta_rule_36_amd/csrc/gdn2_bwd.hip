@@ -659,9 +659,16 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   #pragma unroll
       for (int i = 0; i < 8; ++i) { o1[i] = fz[i] * fw[i]; o2[i] = fz[i] * fv[i]; }
       if (r < cu.nvalid) {
+        // whole rows (VCG lanes of 16 bytes), written once: non-temporal
         const long off = vb0 + (long)r * vstride + vcg * 8;
-        store8(dv + off, o1);
-        if constexpr (!W_S) store8(dw + off, o2);
+        bf16x8 pv, pw;
+  #pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          pv[i] = static_cast<bf16>(o1[i]);
+          pw[i] = static_cast<bf16>(o2[i]);
+        }
+        __builtin_nontemporal_store(pv, reinterpret_cast<bf16x8*>(dv + off));
+        if constexpr (!W_S) __builtin_nontemporal_store(pw, reinterpret_cast<bf16x8*>(dw + off));
       }
       if constexpr (W_S) {  // sum over the token's d_v channels (VCG adjacent lanes)
         float sw = 0.f;
