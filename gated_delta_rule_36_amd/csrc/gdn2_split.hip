@@ -22,6 +22,7 @@
 #include "gdn2_launch.h"
 
 namespace gdn2 {
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ phase 1: factors
 template <int DK, int DV>
@@ -703,11 +704,13 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
     for (int s = 0; s < KSK; ++s) sb[s] = M::from_acc(S, s);
     char* const bunit = const_cast<char*>(ws) + ((slot0 + ci) * H + h) * UNIT;
     const int ctg = slice * Sh::NWV + wave;  // this wave's column tile within d_v
-    if constexpr (STORE) {  // the state entering this chunk
+    if constexpr (STORE) {  // the state entering this chunk (non-temporal, as U below: read
+                            // back by other workgroups of a later launch)
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt)
-        *reinterpret_cast<uint2*>(bunit + LB.h + ((ctg * NMT + mt) * 64 + lane) * 8) =
-            make_uint2(pack_bf16(S[mt][0], S[mt][1]), pack_bf16(S[mt][2], S[mt][3]));
+        __builtin_nontemporal_store(
+            (u32x2){pack_bf16(S[mt][0], S[mt][1]), pack_bf16(S[mt][2], S[mt][3])},
+            reinterpret_cast<u32x2*>(bunit + LB.h + ((ctg * NMT + mt) * 64 + lane) * 8));
     }
     // U = U~ - W S
     f4 U[4];
@@ -754,8 +757,9 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
     if constexpr (STORE) {
 #pragma unroll
       for (int R = 0; R < 4; ++R)
-        *reinterpret_cast<uint2*>(bunit + LB.ub + ((ctg * 4 + R) * 64 + lane) * 8) =
-            make_uint2(pack_bf16(U[R][0], U[R][1]), pack_bf16(U[R][2], U[R][3]));
+        __builtin_nontemporal_store(
+            (u32x2){pack_bf16(U[R][0], U[R][1]), pack_bf16(U[R][2], U[R][3])},
+            reinterpret_cast<u32x2*>(bunit + LB.ub + ((ctg * 4 + R) * 64 + lane) * 8));
     }
     typename M::frag ub[2];
 #pragma unroll
