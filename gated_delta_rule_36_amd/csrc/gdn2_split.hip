@@ -668,7 +668,8 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
 #pragma unroll
     for (int j = 0; j < PPC; ++j) *reinterpret_cast<u32x4*>(buf + piece_off(tid + j * NT)) = stg[j];
   };
-  // output rows of the previous chunk: staging buffer -> HBM (16-byte pieces)
+  // output rows of the previous chunk: staging buffer -> HBM (16-byte pieces, written once:
+  // non-temporal)
   constexpr int OPR = NV / 8;  // pieces per row
   static_assert((C * OPR) % NT == 0, "output pieces per thread");
   auto out_store = [&](const T* so, long c0, int nrows) {
@@ -676,9 +677,11 @@ gdn2_state_kernel(const char* __restrict__ ws, const float* s0, bf16* __restrict
     for (int j = 0; j < C * OPR / NT; ++j) {
       const int p = tid + j * NT;
       const int r = p / OPR, cc = p % OPR;
-      if (r < nrows)
-        *reinterpret_cast<uint4*>(ob + (c0 + r) * vstride + cc * 8) =
-            *reinterpret_cast<const uint4*>(so + r * OP + cc * 8);
+      if (r < nrows) {
+        typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(*reinterpret_cast<const u4*>(so + r * OP + cc * 8),
+                                    reinterpret_cast<u4*>(ob + (c0 + r) * vstride + cc * 8));
+      }
     }
   };
 
