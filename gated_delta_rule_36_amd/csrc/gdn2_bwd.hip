@@ -425,8 +425,8 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // The workgroups are persistent (one per compute unit) and walk the units u = blockIdx.x,
   // + gridDim.x, ... Every global read of a unit is issued before it is needed: the workspace
   // tiles dZ, U, dSn (for the matrix work P1, P2) during the previous unit (dSn before its
-  // elementwise step, dZ and U after its gradient stores, so that they do not queue behind
-  // them); dO and S0 at the start of the unit; g, k once dO is in LDS; v, w after P1; q, b
+  // elementwise step, dZ and U after it, ahead of its gradient row stores); dO and S0 at the
+  // start of the unit; g, k once dO is in LDS; v, w after P1; q, b
   // after P2. Every compute unit starts its units at about the same time, so what is issued
   // at a unit's start competes for HBM with dO, which P1 waits for: issuing the rest at
   // these later points (each a step ahead of its first use) took the backward from 736 to
@@ -769,7 +769,7 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     lds_barrier();
 
     // the next unit's dSn tiles (this unit's are consumed); with both gates scalar the
-    // registers are short here, and they are issued with dZ and U after the stores
+    // registers are short here, and they are issued with dZ and U after the elementwise step
     if constexpr (early_dsn) issue_first_a(u_pre);
     // ---- elementwise: lane = token 16*Tt + m16, channels c0 .. c0 + 3 of this wave
     const int c0 = 16 * wave + 4 * g4;
@@ -780,8 +780,7 @@ gdn2_bwd_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // formed (the Khat and M regions are dead here), dg once the suffix sums over the chunk are
     // done (into the region of the elementwise inputs, after they are read); the rows are then
     // stored whole, 16 bytes per lane. A wave's own results are 32 bytes of each row: stored
-    // directly, each store instruction addressed 16 row pieces, and the vector memory path
-    // carried four times the requests.
+    // directly, each store instruction addressed 16 separate 32-byte row pieces.
     constexpr int LDS_ = Sh::LDSG;
     T* sSq = reinterpret_cast<T*>(smem + Sh::OFF_SG);
     T* sSk = sSq + C * LDS_;
