@@ -1,5 +1,6 @@
-"""Seeded sweep of the forward and backward over mixed small shapes, each call checked in full
-against the float64 oracle (normwise max relative error, 2e-2 for bf16 and 1e-4 for fp32).
+"""Seeded sweep of the forward, the backward and the decode step over mixed small shapes,
+each call checked in full against the float64 oracle (normwise max relative error, 2e-2 for
+bf16 and 1e-4 for fp32).
 
 Each case draws its own combination of element type, head widths, gate layout (per-channel or
 scalar b and / or w), fixed-length or packed batch (empty sequences allowed), ragged lengths,
@@ -115,3 +116,41 @@ def test_backward_sweep(i):
             ref[idx] = ref[idx].sum(axis=-1)
     for name, a, r in zip(GRADS + ("ds0",), out, ref):
         assert_close(name, host64(a), r, TOL["bf16"])
+
+
+def _draw_decode_case(i):
+    rng = np.random.default_rng([20261204, i, 2])
+    return dict(dt=str(rng.choice(["bf16", "bf16", "fp32"])), dk=int(rng.choice([64, 128])),
+                dv=int(rng.choice([64, 128])), layout=str(rng.choice(["", "b", "w", "bw"])),
+                N=int(rng.integers(1, 40)), H=int(rng.integers(1, 5)),
+                steps=int(rng.integers(1, 9)), seed=3000 + i)
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_decode_sweep(i):
+    """Consecutive single-token decode steps on mixed shapes, element types and gate layouts
+    (the fp32 state updated in place), every output and the final states against the
+    oracle's token loop."""
+    import gated_delta_rule_36_amd as G
+    from gdn2_inputs import make_decode_inputs
+    from oracle import gdn2_decode_steps
+    c = _draw_decode_case(i)
+    x = make_decode_inputs(c["N"], c["H"], c["dk"], c["dv"], c["steps"], c["dt"], seed=c["seed"],
+                           s0_std=0.05)
+    gx, rx = dict(x), dict(x)
+    lead = (c["steps"], c["N"], c["H"])
+    for name, d in (("b", c["dk"]), ("w", c["dv"])):
+        if name in c["layout"]:
+            s = make_scalar_gate(lead, c["dt"], seed=c["seed"] + (name == "w"))
+            gx[name] = s
+            rx[name] = np.repeat(s[..., None], d, axis=-1)
+    say("decode sweep", i, c)
+    t = {n: dev_tensor(gx[n], c["dt"]) for n in NAMES}
+    state = torch.from_numpy(x["s0"]).cuda()
+    # each step's inputs as fresh tensors: a step slice of a scalar gate [steps, N, H] is not
+    # 16-byte aligned when N * H is odd, and the entry point requires aligned pointers
+    outs = [G.decode_step(*(t[n][s].clone() for n in NAMES), state) for s in range(c["steps"])]
+    torch.cuda.synchronize()
+    o_ref, s_ref = gdn2_decode_steps(x["s0"], *(rx[n] for n in NAMES))
+    assert_close("o", host64(torch.stack(outs)), o_ref, TOL[c["dt"]])
+    assert_close("S", host64(state), s_ref, TOL[c["dt"]])
