@@ -1,6 +1,6 @@
-"""Seeded sweep of the forward, the backward and the decode step over mixed small shapes,
-each call checked in full against the float64 oracle (normwise max relative error, 2e-2 for
-bf16 and 1e-4 for fp32).
+"""Seeded sweep of the forward, the backward, the decode step and multi-token decode over
+mixed small shapes, each call checked in full against the float64 oracle (normwise max
+relative error, 2e-2 for bf16 and 1e-4 for fp32).
 
 Each case draws its own combination of element type, head widths, gate layout (per-channel or
 scalar b and / or w), fixed-length or packed batch (empty sequences allowed), ragged lengths,
@@ -154,3 +154,42 @@ def test_decode_sweep(i):
     o_ref, s_ref = gdn2_decode_steps(x["s0"], *(rx[n] for n in NAMES))
     assert_close("o", host64(torch.stack(outs)), o_ref, TOL[c["dt"]])
     assert_close("S", host64(state), s_ref, TOL[c["dt"]])
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_decode_tokens_sweep(i):
+    """L tokens per sequence against a pool of states on mixed shapes: pool slots in random
+    order, some sequences without a slot, random committed prefixes; outputs, per-token states
+    and the pool against the oracle, untouched slots unchanged."""
+    import gated_delta_rule_36_amd as G
+    from gdn2_inputs import make_decode_inputs
+    from oracle import gdn2_decode_tokens
+    rng = np.random.default_rng([20261204, i, 3])
+    dt = str(rng.choice(["bf16", "bf16", "fp32"]))
+    dk, dv = int(rng.choice([64, 128])), int(rng.choice([64, 128]))
+    N, L, H = int(rng.integers(1, 21)), int(rng.integers(1, 10)), int(rng.integers(1, 5))
+    P = N + int(rng.integers(0, 6))
+    x = make_decode_inputs(N, H, dk, dv, L, dt, seed=4000 + i, s0_std=0.02)
+    toks = {n: np.ascontiguousarray(np.swapaxes(x[n], 0, 1)) for n in NAMES}  # [N, L, H, d]
+    pool = (0.02 * rng.normal(size=(P, H, dk, dv))).astype(np.float32)
+    idx = rng.permutation(P)[:N].astype(np.int32)
+    idx[rng.random(N) < 0.2] = -1  # sequences without a state
+    commit = rng.integers(0, L + 1, size=N).astype(np.int32)
+    say("decode_tokens sweep", i, dt, dk, dv, f"N{N} L{L} H{H} P{P}", "slots", idx.tolist(),
+        "commit", commit.tolist())
+    pool_t = torch.from_numpy(pool).cuda()
+    t = {n: dev_tensor(toks[n], dt) for n in NAMES}
+    o, steps = G.decode_tokens(*(t[n] for n in NAMES), pool_t,
+                               state_indices=torch.from_numpy(idx).cuda(),
+                               commit_len=torch.from_numpy(commit).cuda(), return_step_states=True)
+    torch.cuda.synchronize()
+    o_ref, st_ref, pool_ref = gdn2_decode_tokens(pool, *(toks[n] for n in NAMES), indices=idx,
+                                                 commit=commit)
+    valid = idx >= 0
+    if valid.any():
+        vt = torch.from_numpy(valid).cuda()  # skipped sequences' outputs are left unwritten
+        assert_close("o", host64(o[vt]), o_ref[valid], TOL[dt])
+        assert_close("step states", host64(steps[vt]), st_ref[valid], TOL[dt])
+    assert_close("pool", host64(pool_t), pool_ref, TOL[dt])
+    untouched = [s for s in range(P) if s not in idx[valid]]
+    assert np.array_equal(pool_t.cpu().numpy()[untouched], pool[untouched])
